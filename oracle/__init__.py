@@ -1,0 +1,11 @@
+"""CPU oracle of the DiT-MoE sparse MoE layer -- test infrastructure only.
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+never by the product path.
+"""
+from .moe_oracle import *  # noqa: F401,F403
+from .moe_oracle import (balance_stats, decision_scores, expert_mlp, forward,
+                         gate_logits, gelu_tanh, layer_output, permute,
+                         race_select, route, routed_output, selection_indicator,
+                         shared_output, slot_weights, softmax, topk_select,
+                         NEAR_TIE, GELU_A, GELU_C)

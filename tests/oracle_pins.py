@@ -1,0 +1,372 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check raises AssertionError when the oracle disagrees with a closed
+form, an invariant, a library routine, a brute force on tiny inputs or a
+hand-worked fixture under tests/golden/.  The checks look the oracle's
+functions up at call time, so the mutation tests can plant a mistake in one
+oracle function and confirm that some check fails.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+from scipy.special import softmax as scipy_softmax
+
+import synth
+from oracle import moe_oracle as om
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _tiny_inputs(seed=0, B=2, T=8, D=16, H=24, E=4, K=2, n_s=1, bias=False,
+                 route="topk", scale=0.3):
+    cfg = synth.LayerConfig("pin", B=B, T=T, D=D, H=H, E=E, K=K, n_s=n_s,
+                            dtype="f32", route=route, logit_bias=bias, seed=seed)
+    r = _rng(seed)
+    x = r.standard_normal((cfg.N, D))
+    wg = r.standard_normal((E, D)) * scale
+    b = r.standard_normal(E) if bias else None
+    w1 = r.standard_normal((E, H, D)) * scale
+    w2 = r.standard_normal((E, D, H)) * scale
+    w1s = r.standard_normal((n_s, H, D)) * scale
+    w2s = r.standard_normal((n_s, D, H)) * scale
+    return synth.LayerInputs(cfg, x, wg, b, w1, w2, w1s, w2s)
+
+
+# ------------------------------------------------------------------ gate --
+
+def check_gate_logits():
+    r = _rng(1)
+    N, D, E = 7, 11, 5
+    x = r.standard_normal((N, D))
+    # one-hot gate rows pick distinct input features: logit_i = x[:, c_i]
+    cols = np.array([3, 0, 9, 4, 7])
+    wg = np.zeros((E, D))
+    wg[np.arange(E), cols] = 1.0
+    assert np.array_equal(om.gate_logits(x, wg), x[:, cols])
+    # a zero gate leaves the bias
+    bias = r.standard_normal(E)
+    assert np.array_equal(om.gate_logits(x, np.zeros((E, D)), bias),
+                          np.broadcast_to(bias, (N, E)))
+    # scaled one-hot plus bias
+    l = om.gate_logits(x, 2.0 * wg, bias)
+    assert np.allclose(l, 2.0 * x[:, cols] + bias, rtol=0, atol=1e-14)
+
+
+def check_softmax():
+    r = _rng(2)
+    l = r.standard_normal((50, 8)) * 3
+    P = om.softmax(l)
+    assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(P, scipy_softmax(l, axis=1), rtol=1e-13, atol=0)
+    assert np.allclose(om.softmax(l + 123.0), P, rtol=1e-12, atol=0)
+    # equal logits: exactly 1/E for E a power of two; E = 1 gives 1
+    for E in (1, 2, 8, 16):
+        assert np.all(om.softmax(np.full((3, E), 0.7)) == 1.0 / E)
+    # large logits do not overflow
+    big = om.softmax(np.array([[1000.0, 999.0, -1000.0]]))
+    assert np.isfinite(big).all() and abs(big[0, 0] / big[0, 1] - math.e) < 1e-12
+
+
+# --------------------------------------------------------------- routing --
+
+def _scores_with_ties(N, E, seed):
+    r = _rng(seed)
+    # quantised probabilities: many exact ties
+    q = r.integers(1, 6, size=(N, E)).astype(np.float64)
+    return q / q.sum(axis=1, keepdims=True)
+
+
+def check_topk():
+    for seed, (N, E, K) in enumerate([(40, 8, 2), (30, 4, 1), (25, 5, 5),
+                                      (20, 16, 3)]):
+        P = _scores_with_ties(N, E, seed + 10)
+        s = P.astype(np.float32)
+        idx, margin = om.topk_select(P, K)
+        assert idx.shape == (N, K)
+        for t in range(N):
+            # brute force: the K-permutation that is largest under the total
+            # order (score desc, index asc) is the sorted prefix
+            best = sorted(range(E), key=lambda i: (-float(s[t, i]), i))[:K]
+            assert list(idx[t]) == best, (t, idx[t], best)
+            sel = set(best)
+            for i in sel:
+                for j in set(range(E)) - sel:
+                    assert s[t, i] > s[t, j] or (s[t, i] == s[t, j] and i < j)
+            if K < E:
+                kth = s[t, best[-1]]
+                nxt = max(float(s[t, j]) for j in range(E) if j not in sel)
+                assert margin[t] == float(kth) - nxt
+    # zero gate: every token picks experts 0..K-1 with zero margin
+    P = om.softmax(np.zeros((6, 8)))
+    idx, margin = om.topk_select(P, 2)
+    assert (idx == np.array([0, 1])).all() and (margin == 0).all()
+
+
+def check_race():
+    for seed, (N, E, K) in enumerate([(12, 4, 2), (9, 8, 1), (10, 3, 3)]):
+        P = _scores_with_ties(N, E, seed + 20)
+        s = P.astype(np.float32)
+        idx, tau, near = om.race_select(P, K)
+        assert idx.shape == (N, E)
+        # brute force: python sort of all (score, flat index) keys
+        keys = sorted(range(N * E), key=lambda f: (-float(s.flat[f]), f))
+        chosen = set(keys[:K * N])
+        got = set()
+        for t in range(N):
+            row = list(idx[t])
+            sel = [i for i in row if i >= 0]
+            assert row == sel + [-1] * (E - len(sel))      # padding at end
+            assert sel == sorted(sel)                      # ascending index
+            got.update(t * E + i for i in sel)
+        assert got == chosen
+        assert len(got) == K * N
+        assert tau == float(s.flat[keys[K * N - 1]])
+    # identical tokens (distinct scores within a token): race == top-K
+    r = _rng(5)
+    row = r.permutation(np.arange(1, 9, dtype=np.float64))
+    P = np.tile(row / row.sum(), (10, 1))
+    idx_r, _, _ = om.race_select(P, 3)
+    idx_k, _ = om.topk_select(P, 3)
+    assert (np.sort(idx_k, axis=1) == idx_r[:, :3]).all()
+    assert (idx_r[:, 3:] == -1).all()
+
+
+def check_permute():
+    r = _rng(3)
+    N, E, Kmax = 37, 6, 3
+    idx = np.full((N, Kmax), -1, dtype=np.int32)
+    for t in range(N):
+        m = r.integers(0, Kmax + 1)
+        idx[t, :m] = r.choice(E, size=m, replace=False)
+    counts, offsets, row_token, slot_row = om.permute(idx, E)
+    # brute force enumeration: expert-major, then token, then slot
+    rows = [(t, k) for e in range(E) for t in range(N) for k in range(Kmax)
+            if idx[t, k] == e]
+    assert list(row_token) == [t for t, _ in rows]
+    for rr, (t, k) in enumerate(rows):
+        assert slot_row[t, k] == rr
+    assert (slot_row[idx < 0] == -1).all()
+    assert list(counts) == [int((idx == e).sum()) for e in range(E)]
+    assert offsets[0] == 0 and list(np.diff(offsets)) == list(counts)
+    assert sorted(slot_row[idx >= 0].tolist()) == list(range(len(rows)))
+
+
+# --------------------------------------------------------------- experts --
+
+def check_gelu():
+    u = np.linspace(-12, 12, 4801)
+    g = om.gelu_tanh(u)
+    ref = F.gelu(torch.from_numpy(u), approximate="tanh").numpy()
+    assert np.allclose(g, ref, rtol=1e-14, atol=1e-15)
+    assert om.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert np.allclose(g - om.gelu_tanh(-u), u, rtol=0, atol=1e-13)
+    assert om.gelu_tanh(np.array([8.0]))[0] == 8.0
+    # the tanh form stays within 6e-4 of the exact erf GELU, and differs
+    exact = 0.5 * u * (1.0 + np.vectorize(math.erf)(u / math.sqrt(2.0)))
+    gap = np.abs(g - exact).max()
+    assert 1e-5 < gap < 6e-4, gap
+
+
+def check_expert_mlp():
+    r = _rng(4)
+    x = r.standard_normal((9, 12))
+    w1 = r.standard_normal((20, 12)) * 0.4
+    w2 = r.standard_normal((12, 20)) * 0.4
+    b1 = r.standard_normal(20)
+    b2 = r.standard_normal(12)
+    tx = torch.from_numpy
+    ref = F.linear(F.gelu(F.linear(tx(x), tx(w1), tx(b1)), approximate="tanh"),
+                   tx(w2), tx(b2)).numpy()
+    assert np.allclose(om.expert_mlp(x, w1, w2, b1, b2), ref, rtol=1e-12,
+                       atol=1e-13)
+
+
+def _dense_mask_reference(inp, idx):
+    """MoE(x) = sum_{i=1..E} g(x)_i e_i(x), evaluated densely with torch on
+    every expert and every token; g is the softmax masked to the selection."""
+    tx = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x = tx(inp.x)
+    l = x @ tx(inp.w_gate).T
+    if inp.bias is not None:
+        l = l + tx(inp.bias)
+    P = torch.softmax(l, dim=1)
+    E = inp.cfg.E
+    mask = torch.zeros_like(P)
+    for t in range(idx.shape[0]):
+        for i in idx[t]:
+            if i >= 0:
+                mask[t, int(i)] = 1.0
+    g = P * mask
+    y = torch.zeros_like(x)
+    for i in range(E):
+        e_i = F.linear(F.gelu(F.linear(x, tx(inp.w1[i])), approximate="tanh"),
+                       tx(inp.w2[i]))
+        y = y + g[:, i:i + 1] * e_i
+    for s in range(inp.cfg.n_s):
+        y = y + F.linear(F.gelu(F.linear(x, tx(inp.w1s[s])), approximate="tanh"),
+                         tx(inp.w2s[s]))
+    return y.numpy(), P.numpy()
+
+
+def check_dense_mask():
+    cases = [dict(E=4, K=2, n_s=1), dict(E=6, K=6, n_s=0),
+             dict(E=5, K=1, n_s=2, bias=True), dict(E=1, K=1, n_s=0),
+             dict(E=8, K=3, n_s=2, route="race")]
+    for seed, kw in enumerate(cases):
+        inp = _tiny_inputs(seed=100 + seed, **kw)
+        out = om.forward(inp)
+        ref, Pref = _dense_mask_reference(inp, out["idx"])
+        assert np.allclose(out["P"], Pref, rtol=1e-13, atol=1e-15)
+        assert np.allclose(out["y"], ref, rtol=1e-11, atol=1e-12), kw
+
+
+def check_dense_mlp_special_case():
+    """E = 1, K = 1, n_s = 0: P = 1 so the layer is the plain MLP."""
+    inp = _tiny_inputs(seed=7, E=1, K=1, n_s=0, bias=True)
+    out = om.forward(inp)
+    assert np.all(out["P"] == 1.0)
+    tx = torch.from_numpy
+    ref = F.linear(F.gelu(F.linear(tx(inp.x), tx(inp.w1[0])), approximate="tanh"),
+                   tx(inp.w2[0])).numpy()
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def check_full_mixture():
+    """K = E keeps every expert: the layer is the full softmax mixture."""
+    inp = _tiny_inputs(seed=8, E=5, K=5, n_s=0)
+    out = om.forward(inp)
+    tx = torch.from_numpy
+    x = tx(inp.x)
+    P = torch.softmax(x @ tx(inp.w_gate).T, dim=1)
+    y = sum(P[:, i:i + 1] * F.linear(F.gelu(F.linear(x, tx(inp.w1[i])),
+                                            approximate="tanh"), tx(inp.w2[i]))
+            for i in range(5))
+    assert np.allclose(out["y"], y.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def one_hot_channel_inputs(cfg, seed=0):
+    """Inputs whose outputs are known exactly (needs D >= E + n_s + 1).
+
+    x[t][D-1] = 1; expert i has W1[0][D-1] = 8 and W2[i][0] = 1/8; shared
+    expert s has W1[0][D-1] = 8 and W2[E+s][0] = 1/8.  Then u_0 = 8,
+    gelu(8) = 8 exactly in fp32 and fp64, every other hidden unit is 0, so
+    y[t][i] = P(t,i) when i is selected (else 0) and y[t][E+s] = 1.
+    All values are exact in bf16.
+    """
+    E, D, H, n_s = cfg.E, cfg.D, cfg.H, cfg.n_s
+    assert D >= E + n_s + 1
+    inp = synth.make_inputs(cfg, seed=seed)
+    x = inp.x.copy()
+    x[:, D - 1] = 1.0
+    w1 = np.zeros_like(inp.w1)
+    w2 = np.zeros_like(inp.w2)
+    w1[:, 0, D - 1] = 8.0
+    for i in range(E):
+        w2[i, i, 0] = 0.125
+    w1s = np.zeros_like(inp.w1s)
+    w2s = np.zeros_like(inp.w2s)
+    w1s[:, 0, D - 1] = 8.0
+    for s in range(n_s):
+        w2s[s, E + s, 0] = 0.125
+    return synth.LayerInputs(cfg, x, inp.w_gate, inp.bias, w1, w2, w1s, w2s)
+
+
+def check_one_hot_channels():
+    for route in ("topk", "race"):
+        cfg = synth.small_config(B=2, T=16, D=32, H=16, E=8, K=2, n_s=2,
+                                 dtype="f32", route=route, seed=9)
+        inp = one_hot_channel_inputs(cfg)
+        out = om.forward(inp)
+        y, P, idx = out["y"], out["P"], out["idx"]
+        E = cfg.E
+        for t in range(cfg.N):
+            sel = set(int(i) for i in idx[t] if i >= 0)
+            for i in range(E):
+                want = P[t, i] if i in sel else 0.0
+                assert y[t, i] == want, (route, t, i)
+            assert (y[t, E:E + cfg.n_s] == 1.0).all()
+            assert (y[t, E + cfg.n_s:] == 0.0).all()
+        if route == "topk":
+            assert all(len(set(idx[t])) == cfg.K for t in range(cfg.N))
+
+
+# --------------------------------------------------------------- balance --
+
+def check_balance_uniform_probs():
+    """Uniform P (zero gate): L = alpha for any routing."""
+    for K, E in [(2, 8), (1, 4), (3, 3)]:
+        B, T = 3, 16
+        P = om.softmax(np.zeros((B * T, E)))
+        idx, _ = om.topk_select(P, K)
+        c, ps, L = om.balance_stats(P, idx, B, T, K, 0.01)
+        assert abs(L - 0.01) <= 1e-17, L
+        r = _rng(6)
+        ridx = np.stack([r.choice(E, size=K, replace=False) for _ in range(B * T)])
+        assert abs(om.balance_stats(P, ridx, B, T, K, 0.01)[2] - 0.01) <= 1e-17
+        assert abs(om.balance_stats(P, ridx, B, T, K, 0.01, "global")[2]
+                   - 0.01) <= 1e-17
+
+
+def uniform_counts_inputs(B=2, T=32, E=8, K=2, D=16, dtype="f32"):
+    """Gate whose top-K counts are exactly K*T/E per expert and image."""
+    assert T % E == 0
+    cfg = synth.small_config(B=B, T=T, D=D, H=16, E=E, K=K, n_s=0, dtype=dtype,
+                             seed=11)
+    inp = synth.make_inputs(cfg)
+    wg = np.zeros((E, D), dtype=np.float32)
+    wg[np.arange(E), np.arange(E)] = 1.0
+    x = np.zeros((B * T, D), dtype=np.float32)
+    t = np.arange(B * T)
+    x[t, t % E] = 4.0
+    x[t, (t + 1) % E] = 3.5
+    return synth.LayerInputs(cfg, x, wg, None, inp.w1, inp.w2, inp.w1s, inp.w2s)
+
+
+def check_balance_uniform_counts():
+    """Equal counts K*T/E for every expert: L = alpha for any P."""
+    inp = uniform_counts_inputs()
+    cfg = inp.cfg
+    out = om.forward(inp)
+    assert (out["bal_counts"] == cfg.K * cfg.T // cfg.E).all()
+    assert abs(out["loss"] - cfg.alpha) < 1e-15
+
+
+def check_balance_invariants():
+    inp = _tiny_inputs(seed=12, B=3, T=10, E=5, K=2, bias=True)
+    out = om.forward(inp)
+    c = out["bal_counts"]
+    # sum_i f_i = n per image with f_i = n/(K T) c_i
+    f = inp.cfg.E / (inp.cfg.K * inp.cfg.T) * c
+    assert np.allclose(f.sum(axis=1), inp.cfg.E, rtol=0, atol=1e-13)
+    assert (c.sum(axis=1) == inp.cfg.K * inp.cfg.T).all()
+    assert np.allclose(out["bal_psum"].sum(axis=1), inp.cfg.T, atol=1e-12)
+
+
+def check_balance_golden():
+    with open(os.path.join(GOLDEN, "balance_tiny.json")) as fh:
+        g = json.load(fh)
+    P = np.array(g["P"], dtype=np.float64)
+    idx, _ = om.topk_select(P, g["K"])
+    assert idx.tolist() == g["idx"]
+    c, ps, L = om.balance_stats(P, idx, g["B"], g["T"], g["K"], g["alpha"])
+    assert c.tolist() == g["counts"]
+    assert abs(L - g["loss"]) < 1e-15, (L, g["loss"])
+
+
+ALL_CHECKS = [check_gate_logits, check_softmax, check_topk, check_race,
+              check_permute, check_gelu, check_expert_mlp, check_dense_mask,
+              check_dense_mlp_special_case, check_full_mixture,
+              check_one_hot_channels, check_balance_uniform_probs,
+              check_balance_uniform_counts, check_balance_invariants,
+              check_balance_golden]
