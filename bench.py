@@ -1,0 +1,207 @@
+"""Benchmark of the DiT-MoE sparse MoE layer on one MI355X.
+
+One step = one forward pass of the whole layer (gate, softmax and top-K,
+permutation, routed expert MLPs, shared expert MLPs, weighted combine,
+balance statistic) over one batch of seeded synthetic input, by default the
+XL/2-8E2A layer at 512x512 (B=32 images x T=1024 tokens, D=1152, E=8, K=2,
+n_s=2, H=4608, bf16).  Inputs and weights are resident in device memory
+before the timed region starts.
+
+Prints one JSON line.  Usage:
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="xl_8e2a_512")
+    ap.add_argument("--x-perm", action="store_true",
+                    help="materialise x_perm instead of gathering rows in GEMM1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def kernel_work(cfg, gather: bool):
+    """Algorithmic work of each call of one step: (kind, amount).
+    FLOPs count 2 per multiply-add; bytes are the unavoidable HBM traffic."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    N, D, H, E, K, A, n_s = cfg.N, cfg.D, cfg.H, cfg.E, cfg.K, cfg.A, cfg.n_s
+    Kmax = cfg.Kmax
+    w = {
+        "gate": ("bytes", N * D * eb + E * D * 4 + N * E * 4 + N * Kmax * 8),
+        "permute": ("bytes", N * Kmax * 4 * 2 + A * 4 +
+                    (0 if gather else N * D * eb + A * D * eb)),
+        "routed_up": ("flops", 2 * A * D * H),
+        "routed_down": ("flops", 2 * A * D * H),
+        "shared_up": ("flops", 2 * N * D * H * n_s),
+        "shared_down": ("flops", 2 * N * D * H * n_s),
+        "combine": ("bytes", A * D * eb + (N * D * eb if n_s else 0) +
+                    N * D * eb + N * Kmax * 8),
+        "balance": ("bytes", N * E * 4 + N * Kmax * 4),
+    }
+    return w
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """The CPU oracle on whole images of the same workload until about
+    ``target_s`` seconds of CPU work: tokens/s."""
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    done_tokens, elapsed, images = 0, 0.0, 0
+    while elapsed < target_s and images < cfg.B:
+        b = images
+        sub_cfg = cfg.with_(B=1)
+        sub = synth.LayerInputs(sub_cfg, inp.x[b * cfg.T:(b + 1) * cfg.T],
+                                inp.w_gate, inp.bias, inp.w1, inp.w2, inp.w1s,
+                                inp.w2s)
+        t0 = time.perf_counter()
+        oracle.forward(sub)
+        elapsed += time.perf_counter() - t0
+        done_tokens += cfg.T
+        images += 1
+    return {"value": done_tokens / elapsed, "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{images} image(s) x {cfg.T} tokens of {cfg.name} "
+                      f"(whole layer in float64 numpy, {elapsed:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                          "--gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import synth
+    from sparse_moe_diffusion_amd import _lib, layer
+
+    _lib.load()
+    cfg = synth.CONFIGS[args.config]
+    gather = not args.x_perm
+    inp = synth.make_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = "cuda"
+    x = layer._to_device(inp.x, dt, dev)
+    wts = layer.LayerWeights.from_inputs(inp, dev)
+    buf = layer.LayerBuffers(cfg, dev, gather=gather)
+    steps = [s for s in layer.STEPS if not (cfg.n_s == 0 and s[0].startswith("shared"))]
+
+    def one_step(evs=None):
+        for i, (_, fn) in enumerate(steps):
+            if evs is not None:
+                evs[i].record()
+            fn(cfg, x, wts, buf)
+        if evs is not None:
+            evs[len(steps)].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    per_call = {}
+    for i, (name, _) in enumerate(steps):
+        per_call[name] = sum(evs[k][i].elapsed_time(evs[k][i + 1])
+                             for k in range(K)) / K
+    work = kernel_work(cfg, gather)
+    kernels = {}
+    for name, ms in per_call.items():
+        kind, amount = work[name]
+        if kind == "flops":
+            ach = amount / (ms * 1e-3) / 1e12
+            kernels[name] = {"ms": round(ms, 4), "tflops": round(ach, 1),
+                             "frac_mfma_peak": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            kernels[name] = {"ms": round(ms, 4), "gbs": round(ach, 1),
+                             "frac_hbm_peak": round(ach / HBM_PEAK_GBS, 4)}
+
+    # dominant kernel: the grouped GEMM stage with the larger total time;
+    # its two launches per step (routed, shared) carry equal FLOPs.
+    up = [n for n in ("routed_up", "shared_up") if n in per_call]
+    down = [n for n in ("routed_down", "shared_down") if n in per_call]
+    t_up = sum(per_call[n] for n in up)
+    t_down = sum(per_call[n] for n in down)
+    dom = up if t_up >= t_down else down
+    dom_name = ("gemm_bf16_kernel<gelu> (expert FFN stage 1)" if dom is up
+                else "gemm_bf16_kernel<store> (expert FFN stage 2)")
+    dom_flops = sum(work[n][1] for n in dom) / len(dom)
+    dom_ms = sum(per_call[n] for n in dom) / len(dom)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+
+    N = cfg.N
+    tokens_per_s = N / (ms_per_step * 1e-3)
+    layer_tflops = cfg.flops_per_token() * N / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = t_up + t_down
+    gemm_tflops = cfg.gemm_flops() / (gemm_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "MoE-layer tokens/sec and TFLOP/s (% bf16 MFMA peak), "
+                  "XL/2-8E2A @512",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
+        "config": {"workload": f"{cfg.name}: DiT-MoE sparse MoE layer, "
+                               f"B={cfg.B} images x T={cfg.T} tokens, D={cfg.D}, "
+                               f"E={cfg.E}, K={cfg.K}, n_s={cfg.n_s}, H={cfg.H}, "
+                               f"{cfg.route} routing",
+                   "tokens": N, "gather_rows_in_gemm": gather},
+        "layer_tflops": round(layer_tflops, 1),
+        "layer_frac_mfma_peak": round(layer_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "expert_gemm_tflops": round(gemm_tflops, 1),
+        "expert_gemm_frac_mfma_peak": round(gemm_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": dom_name, "bound": "mfma",
+                     "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "flops_per_launch": dom_flops,
+                     "avg_launch_ms": round(dom_ms, 4),
+                     "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

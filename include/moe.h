@@ -1,0 +1,247 @@
+/*
+ * moe.h -- C ABI of the DiT-MoE sparse mixture-of-experts feed-forward layer
+ * on one MI355X (gfx950).
+ *
+ * The layer, per image-patch token x (a row of D features):
+ *   y = sum over the token's selected routed experts i of P(t,i) * e_i(x)
+ *     + sum over the n_s shared experts s of e_s(x),
+ *   e(x) = W2 gelu_tanh(W1 x),
+ * with P the softmax of the gate scores over the E routed experts, plus the
+ * expert-level balance statistic of the routing.
+ *
+ * Sources, by page title and section:
+ *   "DiT-MoE" project hub page, section 1 (MoE gate routing): the gate weight
+ *     is [n_routed_experts][gating_dim], softmax scoring, top-k selection and
+ *     an auxiliary balance loss.
+ *   "Scaling Diffusion Transformers to 16 Billion Parameters", Methods: eq.
+ *     MoE(x) = sum_i g(x)_i e_i(x) (MoE recap); eq. MLP(x) = W2 gelu(W1 x),
+ *     shared expert routing and the expert-level balance loss eq. L_balance
+ *     (MoE-DiT).
+ *   "Scalable Diffusion Models with Transformers (DiT)", model architecture:
+ *     the GELU is the tanh approximation.
+ *   "Expert Race: A Flexible Routing Strategy for Scaling Diffusion
+ *     Transformer with Mixture of Experts", abstract: tokens and experts
+ *     compete together for the top candidates.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     allocated and owned by the caller.  The library never allocates,
+ *     frees or synchronises; every call only validates its arguments on the
+ *     host and enqueues kernels on `stream` (asynchronous).
+ *   - All layouts are row-major and dense.  Expert weights follow the
+ *     y = x W^T convention: W1 is [G][H][D], W2 is [G][D][H].
+ *   - A pointer to an empty tensor (a size of 0) may be NULL.
+ *   - A call that fails validation returns a non-zero status and launches
+ *     nothing; moe_last_error() then describes the failure (thread-local).
+ *     MOE_ERR_HIP reports a launch error from the HIP runtime.  Device data
+ *     are not validated: NaN/Inf inputs are outside the contract, and every
+ *     kernel stays in bounds on any input values, except that row indices
+ *     passed in (moe_grouped_ffn's row_index, moe_combine's slot_row) must
+ *     name rows of the matrix they index, or be -1 where documented.
+ *   - The library keeps no state between calls and is thread-safe.
+ *   - Supported ranges: 1 <= E <= 64, 1 <= K <= E, D and H multiples of 8,
+ *     N * Kmax < 2^31, every row count < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, K > E ...  */
+  MOE_ERR_UNSUPPORTED = 2,         /* legal but outside the supported range   */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the queried size  */
+  MOE_ERR_HIP = 4                  /* the HIP runtime reported an error       */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_EXPERT_RACE = 1 } moe_route;
+
+typedef enum { MOE_BAL_PER_SEQUENCE = 0, MOE_BAL_GLOBAL = 1 } moe_balance_mode;
+
+/* Which GEMM stages of moe_grouped_ffn to run (bit mask). */
+typedef enum {
+  MOE_FFN_UP = 1,    /* h = gelu_tanh(W1 a + b1)  */
+  MOE_FFN_DOWN = 2,  /* y = W2 h + b2             */
+  MOE_FFN_BOTH = 3
+} moe_ffn_stages;
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(moe_status status);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_gate_topk needs (0 for top-K routing). */
+size_t moe_gate_workspace_size(int64_t N, int32_t E, int32_t K, moe_route route);
+
+/*
+ * Gate, softmax and expert selection ("DiT-MoE" hub page, section 1;
+ * "Expert Race" abstract for MOE_ROUTE_EXPERT_RACE).
+ *
+ *   logit[t][i] = sum_d x[t][d] * w_gate[i][d] + logit_bias[i]   (fp32)
+ *   probs[t][i] = softmax over the E routed experts of logit[t][.]  (fp32)
+ *
+ * MOE_ROUTE_TOPK (Kmax = K): each token keeps the K experts first in the
+ *   order (probability descending, expert index ascending); slot k of token
+ *   t holds the k-th of them: topk_idx[t][k], topk_w[t][k] = probs[t][idx].
+ * MOE_ROUTE_EXPERT_RACE (Kmax = E): of all N*E probabilities the K*N first
+ *   in the order (probability descending, flat index t*E+i ascending) are
+ *   kept; each token lists its kept experts in ascending index order in
+ *   topk_idx[t][0..], with topk_w the probabilities, and pads the rest of
+ *   its E slots with idx = -1, w = 0.  A token may keep 0..E experts.
+ *
+ *   x          [N][D], x_dtype (MOE_F32 or MOE_BF16)
+ *   w_gate     [E][D] fp32;   logit_bias [E] fp32 or NULL (no bias)
+ *   probs      [N][E] fp32 out
+ *   topk_idx   [N][Kmax] int32 out;  topk_w [N][Kmax] fp32 out
+ *   workspace  device scratch of at least moe_gate_workspace_size() bytes
+ *              (may be NULL when that size is 0)
+ * Errors: INVALID_ARGUMENT for null pointers, N < 0, D < 1, K outside
+ *   [1, E]; UNSUPPORTED for E > 64, D % 8 != 0, N*Kmax >= 2^31 or an unknown
+ *   dtype; WORKSPACE_TOO_SMALL.
+ */
+moe_status moe_gate_topk(const void* x, moe_dtype x_dtype,
+                         const float* w_gate, const float* logit_bias,
+                         int64_t N, int32_t D, int32_t E, int32_t K,
+                         moe_route route, float* probs, int32_t* topk_idx,
+                         float* topk_w, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Bytes of device workspace moe_permute needs. */
+size_t moe_permute_workspace_size(int64_t N, int32_t E, int32_t Kmax);
+
+/*
+ * Group the selected (token, slot) pairs by expert, so that only the
+ * selected experts are evaluated ("Scaling Diffusion Transformers to 16
+ * Billion Parameters", MoE recap: a sparse g needs no unused expert).
+ *
+ * A = K*N routed rows.  Rows of expert e are its selections in ascending
+ * (token, slot) order and occupy [expert_offsets[e], expert_offsets[e+1]).
+ *
+ *   topk_idx        [N][Kmax] int32 in: expert per slot, -1 = empty slot;
+ *                   a token names an expert at most once and exactly A slots
+ *                   in total are non-empty
+ *   expert_counts   [E] int32 out
+ *   expert_offsets  [E+1] int64 out (exclusive scan, offsets[E] = A)
+ *   row_token       [A] int32 out: token of each routed row
+ *   slot_row        [N][Kmax] int32 out: routed row of each slot, -1 if empty
+ *   x_perm          [A][D] dtype out, or NULL: row r = x[row_token[r]]
+ *                   (with NULL only the index tensors are written and the
+ *                   expert FFN gathers rows through row_token instead)
+ * Errors: as moe_gate_topk; Kmax must be K or E.  Slot contents outside
+ *   [-1, E) are not an error: such slots are treated as empty.
+ */
+moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
+                       int64_t N, int32_t D, int32_t E, int32_t Kmax, int32_t K,
+                       int32_t* expert_counts, int64_t* expert_offsets,
+                       int32_t* row_token, int32_t* slot_row, void* x_perm,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * The experts' MLPs over row groups ("Scaling Diffusion Transformers to 16
+ * Billion Parameters", MoE-DiT eq. MLP; "Scalable Diffusion Models with
+ * Transformers (DiT)": tanh GELU):
+ *
+ *   for each group g and each row r in [group_offsets[g], group_offsets[g+1]):
+ *     h[r]      = gelu_tanh(W1[g] a_r + b1[g])         (h_ws, dtype)
+ *     y_rows[r] = W2[g] h[r] + b2[g]                    (y_dtype)
+ *   with a_r = x_rows[row_index[r]] if row_index != NULL, else x_rows[r];
+ *   gelu_tanh(u) = 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))).
+ *
+ * Routed experts: G = E, group_offsets = expert_offsets from moe_permute and
+ * either x_perm or (x, row_token).  Shared experts: G = 1, offsets {0, N},
+ * x itself, and the n_s shared experts stacked into one MLP of hidden width
+ * n_s*H (W1 rows concatenated, W2 columns concatenated) -- their outputs
+ * sum with weight 1, which is exactly that wider MLP.
+ *
+ *   x_rows         [*][D] dtype;  row_index [total_rows] int32 or NULL
+ *                  (row_index entries must be rows of x_rows, and x_rows
+ *                  must span less than 4 GiB when row_index is used)
+ *   group_offsets  [G+1] int64 DEVICE array, non-decreasing, from 0 to
+ *                  total_rows (total_rows is also passed by value)
+ *   w1 [G][H][D], w2 [G][D][H] dtype;  b1 [G][H], b2 [G][D] fp32 or NULL
+ *   h_ws           [total_rows][H] dtype scratch (caller-owned)
+ *   y_rows         [total_rows][D] y_dtype out (MOE_F32, or MOE_BF16 when
+ *                  dtype is MOE_BF16)
+ *   stages         MOE_FFN_BOTH, or one stage alone (MOE_FFN_UP writes h_ws;
+ *                  MOE_FFN_DOWN reads it): the two stages are two kernels,
+ *                  and running them as two calls gives identical results.
+ *                  With MOE_FFN_DOWN alone x_rows, row_index and w1 are not
+ *                  read; with MOE_FFN_UP alone w2 and y_rows are not.
+ * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation; h and bf16
+ *   outputs are rounded to nearest even.  fp32 inputs compute in fp32.
+ * Errors: INVALID_ARGUMENT for null pointers, negative sizes or stages
+ *   outside 1..3; UNSUPPORTED for G > 128, D or H not multiples of 8, an unsupported dtype
+ *   pair or total_rows >= 2^31.
+ */
+moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
+                           moe_dtype dtype, int64_t total_rows,
+                           const int64_t* group_offsets, int32_t G, int32_t D,
+                           int32_t H, const void* w1, const float* b1,
+                           const void* w2, const float* b2, void* h_ws,
+                           void* y_rows, moe_dtype y_dtype,
+                           moe_ffn_stages stages, hipStream_t stream);
+
+/*
+ * Weighted combine ("Scaling Diffusion Transformers to 16 Billion
+ * Parameters": eq. MoE(x) with g(x)_i the gate probability; shared experts
+ * added with weight 1):
+ *
+ *   y[t] = sum over k < Kmax with slot_row[t][k] >= 0 of
+ *            topk_w[t][k] * y_rows[slot_row[t][k]]     (in slot order)
+ *        + y_shared[t]                                 (if not NULL)
+ * accumulated in fp32 and rounded once to out_dtype.
+ *
+ *   y_rows [A][D] y_dtype;  slot_row, topk_w [N][Kmax] (slot_row entries
+ *   are rows of y_rows or -1);
+ *   y_shared [N][D] sh_dtype or NULL;  y [N][D] out_dtype out
+ * Errors: INVALID_ARGUMENT for null pointers, N < 0 or Kmax < 1;
+ *   UNSUPPORTED for D % 8 != 0, Kmax > 64, N*D/8 >= 2^31 or unknown dtypes.
+ */
+moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
+                       const int32_t* slot_row, const float* topk_w, int64_t N,
+                       int32_t D, int32_t Kmax, const void* y_shared,
+                       moe_dtype sh_dtype, void* y, moe_dtype out_dtype,
+                       hipStream_t stream);
+
+/*
+ * Expert-level balance statistic ("Scaling Diffusion Transformers to 16
+ * Billion Parameters", MoE-DiT, eq. L_balance):
+ *
+ *   L = alpha * sum_i (n/(K T) sum_t I(t,i)) * (1/T sum_t P(t,i))
+ *
+ * n = E routed experts, T = tokens per image, I(t,i) = 1 when token t
+ * selected expert i, P = probs.  Per image b (tokens [bT, (b+1)T)):
+ *   counts[b][i]    = sum_t I(t,i)          (int32 out, [B][E])
+ *   prob_sums[b][i] = sum_t P(t,i)          (fp32 out, [B][E])
+ * MOE_BAL_PER_SEQUENCE: loss = mean over b of L_b.
+ * MOE_BAL_GLOBAL: loss = L over one pool of B*T tokens.
+ * Sums use a fixed reduction order: repeated calls give identical bits.
+ *
+ *   probs [B*T][E] fp32;  topk_idx [B*T][Kmax] int32 (-1 = empty);
+ *   loss [1] fp32 device out
+ * Errors: INVALID_ARGUMENT for null pointers, B < 0, T < 1, K outside
+ *   [1, E]; UNSUPPORTED for E > 64.
+ */
+moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
+                             int32_t B, int32_t T, int32_t E, int32_t Kmax,
+                             int32_t K, float alpha, moe_balance_mode mode,
+                             int32_t* counts, float* prob_sums, float* loss,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

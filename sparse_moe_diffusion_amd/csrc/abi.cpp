@@ -1,0 +1,252 @@
+// C ABI of the DiT-MoE layer library: argument validation and launch.
+// The contract of every entry point is documented in include/moe.h.
+#include "moe.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status from_hip(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool valid_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
+
+constexpr int64_t kI32Limit = int64_t(1) << 31;
+constexpr int kMaxE = 64;
+constexpr int kMaxGroups = 128;
+
+#define CHECK_PTR(p)                                                       \
+  do {                                                                     \
+    if ((p) == nullptr)                                                    \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is null", fn, #p);     \
+  } while (0)
+
+// A pointer to an empty tensor may be null.
+#define CHECK_PTR_IF(cond, p)                                              \
+  do {                                                                     \
+    if ((cond) && (p) == nullptr)                                          \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is null", fn, #p);     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_gate_workspace_size(int64_t N, int32_t E, int32_t K,
+                               moe_route route) {
+  (void)N; (void)E; (void)K;
+  return route == MOE_ROUTE_EXPERT_RACE ? moe::race_workspace_bytes() : 0;
+}
+
+moe_status moe_gate_topk(const void* x, moe_dtype x_dtype,
+                         const float* w_gate, const float* logit_bias,
+                         int64_t N, int32_t D, int32_t E, int32_t K,
+                         moe_route route, float* probs, int32_t* topk_idx,
+                         float* topk_w, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const char* fn = "moe_gate_topk";
+  if (N < 0 || D < 1 || E < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, E >= 1", fn);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: K=%d outside [1, E=%d]", fn, K, E);
+  if (route != MOE_ROUTE_TOPK && route != MOE_ROUTE_EXPERT_RACE)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: unknown route %d", fn, (int)route);
+  CHECK_PTR(w_gate);
+  CHECK_PTR_IF(N > 0, x); CHECK_PTR_IF(N > 0, probs);
+  CHECK_PTR_IF(N > 0, topk_idx); CHECK_PTR_IF(N > 0, topk_w);
+  if (!valid_dtype(x_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)x_dtype);
+  if (E > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d above %d", fn, E, kMaxE);
+  if (D % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
+  const int64_t Kmax = route == MOE_ROUTE_TOPK ? K : E;
+  if (N * Kmax >= kI32Limit || N * E >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
+  const size_t need = moe_gate_workspace_size(N, E, K, route);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, need);
+  CHECK_PTR_IF(need > 0, workspace);
+  hipError_t err = moe::launch_gate(x, x_dtype == MOE_BF16, w_gate, logit_bias,
+                                    N, D, E, K, route == MOE_ROUTE_TOPK, probs,
+                                    topk_idx, topk_w, stream);
+  if (err != hipSuccess) return from_hip(err, fn);
+  if (route == MOE_ROUTE_EXPERT_RACE)
+    err = moe::launch_race(probs, N, E, K, topk_idx, topk_w, workspace, stream);
+  return from_hip(err, fn);
+}
+
+size_t moe_permute_workspace_size(int64_t N, int32_t E, int32_t Kmax) {
+  (void)Kmax;
+  if (N < 0 || E < 1) return 0;
+  return moe::permute_workspace_bytes(N, E);
+}
+
+moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
+                       int64_t N, int32_t D, int32_t E, int32_t Kmax, int32_t K,
+                       int32_t* expert_counts, int64_t* expert_offsets,
+                       int32_t* row_token, int32_t* slot_row, void* x_perm,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const char* fn = "moe_permute";
+  if (N < 0 || D < 1 || E < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, E >= 1", fn);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: K=%d outside [1, E=%d]", fn, K, E);
+  if (Kmax != K && Kmax != E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: Kmax=%d must be K or E", fn, Kmax);
+  CHECK_PTR(expert_counts); CHECK_PTR(expert_offsets);
+  CHECK_PTR_IF(N > 0, topk_idx); CHECK_PTR_IF(N > 0, slot_row);
+  CHECK_PTR_IF(N > 0, row_token);
+  CHECK_PTR_IF(N > 0 && x_perm != nullptr, x);
+  if (!valid_dtype(dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dtype);
+  if (E > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d above %d", fn, E, kMaxE);
+  if (D % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
+  if (N * Kmax >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
+  const size_t need = moe_permute_workspace_size(N, E, Kmax);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, need);
+  CHECK_PTR(workspace);
+  const int64_t A = static_cast<int64_t>(K) * N;
+  return from_hip(moe::launch_permute(x, dtype == MOE_BF16, topk_idx, N, D, E,
+                                      Kmax, A, expert_counts, expert_offsets,
+                                      row_token, slot_row, x_perm, workspace,
+                                      stream),
+                  fn);
+}
+
+moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
+                           moe_dtype dtype, int64_t total_rows,
+                           const int64_t* group_offsets, int32_t G, int32_t D,
+                           int32_t H, const void* w1, const float* b1,
+                           const void* w2, const float* b2, void* h_ws,
+                           void* y_rows, moe_dtype y_dtype,
+                           moe_ffn_stages stages, hipStream_t stream) {
+  const char* fn = "moe_grouped_ffn";
+  if (total_rows < 0 || G < 1 || D < 1 || H < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need total_rows >= 0, G >= 1, D >= 1, H >= 1", fn);
+  if (stages < MOE_FFN_UP || stages > MOE_FFN_BOTH)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: stages=%d outside 1..3", fn,
+                (int)stages);
+  const bool up = stages & MOE_FFN_UP, down = stages & MOE_FFN_DOWN;
+  const bool rows = total_rows > 0;
+  CHECK_PTR_IF(up, w1); CHECK_PTR_IF(down, w2);
+  CHECK_PTR_IF(rows && up, x_rows); CHECK_PTR_IF(rows, group_offsets);
+  CHECK_PTR_IF(rows, h_ws); CHECK_PTR_IF(rows && down, y_rows);
+  if (!valid_dtype(dtype) || !valid_dtype(y_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (dtype == MOE_F32 && y_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 inputs need fp32 outputs", fn);
+  if (G > kMaxGroups)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d above %d", fn, G, kMaxGroups);
+  if (D % 8 != 0 || H % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
+                fn, D, H);
+  if (total_rows >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows must stay below 2^31", fn);
+  moe::FfnArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
+                 w1,     b1,        w2,         b2,            h_ws, y_rows,
+                 dtype == MOE_BF16,  y_dtype == MOE_F32};
+  return from_hip(moe::launch_ffn(a, up, down, stream), fn);
+}
+
+moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
+                       const int32_t* slot_row, const float* topk_w, int64_t N,
+                       int32_t D, int32_t Kmax, const void* y_shared,
+                       moe_dtype sh_dtype, void* y, moe_dtype out_dtype,
+                       hipStream_t stream) {
+  const char* fn = "moe_combine";
+  if (N < 0 || D < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, Kmax >= 1",
+                fn);
+  CHECK_PTR_IF(N > 0, y_rows); CHECK_PTR_IF(N > 0, slot_row);
+  CHECK_PTR_IF(N > 0, topk_w); CHECK_PTR_IF(N > 0, y);
+  if (!valid_dtype(y_dtype) || !valid_dtype(out_dtype) ||
+      (y_shared != nullptr && !valid_dtype(sh_dtype)))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (D % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
+  if (Kmax > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: Kmax=%d above %d", fn, Kmax, kMaxE);
+  if (N * (D / 8) >= kI32Limit || N * Kmax >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*D/8 must stay below 2^31", fn);
+  return from_hip(moe::launch_combine(y_rows, y_dtype == MOE_BF16, slot_row,
+                                      topk_w, N, D, Kmax, y_shared,
+                                      sh_dtype == MOE_BF16, y,
+                                      out_dtype == MOE_BF16, stream),
+                  fn);
+}
+
+moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
+                             int32_t B, int32_t T, int32_t E, int32_t Kmax,
+                             int32_t K, float alpha, moe_balance_mode mode,
+                             int32_t* counts, float* prob_sums, float* loss,
+                             hipStream_t stream) {
+  const char* fn = "moe_balance_stats";
+  if (B < 0 || T < 1 || E < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need B >= 0, T >= 1, E >= 1, Kmax >= 1", fn);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: K=%d outside [1, E=%d]", fn, K, E);
+  if (mode != MOE_BAL_PER_SEQUENCE && mode != MOE_BAL_GLOBAL)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: unknown mode %d", fn, (int)mode);
+  CHECK_PTR(loss);
+  CHECK_PTR_IF(B > 0, probs); CHECK_PTR_IF(B > 0, topk_idx);
+  CHECK_PTR_IF(B > 0, counts); CHECK_PTR_IF(B > 0, prob_sums);
+  if (E > kMaxE || Kmax > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d / Kmax=%d above %d", fn, E, Kmax,
+                kMaxE);
+  const int64_t N = static_cast<int64_t>(B) * T;
+  if (N * E >= kI32Limit || N * Kmax >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: B*T*E must stay below 2^31", fn);
+  return from_hip(moe::launch_balance(probs, topk_idx, B, T, E, Kmax, K, alpha,
+                                      mode == MOE_BAL_GLOBAL, counts, prob_sums,
+                                      loss, stream),
+                  fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,439 @@
+// Grouped expert MLPs of the DiT-MoE layer on gfx950.
+//
+// "Scaling Diffusion Transformers to 16 Billion Parameters", MoE-DiT eq. MLP:
+// each expert is W2 gelu(W1 x); "Scalable Diffusion Models with Transformers
+// (DiT)", model architecture: the GELU is the tanh approximation.
+//
+// moe_grouped_ffn runs two grouped GEMMs over G row groups whose bounds
+// live in device memory (no host synchronisation):
+//   stage 1:  h = gelu_tanh(A W1[g]^T + b1[g])   A rows gathered by index
+//   stage 2:  y = h W2[g]^T + b2[g]
+//
+// bf16 path (the hot path): one workgroup computes a 128-row x 128-feature
+// output tile with 4 waves (2 x 2), each wave a 64 x 64 block made of
+// 2 x 2 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.  Operand
+// tiles of 128 rows x 64 k (16 KB each) are staged in LDS, double-buffered:
+// the next k-tile's global loads are in flight while the current one feeds
+// the matrix cores.  Both operands are k-contiguous rows, so each lane moves
+// 16 bytes per load and per LDS read.  LDS rows are 128 bytes; the 16-byte
+// chunk c of row r is stored at slot c ^ ((r ^ (r >> 3)) & 7), which keeps
+// the MFMA fragment reads (16 rows at one chunk) and the tile writes
+// (8 chunks of 2 rows) free of bank conflicts.
+//
+// The MFMA computes out^T: weight rows are the 32-row "A" operand and token
+// rows the "B" operand, so each lane ends up holding 4 consecutive output
+// features of one token and stores 8 (bf16) or 16 (fp32) bytes at a time.
+//
+// Tile order: workgroup ids are dealt round-robin to the 8 XCDs, so the id
+// is remapped to give each XCD a contiguous run of tiles; within a group,
+// tiles go in bands of 8 row-tiles, feature-tile major, so tiles running at
+// once share both their token rows and their weight rows in the XCD's L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+enum Epi { kEpiGelu = 0, kEpiStore = 1 };
+
+struct GemmParams {
+  const void* a;           // activation rows [*][Kd]
+  const int32_t* a_index;  // source row of each output row, or null
+  const void* w;           // [G][Nd][Kd]
+  const float* bias;       // [G][Nd] or null
+  void* c;                 // [total][Nd]
+  const int64_t* offsets;  // [G+1], device
+  int64_t total;
+  int G, Nd, Kd;
+};
+
+struct TileLoc {
+  int g;
+  int64_t row0, row_end;
+  int n0;
+};
+
+// tanh-GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)),
+// z = sqrt(2/pi) (u + 0.044715 u^3); exp through the hardware exp2.
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float kC = 0.7978845608028654f;   // sqrt(2/pi)
+  const float kA = 0.044715f;
+  const float kLog2e = 1.4426950408889634f;
+  const float z = kC * fmaf(kA * u, u * u, u);
+  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * z);
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  const int q = n / 8, r = n % 8;
+  const int xcd = pid % 8, j = pid / 8;
+  return xcd * q + min(xcd, r) + j;
+}
+
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool locate_tile(const GemmParams& p, int L,
+                                            TileLoc& loc) {
+  const int ntn = (p.Nd + BN - 1) / BN;
+  for (int g = 0; g < p.G; ++g) {
+    int64_t r0 = p.offsets[g], r1 = p.offsets[g + 1];
+    r0 = min(max(r0, int64_t(0)), p.total);
+    r1 = min(max(r1, r0), p.total);
+    const int mt = static_cast<int>((r1 - r0 + BM - 1) / BM);
+    const int tiles = mt * ntn;
+    if (L < tiles) {
+      const int band = L / (GM * ntn);
+      const int rem = L - band * GM * ntn;
+      const int m_first = band * GM;
+      const int gm = min(GM, mt - m_first);
+      // All wave-uniform: keep them in scalar registers.
+      loc.g = __builtin_amdgcn_readfirstlane(g);
+      loc.row0 = uniform64(r0 + static_cast<int64_t>(m_first + rem % gm) * BM);
+      loc.row_end = uniform64(r1);
+      loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+      return true;
+    }
+    L -= tiles;
+  }
+  return false;
+}
+
+template <int EPI, bool OUT_BF16>
+__device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
+                                       int f, f32x4 v) {
+  if (p.bias != nullptr) {
+    const float* b = p.bias + static_cast<int64_t>(g) * p.Nd + f;
+    v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+  }
+  if constexpr (EPI == kEpiGelu) {
+    v[0] = gelu_tanh(v[0]); v[1] = gelu_tanh(v[1]);
+    v[2] = gelu_tanh(v[2]); v[3] = gelu_tanh(v[3]);
+  }
+  if constexpr (OUT_BF16) {
+    uint2 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + row * p.Nd + f) = o;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p.c) + row * p.Nd + f) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ------------------------------------------------------- bf16 / MFMA ----
+
+constexpr int kBM = 128, kBN = 128, kBK = 64, kGM = 8;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Buffer descriptor of a byte range; loads beyond `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r,
+                                         uint32_t off) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Offset used for chunks past the k extent: at or beyond every descriptor's
+// num_records, so such loads return zero.
+constexpr uint32_t kOutOfRange = 0xfffffff0u;
+
+template <int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
+
+  TileLoc loc;
+  if (!locate_tile<kBM, kBN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
+    return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;   // token half of the tile
+  const int wn = wave >> 1;  // feature half of the tile
+  const int Kd = p.Kd;
+  const uint32_t row_bytes = static_cast<uint32_t>(Kd) * 2u;
+
+  // Token rows: gathered through a_index from the whole activation matrix,
+  // or read in place starting at the tile's first row.  Rows past the group
+  // end re-read the tile's first row; their results are never stored.
+  const bool gather = p.a_index != nullptr;
+  const uint16_t* a_base = static_cast<const uint16_t*>(p.a) +
+                           (gather ? int64_t(0) : loc.row0 * Kd);
+  const uint32_t a_bytes =
+      gather ? kOutOfRange
+             : static_cast<uint32_t>(min<int64_t>(loc.row_end - loc.row0, kBM)) *
+                   row_bytes;
+  const __amdgpu_buffer_rsrc_t rsA =
+      make_rsrc(reinterpret_cast<const void*>(
+                    uniform64(reinterpret_cast<int64_t>(a_base))),
+                __builtin_amdgcn_readfirstlane(a_bytes));
+  // Weight rows of group g: features past Nd fall outside the descriptor.
+  const uint16_t* w_base = static_cast<const uint16_t*>(p.w) +
+                           (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd;
+  const uint32_t w_bytes =
+      static_cast<uint32_t>(min(p.Nd - loc.n0, kBN)) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rsB =
+      make_rsrc(reinterpret_cast<const void*>(
+                    uniform64(reinterpret_cast<int64_t>(w_base))),
+                __builtin_amdgcn_readfirstlane(w_bytes));
+
+  // This thread's 4 + 4 global 16-byte chunks per k-tile: tile rows
+  // (tid >> 3) + 32 i, chunk tid & 7.
+  const int lrow = tid >> 3, lkc = tid & 7;
+#define MOE_X4(M) M(0) M(1) M(2) M(3)
+#define MOE_ROWSETUP(I)                                                      \
+  uint32_t a_off##I, b_off##I;                                               \
+  int st_off##I;                                                             \
+  {                                                                          \
+    const int row = lrow + 32 * I;                                           \
+    const int64_t grow = loc.row0 + row;                                     \
+    const bool valid = grow < loc.row_end;                                   \
+    if (gather)                                                              \
+      a_off##I = static_cast<uint32_t>(p.a_index[valid ? grow : loc.row0]) * \
+                     row_bytes + lkc * 16u;                                  \
+    else                                                                     \
+      a_off##I = static_cast<uint32_t>(valid ? row : 0) * row_bytes +        \
+                 lkc * 16u;                                                  \
+    b_off##I = static_cast<uint32_t>(row) * row_bytes + lkc * 16u;           \
+    st_off##I = row * kBK + ((lkc ^ swz(row)) * 8);                          \
+  }
+  MOE_X4(MOE_ROWSETUP)
+#undef MOE_ROWSETUP
+
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+
+  // Fragment read offsets: row (lane & 31) of each 32-row block, chunk
+  // 2 ks + (lane >> 5) of the 64-wide k-tile.
+  int fa_row[2], fb_row[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa_row[i] = wn * 64 + i * 32 + (lane & 31);
+    fb_row[i] = wm * 64 + i * 32 + (lane & 31);
+  }
+  const int khalf = lane >> 5;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // k-tile KT: chunks past Kd read as zero (out-of-range offset).
+#define MOE_GLOAD1(I)                                                        \
+  ra##I = bload16(rsA, kin_ ? a_off##I + kb_ : kOutOfRange);                 \
+  rb##I = bload16(rsB, kin_ ? b_off##I + kb_ : kOutOfRange);
+#define MOE_GLOAD(KT)                                                        \
+  do {                                                                       \
+    const int kt_ = (KT);                                                    \
+    const bool kin_ = kt_ * kBK + lkc * 8 < Kd;                              \
+    const uint32_t kb_ = static_cast<uint32_t>(kt_) * (kBK * 2);             \
+    MOE_X4(MOE_GLOAD1)                                                       \
+  } while (0)
+#define MOE_LSTORE1(I)                                                       \
+  *reinterpret_cast<uint4*>(&sA[s_][st_off##I]) = ra##I;                     \
+  *reinterpret_cast<uint4*>(&sB[s_][st_off##I]) = rb##I;
+#define MOE_LSTORE(S)                                                        \
+  do {                                                                       \
+    const int s_ = (S);                                                      \
+    MOE_X4(MOE_LSTORE1)                                                      \
+  } while (0)
+
+  const int nk = (Kd + kBK - 1) / kBK;
+  MOE_GLOAD(0);
+  MOE_LSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int s = kt & 1;
+    if (kt + 1 < nk) MOE_GLOAD(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kc = 2 * ks + khalf;
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(
+            &sB[s][fa_row[i] * kBK + ((kc ^ swz(fa_row[i])) * 8)]);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(
+            &sA[s][fb_row[i] * kBK + ((kc ^ swz(fb_row[i])) * 8)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
+                                                              acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) MOE_LSTORE(s ^ 1);
+    __syncthreads();
+  }
+#undef MOE_GLOAD
+#undef MOE_GLOAD1
+#undef MOE_LSTORE
+#undef MOE_LSTORE1
+#undef MOE_X4
+
+  // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
+  // weight block i, token (lane & 31) of token block j.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t row = loc.row0 + wm * 64 + j * 32 + (lane & 31);
+    if (row >= loc.row_end) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = loc.n0 + wn * 64 + i * 32 + 8 * q + 4 * khalf;
+        if (f >= p.Nd) continue;
+        f32x4 v;
+        v[0] = acc[i][j][4 * q + 0];
+        v[1] = acc[i][j][4 * q + 1];
+        v[2] = acc[i][j][4 * q + 2];
+        v[3] = acc[i][j][4 * q + 3];
+        store4<EPI, OUT_BF16>(p, loc.g, row, f, v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------- fp32 path ----
+// Plain fp32 FMA tiles (64 x 64 x 16, 4 x 4 outputs per thread) for fp32
+// layers; same tile order and epilogue as the bf16 path.
+
+constexpr int kFM = 64, kFN = 64, kFK = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
+  __shared__ float sA[kFK][kFM + 4];
+  __shared__ float sB[kFK][kFN + 4];
+  TileLoc loc;
+  if (!locate_tile<kFM, kFN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
+    return;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int Kd = p.Kd;
+  const float* A = static_cast<const float*>(p.a);
+  const float* W = static_cast<const float*>(p.w) +
+                   static_cast<int64_t>(loc.g) * p.Nd * Kd;
+  // loads: row tid >> 2 (0..63), k quad (tid & 3) * 4
+  const int lrow = tid >> 2, lk = (tid & 3) * 4;
+  const int64_t grow = loc.row0 + lrow;
+  const bool a_ok = grow < loc.row_end;
+  int64_t src = 0;
+  if (a_ok) src = (p.a_index != nullptr) ? p.a_index[grow] : grow;
+  const float* a_src = A + src * Kd + lk;
+  const int f = loc.n0 + lrow;
+  const bool b_ok = f < p.Nd;
+  const float* b_src = W + static_cast<int64_t>(b_ok ? f : 0) * Kd + lk;
+
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+  for (int k0 = 0; k0 < Kd; k0 += kFK) {
+    const bool kok = k0 + lk < Kd;
+    const float4 av = (a_ok && kok) ? *reinterpret_cast<const float4*>(a_src + k0)
+                                    : make_float4(0, 0, 0, 0);
+    const float4 bv = (b_ok && kok) ? *reinterpret_cast<const float4*>(b_src + k0)
+                                    : make_float4(0, 0, 0, 0);
+    sA[lk + 0][lrow] = av.x; sA[lk + 1][lrow] = av.y;
+    sA[lk + 2][lrow] = av.z; sA[lk + 3][lrow] = av.w;
+    sB[lk + 0][lrow] = bv.x; sB[lk + 1][lrow] = bv.y;
+    sB[lk + 2][lrow] = bv.z; sB[lk + 3][lrow] = bv.w;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kFK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sB[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = loc.row0 + ty * 4 + i;
+    const int fo = loc.n0 + tx * 4;
+    if (row < loc.row_end && fo < p.Nd) {
+      f32x4 v;
+      v[0] = acc[i][0]; v[1] = acc[i][1]; v[2] = acc[i][2]; v[3] = acc[i][3];
+      store4<EPI, false>(p, loc.g, row, fo, v);
+    }
+  }
+}
+
+int tile_grid(const GemmParams& p, int BM, int BN) {
+  const int64_t mt = (p.total + static_cast<int64_t>(p.G) * (BM - 1)) / BM;
+  return static_cast<int>(mt * ((p.Nd + BN - 1) / BN));
+}
+
+}  // namespace
+
+hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
+                      hipStream_t stream) {
+  if (a.total_rows == 0) return hipSuccess;
+  GemmParams p1{a.x, a.row_index, a.w1, a.b1, a.h, a.offsets, a.total_rows,
+                a.G, a.H, a.D};
+  GemmParams p2{a.h, nullptr, a.w2, a.b2, a.y, a.offsets, a.total_rows,
+                a.G, a.D, a.H};
+  if (a.bf16) {
+    if (up) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<kEpiGelu, true>),
+                         dim3(tile_grid(p1, kBM, kBN)), dim3(kThreads), 0,
+                         stream, p1);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    if (down) {
+      if (a.y_f32)
+        hipLaunchKernelGGL((gemm_bf16_kernel<kEpiStore, false>),
+                           dim3(tile_grid(p2, kBM, kBN)), dim3(kThreads), 0,
+                           stream, p2);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<kEpiStore, true>),
+                           dim3(tile_grid(p2, kBM, kBN)), dim3(kThreads), 0,
+                           stream, p2);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  if (up) {
+    hipLaunchKernelGGL((gemm_f32_kernel<kEpiGelu>),
+                       dim3(tile_grid(p1, kFM, kFN)), dim3(kThreads), 0, stream,
+                       p1);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (down) {
+    hipLaunchKernelGGL((gemm_f32_kernel<kEpiStore>),
+                       dim3(tile_grid(p2, kFM, kFN)), dim3(kThreads), 0, stream,
+                       p2);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

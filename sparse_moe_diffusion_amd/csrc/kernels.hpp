@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+// Every launcher only enqueues work on `stream` and returns the launch
+// status; argument validation lives in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// gate.hip
+hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
+                       const float* bias, int64_t N, int D, int E, int K,
+                       bool topk, float* probs, int32_t* idx, float* w,
+                       hipStream_t stream);
+size_t race_workspace_bytes();
+hipError_t launch_race(const float* probs, int64_t N, int E, int K,
+                       int32_t* idx, float* w, void* workspace,
+                       hipStream_t stream);
+
+// permute.hip
+size_t permute_workspace_bytes(int64_t N, int E);
+hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
+                          int64_t N, int D, int E, int Kmax, int64_t A,
+                          int32_t* counts, int64_t* offsets, int32_t* row_token,
+                          int32_t* slot_row, void* x_perm, void* workspace,
+                          hipStream_t stream);
+
+// ffn.hip
+struct FfnArgs {
+  const void* x;            // [*][D]
+  const int32_t* row_index; // [total] or null
+  int64_t total_rows;
+  const int64_t* offsets;   // [G+1] device
+  int G, D, H;
+  const void* w1;           // [G][H][D]
+  const float* b1;          // [G][H] or null
+  const void* w2;           // [G][D][H]
+  const float* b2;          // [G][D] or null
+  void* h;                  // [total][H]
+  void* y;                  // [total][D]
+  bool bf16;                // input / weight / h dtype
+  bool y_f32;               // output dtype
+};
+hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
+
+// combine.hip
+hipError_t launch_combine(const void* y_rows, bool y_bf16,
+                          const int32_t* slot_row, const float* w, int64_t N,
+                          int D, int Kmax, const void* y_shared, bool sh_bf16,
+                          void* y, bool out_bf16, hipStream_t stream);
+
+// balance.hip
+hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
+                          int E, int Kmax, int K, float alpha, bool global,
+                          int32_t* counts, float* psum, float* loss,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,192 @@
+// Token permutation by expert for the DiT-MoE layer.
+//
+// "Scaling Diffusion Transformers to 16 Billion Parameters", MoE recap: with
+// a sparse router only the selected experts are evaluated.  The selected
+// (token, slot) pairs are grouped by expert so that each expert's MLP runs
+// as one dense row block.  Rows of expert e are its selections in ascending
+// (token, slot) order.
+//
+// Three launches, no host synchronisation:
+//  1. permute_count_kernel: workgroup b covers 256 consecutive tokens (one
+//     per thread); each token's experts form a bit mask, and one wave ballot
+//     per expert counts the wave's selections.  Writes block_counts[b][e].
+//  2. permute_scan_kernel: one thread per expert scans the block counts in
+//     block order: expert counts, exclusive offsets and block bases.
+//  3. permute_scatter_kernel: repeats the ballots, so a selection's row is
+//     block base + earlier waves' count + set lanes below it; writes slot_row
+//     and row_token, then copies each token row once from HBM to its K
+//     destination rows with 16-byte lanes (row copy skipped when x_perm is
+//     null).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPermTokens = 256;
+constexpr int kPermWaves = kPermTokens / kWave;
+
+__device__ __forceinline__ uint64_t token_mask(const int32_t* __restrict__ idx,
+                                               int64_t t, int Kmax, int E) {
+  uint64_t m = 0;
+  for (int k = 0; k < Kmax; ++k) {
+    const int e = idx[t * Kmax + k];
+    if (e >= 0 && e < E) m |= 1ull << e;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
+    const int32_t* __restrict__ idx, int64_t N, int E, int Kmax,
+    int32_t* __restrict__ block_counts) {
+  __shared__ int32_t wc[kPermWaves][kMaxExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermTokens + threadIdx.x;
+  const uint64_t m = (t < N) ? token_mask(idx, t, Kmax, E) : 0ull;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot((m >> e) & 1ull);
+    if (lane == 0) wc[wave][e] = __popcll(b);
+  }
+  __syncthreads();
+  if (threadIdx.x < E) {
+    int32_t c = 0;
+    for (int w = 0; w < kPermWaves; ++w) c += wc[w][threadIdx.x];
+    block_counts[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x] = c;
+  }
+}
+
+__global__ __launch_bounds__(kWave) void permute_scan_kernel(
+    const int32_t* __restrict__ block_counts, int nblocks, int E,
+    int32_t* __restrict__ counts, int64_t* __restrict__ offsets,
+    int64_t* __restrict__ block_base) {
+  __shared__ int64_t tot[kMaxExperts];
+  const int e = threadIdx.x;
+  int64_t c = 0;
+  if (e < E)
+    for (int b = 0; b < nblocks; ++b) c += block_counts[static_cast<int64_t>(b) * E + e];
+  tot[e] = c;
+  __syncthreads();
+  int64_t run = 0;
+  for (int j = 0; j < e && j < E; ++j) run += tot[j];
+  if (e < E) {
+    counts[e] = static_cast<int32_t>(c);
+    offsets[e] = run;
+    if (e == E - 1) offsets[E] = run + c;
+    for (int b = 0; b < nblocks; ++b) {
+      block_base[static_cast<int64_t>(b) * E + e] = run;
+      run += block_counts[static_cast<int64_t>(b) * E + e];
+    }
+  }
+}
+
+template <int VEC_BYTES>
+__global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
+    const void* __restrict__ x, const int32_t* __restrict__ idx, int64_t N,
+    int row_bytes, int E, int Kmax, int64_t A,
+    const int64_t* __restrict__ block_base, int32_t* __restrict__ slot_row,
+    int32_t* __restrict__ row_token, void* __restrict__ x_perm) {
+  extern __shared__ int32_t s_rows[];  // [kPermTokens][Kmax]
+  __shared__ int32_t wc[kPermWaves][kMaxExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermTokens;
+  const int64_t t = t0 + threadIdx.x;
+  const bool valid = t < N;
+  const uint64_t m = valid ? token_mask(idx, t, Kmax, E) : 0ull;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot((m >> e) & 1ull);
+    if (lane == 0) wc[wave][e] = __popcll(b);
+  }
+  __syncthreads();
+  const int64_t* base = block_base + static_cast<int64_t>(blockIdx.x) * E;
+  for (int k = 0; k < Kmax; ++k) {
+    const int e = valid ? idx[t * Kmax + k] : -1;
+    int32_t row = -1;
+    // The ballot for expert e must be taken by the whole wave: loop over
+    // every expert and keep the rank of the one this slot names.
+    for (int ee = 0; ee < E; ++ee) {
+      const uint64_t b = __ballot((m >> ee) & 1ull);
+      if (ee == e) {
+        int64_t r = base[ee] + lanes_below(b);
+        for (int w = 0; w < wave; ++w) r += wc[w][ee];
+        row = (r < A) ? static_cast<int32_t>(r) : -1;
+      }
+    }
+    if (valid) {
+      slot_row[t * Kmax + k] = row;
+      if (row >= 0) row_token[row] = static_cast<int32_t>(t);
+    }
+    s_rows[threadIdx.x * Kmax + k] = row;
+  }
+  if (x_perm == nullptr) return;
+  __syncthreads();
+
+  // Row copy: each wave takes tokens wave, wave+4, ...; lanes cover the row
+  // in VEC_BYTES pieces.
+  typedef uint4 vec_t;
+  static_assert(VEC_BYTES == 16, "16-byte lanes");
+  const int nvec = row_bytes / VEC_BYTES;
+  const char* xb = static_cast<const char*>(x);
+  char* pb = static_cast<char*>(x_perm);
+  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
+  for (int tl = wave; tl < ntok; tl += kPermWaves) {
+    const vec_t* src = reinterpret_cast<const vec_t*>(xb + (t0 + tl) * row_bytes);
+    for (int c = lane; c < nvec; c += kWave) {
+      const vec_t v = src[c];
+      for (int k = 0; k < Kmax; ++k) {
+        const int32_t r = s_rows[tl * Kmax + k];
+        if (r >= 0)
+          reinterpret_cast<vec_t*>(pb + static_cast<int64_t>(r) * row_bytes)[c] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int64_t N, int E) {
+  const int64_t nb = ceil_div(N, kPermTokens);
+  // block_counts (int32) + block_base (int64), each [nb][E], 256-B aligned
+  const size_t a = ((nb * E * sizeof(int32_t)) + 255) / 256 * 256;
+  return a + nb * E * sizeof(int64_t) + 256;
+}
+
+hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
+                          int64_t N, int D, int E, int Kmax, int64_t A,
+                          int32_t* counts, int64_t* offsets, int32_t* row_token,
+                          int32_t* slot_row, void* x_perm, void* workspace,
+                          hipStream_t stream) {
+  const int64_t nb = ceil_div(N, kPermTokens);
+  int32_t* block_counts = static_cast<int32_t*>(workspace);
+  const size_t a = ((nb * E * sizeof(int32_t)) + 255) / 256 * 256;
+  int64_t* block_base =
+      reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + a);
+  if (nb > 0) {
+    hipLaunchKernelGGL(permute_count_kernel, dim3(static_cast<unsigned>(nb)),
+                       dim3(kPermTokens), 0, stream, idx, N, E, Kmax,
+                       block_counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kWave), 0, stream,
+                     block_counts, static_cast<int>(nb), E, counts, offsets,
+                     block_base);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nb == 0) return err;
+  const int row_bytes = D * (bf16 ? 2 : 4);
+  const size_t shmem = static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
+  if (shmem > 32768) {
+    err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&permute_scatter_kernel<16>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3(static_cast<unsigned>(nb)),
+                     dim3(kPermTokens), shmem, stream, x, idx, N, row_bytes, E,
+                     Kmax, A, block_base, slot_row, row_token, x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,168 @@
+"""The DiT-MoE sparse MoE feed-forward layer as one sequence of C-ABI calls.
+
+    gate -> permute -> routed expert MLPs -> shared expert MLPs -> combine
+         -> balance statistic
+
+("Scaling Diffusion Transformers to 16 Billion Parameters", Methods: eq.
+MoE(x), eq. MLP(x), shared expert routing, eq. L_balance; "DiT-MoE" hub
+page, section 1: the softmax top-k gate; "Expert Race" abstract for the race
+routing.)
+
+This module holds device weights and preallocated buffers and issues the
+calls in order on the current stream.  Every step runs in libmoe.so; torch
+only provides device memory and the stream.  Nothing here synchronises.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib, ops
+
+ROUTES = {"topk": _lib.MOE_ROUTE_TOPK, "race": _lib.MOE_ROUTE_EXPERT_RACE}
+BALANCE = {"sequence": _lib.MOE_BAL_PER_SEQUENCE, "global": _lib.MOE_BAL_GLOBAL}
+
+
+def _to_device(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
+    """Upload an fp32 array holding exact bf16 (or fp32) values."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == torch.bfloat16:
+        # exact: the values are bf16-representable
+        t = t.to(torch.bfloat16)
+    return t.to(device)
+
+
+@dataclass
+class LayerWeights:
+    """Device weights of one layer (layouts of include/moe.h)."""
+    w_gate: torch.Tensor            # [E][D] fp32
+    bias: Optional[torch.Tensor]    # [E] fp32 or None
+    w1: torch.Tensor                # [E][H][D]
+    w2: torch.Tensor                # [E][D][H]
+    w1s: Optional[torch.Tensor]     # [1][n_s*H][D]  shared experts stacked
+    w2s: Optional[torch.Tensor]     # [1][D][n_s*H]
+
+    @staticmethod
+    def from_inputs(inp, device="cuda") -> "LayerWeights":
+        cfg = inp.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        w1s = w2s = None
+        if cfg.n_s > 0:
+            # n_s MLPs summed with weight 1 == one MLP of hidden n_s*H: W1 rows
+            # and W2 columns concatenated.
+            w1s = _to_device(inp.w1s.reshape(1, cfg.n_s * cfg.H, cfg.D), dt, device)
+            w2s = _to_device(np.transpose(inp.w2s, (1, 0, 2)).reshape(
+                1, cfg.D, cfg.n_s * cfg.H), dt, device)
+        return LayerWeights(
+            w_gate=_to_device(inp.w_gate, torch.float32, device),
+            bias=None if inp.bias is None else _to_device(inp.bias, torch.float32,
+                                                           device),
+            w1=_to_device(inp.w1, dt, device),
+            w2=_to_device(inp.w2, dt, device),
+            w1s=w1s, w2s=w2s)
+
+
+class LayerBuffers:
+    """Every intermediate and output tensor of one forward pass, allocated
+    once for a fixed token count."""
+
+    def __init__(self, cfg, device="cuda", gather: bool = False,
+                 y_rows_f32: bool = False):
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        N, D, H, E, K, n_s = cfg.N, cfg.D, cfg.H, cfg.E, cfg.K, cfg.n_s
+        Kmax, A = cfg.Kmax, cfg.A
+        route = ROUTES[cfg.route]
+        f32, i32, i64 = torch.float32, torch.int32, torch.int64
+        dev = device
+        self.gather = gather
+        self.probs = torch.empty(N, E, dtype=f32, device=dev)
+        self.topk_idx = torch.empty(N, Kmax, dtype=i32, device=dev)
+        self.topk_w = torch.empty(N, Kmax, dtype=f32, device=dev)
+        gws = ops.gate_workspace_size(N, E, K, route)
+        self.gate_ws = torch.empty(max(gws, 1), dtype=torch.uint8, device=dev)
+        self.expert_counts = torch.empty(E, dtype=i32, device=dev)
+        self.expert_offsets = torch.empty(E + 1, dtype=i64, device=dev)
+        self.row_token = torch.empty(max(A, 1), dtype=i32, device=dev)
+        self.slot_row = torch.empty(N, Kmax, dtype=i32, device=dev)
+        self.x_perm = None if gather else torch.empty(A, D, dtype=dt, device=dev)
+        pws = ops.permute_workspace_size(N, E, Kmax)
+        self.perm_ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+        self.h = torch.empty(A, H, dtype=dt, device=dev)
+        ydt = f32 if (y_rows_f32 or dt == f32) else dt
+        self.y_rows = torch.empty(A, D, dtype=ydt, device=dev)
+        if n_s > 0:
+            self.shared_offsets = torch.tensor([0, N], dtype=i64, device=dev)
+            self.h_shared = torch.empty(N, n_s * H, dtype=dt, device=dev)
+            self.y_shared = torch.empty(N, D, dtype=dt, device=dev)
+        else:
+            self.shared_offsets = self.h_shared = self.y_shared = None
+        self.y = torch.empty(N, D, dtype=dt, device=dev)
+        self.bal_counts = torch.empty(cfg.B, E, dtype=i32, device=dev)
+        self.bal_psum = torch.empty(cfg.B, E, dtype=f32, device=dev)
+        self.loss = torch.empty(1, dtype=f32, device=dev)
+
+
+def gate(cfg, x, wts: LayerWeights, buf: LayerBuffers):
+    ops.moe_gate_topk(x, wts.w_gate, wts.bias, cfg.K, ROUTES[cfg.route],
+                      buf.probs, buf.topk_idx, buf.topk_w, buf.gate_ws)
+
+
+def permute(cfg, x, buf: LayerBuffers):
+    ops.moe_permute(x, buf.topk_idx, cfg.E, cfg.K, buf.expert_counts,
+                    buf.expert_offsets, buf.row_token, buf.slot_row, buf.x_perm,
+                    buf.perm_ws)
+
+
+def routed_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
+               stages: int = _lib.MOE_FFN_BOTH):
+    if buf.gather:
+        ops.moe_grouped_ffn(x, buf.row_token, cfg.A, buf.expert_offsets, wts.w1,
+                            None, wts.w2, None, buf.h, buf.y_rows, stages)
+    else:
+        ops.moe_grouped_ffn(buf.x_perm, None, cfg.A, buf.expert_offsets, wts.w1,
+                            None, wts.w2, None, buf.h, buf.y_rows, stages)
+
+
+def shared_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
+               stages: int = _lib.MOE_FFN_BOTH):
+    if cfg.n_s > 0:
+        ops.moe_grouped_ffn(x, None, cfg.N, buf.shared_offsets, wts.w1s, None,
+                            wts.w2s, None, buf.h_shared, buf.y_shared, stages)
+
+
+def combine(cfg, buf: LayerBuffers):
+    ops.moe_combine(buf.y_rows, buf.slot_row, buf.topk_w, buf.y_shared, buf.y)
+
+
+def balance(cfg, buf: LayerBuffers, mode: str = "sequence"):
+    ops.moe_balance_stats(buf.probs, buf.topk_idx, cfg.B, cfg.T, cfg.K,
+                          cfg.alpha, BALANCE[mode], buf.bal_counts,
+                          buf.bal_psum, buf.loss)
+
+
+# The layer as a list of single-kernel-group calls, in order (the expert
+# MLPs split into their two GEMM stages): the same work as forward().
+UP, DOWN = _lib.MOE_FFN_UP, _lib.MOE_FFN_DOWN
+STEPS = (("gate", lambda c, x, w, b: gate(c, x, w, b)),
+         ("permute", lambda c, x, w, b: permute(c, x, b)),
+         ("routed_up", lambda c, x, w, b: routed_ffn(c, x, w, b, UP)),
+         ("routed_down", lambda c, x, w, b: routed_ffn(c, x, w, b, DOWN)),
+         ("shared_up", lambda c, x, w, b: shared_ffn(c, x, w, b, UP)),
+         ("shared_down", lambda c, x, w, b: shared_ffn(c, x, w, b, DOWN)),
+         ("combine", lambda c, x, w, b: combine(c, b)),
+         ("balance", lambda c, x, w, b: balance(c, b)))
+
+
+def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
+            balance_mode: str = "sequence") -> LayerBuffers:
+    """One pass of the whole layer; results land in ``buf``."""
+    gate(cfg, x, wts, buf)
+    permute(cfg, x, buf)
+    routed_ffn(cfg, x, wts, buf)
+    shared_ffn(cfg, x, wts, buf)
+    combine(cfg, buf)
+    balance(cfg, buf, balance_mode)
+    return buf

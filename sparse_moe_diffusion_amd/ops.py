@@ -1,0 +1,93 @@
+"""Tensor-level binding of the five C-ABI calls, same names as include/moe.h.
+
+Argument marshalling only: tensors become device pointers, dtypes become
+moe_dtype codes, and every call is enqueued on torch's current HIP stream.
+Outputs are caller-provided tensors (allocate them once and reuse them).
+All arithmetic happens in libmoe.so.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    try:
+        return _DT[t]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def gate_workspace_size(N: int, E: int, K: int, route: int) -> int:
+    return _lib.load().moe_gate_workspace_size(N, E, K, route)
+
+
+def permute_workspace_size(N: int, E: int, Kmax: int) -> int:
+    return _lib.load().moe_permute_workspace_size(N, E, Kmax)
+
+
+def moe_gate_topk(x, w_gate, logit_bias, K: int, route: int, probs, topk_idx,
+                  topk_w, workspace=None):
+    N, D = x.shape
+    E = w_gate.shape[0]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.call("moe_gate_topk", _ptr(x), dtype_code(x.dtype), _ptr(w_gate),
+              _ptr(logit_bias), N, D, E, K, route, _ptr(probs), _ptr(topk_idx),
+              _ptr(topk_w), _ptr(workspace), ws, _stream())
+
+
+def moe_permute(x, topk_idx, E: int, K: int, expert_counts, expert_offsets,
+                row_token, slot_row, x_perm, workspace):
+    N, D = x.shape
+    Kmax = topk_idx.shape[1]
+    ws = workspace.numel() * workspace.element_size()
+    _lib.call("moe_permute", _ptr(x), dtype_code(x.dtype), _ptr(topk_idx), N,
+              D, E, Kmax, K, _ptr(expert_counts), _ptr(expert_offsets),
+              _ptr(row_token), _ptr(slot_row), _ptr(x_perm), _ptr(workspace),
+              ws, _stream())
+
+
+def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
+                    w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH):
+    G, H, D = w1.shape
+    _lib.call("moe_grouped_ffn", _ptr(x_rows), _ptr(row_index),
+              dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(y_rows),
+              dtype_code(y_rows.dtype), stages, _stream())
+
+
+def moe_combine(y_rows, slot_row, topk_w, y_shared, y):
+    N, D = y.shape
+    Kmax = slot_row.shape[1]
+    sh = _lib.MOE_F32 if y_shared is None else dtype_code(y_shared.dtype)
+    _lib.call("moe_combine", _ptr(y_rows), dtype_code(y_rows.dtype),
+              _ptr(slot_row), _ptr(topk_w), N, D, Kmax, _ptr(y_shared), sh,
+              _ptr(y), dtype_code(y.dtype), _stream())
+
+
+def moe_balance_stats(probs, topk_idx, B: int, T: int, K: int, alpha: float,
+                      mode: int, counts, prob_sums, loss):
+    E = probs.shape[1]
+    Kmax = topk_idx.shape[1]
+    _lib.call("moe_balance_stats", _ptr(probs), _ptr(topk_idx), B, T, E, Kmax,
+              K, alpha, mode, _ptr(counts), _ptr(prob_sums), _ptr(loss),
+              _stream())

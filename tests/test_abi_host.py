@@ -1,0 +1,157 @@
+"""The C ABI on the host (no GPU): every symbol of include/moe.h is
+exported, workspace queries answer, and invalid arguments are rejected with
+the documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_diffusion_amd import _lib
+from libmoe_build import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ensure_built()
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding covers every declared entry point, same names
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    ensure_built()
+    for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"),
+                       (2, "MOE_ERR_UNSUPPORTED"),
+                       (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP")]:
+        assert _lib.status_string(code) == name
+
+
+def test_workspace_queries():
+    lib = ensure_built()
+    assert lib.moe_gate_workspace_size(1000, 8, 2, _lib.MOE_ROUTE_TOPK) == 0
+    assert lib.moe_gate_workspace_size(1000, 16, 2, _lib.MOE_ROUTE_EXPERT_RACE) > 0
+    a = lib.moe_permute_workspace_size(32768, 8, 2)
+    b = lib.moe_permute_workspace_size(65536, 8, 2)
+    assert 0 < a < b
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+def _gate(**kw):
+    a = dict(x=FAKE, dt=_lib.MOE_BF16, wg=FAKE, bias=None, N=64, D=128, E=8,
+             K=2, route=_lib.MOE_ROUTE_TOPK, probs=FAKE, idx=FAKE, w=FAKE,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_gate_topk", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(wg=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(probs=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=9), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(route=7), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=65, K=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=5), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(N=1 << 30, K=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(route=_lib.MOE_ROUTE_EXPERT_RACE), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_gate_rejects(kw, status):
+    ensure_built()
+    assert _gate(**kw) == status
+    assert _lib.last_error()
+
+
+def _permute(**kw):
+    a = dict(x=FAKE, dt=_lib.MOE_BF16, idx=FAKE, N=64, D=128, E=8, Kmax=2, K=2,
+             counts=FAKE, offsets=FAKE, row_token=FAKE, slot_row=FAKE,
+             x_perm=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_permute", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(Kmax=3), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=70, K=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=12), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(wsb=0), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_permute_rejects(kw, status):
+    ensure_built()
+    assert _permute(**kw) == status
+
+
+def _ffn(**kw):
+    a = dict(x=FAKE, idx=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
+             D=128, H=512, w1=FAKE, b1=None, w2=FAKE, b2=None, h=FAKE, y=FAKE,
+             ydt=_lib.MOE_BF16, stages=_lib.MOE_FFN_BOTH, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_grouped_ffn", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(offs=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(h=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(G=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(total=-5), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(stages=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(stages=4), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(w1=None, stages=_lib.MOE_FFN_UP), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(y=None, stages=_lib.MOE_FFN_DOWN), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(H=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_BF16), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(total=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_ffn_rejects(kw, status):
+    ensure_built()
+    assert _ffn(**kw) == status
+
+
+def test_combine_and_balance_reject():
+    ensure_built()
+    args = dict(yr=FAKE, ydt=_lib.MOE_BF16, sr=FAKE, w=FAKE, N=10, D=64, Kmax=2,
+                ysh=None, shdt=_lib.MOE_BF16, y=FAKE, odt=_lib.MOE_BF16,
+                stream=None)
+    for kw, st in [(dict(sr=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(Kmax=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(D=60), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(odt=9), _lib.MOE_ERR_UNSUPPORTED)]:
+        a = dict(args); a.update(kw)
+        assert _lib.call_status("moe_combine", *a.values()) == st
+    bargs = dict(p=FAKE, idx=FAKE, B=4, T=16, E=8, Kmax=2, K=2,
+                 alpha=ctypes.c_float(0.01), mode=_lib.MOE_BAL_PER_SEQUENCE,
+                 counts=FAKE, ps=FAKE, loss=FAKE, stream=None)
+    for kw, st in [(dict(loss=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(T=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(K=9), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(mode=3), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(E=80, K=2), _lib.MOE_ERR_UNSUPPORTED)]:
+        a = dict(bargs); a.update(kw)
+        assert _lib.call_status("moe_balance_stats", *a.values()) == st
+
+
+def test_binding_raises_on_error():
+    ensure_built()
+    with pytest.raises(_lib.MoEError, match="MOE_ERR_INVALID_ARGUMENT"):
+        _lib.call("moe_gate_topk", None, 1, None, None, 1, 8, 8, 2, 0, None,
+                  None, None, None, 0, None)

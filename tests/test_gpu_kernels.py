@@ -1,0 +1,311 @@
+"""Per-call parity of the C ABI entry points against the CPU oracle, on
+edge shapes: empty and single-token inputs, ragged tails, empty expert
+groups, K = E, E = 1 and E = 64, ties, biases, both dtypes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (TOL, assert_close, near_topk, reconcile_race,
+                    reconcile_topk, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _bits_tensor(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.to(DEV)
+
+
+def _ops():
+    from sparse_moe_diffusion_amd import _lib, ops
+    return _lib, ops
+
+
+def _run_gate(x32, wg, bias, K, route, dtype):
+    _lib, ops = _ops()
+    N, D = x32.shape
+    E = wg.shape[0]
+    Kmax = E if route == "race" else K
+    x = _bits_tensor(x32, dtype)
+    wgt = torch.from_numpy(wg).to(DEV)
+    bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+    probs = torch.empty(N, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(N, Kmax, dtype=torch.int32, device=DEV)
+    w = torch.empty(N, Kmax, dtype=torch.float32, device=DEV)
+    rc = _lib.MOE_ROUTE_EXPERT_RACE if route == "race" else _lib.MOE_ROUTE_TOPK
+    ws = torch.empty(max(ops.gate_workspace_size(N, E, K, rc), 1),
+                     dtype=torch.uint8, device=DEV)
+    ops.moe_gate_topk(x, wgt, bt, K, rc, probs, idx, w, ws)
+    torch.cuda.synchronize()
+    return to_np(probs), to_np(idx), to_np(w)
+
+
+GATE_CASES = [  # N, D, E, K, bias, dtype
+    (1, 8, 1, 1, False, "bf16"), (63, 128, 8, 2, False, "bf16"),
+    (64, 128, 8, 2, True, "bf16"), (65, 1152, 8, 2, False, "bf16"),
+    (1000, 384, 16, 2, True, "bf16"), (300, 2048, 16, 2, False, "bf16"),
+    (257, 72, 3, 3, True, "f32"), (200, 136, 33, 5, True, "bf16"),
+    (130, 64, 64, 7, False, "f32"), (500, 384, 8, 1, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,D,E,K,bias,dtype", GATE_CASES)
+def test_gate_topk(N, D, E, K, bias, dtype):
+    rng = np.random.default_rng(N * 31 + D + E)
+    x = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((N, D)).astype(np.float32)))
+    if dtype == "f32":
+        x = rng.standard_normal((N, D)).astype(np.float32)
+    wg = (rng.standard_normal((E, D)) * 0.05).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32) if bias else None
+    probs, idx, w = _run_gate(x, wg, b, K, "topk", dtype)
+    P = oracle.softmax(oracle.gate_logits(x, wg, b))
+    assert np.abs(probs - P).max() <= 1e-6
+    idx_o, _ = oracle.topk_select(P, K)
+    rec, bad, near = reconcile_topk(P, idx_o, idx)
+    assert not bad
+    assert np.array_equal(idx, rec)
+    assert np.abs(w - oracle.slot_weights(P, idx)).max() <= 1e-6
+
+
+def test_gate_zero_weights_ties():
+    """Zero gate: probabilities exactly 1/E, ties resolved to low indices."""
+    N, D, E, K = 100, 64, 8, 3
+    x = np.random.default_rng(0).standard_normal((N, D)).astype(np.float32)
+    probs, idx, w = _run_gate(x, np.zeros((E, D), np.float32), None, K, "topk",
+                              "f32")
+    assert np.all(probs == np.float32(1.0 / E))
+    assert np.all(idx == np.arange(K)) and np.all(w == np.float32(1.0 / E))
+
+
+def test_gate_empty():
+    probs, idx, w = _run_gate(np.zeros((0, 64), np.float32),
+                              np.ones((8, 64), np.float32), None, 2, "topk",
+                              "bf16")
+    assert probs.shape == (0, 8)
+
+
+@pytest.mark.parametrize("N,D,E,K", [(10, 64, 4, 2), (333, 128, 16, 2),
+                                     (64, 72, 5, 3), (1, 64, 8, 8),
+                                     (2048, 256, 16, 2), (97, 64, 64, 5)])
+def test_race_select(N, D, E, K):
+    rng = np.random.default_rng(N + E)
+    x = rng.standard_normal((N, D)).astype(np.float32)
+    wg = (rng.standard_normal((E, D)) * 0.1).astype(np.float32)
+    probs, idx, w = _run_gate(x, wg, None, K, "race", "f32")
+    P = oracle.softmax(oracle.gate_logits(x, wg))
+    idx_o, tau, near = oracle.race_select(P, K)
+    rec, bad = reconcile_race(P, K, idx_o, idx, tau)
+    assert not bad
+    assert np.array_equal(idx, rec)
+    assert int((idx >= 0).sum()) == K * N
+    assert np.all(w[idx < 0] == 0)
+
+
+def test_race_all_ties():
+    """Zero gate: every score is exactly 1/E; the first K*N flat entries
+    win, so the first K*N/E tokens take every expert."""
+    N, D, E, K = 40, 64, 4, 2
+    x = np.random.default_rng(1).standard_normal((N, D)).astype(np.float32)
+    probs, idx, w = _run_gate(x, np.zeros((E, D), np.float32), None, K, "race",
+                              "f32")
+    full = K * N // E
+    assert np.all(idx[:full] == np.arange(E))
+    assert np.all(idx[full:] == -1)
+
+
+def test_race_identical_tokens_equals_topk():
+    N, D, E, K = 256, 64, 16, 2
+    rng = np.random.default_rng(2)
+    x = np.tile(rng.standard_normal((1, D)).astype(np.float32), (N, 1))
+    wg = (rng.standard_normal((E, D)) * 0.3).astype(np.float32)
+    _, idx_r, _ = _run_gate(x, wg, None, K, "race", "f32")
+    _, idx_k, _ = _run_gate(x, wg, None, K, "topk", "f32")
+    assert np.array_equal(idx_r[:, :K], np.sort(idx_k, axis=1))
+    assert np.all(idx_r[:, K:] == -1)
+
+
+def _run_permute(x32, idx, E, K, dtype, with_copy=True):
+    _lib, ops = _ops()
+    N, D = x32.shape
+    Kmax = idx.shape[1]
+    A = K * N
+    x = _bits_tensor(x32, dtype)
+    it = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offs = torch.empty(E + 1, dtype=torch.int64, device=DEV)
+    rt = torch.full((max(A, 1),), -7, dtype=torch.int32, device=DEV)
+    sr = torch.empty(N, Kmax, dtype=torch.int32, device=DEV)
+    xp = torch.empty(A, D, dtype=x.dtype, device=DEV) if with_copy else None
+    ws = torch.empty(ops.permute_workspace_size(N, E, Kmax), dtype=torch.uint8,
+                     device=DEV)
+    ops.moe_permute(x, it, E, K, counts, offs, rt, sr, xp, ws)
+    torch.cuda.synchronize()
+    return (to_np(counts), to_np(offs), to_np(rt)[:A], to_np(sr),
+            None if xp is None else to_np(xp))
+
+
+@pytest.mark.parametrize("N,D,E,Kmax,K,dtype", [
+    (1, 64, 8, 2, 2, "bf16"), (255, 128, 8, 2, 2, "bf16"),
+    (257, 1152, 8, 2, 2, "bf16"), (1000, 64, 16, 16, 2, "bf16"),
+    (513, 72, 5, 3, 3, "f32"), (300, 64, 64, 64, 4, "bf16"),
+    (4096, 256, 8, 1, 1, "bf16"), (700, 128, 1, 1, 1, "f32")])
+def test_permute(N, D, E, Kmax, K, dtype):
+    rng = np.random.default_rng(N + 7 * E)
+    if Kmax == K:  # top-K form: K distinct experts per token, some skewed
+        p = rng.dirichlet(np.ones(E) * 0.3)
+        idx = np.stack([rng.choice(E, size=K, replace=False, p=p) for _ in range(N)])
+    else:  # race form: exactly K*N kept slots, 0..E per token
+        keep = np.zeros(N * E, bool)
+        keep[rng.choice(N * E, size=K * N, replace=False)] = True
+        keep = keep.reshape(N, E)
+        idx = np.full((N, E), -1)
+        for t in range(N):
+            sel = np.nonzero(keep[t])[0]
+            idx[t, :sel.size] = sel
+    x = rng.standard_normal((N, D)).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.bf16_to_f32(synth.bf16_bits(x))
+    counts, offs, rt, sr, xp = _run_permute(x, idx, E, K, dtype)
+    c_o, o_o, rt_o, sr_o = oracle.permute(idx.astype(np.int32), E)
+    assert np.array_equal(counts, c_o)
+    assert np.array_equal(offs, o_o)
+    assert np.array_equal(rt, rt_o)
+    assert np.array_equal(sr, sr_o)
+    assert np.array_equal(xp, x[rt_o])  # bitwise row copies
+    # index-only mode writes the same indices
+    c2, o2, rt2, sr2, _ = _run_permute(x, idx, E, K, dtype, with_copy=False)
+    assert np.array_equal(rt2, rt_o) and np.array_equal(sr2, sr_o)
+
+
+def _run_ffn(xs, offsets, w1, w2, b1, b2, dtype, row_index=None, y_f32=False):
+    _, ops = _ops()
+    G, H, D = w1.shape
+    total = int(offsets[-1])
+    x = _bits_tensor(xs, dtype)
+    ri = None if row_index is None else torch.from_numpy(
+        row_index.astype(np.int32)).to(DEV)
+    ot = torch.from_numpy(offsets.astype(np.int64)).to(DEV)
+    w1t, w2t = _bits_tensor(w1, dtype), _bits_tensor(w2, dtype)
+    b1t = None if b1 is None else torch.from_numpy(b1).to(DEV)
+    b2t = None if b2 is None else torch.from_numpy(b2).to(DEV)
+    h = torch.empty(total, H, dtype=x.dtype, device=DEV)
+    ydt = torch.float32 if (y_f32 or dtype == "f32") else torch.bfloat16
+    y = torch.full((total, D), float("nan"), dtype=ydt, device=DEV)
+    ops.moe_grouped_ffn(x, ri, total, ot, w1t, b1t, w2t, b2t, h, y)
+    torch.cuda.synchronize()
+    return to_np(y)
+
+
+@pytest.mark.parametrize("sizes,D,H,dtype,gather,bias", [
+    ([100, 0, 129, 1, 256, 0, 0, 300], 128, 256, "bf16", False, False),
+    ([100, 0, 129, 1, 256, 0, 0, 300], 128, 256, "bf16", True, True),
+    ([0, 0, 0], 64, 128, "bf16", False, False),
+    ([513], 136, 264, "bf16", False, True),
+    ([77, 3, 200], 1152, 4608, "bf16", True, False),
+    ([31, 64, 0, 97], 72, 136, "f32", True, True),
+    ([128, 128], 256, 512, "f32", False, False),
+])
+def test_grouped_ffn(sizes, D, H, dtype, gather, bias):
+    rng = np.random.default_rng(sum(sizes) + D)
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)])
+    total = int(offsets[-1])
+    rnd = lambda *s: (rng.standard_normal(s) * 0.05).astype(np.float32)
+    q = (lambda a: synth.bf16_to_f32(synth.bf16_bits(a))) if dtype == "bf16" else (lambda a: a)
+    nsrc = total + 13
+    xsrc = q(rng.standard_normal((nsrc, D)).astype(np.float32))
+    w1, w2 = q(rnd(G, H, D)), q(rnd(G, D, H))
+    b1 = rnd(G, H) if bias else None
+    b2 = rnd(G, D) if bias else None
+    ri = rng.permutation(nsrc)[:total] if gather else None
+    y = _run_ffn(xsrc if gather else xsrc[:total], offsets, w1, w2, b1, b2, dtype,
+                 row_index=ri)
+    if total == 0:
+        return
+    rows = xsrc[ri] if gather else xsrc[:total]
+    ref = np.zeros((total, D))
+    for g in range(G):
+        a, b = offsets[g], offsets[g + 1]
+        if b > a:
+            ref[a:b] = oracle.expert_mlp(rows[a:b], w1[g], w2[g],
+                                         None if b1 is None else b1[g],
+                                         None if b2 is None else b2[g])
+    assert_close(y, ref, dtype, "grouped ffn")
+
+
+def test_grouped_ffn_bf16_rows_fp32_out():
+    rng = np.random.default_rng(3)
+    q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
+    offsets = np.array([0, 70, 70, 200])
+    x = q(rng.standard_normal((200, 128)))
+    w1 = q(rng.standard_normal((3, 256, 128)) * 0.05)
+    w2 = q(rng.standard_normal((3, 128, 256)) * 0.05)
+    y = _run_ffn(x, offsets, w1, w2, None, None, "bf16", y_f32=True)
+    ref = np.concatenate([oracle.expert_mlp(x[a:b], w1[g], w2[g])
+                          for g, (a, b) in enumerate(zip(offsets[:-1], offsets[1:]))
+                          if b > a])
+    assert_close(y, ref, "bf16", "grouped ffn fp32 out")
+
+
+@pytest.mark.parametrize("N,D,Kmax,dtype,shared", [
+    (1, 64, 2, "bf16", True), (1000, 1152, 2, "bf16", True),
+    (300, 72, 5, "f32", False), (129, 256, 16, "bf16", True)])
+def test_combine(N, D, Kmax, dtype, shared):
+    _, ops = _ops()
+    rng = np.random.default_rng(N + D)
+    A = N * Kmax
+    q = (lambda a: synth.bf16_to_f32(synth.bf16_bits(a))) if dtype == "bf16" else (lambda a: a)
+    yr = q(rng.standard_normal((A, D)).astype(np.float32))
+    sr = rng.permutation(A).reshape(N, Kmax).astype(np.int32)
+    sr[rng.random((N, Kmax)) < 0.2] = -1
+    w = rng.random((N, Kmax)).astype(np.float32)
+    ysh = q(rng.standard_normal((N, D)).astype(np.float32)) if shared else None
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.empty(N, D, dtype=dt, device=DEV)
+    ops.moe_combine(_bits_tensor(yr, dtype), torch.from_numpy(sr).to(DEV),
+                    torch.from_numpy(w).to(DEV),
+                    None if ysh is None else _bits_tensor(ysh, dtype), y)
+    torch.cuda.synchronize()
+    ref = np.zeros((N, D))
+    for k in range(Kmax):
+        m = sr[:, k] >= 0
+        ref[m] += w[m, k, None].astype(np.float64) * yr[sr[m, k]]
+    if shared:
+        ref += ysh
+    assert_close(to_np(y), ref, dtype, "combine")
+
+
+@pytest.mark.parametrize("B,T,E,K,race,mode", [
+    (1, 1, 1, 1, False, "sequence"), (4, 256, 8, 2, False, "sequence"),
+    (3, 100, 16, 2, True, "sequence"), (5, 64, 5, 3, False, "global"),
+    (2, 1024, 64, 4, True, "global"), (32, 1024, 8, 2, False, "sequence")])
+def test_balance(B, T, E, K, race, mode):
+    _lib, ops = _ops()
+    rng = np.random.default_rng(B * T + E)
+    N = B * T
+    P = oracle.softmax(rng.standard_normal((N, E)))
+    P32 = P.astype(np.float32)
+    if race:
+        idx, _, _ = oracle.race_select(P32.astype(np.float64), K)
+    else:
+        idx, _ = oracle.topk_select(P32.astype(np.float64), K)
+    counts = torch.empty(B, E, dtype=torch.int32, device=DEV)
+    ps = torch.empty(B, E, dtype=torch.float32, device=DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    ops.moe_balance_stats(torch.from_numpy(P32).to(DEV),
+                          torch.from_numpy(idx.astype(np.int32)).to(DEV), B, T,
+                          K, 0.01,
+                          _lib.MOE_BAL_GLOBAL if mode == "global" else _lib.MOE_BAL_PER_SEQUENCE,
+                          counts, ps, loss)
+    torch.cuda.synchronize()
+    c_o, p_o, l_o = oracle.balance_stats(P32.astype(np.float64), idx, B, T, K,
+                                         0.01, mode)
+    assert np.array_equal(to_np(counts), c_o)
+    assert np.allclose(to_np(ps), p_o, rtol=1e-5, atol=1e-5)
+    assert abs(float(to_np(loss)[0]) - l_o) <= 1e-5 * abs(l_o)
