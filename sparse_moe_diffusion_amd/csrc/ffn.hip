@@ -9,16 +9,17 @@
 //   stage 1:  h = gelu_tanh(A W1[g]^T + b1[g])   A rows gathered by index
 //   stage 2:  y = h W2[g]^T + b2[g]
 //
-// bf16 path (the hot path): one workgroup computes a 128-row x 128-feature
-// output tile with 4 waves (2 x 2), each wave a 64 x 64 block made of
-// 2 x 2 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.  Operand
-// tiles of 128 rows x 64 k (16 KB each) are staged in LDS, double-buffered:
-// the next k-tile's global loads are in flight while the current one feeds
-// the matrix cores.  Both operands are k-contiguous rows, so each lane moves
-// 16 bytes per load and per LDS read.  LDS rows are 128 bytes; the 16-byte
-// chunk c of row r is stored at slot c ^ ((r ^ (r >> 3)) & 7), which keeps
-// the MFMA fragment reads (16 rows at one chunk) and the tile writes
-// (8 chunks of 2 rows) free of bank conflicts.
+// bf16 path (the hot path): one workgroup of 8 waves (two per SIMD) owns a
+// 256-token x 256-feature (up-projection) or 256 x 192 (down-projection)
+// output tile; each wave accumulates its 128 x 64 or 64 x 96 slice with
+// v_mfma_f32_32x32x16_bf16 in fp32.  Operands move from HBM straight into
+// LDS with buffer_load ... lds transfers (no staging registers), two
+// 64-wide k stages deep: the next stage is in flight while the current one
+// feeds the matrix cores.  Both operands are k-contiguous rows; LDS rows are
+// 128 bytes and the 16-byte chunk c of row r sits at slot c ^ swz(r), which
+// keeps the MFMA fragment reads free of bank conflicts (measured: zero).
+// Buffer descriptors make out-of-range rows and k chunks load as zero, so
+// ragged tiles need no branches.
 //
 // The MFMA computes out^T: weight rows are the 32-row "A" operand and token
 // rows the "B" operand, so each lane ends up holding 4 consecutive output
@@ -129,8 +130,9 @@ __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
 
 // ------------------------------------------------------- bf16 / MFMA ----
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kGM = 8;
-constexpr int kThreads = 256;
+constexpr int kBK = 64, kGM = 8;
+constexpr int kThreads = 512;   // 8 waves, two per SIMD
+constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -141,42 +143,73 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r,
-                                         uint32_t off) {
-  return __builtin_bit_cast(uint4,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // Offset used for chunks past the k extent: at or beyond every descriptor's
 // num_records, so such loads return zero.
 constexpr uint32_t kOutOfRange = 0xfffffff0u;
 
-template <int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until this wave's global->LDS transfers have landed (vmcnt = 0) and
+// its LDS reads have returned (lgkmcnt = 0), then the workgroup barrier:
+// afterwards every wave may read the new stage and refill the old one.
+__device__ __forceinline__ void stage_barrier() {
+  // s_waitcnt fields on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4],
+  // lgkmcnt [11:8]; expcnt all-ones leaves it unconstrained.
+  __builtin_amdgcn_s_waitcnt(0x7 << 4);
+  __builtin_amdgcn_s_barrier();
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes bytes [16 l, 16 l + 16) of the 1 KB block at `dst`.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst,
+                                      uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, off, 0, 0,
+                                           0);
+}
+
+// Tile of BM token rows x BN output features; waves form a WT x WF grid, each
+// owning (BM/WT) tokens x (BN/WF) features as (BN/WF/32) x (BM/WT/32)
+// v_mfma_f32_32x32x16_bf16 tiles.  LDS holds two k-stages of both operands
+// (rows of 64 k = 128 bytes, 16-byte chunks swizzled by swz(row)).  Each
+// k-stage is loaded by (BM+BN)/8 wave-wide 1 KB DMA transfers; lane l of a
+// transfer covering rows r0..r0+7 fetches chunk (l % 8) ^ swz(r0 + l / 8) of
+// row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
+// workgroup per CU.
+template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(WT * WF == kWaves, "wave grid");
+  constexpr int TB = BM / WT / 32;   // token blocks per wave
+  constexpr int FB = BN / WF / 32;   // feature blocks per wave
+  constexpr int NQ = (BM + BN) / 8 / kWaves;  // DMA transfers per wave per stage
+  constexpr int QA = BM / 8 / kWaves;         // ... of which token rows
+  static_assert((BM + BN) % (8 * kWaves) == 0 && BM % (8 * kWaves) == 0,
+                "whole transfers");
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * kBK];
 
   TileLoc loc;
-  if (!locate_tile<kBM, kBN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
+  if (!locate_tile<BM, BN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
     return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;   // token half of the tile
-  const int wn = wave >> 1;  // feature half of the tile
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave % WT;   // token slice of the tile
+  const int wf = wave / WT;   // feature slice of the tile
   const int Kd = p.Kd;
   const uint32_t row_bytes = static_cast<uint32_t>(Kd) * 2u;
 
   // Token rows: gathered through a_index from the whole activation matrix,
-  // or read in place starting at the tile's first row.  Rows past the group
-  // end re-read the tile's first row; their results are never stored.
+  // or read in place from the tile's first row.  Rows past the group end
+  // re-read the tile's first row; their results are never stored.
   const bool gather = p.a_index != nullptr;
   const uint16_t* a_base = static_cast<const uint16_t*>(p.a) +
                            (gather ? int64_t(0) : loc.row0 * Kd);
   const uint32_t a_bytes =
       gather ? kOutOfRange
-             : static_cast<uint32_t>(min<int64_t>(loc.row_end - loc.row0, kBM)) *
+             : static_cast<uint32_t>(min<int64_t>(loc.row_end - loc.row0, BM)) *
                    row_bytes;
   const __amdgpu_buffer_rsrc_t rsA =
       make_rsrc(reinterpret_cast<const void*>(
@@ -186,120 +219,109 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
   const uint16_t* w_base = static_cast<const uint16_t*>(p.w) +
                            (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd;
   const uint32_t w_bytes =
-      static_cast<uint32_t>(min(p.Nd - loc.n0, kBN)) * row_bytes;
+      static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(w_base))),
                 __builtin_amdgcn_readfirstlane(w_bytes));
 
-  // This thread's 4 + 4 global 16-byte chunks per k-tile: tile rows
-  // (tid >> 3) + 32 i, chunk tid & 7.
-  const int lrow = tid >> 3, lkc = tid & 7;
-#define MOE_X4(M) M(0) M(1) M(2) M(3)
-#define MOE_ROWSETUP(I)                                                      \
-  uint32_t a_off##I, b_off##I;                                               \
-  int st_off##I;                                                             \
-  {                                                                          \
-    const int row = lrow + 32 * I;                                           \
-    const int64_t grow = loc.row0 + row;                                     \
-    const bool valid = grow < loc.row_end;                                   \
-    if (gather)                                                              \
-      a_off##I = static_cast<uint32_t>(p.a_index[valid ? grow : loc.row0]) * \
-                     row_bytes + lkc * 16u;                                  \
-    else                                                                     \
-      a_off##I = static_cast<uint32_t>(valid ? row : 0) * row_bytes +        \
-                 lkc * 16u;                                                  \
-    b_off##I = static_cast<uint32_t>(row) * row_bytes + lkc * 16u;           \
-    st_off##I = row * kBK + ((lkc ^ swz(row)) * 8);                          \
-  }
-  MOE_X4(MOE_ROWSETUP)
-#undef MOE_ROWSETUP
-
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-
-  // Fragment read offsets: row (lane & 31) of each 32-row block, chunk
-  // 2 ks + (lane >> 5) of the 64-wide k-tile.
-  int fa_row[2], fb_row[2];
+  // Per DMA transfer q of this wave: byte offset of this lane's chunk at
+  // k = 0, the chunk's k index, and the LDS destination (elements).
+  uint32_t goff[NQ];
+  int gk[NQ];
+  int ldst[NQ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    fa_row[i] = wn * 64 + i * 32 + (lane & 31);
-    fb_row[i] = wm * 64 + i * 32 + (lane & 31);
+  for (int q = 0; q < NQ; ++q) {
+    const int t = wave + kWaves * q;          // transfer index in the stage
+    const bool isA = q < QA;                  // uniform across the wave
+    const int r0 = (isA ? t : t - BM / 8) * 8;
+    const int r = r0 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    gk[q] = c * 8;
+    ldst[q] = r0 * kBK;
+    if (isA) {
+      const int64_t grow = loc.row0 + r;
+      const bool valid = grow < loc.row_end;
+      const uint32_t src =
+          gather ? static_cast<uint32_t>(p.a_index[valid ? grow : loc.row0])
+                 : static_cast<uint32_t>(valid ? r : 0);
+      goff[q] = src * row_bytes + c * 16u;
+    } else {
+      goff[q] = static_cast<uint32_t>(r) * row_bytes + c * 16u;
+    }
   }
+
+  const int nk = (Kd + kBK - 1) / kBK;
+  auto issue = [&](int kt, uint16_t* dA, uint16_t* dB) {
+    const bool full = (kt + 1) * kBK <= Kd;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bool isA = q < QA;
+      uint32_t off = goff[q] + static_cast<uint32_t>(kt) * (kBK * 2);
+      if (!full && kt * kBK + gk[q] >= Kd) off = kOutOfRange;
+      dma16(isA ? rsA : rsB, (isA ? dA : dB) + ldst[q], off);
+    }
+  };
+
+  // Fragment rows: (lane & 31) within each 32-row block; k chunk
+  // 2 ks + (lane >> 5) of the 64-wide stage.
   const int khalf = lane >> 5;
+  int fa_row[FB], fb_row[TB];
+#pragma unroll
+  for (int i = 0; i < FB; ++i) fa_row[i] = wf * (BN / WF) + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < TB; ++j) fb_row[j] = wt * (BM / WT) + j * 32 + (lane & 31);
 
-  f32x16 acc[2][2];
+  f32x16 acc[FB][TB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // k-tile KT: chunks past Kd read as zero (out-of-range offset).
-#define MOE_GLOAD1(I)                                                        \
-  ra##I = bload16(rsA, kin_ ? a_off##I + kb_ : kOutOfRange);                 \
-  rb##I = bload16(rsB, kin_ ? b_off##I + kb_ : kOutOfRange);
-#define MOE_GLOAD(KT)                                                        \
-  do {                                                                       \
-    const int kt_ = (KT);                                                    \
-    const bool kin_ = kt_ * kBK + lkc * 8 < Kd;                              \
-    const uint32_t kb_ = static_cast<uint32_t>(kt_) * (kBK * 2);             \
-    MOE_X4(MOE_GLOAD1)                                                       \
-  } while (0)
-#define MOE_LSTORE1(I)                                                       \
-  *reinterpret_cast<uint4*>(&sA[s_][st_off##I]) = ra##I;                     \
-  *reinterpret_cast<uint4*>(&sB[s_][st_off##I]) = rb##I;
-#define MOE_LSTORE(S)                                                        \
-  do {                                                                       \
-    const int s_ = (S);                                                      \
-    MOE_X4(MOE_LSTORE1)                                                      \
-  } while (0)
-
-  const int nk = (Kd + kBK - 1) / kBK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
-  __syncthreads();
+  issue(0, sA0, sB0);
+  stage_barrier();
   for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) MOE_GLOAD(kt + 1);
+    const bool odd = kt & 1;
+    const uint16_t* cA = odd ? sA1 : sA0;
+    const uint16_t* cB = odd ? sB1 : sB0;
+    if (kt + 1 < nk) issue(kt + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kc = 2 * ks + khalf;
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[FB], bfr[TB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < FB; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(
-            &sB[s][fa_row[i] * kBK + ((kc ^ swz(fa_row[i])) * 8)]);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(
-            &sA[s][fb_row[i] * kBK + ((kc ^ swz(fb_row[i])) * 8)]);
-      }
+            &cB[fa_row[i] * kBK + ((kc ^ swz(fa_row[i])) * 8)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TB; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(
+            &cA[fb_row[j] * kBK + ((kc ^ swz(fb_row[j])) * 8)]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
                                                               acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) MOE_LSTORE(s ^ 1);
-    __syncthreads();
+    // This wave's DMA for the next stage has landed and every wave is done
+    // reading this stage: the next stage may be read and this one refilled.
+    stage_barrier();
   }
-#undef MOE_GLOAD
-#undef MOE_GLOAD1
-#undef MOE_LSTORE
-#undef MOE_LSTORE1
-#undef MOE_X4
 
   // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
-  // weight block i, token (lane & 31) of token block j.
+  // feature block i, token (lane & 31) of token block j.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t row = loc.row0 + wm * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < TB; ++j) {
+    const int64_t row = loc.row0 + wt * (BM / WT) + j * 32 + (lane & 31);
     if (row >= loc.row_end) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < FB; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int f = loc.n0 + wn * 64 + i * 32 + 8 * q + 4 * khalf;
+        const int f = loc.n0 + wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
         if (f >= p.Nd) continue;
         f32x4 v;
         v[0] = acc[i][j][4 * q + 0];
@@ -312,14 +334,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
   }
 }
 
+// Tile shapes: the up-projection (N = H, a multiple of 256 in every DiT-MoE
+// shape) uses 256 x 256 tiles, 2 x 4 waves of 128 tokens x 64 features; the
+// down-projection (N = D, e.g. 1152 = 6 x 192) uses 256 x 192 tiles, 4 x 2
+// waves of 64 tokens x 96 features.
+constexpr int kUpBM = 256, kUpBN = 256, kUpWT = 2, kUpWF = 4;
+constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
+
 // ---------------------------------------------------------- fp32 path ----
 // Plain fp32 FMA tiles (64 x 64 x 16, 4 x 4 outputs per thread) for fp32
 // layers; same tile order and epilogue as the bf16 path.
 
 constexpr int kFM = 64, kFN = 64, kFK = 16;
+constexpr int kF32Threads = 256;
 
 template <int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
+__global__ __launch_bounds__(kF32Threads) void gemm_f32_kernel(GemmParams p) {
   __shared__ float sA[kFK][kFM + 4];
   __shared__ float sB[kFK][kFN + 4];
   TileLoc loc;
@@ -401,36 +431,36 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
                 a.G, a.D, a.H};
   if (a.bf16) {
     if (up) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kEpiGelu, true>),
-                         dim3(tile_grid(p1, kBM, kBN)), dim3(kThreads), 0,
-                         stream, p1);
+      hipLaunchKernelGGL(
+          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF>),
+          dim3(tile_grid(p1, kUpBM, kUpBN)), dim3(kThreads), 0, stream, p1);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
     if (down) {
       if (a.y_f32)
-        hipLaunchKernelGGL((gemm_bf16_kernel<kEpiStore, false>),
-                           dim3(tile_grid(p2, kBM, kBN)), dim3(kThreads), 0,
-                           stream, p2);
+        hipLaunchKernelGGL(
+            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF>),
+            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(kThreads), 0, stream, p2);
       else
-        hipLaunchKernelGGL((gemm_bf16_kernel<kEpiStore, true>),
-                           dim3(tile_grid(p2, kBM, kBN)), dim3(kThreads), 0,
-                           stream, p2);
+        hipLaunchKernelGGL(
+            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF>),
+            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(kThreads), 0, stream, p2);
       return hipGetLastError();
     }
     return hipSuccess;
   }
   if (up) {
     hipLaunchKernelGGL((gemm_f32_kernel<kEpiGelu>),
-                       dim3(tile_grid(p1, kFM, kFN)), dim3(kThreads), 0, stream,
-                       p1);
+                       dim3(tile_grid(p1, kFM, kFN)), dim3(kF32Threads), 0,
+                       stream, p1);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (down) {
     hipLaunchKernelGGL((gemm_f32_kernel<kEpiStore>),
-                       dim3(tile_grid(p2, kFM, kFN)), dim3(kThreads), 0, stream,
-                       p2);
+                       dim3(tile_grid(p2, kFM, kFN)), dim3(kF32Threads), 0,
+                       stream, p2);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -7,12 +7,12 @@
 // candidates.
 //
 // Kernel layout (gfx950):
-//  * gate_kernel: one workgroup = 64 tokens (one per lane) x 4 waves; wave w
-//    accumulates the fp32 logits of its 64 tokens over the w-th quarter of
-//    the features.  Gate weights are wave-uniform and arrive through scalar
-//    loads; each lane streams its own token row with 16-byte loads.  The
-//    four partial sums meet in LDS in a fixed order, then wave 0 runs the
-//    softmax and the top-K selection in registers (ties: lower index).
+//  * gate_mfma_kernel (bf16 tokens): logits on the matrix cores from an
+//    exact three-way bf16 split of the fp32 gate weights, partial sums
+//    added in fp64; see the kernel.  gate_f32_kernel (fp32 tokens): the same
+//    logits from VALU fp64 FMAs.  Both leave 64 tokens' logits in LDS after
+//    a fixed-order sum over 4 waves, and wave 0 runs the fp32 softmax and the
+//    top-K selection in registers, one token per lane (ties: lower index).
 //  * race_select_kernel: one 1024-thread workgroup finds the exact K*N-th
 //    largest probability key by an MSB-first radix select (4 passes of 8
 //    bits, per-wave LDS histograms) and the flat index of the last kept
@@ -29,78 +29,21 @@ namespace {
 constexpr int kGateTokens = 64;
 constexpr int kGateWaves = 4;
 
-template <bool BF16>
-__device__ __forceinline__ void load_x8(const void* x, int64_t row, int D,
-                                        int chunk, float* f) {
-  if constexpr (BF16) {
-    const uint4 v =
-        reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) +
-                                       row * D)[chunk];
-    unpack8(v, f);
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(
-        static_cast<const float*>(x) + row * D) + 2 * chunk;
-    const float4 a = p[0], b = p[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-}
-
 // Selection key of a probability: NaN ranks below every number.
 __device__ __forceinline__ float sel_key(float p) { return p == p ? p : -1.0f; }
 
-template <int EP, bool BF16>
-__global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_kernel(
-    const void* __restrict__ x, const float* __restrict__ wg,
-    const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
-    float* __restrict__ probs, int32_t* __restrict__ idx,
-    float* __restrict__ wout) {
-  __shared__ float part[kGateWaves][EP][kGateTokens];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kGateTokens + lane;
-  const bool valid = t < N;
-  const int nchunk = D / 8;
-  const int c0 = wave * nchunk / kGateWaves;
-  const int c1 = (wave + 1) * nchunk / kGateWaves;
-
-  float acc[EP];
-#pragma unroll
-  for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
-
-  if (valid) {
-#pragma unroll 2
-    for (int c = c0; c < c1; ++c) {
-      float xf[8];
-      load_x8<BF16>(x, t, D, c, xf);
-#pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        if (e < E) {
-          const float* w = wg + static_cast<int64_t>(e) * D + 8 * c;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[e] = fmaf(xf[j], w[j], acc[e]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < EP; ++e) part[wave][e][lane] = acc[e];
-  __syncthreads();
-  if (wave != 0 || !valid) return;
-
-  float p[EP];
+// Softmax over the E logits of one token (one lane) and, for top-K routing,
+// the K experts first in (probability descending, index ascending) order.
+template <int EP>
+__device__ __forceinline__ void softmax_topk(float (&p)[EP], int64_t t, int E,
+                                             int K, bool topk,
+                                             float* __restrict__ probs,
+                                             int32_t* __restrict__ idx,
+                                             float* __restrict__ wout) {
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < EP; ++e) {
-    if (e < E) {
-      float l = part[0][e][lane] + part[1][e][lane];
-      l += part[2][e][lane];
-      l += part[3][e][lane];
-      if (bias != nullptr) l += bias[e];
-      p[e] = l;
-      m = fmaxf(m, l);
-    }
-  }
+  for (int e = 0; e < EP; ++e)
+    if (e < E) m = fmaxf(m, p[e]);
   float s = 0.0f;
 #pragma unroll
   for (int e = 0; e < EP; ++e) {
@@ -117,7 +60,6 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_kernel(
     }
   }
   if (!topk) return;
-
   uint64_t taken = 0;
   for (int k = 0; k < K; ++k) {
     int best = -1;
@@ -137,6 +79,172 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_kernel(
     idx[t * K + k] = best;
     wout[t * K + k] = bp;
   }
+}
+
+// fp32 tokens: VALU dot products with fp64 accumulation.  One workgroup =
+// 64 tokens (one per lane) x 4 waves; wave w covers the w-th quarter of the
+// features, with the gate weights as wave-uniform scalar loads.
+template <int EP>
+__global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
+    float* __restrict__ probs, int32_t* __restrict__ idx,
+    float* __restrict__ wout) {
+  __shared__ double red[kGateTokens][EP];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kGateTokens + lane;
+  const bool valid = t < N;
+  const int c0 = wave * D / kGateWaves, c1 = (wave + 1) * D / kGateWaves;
+  double acc[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) acc[e] = 0.0;
+  if (valid) {
+    for (int c = c0; c < c1; ++c) {
+      const double xv = x[t * D + c];
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        if (e < E) acc[e] = fma(xv, static_cast<double>(wg[e * D + c]), acc[e]);
+    }
+  }
+  // fixed-order cross-wave sum
+  for (int w = 0; w < kGateWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        red[lane][e] = (w == 0) ? acc[e] : red[lane][e] + acc[e];
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || !valid) return;
+  float p[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e)
+    if (e < E)
+      p[e] = static_cast<float>(red[lane][e] + (bias ? bias[e] : 0.0));
+  softmax_topk<EP>(p, t, E, K, topk != 0, probs, idx, wout);
+}
+
+// bf16 tokens on the matrix cores.  The fp32 gate weight is split exactly
+// into three bf16 parts, w = hi + mid + lo (each remainder of a
+// round-to-nearest-even has at most 16, then 8, significant bits), so
+// x * w = x*hi + x*mid + x*lo with every product exact in fp32.  One
+// v_mfma_f32_16x16x32_bf16 per part sums a 32-wide k slice for 16 experts x
+// 16 tokens; the fp32 slice sums are added in fp64, and the logit is
+// rounded once to fp32.
+//
+// Workgroup: 64 tokens x 4 waves; wave w covers the w-th quarter of the
+// 32-wide k slices for all 64 tokens (4 groups of 16).  MFMA operands come
+// straight from memory: lane l loads 8 consecutive features (16 bytes) of
+// token (l % 16) and the matching 8 gate weights of expert (l % 16); lane
+// l's results are token (l % 16), experts 4 (l / 16) + 0..3.
+template <int EB>
+__global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
+    float* __restrict__ probs, int32_t* __restrict__ idx,
+    float* __restrict__ wout) {
+  constexpr int EP = 16 * EB;
+  __shared__ double red[kGateTokens][EP];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGateTokens;
+  const int nsteps = (D + 31) / 32;
+  const int s0 = wave * nsteps / kGateWaves;
+  const int s1 = (wave + 1) * nsteps / kGateWaves;
+
+  bool tok_ok[4];
+  const uint16_t* xrow[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t t = t0 + g * 16 + col;
+    tok_ok[g] = t < N;
+    xrow[g] = x + (tok_ok[g] ? t : 0) * D;
+  }
+  bool e_ok[EB];
+  const float* wrow[EB];
+#pragma unroll
+  for (int b = 0; b < EB; ++b) {
+    const int e = b * 16 + col;
+    e_ok[b] = e < E;
+    wrow[b] = wg + static_cast<int64_t>(e_ok[b] ? e : 0) * D;
+  }
+
+  double acc[4][EB][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int b = 0; b < EB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[g][b][i] = 0.0;
+
+  for (int st = s0; st < s1; ++st) {
+    const int k0 = st * 32 + kq * 8;
+    const bool k_ok = k0 < D;
+    bf16x8 whi[EB], wmid[EB], wlo[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+      float4 wa = make_float4(0, 0, 0, 0), wb = wa;
+      if (e_ok[b] && k_ok) {
+        wa = *reinterpret_cast<const float4*>(wrow[b] + k0);
+        wb = *reinterpret_cast<const float4*>(wrow[b] + k0 + 4);
+      }
+      const float w8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      uint32_t h[4], m[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = w8[2 * j], a1 = w8[2 * j + 1];
+        h[j] = pack_bf16x2(a0, a1);
+        const float r0 = a0 - bf16_lo(h[j]), r1 = a1 - bf16_hi(h[j]);
+        m[j] = pack_bf16x2(r0, r1);
+        const float q0 = r0 - bf16_lo(m[j]), q1 = r1 - bf16_hi(m[j]);
+        l[j] = pack_bf16x2(q0, q1);
+      }
+      whi[b] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+      wmid[b] = __builtin_bit_cast(bf16x8, make_uint4(m[0], m[1], m[2], m[3]));
+      wlo[b] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint4 xv = make_uint4(0, 0, 0, 0);
+      if (tok_ok[g] && k_ok) xv = *reinterpret_cast<const uint4*>(xrow[g] + k0);
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+      for (int b = 0; b < EB; ++b) {
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[b], xb, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wmid[b], xb, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[b], xb, a, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][b][i] += static_cast<double>(a[i]);
+      }
+    }
+  }
+  // fixed-order cross-wave sum into red[token][expert]
+  for (int w = 0; w < kGateWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int b = 0; b < EB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            double& r = red[g * 16 + col][b * 16 + kq * 4 + i];
+            r = (w == 0) ? acc[g][b][i] : r + acc[g][b][i];
+          }
+    }
+    __syncthreads();
+  }
+  const int64_t t = t0 + lane;
+  if (wave != 0 || t >= N) return;
+  float p[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e)
+    if (e < E)
+      p[e] = static_cast<float>(red[lane][e] + (bias ? bias[e] : 0.0));
+  softmax_topk<EP>(p, t, E, K, topk != 0, probs, idx, wout);
 }
 
 // ---------------------------------------------------------- Expert Race --
@@ -255,19 +363,21 @@ __global__ __launch_bounds__(256) void race_emit_kernel(
   }
 }
 
-template <int EP>
-hipError_t launch_gate_ep(const void* x, bool bf16, const float* wg,
+template <int EB>
+hipError_t launch_gate_eb(const void* x, bool bf16, const float* wg,
                           const float* bias, int64_t N, int D, int E, int K,
                           bool topk, float* probs, int32_t* idx, float* w,
                           hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(ceil_div(N, kGateTokens)));
   const dim3 block(kGateTokens * kGateWaves);
   if (bf16)
-    hipLaunchKernelGGL((gate_kernel<EP, true>), grid, block, 0, stream, x, wg,
-                       bias, N, D, E, K, topk ? 1 : 0, probs, idx, w);
+    hipLaunchKernelGGL((gate_mfma_kernel<EB>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), wg, bias, N, D, E, K,
+                       topk ? 1 : 0, probs, idx, w);
   else
-    hipLaunchKernelGGL((gate_kernel<EP, false>), grid, block, 0, stream, x,
-                       wg, bias, N, D, E, K, topk ? 1 : 0, probs, idx, w);
+    hipLaunchKernelGGL((gate_f32_kernel<16 * EB>), grid, block, 0, stream,
+                       static_cast<const float*>(x), wg, bias, N, D, E, K,
+                       topk ? 1 : 0, probs, idx, w);
   return hipGetLastError();
 }
 
@@ -278,17 +388,14 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
                        bool topk, float* probs, int32_t* idx, float* w,
                        hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  if (E <= 8)
-    return launch_gate_ep<8>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
-                             idx, w, stream);
   if (E <= 16)
-    return launch_gate_ep<16>(x, x_bf16, w_gate, bias, N, D, E, K, topk,
-                              probs, idx, w, stream);
+    return launch_gate_eb<1>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
+                             idx, w, stream);
   if (E <= 32)
-    return launch_gate_ep<32>(x, x_bf16, w_gate, bias, N, D, E, K, topk,
-                              probs, idx, w, stream);
-  return launch_gate_ep<64>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
-                            idx, w, stream);
+    return launch_gate_eb<2>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
+                             idx, w, stream);
+  return launch_gate_eb<4>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
+                           idx, w, stream);
 }
 
 size_t race_workspace_bytes() { return 256; }
