@@ -26,6 +26,8 @@ FLAGS = [
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # a variable read before it is set is an error, not a warning
+    "-Werror=uninitialized", "-Werror=sometimes-uninitialized",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
