@@ -36,7 +36,52 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes five "
+                         "times (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+# Measured HBM traffic of the dominant kernel lives in a profile summary,
+# together with the SHA-256 of the kernel source it was measured on; a
+# changed source means the figure no longer applies.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_up_xl_8e2a_512.md")
+FFN_SOURCE = os.path.join(ROOT, "sparse_moe_diffusion_amd", "csrc", "ffn.hip")
+
+
+def measured_traffic():
+    """Bytes per launch of the stage-1 GEMM from the counter summary, or
+    None when it is missing or was taken on another version of ffn.hip."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().strip("-").strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip().lower()] = v.strip().strip("`")
+    want = fields.get("ffn.hip sha256")
+    val = fields.get("traffic bytes per launch")
+    if not want or not val:
+        return None
+    have = hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()
+    return float(val) if have == want else None
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}),
+          flush=True)
 
 
 def kernel_work(cfg, gather: bool):
@@ -92,6 +137,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; "
                           "--gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import synth
     from sparse_moe_diffusion_amd import _lib, layer
@@ -195,7 +243,8 @@ def main():
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "flops_per_launch": dom_flops,
                      "avg_launch_ms": round(dom_ms, 4),
-                     "traffic": None},
+                     "traffic": (measured_traffic() if dom is up and
+                                 cfg.name == "xl_8e2a_512" and gather else None)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

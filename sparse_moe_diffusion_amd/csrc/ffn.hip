@@ -15,11 +15,14 @@
 // v_mfma_f32_32x32x16_bf16 in fp32.  Operands move from HBM straight into
 // LDS with buffer_load ... lds transfers (no staging registers), two
 // 64-wide k stages deep: the next stage is in flight while the current one
-// feeds the matrix cores.  Both operands are k-contiguous rows; LDS rows are
-// 128 bytes and the 16-byte chunk c of row r sits at slot c ^ swz(r), which
-// keeps the MFMA fragment reads free of bank conflicts (measured: zero).
-// Buffer descriptors make out-of-range rows and k chunks load as zero, so
-// ragged tiles need no branches.
+// feeds the matrix cores, and its transfers are spread between the MFMAs.
+// Both operands are k-contiguous rows; LDS rows are 128 bytes and the
+// 16-byte chunk c of row r sits at slot c ^ swz(r), which keeps the MFMA
+// fragment reads free of bank conflicts (measured: zero).  Fragments are
+// read one k step ahead of the MFMAs that use them.  Buffer descriptors
+// make out-of-range rows and k chunks load as zero, so ragged tiles need no
+// branches.  With bf16 output the finished tile goes through LDS and leaves
+// in row-contiguous 16-byte stores.
 //
 // The MFMA computes out^T: weight rows are the 32-row "A" operand and token
 // rows the "B" operand, so each lane ends up holding 4 consecutive output
@@ -56,13 +59,12 @@ struct TileLoc {
 };
 
 // tanh-GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)),
-// z = sqrt(2/pi) (u + 0.044715 u^3); exp through the hardware exp2.
+// z = sqrt(2/pi) (u + 0.044715 u^3).  The exponent -2 z log2(e) is formed as
+// u (c1 + c2 u^2) with the constants folded, then the hardware exp2.
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float kC = 0.7978845608028654f;   // sqrt(2/pi)
-  const float kA = 0.044715f;
-  const float kLog2e = 1.4426950408889634f;
-  const float z = kC * fmaf(kA * u, u * u, u);
-  const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * z);
+  constexpr float kC1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
+  constexpr float kC2 = kC1 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(u * fmaf(kC2, u * u, kC1));
   return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
@@ -106,9 +108,10 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int L,
   return false;
 }
 
-template <int EPI, bool OUT_BF16>
-__device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
-                                       int f, f32x4 v) {
+// Bias and activation of 4 consecutive output features f..f+3 of group g.
+template <int EPI>
+__device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g, int f,
+                                         f32x4 v) {
   if (p.bias != nullptr) {
     const float* b = p.bias + static_cast<int64_t>(g) * p.Nd + f;
     v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
@@ -117,6 +120,13 @@ __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
     v[0] = gelu_tanh(v[0]); v[1] = gelu_tanh(v[1]);
     v[2] = gelu_tanh(v[2]); v[3] = gelu_tanh(v[3]);
   }
+  return v;
+}
+
+template <int EPI, bool OUT_BF16>
+__device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
+                                       int f, f32x4 v) {
+  v = finish4<EPI>(p, g, f, v);
   if constexpr (OUT_BF16) {
     uint2 o;
     o.x = pack_bf16x2(v[0], v[1]);
@@ -131,8 +141,6 @@ __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
 // ------------------------------------------------------- bf16 / MFMA ----
 
 constexpr int kBK = 64, kGM = 8;
-constexpr int kThreads = 512;   // 8 waves, two per SIMD
-constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -160,11 +168,19 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// writes bytes [16 l, 16 l + 16) of the 1 KB block at `dst`.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst,
-                                      uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst), 16, off, 0, 0,
-                                           0);
+// writes bytes [16 l, 16 l + 16) of the 1 KB block at `dst`.  The LDS
+// destination reaches the instruction as a plain wave-uniform 32-bit
+// address, so the compiler cannot attribute the transfer to a particular
+// LDS region and adds no waits of its own before LDS reads (its alias
+// tracking would otherwise wait for transfers into other stages); the
+// kernel orders every transfer against its readers explicitly (vmcnt wait,
+// then workgroup barrier).
+__device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t r,
+                                                uint16_t* dst, uint32_t off) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((lds_void*)(dst))));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (lds_void*)(static_cast<uintptr_t>(a)), 16, off, 0, 0, 0);
 }
 
 // Tile of BM token rows x BN output features; waves form a WT x WF grid, each
@@ -176,18 +192,26 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* dst,
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
-  static_assert(WT * WF == kWaves, "wave grid");
+__global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int kWaves = WT * WF;
   constexpr int TB = BM / WT / 32;   // token blocks per wave
   constexpr int FB = BN / WF / 32;   // feature blocks per wave
   constexpr int NQ = (BM + BN) / 8 / kWaves;  // DMA transfers per wave per stage
   constexpr int QA = BM / 8 / kWaves;         // ... of which token rows
   static_assert((BM + BN) % (8 * kWaves) == 0 && BM % (8 * kWaves) == 0,
                 "whole transfers");
-  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * kBK];
+  // LDS: the two k stages during the main loop; afterwards (bf16 output)
+  // the finished tile, row-major with a 16-byte pad per row, so that it
+  // leaves in whole-row 16-byte-per-lane stores.
+  constexpr int kStageBytes = 2 * (BM + BN) * kBK * 2;
+  constexpr int kOutPitch = BN + 8;   // staged row pitch, elements
+  constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
+  __shared__ __attribute__((aligned(1024)))
+  uint16_t lds[(kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2];
+  uint16_t* const sA0 = lds;
+  uint16_t* const sA1 = sA0 + BM * kBK;
+  uint16_t* const sB0 = sA1 + BM * kBK;
+  uint16_t* const sB1 = sB0 + BN * kBK;
 
   TileLoc loc;
   if (!locate_tile<BM, BN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
@@ -252,25 +276,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
   }
 
   const int nk = (Kd + kBK - 1) / kBK;
-  auto issue = [&](int kt, uint16_t* dA, uint16_t* dB) {
-    const bool full = (kt + 1) * kBK <= Kd;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const bool isA = q < QA;
-      uint32_t off = goff[q] + static_cast<uint32_t>(kt) * (kBK * 2);
-      if (!full && kt * kBK + gk[q] >= Kd) off = kOutOfRange;
-      dma16(isA ? rsA : rsB, (isA ? dA : dB) + ldst[q], off);
-    }
-  };
 
-  // Fragment rows: (lane & 31) within each 32-row block; k chunk
-  // 2 ks + (lane >> 5) of the 64-wide stage.
+// DMA transfers Q0 <= q < Q1 of k-stage KT into the LDS buffers DA / DB.
+#define MOE_ISSUE(KT, DA, DB, Q0, Q1)                                        \
+  do {                                                                       \
+    const int ikt_ = (KT);                                                   \
+    const bool full_ = (ikt_ + 1) * kBK <= Kd;                               \
+    _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                    \
+      const bool isA_ = q < QA;                                              \
+      uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);     \
+      if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;            \
+      dma16_untracked(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
+    }                                                                        \
+  } while (0)
+
+  // Fragment rows: (lane & 31) within each 32-row block; at k step ks of a
+  // stage the lane reads chunk kc = 2 ks + (lane >> 5), stored at slot
+  // kc ^ swz(row).  Element offsets for all four k steps are precomputed.
   const int khalf = lane >> 5;
-  int fa_row[FB], fb_row[TB];
+  int oa[FB][4], ob[TB][4];
 #pragma unroll
-  for (int i = 0; i < FB; ++i) fa_row[i] = wf * (BN / WF) + i * 32 + (lane & 31);
+  for (int i = 0; i < FB; ++i) {
+    const int row = wf * (BN / WF) + i * 32 + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < TB; ++j) fb_row[j] = wt * (BM / WT) + j * 32 + (lane & 31);
+    for (int ks = 0; ks < 4; ++ks)
+      oa[i][ks] = row * kBK + (((2 * ks + khalf) ^ swz(row)) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int row = wt * (BM / WT) + j * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ob[j][ks] = row * kBK + (((2 * ks + khalf) ^ swz(row)) * 8);
+  }
 
   f32x16 acc[FB][TB];
 #pragma unroll
@@ -280,55 +318,153 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  issue(0, sA0, sB0);
+  // Two fragment register sets: while the MFMAs of k step ks run on one,
+  // the LDS reads of step ks + 1 fill the other.
+  bf16x8 fa0[FB], fb0[TB], fa1[FB], fb1[TB];
+
+#define MOE_FRAGS(FA, FB_, SA, SB, KS)                                       \
+  do {                                                                       \
+    _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                   \
+        *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][KS]]);                  \
+    _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                  \
+        *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][KS]]);                  \
+  } while (0)
+
+#define MOE_MFMAS(FA, FB_, I0, I1)                                           \
+  do {                                                                       \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i)                      \
+      _Pragma("unroll") for (int j = 0; j < TB; ++j) acc[i][j] =             \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[i], FB_[j], acc[i][j],  \
+                                                  0, 0, 0);                  \
+  } while (0)
+
+  // One 64-wide k stage read from CA / CB while stage KT + 1 streams into
+  // NA / NB.  The order of the groups is pinned with scheduling barriers.
+  // The next stage's transfers are spread over the MFMAs of the first two
+  // k steps (one transfer per MFMA_PER_DMA MFMAs): issued in one burst they
+  // fill the address unit's queue and stall every wave at issue, leaving
+  // the matrix cores idle.  The last k step's MFMAs straddle the stage
+  // barrier so that the matrix cores stay busy while the next stage's first
+  // fragments are read.
+  constexpr int kQH = (NQ + 1) / 2;                 // transfers in k step 0
+  constexpr int kMfmaPerDma = (FB * TB) / kQH > 0 ? (FB * TB) / kQH : 1;
+#define MOE_INTERLEAVE(NDMA)                                                 \
+  do {                                                                       \
+    _Pragma("unroll") for (int d_ = 0; d_ < (NDMA); ++d_) {                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                     \
+    }                                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x008, FB * TB, 0);                 \
+  } while (0)
+
+#define MOE_STAGE(KT, CA, CB, NA, NB)                                        \
+  do {                                                                       \
+    const int skt_ = (KT);                                                   \
+    const bool more_ = skt_ + 1 < nk;                                        \
+    MOE_FRAGS(fa1, fb1, CA, CB, 1);                                          \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_MFMAS(fa0, fb0, 0, FB);                                              \
+    MOE_ISSUE(skt_ + 1, NA, NB, 0, kQH);                                     \
+    MOE_INTERLEAVE(kQH);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_FRAGS(fa0, fb0, CA, CB, 2);                                          \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_MFMAS(fa1, fb1, 0, FB);                                              \
+    MOE_ISSUE(skt_ + 1, NA, NB, kQH, NQ);                                    \
+    MOE_INTERLEAVE(NQ - kQH);                                                \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_FRAGS(fa1, fb1, CA, CB, 3);                                          \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_MFMAS(fa0, fb0, 0, FB);                                              \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_MFMAS(fa1, fb1, 0, FB - FB / 2);                                     \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    if (more_) {                                                             \
+      stage_barrier();                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                     \
+      MOE_FRAGS(fa0, fb0, NA, NB, 0);                                        \
+    }                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    MOE_MFMAS(fa1, fb1, FB - FB / 2, FB);                                    \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+  } while (0)
+
+  MOE_ISSUE(0, sA0, sB0, 0, NQ);
   stage_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool odd = kt & 1;
-    const uint16_t* cA = odd ? sA1 : sA0;
-    const uint16_t* cB = odd ? sB1 : sB0;
-    if (kt + 1 < nk) issue(kt + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kc = 2 * ks + khalf;
-      bf16x8 af[FB], bfr[TB];
-#pragma unroll
-      for (int i = 0; i < FB; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(
-            &cB[fa_row[i] * kBK + ((kc ^ swz(fa_row[i])) * 8)]);
-#pragma unroll
-      for (int j = 0; j < TB; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(
-            &cA[fb_row[j] * kBK + ((kc ^ swz(fb_row[j])) * 8)]);
-#pragma unroll
-      for (int i = 0; i < FB; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    // This wave's DMA for the next stage has landed and every wave is done
-    // reading this stage: the next stage may be read and this one refilled.
-    stage_barrier();
+  MOE_FRAGS(fa0, fb0, sA0, sB0, 0);
+  // Stages alternate between the two buffers.  The last stage's transfers
+  // address k-stage nk, which lies wholly past Kd: they load zeros into the
+  // idle buffer (no branch around them, so they interleave with the MFMAs)
+  // and are drained before the epilogue.
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_STAGE(kt, sA0, sB0, sA1, sB1);
+    if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA0, sB0);
   }
+  __builtin_amdgcn_s_waitcnt(0x7 << 4);
+#undef MOE_STAGE
+#undef MOE_INTERLEAVE
+#undef MOE_MFMAS
+#undef MOE_FRAGS
+#undef MOE_ISSUE
 
   // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
   // feature block i, token (lane & 31) of token block j.
+  if constexpr (OUT_BF16) {
+    // Every wave is done with the stages: stage the tile in LDS.
+    stage_barrier();
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int64_t row = loc.row0 + wt * (BM / WT) + j * 32 + (lane & 31);
-    if (row >= loc.row_end) continue;
+    for (int j = 0; j < TB; ++j) {
+      const int t = wt * (BM / WT) + j * 32 + (lane & 31);
+      if (loc.row0 + t >= loc.row_end) continue;
 #pragma unroll
-    for (int i = 0; i < FB; ++i) {
+      for (int i = 0; i < FB; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = loc.n0 + wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
-        if (f >= p.Nd) continue;
-        f32x4 v;
-        v[0] = acc[i][j][4 * q + 0];
-        v[1] = acc[i][j][4 * q + 1];
-        v[2] = acc[i][j][4 * q + 2];
-        v[3] = acc[i][j][4 * q + 3];
-        store4<EPI, OUT_BF16>(p, loc.g, row, f, v);
+        for (int q = 0; q < 4; ++q) {
+          const int fl = wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
+          if (loc.n0 + fl >= p.Nd) continue;
+          f32x4 v;
+          v[0] = acc[i][j][4 * q + 0];
+          v[1] = acc[i][j][4 * q + 1];
+          v[2] = acc[i][j][4 * q + 2];
+          v[3] = acc[i][j][4 * q + 3];
+          v = finish4<EPI>(p, loc.g, loc.n0 + fl, v);
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(&lds[t * kOutPitch + fl]) = o;
+        }
+      }
+    }
+    stage_barrier();
+    // Copy out: 16 bytes per lane, consecutive lanes along a row.
+    constexpr int kChunks = BN / 8;
+    uint16_t* const c = static_cast<uint16_t*>(p.c);
+    for (int idx = tid; idx < BM * kChunks; idx += 64 * kWaves) {
+      const int r = idx / kChunks;
+      const int f = loc.n0 + (idx - r * kChunks) * 8;
+      const int64_t row = loc.row0 + r;
+      if (row < loc.row_end && f < p.Nd)
+        *reinterpret_cast<uint4*>(c + row * p.Nd + f) =
+            *reinterpret_cast<const uint4*>(&lds[r * kOutPitch + (f - loc.n0)]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int64_t row = loc.row0 + wt * (BM / WT) + j * 32 + (lane & 31);
+      if (row >= loc.row_end) continue;
+#pragma unroll
+      for (int i = 0; i < FB; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = loc.n0 + wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
+          if (f >= p.Nd) continue;
+          f32x4 v;
+          v[0] = acc[i][j][4 * q + 0];
+          v[1] = acc[i][j][4 * q + 1];
+          v[2] = acc[i][j][4 * q + 2];
+          v[3] = acc[i][j][4 * q + 3];
+          store4<EPI, OUT_BF16>(p, loc.g, row, f, v);
+        }
       }
     }
   }
@@ -433,7 +569,8 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
     if (up) {
       hipLaunchKernelGGL(
           (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF>),
-          dim3(tile_grid(p1, kUpBM, kUpBN)), dim3(kThreads), 0, stream, p1);
+          dim3(tile_grid(p1, kUpBM, kUpBN)), dim3(64 * kUpWT * kUpWF), 0,
+          stream, p1);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
@@ -441,11 +578,13 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
       if (a.y_f32)
         hipLaunchKernelGGL(
             (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF>),
-            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(kThreads), 0, stream, p2);
+            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
+            stream, p2);
       else
         hipLaunchKernelGGL(
             (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF>),
-            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(kThreads), 0, stream, p2);
+            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
+            stream, p2);
       return hipGetLastError();
     }
     return hipSuccess;
