@@ -6,9 +6,10 @@
 // P(t,i) the token's probability of expert i.
 //
 //  * balance_seq_kernel: workgroup b owns image b.  Thread (r, e) of an
-//    R x E grid sums tokens t = r, r+R, ... of expert e in order; the R
-//    partial sums of each expert are then added in row order by one thread.
-//    Counts are exact integers.  Same inputs, same bits.
+//    R x E grid (R = 1024 / E) sums tokens t = r, r+R, ... of expert e in
+//    order; the R partial sums of each expert are then added by a
+//    fixed-order tree in LDS.  Counts are exact integers.  Same inputs, same
+//    bits.
 //  * balance_loss_kernel: one workgroup turns counts and prob_sums into the
 //    loss, summing in a fixed order (per image, then over images).
 #include "common.hpp"
@@ -19,20 +20,34 @@ namespace moe {
 namespace {
 
 constexpr int kBalThreads = 256;
+constexpr int kSeqThreads = 1024;
 
-__global__ __launch_bounds__(kBalThreads) void balance_seq_kernel(
+__global__ __launch_bounds__(kSeqThreads) void balance_seq_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx, int T,
     int E, int Kmax, int32_t* __restrict__ counts, float* __restrict__ psum) {
-  __shared__ float sp[kBalThreads];
-  __shared__ int32_t sc[kBalThreads];
-  const int R = kBalThreads / E;
+  __shared__ float sp[kSeqThreads];
+  __shared__ int32_t sc[kSeqThreads];
+  const int R = kSeqThreads / E;
   const int r = threadIdx.x / E;
   const int e = threadIdx.x - r * E;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * T;
   float p = 0.0f;
   int32_t c = 0;
   if (r < R) {
-    for (int t = r; t < T; t += R) {
+    // tokens r, r + R, ...; unrolled so that several loads are in flight
+    int t = r;
+    for (; t + 3 * R < T; t += 4 * R) {
+      float q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = probs[(t0 + t + u * R) * E + e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p += q[u];
+        const int64_t tt = t0 + t + u * R;
+        for (int k = 0; k < Kmax; ++k) c += (idx[tt * Kmax + k] == e) ? 1 : 0;
+      }
+    }
+    for (; t < T; t += R) {
       const int64_t tt = t0 + t;
       p += probs[tt * E + e];
       for (int k = 0; k < Kmax; ++k) c += (idx[tt * Kmax + k] == e) ? 1 : 0;
@@ -41,15 +56,17 @@ __global__ __launch_bounds__(kBalThreads) void balance_seq_kernel(
   sp[threadIdx.x] = p;
   sc[threadIdx.x] = c;
   __syncthreads();
-  if (threadIdx.x < E) {
-    float s = 0.0f;
-    int32_t n = 0;
-    for (int rr = 0; rr < R; ++rr) {
-      s += sp[rr * E + threadIdx.x];
-      n += sc[rr * E + threadIdx.x];
+  // fixed-order tree over the R rows of each expert
+  for (int h = 1; h < R; h *= 2) {
+    if (r < R && (r % (2 * h)) == 0 && r + h < R) {
+      sp[threadIdx.x] += sp[threadIdx.x + h * E];
+      sc[threadIdx.x] += sc[threadIdx.x + h * E];
     }
-    psum[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x] = s;
-    counts[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x] = n;
+    __syncthreads();
+  }
+  if (threadIdx.x < E) {
+    psum[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x] = sp[threadIdx.x];
+    counts[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x] = sc[threadIdx.x];
   }
 }
 
@@ -108,7 +125,7 @@ hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int32_t* counts, float* psum, float* loss,
                           hipStream_t stream) {
   if (B > 0) {
-    hipLaunchKernelGGL(balance_seq_kernel, dim3(B), dim3(kBalThreads), 0,
+    hipLaunchKernelGGL(balance_seq_kernel, dim3(B), dim3(kSeqThreads), 0,
                        stream, probs, idx, T, E, Kmax, counts, psum);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -50,6 +50,8 @@ __device__ __forceinline__ void store8(void* base, int64_t row, int D, int c,
   }
 }
 
+constexpr int kSlotGroup = 4;
+
 template <bool YB, bool SB, bool OB>
 __global__ __launch_bounds__(256) void combine_kernel(
     const void* __restrict__ y_rows, const int32_t* __restrict__ slot_row,
@@ -65,14 +67,31 @@ __global__ __launch_bounds__(256) void combine_kernel(
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int k = 0; k < Kmax; ++k) {
-    const int32_t r = slot_row[t * Kmax + k];
-    if (r < 0) continue;
-    const float wk = w[t * Kmax + k];
-    float v[8];
-    load8<YB>(y_rows, r, D, c, v);
+  // Slots go in groups of kSlotGroup: the group's slot rows, weights and
+  // expert-output rows are all loaded before the first multiply-add, so the
+  // row loads do not wait on one another; the sum stays in slot order.
+  for (int k0 = 0; k0 < Kmax; k0 += kSlotGroup) {
+    int32_t r[kSlotGroup];
+    float wk[kSlotGroup];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
+    for (int q = 0; q < kSlotGroup; ++q) {
+      r[q] = -1;
+      wk[q] = 0.0f;
+      if (k0 + q < Kmax) {
+        r[q] = slot_row[t * Kmax + k0 + q];
+        wk[q] = w[t * Kmax + k0 + q];
+      }
+    }
+    float v[kSlotGroup][8];
+#pragma unroll
+    for (int q = 0; q < kSlotGroup; ++q)
+      if (r[q] >= 0) load8<YB>(y_rows, r[q], D, c, v[q]);
+#pragma unroll
+    for (int q = 0; q < kSlotGroup; ++q)
+      if (r[q] >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wk[q], v[q][j], acc[j]);
+      }
   }
   if (y_shared != nullptr) {
     float v[8];

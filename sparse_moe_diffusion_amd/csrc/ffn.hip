@@ -436,16 +436,20 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       }
     }
     stage_barrier();
-    // Copy out: 16 bytes per lane, consecutive lanes along a row.
+    // Copy out: 16 bytes per lane, consecutive lanes along a row, as
+    // non-temporal stores (the tile is not read again by this kernel; without
+    // the hint the write burst at the end of every tile allocates L2 lines).
     constexpr int kChunks = BN / 8;
     uint16_t* const c = static_cast<uint16_t*>(p.c);
     for (int idx = tid; idx < BM * kChunks; idx += 64 * kWaves) {
       const int r = idx / kChunks;
       const int f = loc.n0 + (idx - r * kChunks) * 8;
       const int64_t row = loc.row0 + r;
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
       if (row < loc.row_end && f < p.Nd)
-        *reinterpret_cast<uint4*>(c + row * p.Nd + f) =
-            *reinterpret_cast<const uint4*>(&lds[r * kOutPitch + (f - loc.n0)]);
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4*>(&lds[r * kOutPitch + (f - loc.n0)]),
+            reinterpret_cast<u32x4*>(c + row * p.Nd + f));
     }
   } else {
 #pragma unroll

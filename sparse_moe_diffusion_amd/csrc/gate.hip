@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kGateTokens = 64;
 constexpr int kGateWaves = 4;
+constexpr int kGateChunk = 3;   // 32-wide k slices loaded ahead per wave
 
 // Selection key of a probability: NaN ranks below every number.
 __device__ __forceinline__ float sel_key(float p) { return p == p ? p : -1.0f; }
@@ -180,45 +181,65 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[g][b][i] = 0.0;
 
-  for (int st = s0; st < s1; ++st) {
-    const int k0 = st * 32 + kq * 8;
-    const bool k_ok = k0 < D;
-    bf16x8 whi[EB], wmid[EB], wlo[EB];
+  // Slices go in chunks of kGateChunk: the chunk's token and weight loads
+  // are all issued before its first MFMA, so several slices of x are in
+  // flight per wave (a dependent load per slice leaves HBM idle).
+  for (int st0 = s0; st0 < s1; st0 += kGateChunk) {
+    uint4 xv[kGateChunk][4];
+    float4 wv[kGateChunk][EB][2];
 #pragma unroll
-    for (int b = 0; b < EB; ++b) {
-      float4 wa = make_float4(0, 0, 0, 0), wb = wa;
-      if (e_ok[b] && k_ok) {
-        wa = *reinterpret_cast<const float4*>(wrow[b] + k0);
-        wb = *reinterpret_cast<const float4*>(wrow[b] + k0 + 4);
+    for (int c = 0; c < kGateChunk; ++c) {
+      const int k0 = (st0 + c) * 32 + kq * 8;
+      const bool k_ok = st0 + c < s1 && k0 < D;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        xv[c][g] = make_uint4(0, 0, 0, 0);
+        if (tok_ok[g] && k_ok) xv[c][g] = *reinterpret_cast<const uint4*>(xrow[g] + k0);
       }
-      const float w8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-      uint32_t h[4], m[4], l[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a0 = w8[2 * j], a1 = w8[2 * j + 1];
-        h[j] = pack_bf16x2(a0, a1);
-        const float r0 = a0 - bf16_lo(h[j]), r1 = a1 - bf16_hi(h[j]);
-        m[j] = pack_bf16x2(r0, r1);
-        const float q0 = r0 - bf16_lo(m[j]), q1 = r1 - bf16_hi(m[j]);
-        l[j] = pack_bf16x2(q0, q1);
-      }
-      whi[b] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-      wmid[b] = __builtin_bit_cast(bf16x8, make_uint4(m[0], m[1], m[2], m[3]));
-      wlo[b] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint4 xv = make_uint4(0, 0, 0, 0);
-      if (tok_ok[g] && k_ok) xv = *reinterpret_cast<const uint4*>(xrow[g] + k0);
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
       for (int b = 0; b < EB; ++b) {
-        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[b], xb, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wmid[b], xb, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[b], xb, a, 0, 0, 0);
+        wv[c][b][0] = make_float4(0, 0, 0, 0);
+        wv[c][b][1] = wv[c][b][0];
+        if (e_ok[b] && k_ok) {
+          wv[c][b][0] = *reinterpret_cast<const float4*>(wrow[b] + k0);
+          wv[c][b][1] = *reinterpret_cast<const float4*>(wrow[b] + k0 + 4);
+        }
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][b][i] += static_cast<double>(a[i]);
+    for (int c = 0; c < kGateChunk; ++c) {
+      if (st0 + c >= s1) break;
+      bf16x8 whi[EB], wmid[EB], wlo[EB];
+#pragma unroll
+      for (int b = 0; b < EB; ++b) {
+        const float4 wa = wv[c][b][0], wb = wv[c][b][1];
+        const float w8[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        uint32_t h[4], m[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a0 = w8[2 * j], a1 = w8[2 * j + 1];
+          h[j] = pack_bf16x2(a0, a1);
+          const float r0 = a0 - bf16_lo(h[j]), r1 = a1 - bf16_hi(h[j]);
+          m[j] = pack_bf16x2(r0, r1);
+          const float q0 = r0 - bf16_lo(m[j]), q1 = r1 - bf16_hi(m[j]);
+          l[j] = pack_bf16x2(q0, q1);
+        }
+        whi[b] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+        wmid[b] = __builtin_bit_cast(bf16x8, make_uint4(m[0], m[1], m[2], m[3]));
+        wlo[b] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[c][g]);
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+          f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[b], xb, a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wmid[b], xb, a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[b], xb, a, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[g][b][i] += static_cast<double>(a[i]);
+        }
       }
     }
   }

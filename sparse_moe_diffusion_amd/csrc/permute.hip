@@ -10,8 +10,9 @@
 //  1. permute_count_kernel: workgroup b covers 256 consecutive tokens (one
 //     per thread); each token's experts form a bit mask, and one wave ballot
 //     per expert counts the wave's selections.  Writes block_counts[b][e].
-//  2. permute_scan_kernel: one thread per expert scans the block counts in
-//     block order: expert counts, exclusive offsets and block bases.
+//  2. permute_scan_kernel: one 1024-thread workgroup scans the block counts
+//     (chunks of blocks x experts, then a scan over chunks and experts):
+//     expert counts, exclusive offsets and block bases.
 //  3. permute_scatter_kernel: repeats the ballots, so a selection's row is
 //     block base + earlier waves' count + set lanes below it; writes slot_row
 //     and row_token, then copies each token row once from HBM to its K
@@ -26,6 +27,7 @@ namespace {
 
 constexpr int kPermTokens = 256;
 constexpr int kPermWaves = kPermTokens / kWave;
+constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ uint64_t token_mask(const int32_t* __restrict__ idx,
                                                int64_t t, int Kmax, int E) {
@@ -57,27 +59,52 @@ __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
   }
 }
 
-__global__ __launch_bounds__(kWave) void permute_scan_kernel(
+// Thread (c, e) of a C x E grid (C = 1024 / E chunks of consecutive count
+// blocks) sums its chunk's counts of expert e; a scan over the chunks in
+// LDS gives each chunk its base within the expert, a scan over the experts
+// gives the expert offsets, and each thread then writes the block bases of
+// its chunk in block order.
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     const int32_t* __restrict__ block_counts, int nblocks, int E,
     int32_t* __restrict__ counts, int64_t* __restrict__ offsets,
     int64_t* __restrict__ block_base) {
+  __shared__ int64_t part[kScanThreads];
   __shared__ int64_t tot[kMaxExperts];
-  const int e = threadIdx.x;
-  int64_t c = 0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) c += block_counts[static_cast<int64_t>(b) * E + e];
-  tot[e] = c;
+  const int C = kScanThreads / E;
+  const int tid = threadIdx.x;
+  const int c = tid / E;
+  const int e = tid - c * E;
+  const bool active = c < C;
+  const int b0 = static_cast<int>(static_cast<int64_t>(c) * nblocks / C);
+  const int b1 = static_cast<int>(static_cast<int64_t>(c + 1) * nblocks / C);
+  int64_t sum = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b)
+      sum += block_counts[static_cast<int64_t>(b) * E + e];
+  part[tid] = sum;
   __syncthreads();
-  int64_t run = 0;
-  for (int j = 0; j < e && j < E; ++j) run += tot[j];
-  if (e < E) {
-    counts[e] = static_cast<int32_t>(c);
-    offsets[e] = run;
-    if (e == E - 1) offsets[E] = run + c;
-    for (int b = 0; b < nblocks; ++b) {
-      block_base[static_cast<int64_t>(b) * E + e] = run;
-      run += block_counts[static_cast<int64_t>(b) * E + e];
-    }
+  // inclusive scan over chunks, per expert (Hillis-Steele)
+  for (int off = 1; off < C; off *= 2) {
+    int64_t v = part[tid];
+    if (active && c >= off) v += part[tid - off * E];
+    __syncthreads();
+    part[tid] = v;
+    __syncthreads();
+  }
+  if (active && c == C - 1) tot[e] = part[tid];
+  __syncthreads();
+  if (!active) return;
+  int64_t base = 0;
+  for (int j = 0; j < e; ++j) base += tot[j];
+  if (c == 0) {
+    counts[e] = static_cast<int32_t>(tot[e]);
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = base + tot[e];
+  }
+  int64_t run = base + (c > 0 ? part[tid - E] : 0);
+  for (int b = b0; b < b1; ++b) {
+    block_base[static_cast<int64_t>(b) * E + e] = run;
+    run += block_counts[static_cast<int64_t>(b) * E + e];
   }
 }
 
@@ -170,7 +197,7 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kWave), 0, stream,
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      block_counts, static_cast<int>(nb), E, counts, offsets,
                      block_base);
   hipError_t err = hipGetLastError();
