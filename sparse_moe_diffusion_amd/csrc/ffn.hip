@@ -30,7 +30,7 @@
 //
 // Tile order: workgroup ids are dealt round-robin to the 8 XCDs, so the id
 // is remapped to give each XCD a contiguous run of tiles; within a group,
-// tiles go in bands of 8 row-tiles, feature-tile major, so tiles running at
+// tiles go in bands of GM row-tiles, feature-tile major, so tiles running at
 // once share both their token rows and their weight rows in the XCD's L2.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -140,7 +140,7 @@ __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
 
 // ------------------------------------------------------- bf16 / MFMA ----
 
-constexpr int kBK = 64, kGM = 8;
+constexpr int kBK = 64, kGM = 8;   // kGM: band of the fp32 path
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -191,7 +191,7 @@ __device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t r,
 // transfer covering rows r0..r0+7 fetches chunk (l % 8) ^ swz(r0 + l / 8) of
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
-template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF>
+template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
   constexpr int kWaves = WT * WF;
   constexpr int TB = BM / WT / 32;   // token blocks per wave
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   uint16_t* const sB1 = sB0 + BN * kBK;
 
   TileLoc loc;
-  if (!locate_tile<BM, BN, kGM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
+  if (!locate_tile<BM, BN, GM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
     return;
 
   const int tid = threadIdx.x;
@@ -480,6 +480,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 // waves of 64 tokens x 96 features.
 constexpr int kUpBM = 256, kUpBN = 256, kUpWT = 2, kUpWF = 4;
 constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
+// Tile order within a group (bands of GM row-tiles, feature-tile major).
+// Stage 2 has few feature tiles (1152 / 192 = 6) and a large token operand
+// (h): with GM = 1 all feature tiles of a row-tile run at once, so each row
+// of h leaves HBM once.  Stage 1 (18+ feature tiles) keeps bands of 8.
+constexpr int kUpGM = 8, kDnGM = 1;
 
 // ---------------------------------------------------------- fp32 path ----
 // Plain fp32 FMA tiles (64 x 64 x 16, 4 x 4 outputs per thread) for fp32
@@ -572,7 +577,7 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
   if (a.bf16) {
     if (up) {
       hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF>),
+          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM>),
           dim3(tile_grid(p1, kUpBM, kUpBN)), dim3(64 * kUpWT * kUpWF), 0,
           stream, p1);
       hipError_t err = hipGetLastError();
@@ -581,12 +586,12 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
     if (down) {
       if (a.y_f32)
         hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF>),
+            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM>),
             dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
             stream, p2);
       else
         hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF>),
+            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM>),
             dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
             stream, p2);
       return hipGetLastError();

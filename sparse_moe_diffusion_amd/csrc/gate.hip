@@ -28,7 +28,8 @@ namespace {
 
 constexpr int kGateTokens = 64;
 constexpr int kGateWaves = 4;
-constexpr int kGateChunk = 3;   // 32-wide k slices loaded ahead per wave
+constexpr int kGateChunk = 5;   // 32-wide k slices loaded ahead per wave
+constexpr int kGateGroups = 4;  // 16-token groups per workgroup (MFMA path)
 
 // Selection key of a probability: NaN ranks below every number.
 __device__ __forceinline__ float sel_key(float p) { return p == p ? p : -1.0f; }
@@ -134,32 +135,33 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_f32_kernel(
 // 16 tokens; the fp32 slice sums are added in fp64, and the logit is
 // rounded once to fp32.
 //
-// Workgroup: 64 tokens x 4 waves; wave w covers the w-th quarter of the
-// 32-wide k slices for all 64 tokens (4 groups of 16).  MFMA operands come
+// Workgroup: 16 GG tokens (GG groups of 16) x 4 waves; wave w covers the
+// w-th quarter of the 32-wide k slices for all of them.  MFMA operands come
 // straight from memory: lane l loads 8 consecutive features (16 bytes) of
 // token (l % 16) and the matching 8 gate weights of expert (l % 16); lane
 // l's results are token (l % 16), experts 4 (l / 16) + 0..3.
-template <int EB>
-__global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
+template <int EB, int GG>
+__global__ __launch_bounds__(64 * kGateWaves) void gate_mfma_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wg,
     const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
     float* __restrict__ probs, int32_t* __restrict__ idx,
     float* __restrict__ wout) {
   constexpr int EP = 16 * EB;
-  __shared__ double red[kGateTokens][EP];
+  constexpr int TPB = 16 * GG;   // tokens per workgroup
+  __shared__ double red[TPB][EP];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15;
   const int kq = lane >> 4;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGateTokens;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPB;
   const int nsteps = (D + 31) / 32;
   const int s0 = wave * nsteps / kGateWaves;
   const int s1 = (wave + 1) * nsteps / kGateWaves;
 
-  bool tok_ok[4];
-  const uint16_t* xrow[4];
+  bool tok_ok[GG];
+  const uint16_t* xrow[GG];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < GG; ++g) {
     const int64_t t = t0 + g * 16 + col;
     tok_ok[g] = t < N;
     xrow[g] = x + (tok_ok[g] ? t : 0) * D;
@@ -173,9 +175,9 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
     wrow[b] = wg + static_cast<int64_t>(e_ok[b] ? e : 0) * D;
   }
 
-  double acc[4][EB][4];
+  double acc[GG][EB][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < GG; ++g)
 #pragma unroll
     for (int b = 0; b < EB; ++b)
 #pragma unroll
@@ -185,14 +187,14 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
   // are all issued before its first MFMA, so several slices of x are in
   // flight per wave (a dependent load per slice leaves HBM idle).
   for (int st0 = s0; st0 < s1; st0 += kGateChunk) {
-    uint4 xv[kGateChunk][4];
+    uint4 xv[kGateChunk][GG];
     float4 wv[kGateChunk][EB][2];
 #pragma unroll
     for (int c = 0; c < kGateChunk; ++c) {
       const int k0 = (st0 + c) * 32 + kq * 8;
       const bool k_ok = st0 + c < s1 && k0 < D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < GG; ++g) {
         xv[c][g] = make_uint4(0, 0, 0, 0);
         if (tok_ok[g] && k_ok) xv[c][g] = *reinterpret_cast<const uint4*>(xrow[g] + k0);
       }
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
         wlo[b] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < GG; ++g) {
         const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[c][g]);
 #pragma unroll
         for (int b = 0; b < EB; ++b) {
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
   for (int w = 0; w < kGateWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < GG; ++g)
 #pragma unroll
         for (int b = 0; b < EB; ++b)
 #pragma unroll
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kGateTokens * kGateWaves) void gate_mfma_kernel(
     __syncthreads();
   }
   const int64_t t = t0 + lane;
-  if (wave != 0 || t >= N) return;
+  if (wave != 0 || lane >= TPB || t >= N) return;
   float p[EP];
 #pragma unroll
   for (int e = 0; e < EP; ++e)
@@ -389,16 +391,17 @@ hipError_t launch_gate_eb(const void* x, bool bf16, const float* wg,
                           const float* bias, int64_t N, int D, int E, int K,
                           bool topk, float* probs, int32_t* idx, float* w,
                           hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, kGateTokens)));
-  const dim3 block(kGateTokens * kGateWaves);
+  const dim3 block(64 * kGateWaves);
   if (bf16)
-    hipLaunchKernelGGL((gate_mfma_kernel<EB>), grid, block, 0, stream,
-                       static_cast<const uint16_t*>(x), wg, bias, N, D, E, K,
-                       topk ? 1 : 0, probs, idx, w);
+    hipLaunchKernelGGL((gate_mfma_kernel<EB, kGateGroups>),
+                       dim3(static_cast<unsigned>(ceil_div(N, 16 * kGateGroups))),
+                       block, 0, stream, static_cast<const uint16_t*>(x), wg,
+                       bias, N, D, E, K, topk ? 1 : 0, probs, idx, w);
   else
-    hipLaunchKernelGGL((gate_f32_kernel<16 * EB>), grid, block, 0, stream,
-                       static_cast<const float*>(x), wg, bias, N, D, E, K,
-                       topk ? 1 : 0, probs, idx, w);
+    hipLaunchKernelGGL((gate_f32_kernel<16 * EB>),
+                       dim3(static_cast<unsigned>(ceil_div(N, kGateTokens))),
+                       block, 0, stream, static_cast<const float*>(x), wg, bias,
+                       N, D, E, K, topk ? 1 : 0, probs, idx, w);
   return hipGetLastError();
 }
 
