@@ -42,16 +42,16 @@ def parse():
     return ap.parse_args()
 
 
-# Measured HBM traffic of the dominant kernel lives in a profile summary,
+# Measured HBM traffic of the expert GEMM kernels lives in a profile summary,
 # together with the SHA-256 of the kernel source it was measured on; a
-# changed source means the figure no longer applies.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_up_xl_8e2a_512.md")
+# changed source means the figures no longer apply.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_expert_gemm_xl_8e2a_512.md")
 FFN_SOURCE = os.path.join(ROOT, "sparse_moe_diffusion_amd", "csrc", "ffn.hip")
 
 
-def measured_traffic():
-    """Bytes per launch of the stage-1 GEMM from the counter summary, or
-    None when it is missing or was taken on another version of ffn.hip."""
+def measured_traffic(stage):
+    """Bytes per launch of expert GEMM stage 1 or 2 from the counter summary,
+    or None when it is missing or was taken on another version of ffn.hip."""
     import hashlib
     try:
         text = open(TRAFFIC_FILE).read()
@@ -64,7 +64,7 @@ def measured_traffic():
             k, v = line.split(":", 1)
             fields[k.strip().lower()] = v.strip().strip("`")
     want = fields.get("ffn.hip sha256")
-    val = fields.get("traffic bytes per launch")
+    val = fields.get(f"stage {stage} traffic bytes per launch")
     if not want or not val:
         return None
     have = hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()
@@ -243,8 +243,9 @@ def main():
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "flops_per_launch": dom_flops,
                      "avg_launch_ms": round(dom_ms, 4),
-                     "traffic": (measured_traffic() if dom is up and
-                                 cfg.name == "xl_8e2a_512" and gather else None)},
+                     "traffic": (measured_traffic(1 if dom is up else 2)
+                                 if cfg.name == "xl_8e2a_512" and gather
+                                 else None)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
