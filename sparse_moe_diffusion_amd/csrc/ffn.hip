@@ -28,10 +28,13 @@
 // rows the "B" operand, so each lane ends up holding 4 consecutive output
 // features of one token and stores 8 (bf16) or 16 (fp32) bytes at a time.
 //
-// Tile order: workgroup ids are dealt round-robin to the 8 XCDs, so the id
-// is remapped to give each XCD a contiguous run of tiles; within a group,
-// tiles go in bands of GM row-tiles, feature-tile major, so tiles running at
-// once share both their token rows and their weight rows in the XCD's L2.
+// Tile order: the bf16 kernels are persistent, about one workgroup per CU;
+// workgroups are dealt round-robin to the 8 XCDs, and the workgroups of an
+// XCD walk chunks of consecutive tiles; within a group, tiles go in bands of
+// GM row-tiles, feature-tile major, so tiles running at once share both
+// their token rows and their weight rows in the XCD's L2.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -191,7 +194,8 @@ __device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t r,
 // transfer covering rows r0..r0+7 fetches chunk (l % 8) ^ swz(r0 + l / 8) of
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
-template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM>
+template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
+          bool PF>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
   constexpr int kWaves = WT * WF;
   constexpr int TB = BM / WT / 32;   // token blocks per wave
@@ -207,15 +211,25 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   constexpr int kOutPitch = BN + 8;   // staged row pitch, elements
   constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
   __shared__ __attribute__((aligned(1024)))
-  uint16_t lds[(kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2];
+  uint16_t lds[(kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2 +
+              (PF ? 256 : 0)];
   uint16_t* const sA0 = lds;
   uint16_t* const sA1 = sA0 + BM * kBK;
   uint16_t* const sB0 = sA1 + BM * kBK;
   uint16_t* const sB1 = sB0 + BN * kBK;
 
+  // Persistent: the grid is a multiple of 8 workgroups, about one per CU,
+  // dealt round-robin to the 8 XCDs.  The pw workgroups of one XCD take
+  // chunks of pw consecutive tiles (chunks dealt round-robin to the XCDs), so
+  // the tiles running at once on an XCD are neighbours in tile order.  The
+  // loop ends when the tile index passes the last tile of the last group.
+  const int pj = blockIdx.x >> 3, pxcd = blockIdx.x & 7, pw = gridDim.x >> 3;
+  for (int pc = pxcd;; pc += 8) {
   TileLoc loc;
-  if (!locate_tile<BM, BN, GM>(p, xcd_remap(blockIdx.x, gridDim.x), loc))
+  if (!locate_tile<BM, BN, GM>(p, pc * pw + pj, loc))
     return;
+  // The previous tile's readers of the LDS are done.
+  __builtin_amdgcn_s_barrier();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -276,6 +290,44 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
 
   const int nk = (Kd + kBK - 1) / kBK;
+
+  // L2 prefetch (PF, in-place token rows only): the tiles an XCD runs at once
+  // read the same row chunks at about the same time, so without it they all
+  // wait on the same misses.  Each tile touches one dword of its share of the
+  // rows two stages ahead: token rows split by feature tile (all feature
+  // tiles of a row-tile run together), weight rows split by row-tile index
+  // mod 4.  Wave 0 touches token rows, wave 1 weight rows; the landing area
+  // in LDS is never read.
+  uint32_t pf_off = kOutOfRange;
+  __amdgpu_buffer_rsrc_t pf_rs = rsB;
+  if constexpr (PF) {
+    const int ntn = (p.Nd + BN - 1) / BN;
+    if (wave == 0) {
+      const int r = (loc.n0 / BN) + ntn * lane;
+      pf_rs = rsA;
+      if (!gather && r < BM) pf_off = static_cast<uint32_t>(r) * row_bytes;
+    } else if (wave == 1) {
+      const int r = static_cast<int>((loc.row0 / BM) & 3) + 4 * lane;
+      if (r < BN) pf_off = static_cast<uint32_t>(r) * row_bytes;
+    }
+  }
+  uint16_t* const pf_lds = lds + (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2 +
+                           (wave & 1) * 128;
+#define MOE_PREFETCH(KT)                                                     \
+  do {                                                                       \
+    if constexpr (PF) {                                                      \
+      if (wave < 2) {                                                        \
+        const int pkt_ = (KT);                                               \
+        const uint32_t o_ = (pf_off == kOutOfRange || pkt_ * kBK >= Kd)      \
+                                ? kOutOfRange                                \
+                                : pf_off + static_cast<uint32_t>(pkt_) * (kBK * 2); \
+        const uint32_t a_ = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>( \
+            reinterpret_cast<uintptr_t>((lds_void*)(pf_lds))));              \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                            \
+            pf_rs, (lds_void*)(static_cast<uintptr_t>(a_)), 4, o_, 0, 0, 0); \
+      }                                                                      \
+    }                                                                        \
+  } while (0)
 
 // DMA transfers Q0 <= q < Q1 of k-stage KT into the LDS buffers DA / DB.
 #define MOE_ISSUE(KT, DA, DB, Q0, Q1)                                        \
@@ -361,6 +413,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   do {                                                                       \
     const int skt_ = (KT);                                                   \
     const bool more_ = skt_ + 1 < nk;                                        \
+    MOE_PREFETCH(skt_ + 2);                                                  \
     MOE_FRAGS(fa1, fb1, CA, CB, 1);                                          \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_MFMAS(fa0, fb0, 0, FB);                                              \
@@ -402,6 +455,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
   __builtin_amdgcn_s_waitcnt(0x7 << 4);
 #undef MOE_STAGE
+#undef MOE_PREFETCH
 #undef MOE_INTERLEAVE
 #undef MOE_MFMAS
 #undef MOE_FRAGS
@@ -472,6 +526,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       }
     }
   }
+  }  // tile loop
 }
 
 // Tile shapes: the up-projection (N = H, a multiple of 256 in every DiT-MoE
@@ -485,6 +540,7 @@ constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
 // (h): with GM = 1 all feature tiles of a row-tile run at once, so each row
 // of h leaves HBM once.  Stage 1 (18+ feature tiles) keeps bands of 8.
 constexpr int kUpGM = 8, kDnGM = 1;
+constexpr bool kDnPF = true;
 
 // ---------------------------------------------------------- fp32 path ----
 // Plain fp32 FMA tiles (64 x 64 x 16, 4 x 4 outputs per thread) for fp32
@@ -565,6 +621,26 @@ int tile_grid(const GemmParams& p, int BM, int BN) {
   return static_cast<int>(mt * ((p.Nd + BN - 1) / BN));
 }
 
+// Workgroups of a persistent launch: the CU count of the current device
+// (read once per device), rounded down to a multiple of 8, and no more than
+// the tile bound rounded up to a multiple of 8.
+int persistent_grid(int tiles) {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        n < 8)
+      n = 8;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  const int cap = n / 8 * 8;
+  const int want = (tiles + 7) / 8 * 8;
+  return want < cap ? want : cap;
+}
+
 }  // namespace
 
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
@@ -577,23 +653,23 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
   if (a.bf16) {
     if (up) {
       hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM>),
-          dim3(tile_grid(p1, kUpBM, kUpBN)), dim3(64 * kUpWT * kUpWF), 0,
-          stream, p1);
+          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
+          dim3(persistent_grid(tile_grid(p1, kUpBM, kUpBN))),
+          dim3(64 * kUpWT * kUpWF), 0, stream, p1);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
     if (down) {
       if (a.y_f32)
         hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM>),
-            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
-            stream, p2);
+            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
+            dim3(persistent_grid(tile_grid(p2, kDnBM, kDnBN))),
+            dim3(64 * kDnWT * kDnWF), 0, stream, p2);
       else
         hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM>),
-            dim3(tile_grid(p2, kDnBM, kDnBN)), dim3(64 * kDnWT * kDnWF), 0,
-            stream, p2);
+            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
+            dim3(persistent_grid(tile_grid(p2, kDnBM, kDnBN))),
+            dim3(64 * kDnWT * kDnWF), 0, stream, p2);
       return hipGetLastError();
     }
     return hipSuccess;
