@@ -210,6 +210,12 @@ def _run_ffn(xs, offsets, w1, w2, b1, b2, dtype, row_index=None, y_f32=False):
     ([77, 3, 200], 1152, 4608, "bf16", True, False),
     ([31, 64, 0, 97], 72, 136, "f32", True, True),
     ([128, 128], 256, 512, "f32", False, False),
+    # many ragged groups, some empty: the device-side tile scheduler walks 64
+    # and 128 (the maximum) groups
+    ([(i * 37) % 23 * 3 for i in range(64)], 128, 256, "bf16", True, False),
+    ([(i * 11) % 7 for i in range(128)], 64, 128, "bf16", False, True),
+    # more tiles than workgroups: every persistent workgroup takes several
+    ([5000, 0, 5240], 64, 2048, "bf16", True, False),
 ])
 def test_grouped_ffn(sizes, D, H, dtype, gather, bias):
     rng = np.random.default_rng(sum(sizes) + D)
