@@ -37,7 +37,7 @@ bool valid_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
 
 constexpr int64_t kI32Limit = int64_t(1) << 31;
 constexpr int kMaxE = 64;
-constexpr int kMaxGroups = 128;
+constexpr int kMaxGroups = moe::kMaxFfnGroups;
 
 #define CHECK_PTR(p)                                                       \
   do {                                                                     \

@@ -111,6 +111,87 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int L,
   return false;
 }
 
+// Group table of the persistent kernels, in LDS: for every group g its
+// clamped row range [row0, row_end) and the index of its first tile; entry G
+// of the first-tile column holds the total tile count.  Built once per
+// workgroup, so that finding a tile reads no global memory: a global load at
+// a tile boundary would wait on the previous tile's output stores (the
+// vector-memory counter retires in order).
+constexpr int kTabCol = kMaxFfnGroups + 1;
+constexpr int kTabInts = 3 * kTabCol;
+
+template <int BM, int BN>
+__device__ void build_group_table(const GemmParams& p, int32_t* tab, int wave,
+                                  int lane) {
+  if (wave == 0) {
+    const int ntn = (p.Nd + BN - 1) / BN;
+    int base = 0;
+    for (int c = 0; c < p.G; c += 64) {
+      const int g = c + lane;
+      int64_t r0 = 0, r1 = 0;
+      int tiles = 0;
+      if (g < p.G) {
+        r0 = min(max(p.offsets[g], int64_t(0)), p.total);
+        r1 = min(max(p.offsets[g + 1], r0), p.total);
+        tiles = static_cast<int>((r1 - r0 + BM - 1) / BM) * ntn;
+      }
+      int inc = tiles;   // inclusive scan of tile counts over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d);
+        if (lane >= d) inc += v;
+      }
+      if (g < p.G) {
+        tab[g] = static_cast<int32_t>(r0);
+        tab[kTabCol + g] = static_cast<int32_t>(r1);
+        tab[2 * kTabCol + g] = base + inc - tiles;
+      }
+      base += __shfl(inc, 63);
+    }
+    if (lane == 0) tab[2 * kTabCol + p.G] = base;
+  }
+  __syncthreads();
+}
+
+// Tile L of the launch from the group table (same order as locate_tile).
+// Every lane of the wave must take part.  Table entries are read at
+// wave-uniform addresses and declared uniform, so that the branches and the
+// descriptors built from them stay scalar.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool locate_tile_tab(const GemmParams& p,
+                                                const int32_t* tab, int lane,
+                                                int L, TileLoc& loc) {
+  const int32_t* const first = tab + 2 * kTabCol;
+  if (L >= __builtin_amdgcn_readfirstlane(first[p.G])) return false;
+  // The one group whose tile range holds L (empty groups have none).
+  int g = 0;
+  for (int c = 0; c < p.G; c += 64) {
+    const int gg = c + lane;
+    const bool in = gg < p.G && first[gg] <= L && L < first[gg + 1];
+    const uint64_t m = __ballot(in);
+    if (m != 0) {
+      g = c + __builtin_ctzll(m);
+      break;
+    }
+  }
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int r0 = __builtin_amdgcn_readfirstlane(tab[g]);
+  const int r1 = __builtin_amdgcn_readfirstlane(tab[kTabCol + g]);
+  const int ntn = (p.Nd + BN - 1) / BN;
+  const int mt = (r1 - r0 + BM - 1) / BM;
+  const int Lg = L - __builtin_amdgcn_readfirstlane(first[g]);
+  const int band = Lg / (GM * ntn);
+  const int rem = Lg - band * GM * ntn;
+  const int m_first = band * GM;
+  const int gm = min(GM, mt - m_first);
+  loc.g = g;
+  loc.row0 = uniform64(static_cast<int64_t>(r0) +
+                       static_cast<int64_t>(m_first + rem % gm) * BM);
+  loc.row_end = uniform64(r1);
+  loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+  return true;
+}
+
 // Bias and activation of 4 consecutive output features f..f+3 of group g.
 template <int EPI>
 __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g, int f,
@@ -170,20 +251,30 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// writes bytes [16 l, 16 l + 16) of the 1 KB block at `dst`.  The LDS
-// destination reaches the instruction as a plain wave-uniform 32-bit
-// address, so the compiler cannot attribute the transfer to a particular
-// LDS region and adds no waits of its own before LDS reads (its alias
-// tracking would otherwise wait for transfers into other stages); the
-// kernel orders every transfer against its readers explicitly (vmcnt wait,
-// then workgroup barrier).
-__device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t r,
-                                                uint16_t* dst, uint32_t off) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((lds_void*)(dst))));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (lds_void*)(static_cast<uintptr_t>(a)), 16, off, 0, 0, 0);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((lds_void*)(const_cast<void*>(p))));
+}
+
+// SZ bytes per lane (16 or 4) from global memory straight into LDS: lane l
+// of the wave writes bytes [SZ l, SZ l + SZ) of the block at LDS byte
+// address `dst`.  The destination reaches the instruction as a plain
+// wave-uniform 32-bit address, so the compiler cannot attribute the
+// transfer to a particular LDS region and adds no waits of its own before
+// LDS reads (its alias tracking would otherwise wait for transfers into
+// other stages); the kernel orders every transfer against its readers
+// explicitly (vmcnt wait, then workgroup barrier).
+template <int SZ>
+__device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
+                                              uint32_t dst, uint32_t off) {
+  static_assert(SZ == 16 || SZ == 4, "16- or 4-byte transfers");
+  lds_void* const a = (lds_void*)(
+      static_cast<uintptr_t>(__builtin_amdgcn_readfirstlane(dst)));
+  if constexpr (SZ == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, a, 16, off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, a, 4, off, 0, 0, 0);
 }
 
 // Tile of BM token rows x BN output features; waves form a WT x WF grid, each
@@ -210,44 +301,78 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   constexpr int kStageBytes = 2 * (BM + BN) * kBK * 2;
   constexpr int kOutPitch = BN + 8;   // staged row pitch, elements
   constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
+  constexpr int kMainElems = (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2;
+  constexpr int kPfElems = PF ? 256 : 0;
   __shared__ __attribute__((aligned(1024)))
-  uint16_t lds[(kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2 +
-              (PF ? 256 : 0)];
+  uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM)];
+  int32_t* const tab = reinterpret_cast<int32_t*>(lds + kMainElems + kPfElems);
+  int32_t* const sidx = tab + kTabInts;   // 2 x BM gathered source rows
   uint16_t* const sA0 = lds;
   uint16_t* const sA1 = sA0 + BM * kBK;
   uint16_t* const sB0 = sA1 + BM * kBK;
   uint16_t* const sB1 = sB0 + BN * kBK;
+  // The same as LDS byte addresses, for the transfers.
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t bA0 = lds0, bA1 = bA0 + BM * kBK * 2;
+  const uint32_t bB0 = bA1 + BM * kBK * 2, bB1 = bB0 + BN * kBK * 2;
+  const uint32_t bPf = lds0 + kMainElems * 2;
+  const uint32_t bIdx = bPf + kPfElems * 2 + kTabInts * 4;
 
   // Persistent: the grid is a multiple of 8 workgroups, about one per CU,
   // dealt round-robin to the 8 XCDs.  The pw workgroups of one XCD take
   // chunks of pw consecutive tiles (chunks dealt round-robin to the XCDs), so
   // the tiles running at once on an XCD are neighbours in tile order.  The
   // loop ends when the tile index passes the last tile of the last group.
-  const int pj = blockIdx.x >> 3, pxcd = blockIdx.x & 7, pw = gridDim.x >> 3;
-  for (int pc = pxcd;; pc += 8) {
-  TileLoc loc;
-  if (!locate_tile<BM, BN, GM>(p, pc * pw + pj, loc))
-    return;
-  // The previous tile's readers of the LDS are done.
-  __builtin_amdgcn_s_barrier();
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid0 = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int wt = wave % WT;   // token slice of the tile
   const int wf = wave / WT;   // feature slice of the tile
   const int Kd = p.Kd;
   const uint32_t row_bytes = static_cast<uint32_t>(Kd) * 2u;
+  build_group_table<BM, BN>(p, tab, wave, tid0 & 63);
 
   // Token rows: gathered through a_index from the whole activation matrix,
   // or read in place from the tile's first row.  Rows past the group end
-  // re-read the tile's first row; their results are never stored.
+  // re-read row 0 (gather) or the tile's first row; their results are never
+  // stored.  In gather mode the tile's source rows sit in LDS buffer
+  // (tile count & 1) of sidx: the next tile's are transferred there before
+  // this tile's first k stage, so a tile starts without waiting on global
+  // memory.
   const bool gather = p.a_index != nullptr;
+#define MOE_FETCH_ROWS(L, B, LANE)                                           \
+  do {                                                                       \
+    if (wave < BM / 64) {                                                    \
+      const uint32_t n_ =                                                    \
+          static_cast<uint32_t>(min(static_cast<int>((L).row_end - (L).row0), BM)); \
+      const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(                          \
+          reinterpret_cast<const void*>(uniform64(                           \
+              reinterpret_cast<int64_t>(p.a_index + (L).row0))),             \
+          __builtin_amdgcn_readfirstlane(n_ * 4u));                          \
+      dma_untracked<4>(rs_, bIdx + ((B) * BM + wave * 64) * 4,               \
+                       static_cast<uint32_t>(wave * 64 + (LANE)) * 4u);      \
+    }                                                                        \
+  } while (0)
+  const int pj = blockIdx.x >> 3, pxcd = blockIdx.x & 7, pw = gridDim.x >> 3;
+  int pc = pxcd, it = 0;
+  TileLoc loc;
+  bool have = locate_tile_tab<BM, BN, GM>(p, tab, tid0 & 63, pc * pw + pj, loc);
+  if (gather && have) MOE_FETCH_ROWS(loc, 0, tid0 & 63);
+  stage_barrier();
+  while (have) {
+  // A fresh, opaque copy of the thread index per tile: no lane-dependent
+  // value is hoisted out of the tile loop (it would stay live through the
+  // main loop and spill).
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  // The previous tile's readers of the LDS are done.
+  __builtin_amdgcn_s_barrier();
+
   const uint16_t* a_base = static_cast<const uint16_t*>(p.a) +
                            (gather ? int64_t(0) : loc.row0 * Kd);
   const uint32_t a_bytes =
       gather ? kOutOfRange
-             : static_cast<uint32_t>(min<int64_t>(loc.row_end - loc.row0, BM)) *
+             : static_cast<uint32_t>(min(static_cast<int>(loc.row_end - loc.row0), BM)) *
                    row_bytes;
   const __amdgpu_buffer_rsrc_t rsA =
       make_rsrc(reinterpret_cast<const void*>(
@@ -267,7 +392,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // k = 0, the chunk's k index, and the LDS destination (elements).
   uint32_t goff[NQ];
   int gk[NQ];
-  int ldst[NQ];
+  uint32_t ldst[NQ];   // LDS byte offset of the transfer in its stage
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int t = wave + kWaves * q;          // transfer index in the stage
@@ -276,12 +401,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     const int r = r0 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     gk[q] = c * 8;
-    ldst[q] = r0 * kBK;
+    ldst[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r0 * kBK * 2));
     if (isA) {
-      const int64_t grow = loc.row0 + r;
-      const bool valid = grow < loc.row_end;
+      const bool valid = loc.row0 + r < loc.row_end;
       const uint32_t src =
-          gather ? static_cast<uint32_t>(p.a_index[valid ? grow : loc.row0])
+          gather ? static_cast<uint32_t>(sidx[(it & 1) * BM + r])
                  : static_cast<uint32_t>(valid ? r : 0);
       goff[q] = src * row_bytes + c * 16u;
     } else {
@@ -311,8 +435,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       if (r < BN) pf_off = static_cast<uint32_t>(r) * row_bytes;
     }
   }
-  uint16_t* const pf_lds = lds + (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2 +
-                           (wave & 1) * 128;
+  const uint32_t pf_lds = bPf + (wave & 1) * 256;
 #define MOE_PREFETCH(KT)                                                     \
   do {                                                                       \
     if constexpr (PF) {                                                      \
@@ -321,15 +444,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
         const uint32_t o_ = (pf_off == kOutOfRange || pkt_ * kBK >= Kd)      \
                                 ? kOutOfRange                                \
                                 : pf_off + static_cast<uint32_t>(pkt_) * (kBK * 2); \
-        const uint32_t a_ = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>( \
-            reinterpret_cast<uintptr_t>((lds_void*)(pf_lds))));              \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                            \
-            pf_rs, (lds_void*)(static_cast<uintptr_t>(a_)), 4, o_, 0, 0, 0); \
+        dma_untracked<4>(pf_rs, pf_lds, o_);                                 \
       }                                                                      \
     }                                                                        \
   } while (0)
 
-// DMA transfers Q0 <= q < Q1 of k-stage KT into the LDS buffers DA / DB.
+// DMA transfers Q0 <= q < Q1 of k-stage KT into the LDS buffers at byte
+// addresses DA / DB.
 #define MOE_ISSUE(KT, DA, DB, Q0, Q1)                                        \
   do {                                                                       \
     const int ikt_ = (KT);                                                   \
@@ -338,7 +459,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       const bool isA_ = q < QA;                                              \
       uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);     \
       if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;            \
-      dma16_untracked(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
+      dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
     }                                                                        \
   } while (0)
 
@@ -409,7 +530,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     __builtin_amdgcn_sched_group_barrier(0x008, FB * TB, 0);                 \
   } while (0)
 
-#define MOE_STAGE(KT, CA, CB, NA, NB)                                        \
+#define MOE_STAGE(KT, CA, CB, NA, NB, DNA, DNB)                              \
   do {                                                                       \
     const int skt_ = (KT);                                                   \
     const bool more_ = skt_ + 1 < nk;                                        \
@@ -417,13 +538,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     MOE_FRAGS(fa1, fb1, CA, CB, 1);                                          \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_MFMAS(fa0, fb0, 0, FB);                                              \
-    MOE_ISSUE(skt_ + 1, NA, NB, 0, kQH);                                     \
+    MOE_ISSUE(skt_ + 1, DNA, DNB, 0, kQH);                                   \
     MOE_INTERLEAVE(kQH);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_FRAGS(fa0, fb0, CA, CB, 2);                                          \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_MFMAS(fa1, fb1, 0, FB);                                              \
-    MOE_ISSUE(skt_ + 1, NA, NB, kQH, NQ);                                    \
+    MOE_ISSUE(skt_ + 1, DNA, DNB, kQH, NQ);                                  \
     MOE_INTERLEAVE(NQ - kQH);                                                \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_FRAGS(fa1, fb1, CA, CB, 3);                                          \
@@ -442,7 +563,14 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     __builtin_amdgcn_sched_barrier(0);                                       \
   } while (0)
 
-  MOE_ISSUE(0, sA0, sB0, 0, NQ);
+  // In gather mode, the source rows of this workgroup's next tile.
+  if (gather) {
+    TileLoc nloc;
+    if (locate_tile_tab<BM, BN, GM>(p, tab, lane, (pc + 8) * pw + pj, nloc))
+      MOE_FETCH_ROWS(nloc, (it + 1) & 1, lane);
+  }
+
+  MOE_ISSUE(0, bA0, bB0, 0, NQ);
   stage_barrier();
   MOE_FRAGS(fa0, fb0, sA0, sB0, 0);
   // Stages alternate between the two buffers.  The last stage's transfers
@@ -450,8 +578,8 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // idle buffer (no branch around them, so they interleave with the MFMAs)
   // and are drained before the epilogue.
   for (int kt = 0; kt < nk; kt += 2) {
-    MOE_STAGE(kt, sA0, sB0, sA1, sB1);
-    if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA0, sB0);
+    MOE_STAGE(kt, sA0, sB0, sA1, sB1, bA1, bB1);
+    if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA0, sB0, bA0, bB0);
   }
   __builtin_amdgcn_s_waitcnt(0x7 << 4);
 #undef MOE_STAGE
@@ -526,6 +654,9 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       }
     }
   }
+  pc += 8;
+  ++it;
+  have = locate_tile_tab<BM, BN, GM>(p, tab, lane, pc * pw + pj, loc);
   }  // tile loop
 }
 

@@ -27,6 +27,8 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                           hipStream_t stream);
 
 // ffn.hip
+// Most groups (experts) one grouped-FFN launch takes.
+constexpr int kMaxFfnGroups = 128;
 struct FfnArgs {
   const void* x;            // [*][D]
   const int32_t* row_index; // [total] or null
