@@ -50,6 +50,18 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __popcll(mask & below);
 }
 
+// Buffer descriptor of a byte range: loads at offsets past `bytes` return
+// zero and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
+                                           0x00020000);
+}
+
+// Offset used for chunks that lie outside the data: at or beyond every
+// descriptor's byte count, so such loads return zero.
+constexpr uint32_t kOutOfRange = 0xfffffff0u;
+
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) {
   return (a + b - 1) / b;
 }

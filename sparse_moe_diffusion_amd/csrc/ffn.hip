@@ -228,16 +228,6 @@ constexpr int kBK = 64, kGM = 8;   // kGM: band of the fp32 path
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Buffer descriptor of a byte range; loads beyond `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
-                                                            uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
-                                           0x00020000);
-}
-
-// Offset used for chunks past the k extent: at or beyond every descriptor's
-// num_records, so such loads return zero.
-constexpr uint32_t kOutOfRange = 0xfffffff0u;
 
 typedef __attribute__((address_space(3))) void lds_void;
 

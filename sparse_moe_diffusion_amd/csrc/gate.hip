@@ -19,6 +19,8 @@
 //    entry among keys equal to it.
 //  * race_emit_kernel: one thread per token writes its kept experts in
 //    ascending order.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -270,6 +272,190 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_mfma_kernel(
   softmax_topk<EP>(p, t, E, K, topk != 0, probs, idx, wout);
 }
 
+// bf16 tokens, E <= 16, streaming form of the same arithmetic: three MFMAs
+// per 32-wide slice on the exact split of the gate weight, slice sums added
+// in fp64 in slice order, one rounding to fp32.
+//
+// Each workgroup first splits the fp32 gate weight into its three bf16
+// parts once, into LDS; chunk ((part * nsteps + s) * 4 + kq) * EC + e holds
+// the 8 bf16 of part `part` (hi, mid, lo) of expert e for features
+// 32 s + 8 kq .. 32 s + 8 kq + 7, so the lanes of a wave read one slice's
+// operand as consecutive 16-byte chunks.  Each wave then streams the
+// features of its own 16 tokens with kRing 32-wide slices in flight (a ring
+// of register loads refilled as each slice is consumed), so HBM sees a
+// steady stream instead of bursts, and keeps its tokens' logits in
+// registers: no cross-wave sum.  Lane l's logits are token (l % 16),
+// experts 4 (l / 16) + 0..3; the wave passes them through LDS to lanes
+// 0..15, one token each, for the softmax and selection.
+constexpr int kStreamWaves = 8;            // 16 tokens per wave
+constexpr int kRing = 12;                  // slices in flight per wave
+constexpr int kStreamLdsMax = 144 * 1024;  // split weights, bytes
+
+__host__ __device__ constexpr size_t stream_lds_bytes(int D, int EC) {
+  return static_cast<size_t>(3) * ((D + 31) / 32) * 4 * EC * 16;
+}
+
+template <int EC>
+__global__ __launch_bounds__(64 * kStreamWaves) void gate_stream_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
+    float* __restrict__ probs, int32_t* __restrict__ idx,
+    float* __restrict__ wout) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ u32x4 wsplit[];
+  __shared__ float lg[kStreamWaves][16][17];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane & 15;
+  const int kq = lane >> 4;
+  const int nsteps = (D + 31) / 32;
+  const int stride = nsteps * 4 * EC;   // chunks per part
+
+  // This wave's 16 token rows; rows past N read zero.
+  const int64_t t0 =
+      static_cast<int64_t>(blockIdx.x) * (16 * kStreamWaves) + 16 * wave;
+  const int64_t left = N - t0;
+  const int nrows = left <= 0 ? 0 : (left >= 16 ? 16 : static_cast<int>(left));
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+      x + (nrows > 0 ? t0 : int64_t(0)) * D,
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(nrows) * row_bytes));
+  const uint32_t off0 = static_cast<uint32_t>(col) * row_bytes + kq * 16u;
+  // Byte offset of this lane's 8 features of slice s (zero past D).
+  auto xoff = [&](int s) -> uint32_t {
+    return (s * 32 + kq * 8 < D) ? off0 + static_cast<uint32_t>(s) * 64u
+                                 : kOutOfRange;
+  };
+
+  u32x4 xr[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing; ++j)
+    xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff(j), 0, 0);
+
+  // The split, while the first slices are in flight.  Thread i takes the
+  // 8-feature chunks i, i + 256, ... (chunk c: expert c % EC, features
+  // 8 (c / EC) ..); a batch's weights are all loaded before any is used.
+  constexpr int kBatch = 6;
+  const int nchunks = EC * nsteps * 4;
+  for (int c0 = tid; c0 < nchunks; c0 += 64 * kStreamWaves * kBatch) {
+    float4 wa[kBatch], wb[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 64 * kStreamWaves * b;
+      const int e = c % EC;
+      const int k = 8 * (c / EC);
+      wa[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      wb[b] = wa[b];
+      if (c < nchunks && e < E && k < D) {
+        const float* src = wg + static_cast<int64_t>(e) * D + k;
+        wa[b] = *reinterpret_cast<const float4*>(src);
+        wb[b] = *reinterpret_cast<const float4*>(src + 4);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + 64 * kStreamWaves * b;
+      if (c >= nchunks) break;
+      const int e = c % EC;
+      const int k = 8 * (c / EC);
+      const float w8[8] = {wa[b].x, wa[b].y, wa[b].z, wa[b].w,
+                           wb[b].x, wb[b].y, wb[b].z, wb[b].w};
+      u32x4 h, m, l;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = w8[2 * q], a1 = w8[2 * q + 1];
+        h[q] = pack_bf16x2(a0, a1);
+        const float r0 = a0 - bf16_lo(h[q]), r1 = a1 - bf16_hi(h[q]);
+        m[q] = pack_bf16x2(r0, r1);
+        l[q] = pack_bf16x2(r0 - bf16_lo(m[q]), r1 - bf16_hi(m[q]));
+      }
+      const int chunk = ((k >> 5) * 4 + ((k >> 3) & 3)) * EC + e;
+      wsplit[chunk] = h;
+      wsplit[stride + chunk] = m;
+      wsplit[2 * stride + chunk] = l;
+    }
+  }
+  __syncthreads();
+
+  // Straight-line ring: a slice at or past nsteps loads zero features and
+  // reads the (finite) weights of the last slice, so it adds exactly zero.
+  // Lanes past the stored expert columns (E <= 8) read expert 0's chunk:
+  // their output rows are experts >= E, never used.  The three weight parts
+  // of slice s + 1 are read from LDS while slice s is multiplied (kRing is even, so the two register sets alternate in a
+  // fixed pattern).
+  static_assert(kRing % 2 == 0, "even ring");
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const u32x4* const wl = wsplit + kq * EC + (col < EC ? col : 0);
+  auto wslice = [&](int s, u32x4 (&w)[3]) {
+    const int sw = (s < nsteps ? s : nsteps - 1) * 4 * EC;
+    w[0] = wl[sw];
+    w[1] = wl[stride + sw];
+    w[2] = wl[2 * stride + sw];
+  };
+  u32x4 wa[3], wb[3];
+  wslice(0, wa);
+  for (int s0 = 0; s0 < nsteps; s0 += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int s = s0 + j;
+      u32x4 (&cur)[3] = (j % 2 == 0) ? wa : wb;
+      u32x4 (&nxt)[3] = (j % 2 == 0) ? wb : wa;
+      wslice(s + 1, nxt);
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, xr[j]);
+      xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff(s + kRing), 0, 0);
+      f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, cur[part]), xb, a, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += static_cast<double>(a[i]);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * kq + i;
+    const double b = (bias != nullptr && e < E) ? static_cast<double>(bias[e]) : 0.0;
+    lg[wave][col][e] = static_cast<float>(acc[i] + b);
+  }
+  __syncthreads();
+  const int64_t t = t0 + lane;
+  if (lane >= 16 || t >= N) return;
+  float p[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) p[e] = lg[wave][lane][e];
+  softmax_topk<16>(p, t, E, K, topk != 0, probs, idx, wout);
+}
+
+// Split weights of E experts over D features fit the streaming kernel's LDS.
+bool gate_stream_fits(int D, int E) {
+  return E <= 16 && stream_lds_bytes(D, E <= 8 ? 8 : 16) <= kStreamLdsMax;
+}
+
+template <int EC>
+hipError_t launch_gate_stream(const void* x, const float* wg, const float* bias,
+                              int64_t N, int D, int E, int K, bool topk,
+                              float* probs, int32_t* idx, float* w,
+                              hipStream_t stream) {
+  static std::atomic<bool> lds_opt_in{false};
+  if (!lds_opt_in.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gate_stream_kernel<EC>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLdsMax);
+    if (e != hipSuccess) return e;
+    lds_opt_in.store(true, std::memory_order_release);
+  }
+  hipLaunchKernelGGL((gate_stream_kernel<EC>),
+                     dim3(static_cast<unsigned>(ceil_div(N, 16 * kStreamWaves))),
+                     dim3(64 * kStreamWaves),
+                     static_cast<unsigned>(stream_lds_bytes(D, EC)), stream,
+                     static_cast<const uint16_t*>(x), wg, bias, N, D, E, K,
+                     topk ? 1 : 0, probs, idx, w);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------- Expert Race --
 
 constexpr int kRaceThreads = 1024;
@@ -412,6 +598,11 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
                        bool topk, float* probs, int32_t* idx, float* w,
                        hipStream_t stream) {
   if (N == 0) return hipSuccess;
+  if (x_bf16 && gate_stream_fits(D, E))
+    return E <= 8 ? launch_gate_stream<8>(x, w_gate, bias, N, D, E, K, topk,
+                                          probs, idx, w, stream)
+                  : launch_gate_stream<16>(x, w_gate, bias, N, D, E, K, topk,
+                                           probs, idx, w, stream);
   if (E <= 16)
     return launch_gate_eb<1>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
                              idx, w, stream);

@@ -144,13 +144,17 @@ def balance(cfg, buf: LayerBuffers, mode: str = "sequence"):
 
 
 # The layer as a list of single-kernel-group calls, in order (the expert
-# MLPs split into their two GEMM stages): the same work as forward().
+# MLPs split into their two GEMM stages): the same work as forward().  Both
+# up-projections run before both down-projections: the shared one then reads
+# x while the gate's and the routed stage's reads of it still sit in the
+# 256 MB memory-side cache, instead of after 604 MB of h have streamed
+# through it (measured: 2% less time per layer than routed MLP, then shared).
 UP, DOWN = _lib.MOE_FFN_UP, _lib.MOE_FFN_DOWN
 STEPS = (("gate", lambda c, x, w, b: gate(c, x, w, b)),
          ("permute", lambda c, x, w, b: permute(c, x, b)),
          ("routed_up", lambda c, x, w, b: routed_ffn(c, x, w, b, UP)),
-         ("routed_down", lambda c, x, w, b: routed_ffn(c, x, w, b, DOWN)),
          ("shared_up", lambda c, x, w, b: shared_ffn(c, x, w, b, UP)),
+         ("routed_down", lambda c, x, w, b: routed_ffn(c, x, w, b, DOWN)),
          ("shared_down", lambda c, x, w, b: shared_ffn(c, x, w, b, DOWN)),
          ("combine", lambda c, x, w, b: combine(c, b)),
          ("balance", lambda c, x, w, b: balance(c, b)))
@@ -161,8 +165,10 @@ def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
     """One pass of the whole layer; results land in ``buf``."""
     gate(cfg, x, wts, buf)
     permute(cfg, x, buf)
-    routed_ffn(cfg, x, wts, buf)
-    shared_ffn(cfg, x, wts, buf)
+    routed_ffn(cfg, x, wts, buf, UP)
+    shared_ffn(cfg, x, wts, buf, UP)
+    routed_ffn(cfg, x, wts, buf, DOWN)
+    shared_ffn(cfg, x, wts, buf, DOWN)
     combine(cfg, buf)
     balance(cfg, buf, balance_mode)
     return buf

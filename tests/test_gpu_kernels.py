@@ -52,6 +52,9 @@ GATE_CASES = [  # N, D, E, K, bias, dtype
     (1000, 384, 16, 2, True, "bf16"), (300, 2048, 16, 2, False, "bf16"),
     (257, 72, 3, 3, True, "f32"), (200, 136, 33, 5, True, "bf16"),
     (130, 64, 64, 7, False, "f32"), (500, 384, 8, 1, False, "f32"),
+    # bf16, E <= 16 with unused expert columns and a partial last 32-wide
+    # feature slice; N leaves part of the last workgroup empty
+    (777, 72, 12, 3, True, "bf16"), (129, 200, 5, 2, False, "bf16"),
 ]
 
 
@@ -105,6 +108,22 @@ def test_race_select(N, D, E, K):
     assert np.array_equal(idx, rec)
     assert int((idx >= 0).sum()) == K * N
     assert np.all(w[idx < 0] == 0)
+
+
+@pytest.mark.parametrize("N,D,E,K", [(333, 128, 16, 2), (1000, 200, 8, 2)])
+def test_race_select_bf16(N, D, E, K):
+    """Race on bf16 tokens (probabilities from the bf16 gate path)."""
+    rng = np.random.default_rng(N + 7 * E)
+    x = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((N, D)).astype(np.float32)))
+    wg = (rng.standard_normal((E, D)) * 0.1).astype(np.float32)
+    probs, idx, w = _run_gate(x, wg, None, K, "race", "bf16")
+    P = oracle.softmax(oracle.gate_logits(x, wg))
+    assert np.abs(probs - P).max() <= 1e-6
+    idx_o, tau, near = oracle.race_select(P, K)
+    rec, bad = reconcile_race(P, K, idx_o, idx, tau)
+    assert not bad
+    assert np.array_equal(idx, rec)
+    assert int((idx >= 0).sum()) == K * N
 
 
 def test_race_all_ties():
