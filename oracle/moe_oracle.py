@@ -272,6 +272,40 @@ def balance_stats(P, idx, B, T, K, alpha, mode="sequence"):
     return counts, psum, loss
 
 
+# ---------------------------------------------------- routing analytics ----
+
+def routing_histogram(idx, B, T, E, tags=None, n_tags=0):
+    """[paper] Expert Specialization Analysis: how often each expert is
+    selected, seen by spatial position and by image class or denoising time
+    step; [hub] section 4 (expert activation frequency per class, heatmaps by
+    class, patch and step).
+
+    idx [B*T][Kmax]: the routing of B images of T tokens.
+      pos[p][i] = number of (image b, slot k) with idx[b*T + p][k] == i
+      tag[g][i] = number of (token t, slot k) of the images b with
+                  tags[b] == g and idx[t][k] == i
+    Entries outside [0, E) (the -1 of an empty race slot) count nowhere; an
+    image whose tag lies outside [0, n_tags) counts only by position.
+    Returns (pos [T][E] int64, tag [n_tags][E] int64 or None).
+    """
+    idx = np.asarray(idx)
+    N, Kmax = idx.shape
+    if N != B * T:
+        raise ValueError("idx must hold B*T rows")
+    valid = (idx >= 0) & (idx < E)
+    position = np.broadcast_to((np.arange(N) % T)[:, None], idx.shape)
+    pos = np.zeros((T, E), np.int64)
+    np.add.at(pos, (position[valid], idx[valid]), 1)
+    if tags is None:
+        return pos, None
+    tag_of_token = np.repeat(np.asarray(tags, np.int64), T)
+    g = np.broadcast_to(tag_of_token[:, None], idx.shape)
+    ok = valid & (g >= 0) & (g < n_tags)
+    tag = np.zeros((n_tags, E), np.int64)
+    np.add.at(tag, (g[ok], idx[ok]), 1)
+    return pos, tag
+
+
 # --------------------------------------------------------- whole layer ----
 
 def route(inputs):

@@ -364,9 +364,70 @@ def check_balance_golden():
     assert abs(L - g["loss"]) < 1e-15, (L, g["loss"])
 
 
+# ----------------------------------------------------- routing analytics --
+
+def check_routing_histogram_golden():
+    with open(os.path.join(GOLDEN, "routing_histogram_tiny.json")) as fh:
+        g = json.load(fh)
+    pos, tag = om.routing_histogram(np.array(g["idx"]), g["B"], g["T"], g["E"],
+                                    tags=g["tags"], n_tags=g["n_tags"])
+    assert pos.tolist() == g["pos"]
+    assert tag.tolist() == g["tag"]
+
+
+def check_routing_histogram_brute():
+    r = _rng(21)
+    B, T, E, Kmax = 3, 5, 6, 3
+    idx = r.integers(-1, E + 2, size=(B * T, Kmax))   # includes -1 and >= E
+    tags = np.array([2, -1, 0])
+    n_tags = 3
+    pos_bf = [[0] * E for _ in range(T)]
+    tag_bf = [[0] * E for _ in range(n_tags)]
+    for b in range(B):
+        for p in range(T):
+            for k in range(Kmax):
+                e = int(idx[b * T + p][k])
+                if 0 <= e < E:
+                    pos_bf[p][e] += 1
+                    if 0 <= tags[b] < n_tags:
+                        tag_bf[tags[b]][e] += 1
+    pos, tag = om.routing_histogram(idx, B, T, E, tags=tags, n_tags=n_tags)
+    assert pos.tolist() == pos_bf and tag.tolist() == tag_bf
+
+
+def check_routing_histogram_invariants():
+    # top-K routing of random probabilities: every position sees B*K
+    # selections; per-image tags reproduce the balance statistic's counts; a
+    # single tag holds the column sums of the position histogram
+    inp = _tiny_inputs(seed=23, B=4, T=9, E=6, K=2)
+    cfg = inp.cfg
+    P = om.softmax(om.gate_logits(inp.x, inp.w_gate))
+    idx, _ = om.topk_select(P, cfg.K)
+    pos, tag = om.routing_histogram(idx, cfg.B, cfg.T, cfg.E,
+                                    tags=np.arange(cfg.B), n_tags=cfg.B)
+    assert (pos.sum(axis=1) == cfg.B * cfg.K).all()
+    counts, _, _ = om.balance_stats(P, idx, cfg.B, cfg.T, cfg.K, 0.01)
+    assert np.array_equal(tag, counts)
+    _, tag1 = om.routing_histogram(idx, cfg.B, cfg.T, cfg.E,
+                                   tags=np.zeros(cfg.B, np.int64), n_tags=1)
+    assert np.array_equal(tag1[0], pos.sum(axis=0))
+    # race: K*N selections in all, empty slots count nowhere
+    ridx, _, _ = om.race_select(P, cfg.K)
+    rpos, _ = om.routing_histogram(ridx, cfg.B, cfg.T, cfg.E)
+    assert rpos.sum() == cfg.K * cfg.N
+    # a zero gate: every token keeps experts 0..K-1
+    P0 = om.softmax(om.gate_logits(inp.x, np.zeros_like(inp.w_gate)))
+    zidx, _ = om.topk_select(P0, cfg.K)
+    zpos, _ = om.routing_histogram(zidx, cfg.B, cfg.T, cfg.E)
+    expect = np.zeros((cfg.T, cfg.E), np.int64)
+    expect[:, :cfg.K] = cfg.B
+    assert np.array_equal(zpos, expect)
+
+
 ALL_CHECKS = [check_gate_logits, check_softmax, check_topk, check_race,
               check_permute, check_gelu, check_expert_mlp, check_dense_mask,
               check_dense_mlp_special_case, check_full_mixture,
               check_one_hot_channels, check_balance_uniform_probs,
               check_balance_uniform_counts, check_balance_invariants,
-              check_balance_golden]
+              check_balance_golden, check_routing_histogram_golden,
+              check_routing_histogram_brute, check_routing_histogram_invariants]

@@ -127,6 +127,36 @@ def _permute_unstable(idx, E):
     return counts, offsets, rt, sr
 
 
+def _hist_wraps_empty(idx, B, T, E, tags=None, n_tags=0):
+    # an empty slot (-1) counted as the last expert (Python's negative index)
+    idx = np.asarray(idx)
+    return _orig["routing_histogram"](np.where(idx < 0, E - 1, idx), B, T, E,
+                                      tags, n_tags)
+
+
+def _hist_position_by_image(idx, B, T, E, tags=None, n_tags=0):
+    # rows taken image-major as position-major: position = t // B
+    idx = np.asarray(idx)
+    N = idx.shape[0]
+    perm = (np.arange(N) % B) * T + np.arange(N) // B
+    return _orig["routing_histogram"](idx[perm], B, T, E, tags, n_tags)
+
+
+def _hist_tag_by_position(idx, B, T, E, tags=None, n_tags=0):
+    # the tag looked up by token position instead of by image
+    pos, tag = _orig["routing_histogram"](idx, B, T, E, None, 0)
+    if tags is None:
+        return pos, None
+    out = np.zeros((n_tags, E), np.int64)
+    idx = np.asarray(idx)
+    for t in range(idx.shape[0]):
+        g = tags[(t % T) % len(tags)]
+        for e in idx[t]:
+            if 0 <= e < E and 0 <= g < n_tags:
+                out[g, e] += 1
+    return pos, out
+
+
 MUTATIONS = {
     "gelu_no_cubic": ("gelu_tanh", _gelu_no_cubic),
     "gelu_wrong_constant": ("gelu_tanh", _gelu_wrong_const),
@@ -147,6 +177,9 @@ MUTATIONS = {
     "balance_drops_K": ("balance_stats", _balance_no_K),
     "balance_selected_probs": ("balance_stats", _balance_selected_probs),
     "permute_unstable": ("permute", _permute_unstable),
+    "histogram_counts_empty_slots": ("routing_histogram", _hist_wraps_empty),
+    "histogram_position_by_image": ("routing_histogram", _hist_position_by_image),
+    "histogram_tag_by_position": ("routing_histogram", _hist_tag_by_position),
 }
 
 
