@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes five "
                          "times (reference for the HBM byte counters)")
+    ap.add_argument("--analytics", action="store_true",
+                    help="instead of the layer, time the routing histogram "
+                         "(counts by patch position and by image tag) on the "
+                         "layer's routing")
     return ap.parse_args()
 
 
@@ -105,6 +109,56 @@ def kernel_work(cfg, gather: bool):
     return w
 
 
+def analytics_bench(args):
+    """Time moe_routing_histogram on one batch's top-K routing of the
+    configured layer, with one class tag per image out of 1000."""
+    import torch
+    import synth
+    from sparse_moe_diffusion_amd import _lib, layer, ops
+
+    _lib.load()
+    cfg = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    x = layer._to_device(inp.x, dt, "cuda")
+    wts = layer.LayerWeights.from_inputs(inp, "cuda")
+    buf = layer.LayerBuffers(cfg, "cuda", gather=True)
+    layer.gate(cfg, x, wts, buf)
+    n_tags = 1000
+    tags = (torch.arange(cfg.B, device="cuda", dtype=torch.int32) * 37) % n_tags
+    pos = torch.zeros(cfg.T, cfg.E, dtype=torch.int64, device="cuda")
+    tag = torch.zeros(n_tags, cfg.E, dtype=torch.int64, device="cuda")
+
+    def call():
+        ops.moe_routing_histogram(buf.topk_idx, cfg.B, cfg.T, cfg.E, pos, tags,
+                                  tag)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = (cfg.N * cfg.Kmax * 4 + cfg.B * 4 + 2 * cfg.T * cfg.E * 8
+              + 2 * n_tags * cfg.E * 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "routing histogram by patch position and image "
+                      "tag (one batch)", "value": round(ms * 1e3, 2),
+                      "unit": "us per call", "higher_is_better": False,
+                      "steps": args.steps, "warmup": args.warmup,
+                      "config": {"workload": cfg.name, "images": cfg.B,
+                                 "tokens_per_image": cfg.T, "experts": cfg.E,
+                                 "slots": cfg.Kmax, "tags": n_tags},
+                      "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 5),
+                      "bound": "launch latency"}), flush=True)
+
+
 def cpu_baseline(cfg, inp, target_s):
     """The CPU oracle on whole images of the same workload until about
     ``target_s`` seconds of CPU work: tokens/s."""
@@ -139,6 +193,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.analytics:
+        analytics_bench(args)
         return
     import torch
     import synth

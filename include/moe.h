@@ -240,6 +240,37 @@ moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                              int32_t* counts, float* prob_sums, float* loss,
                              hipStream_t stream);
 
+/*
+ * Routing analytics ("Scaling Diffusion Transformers to 16 Billion
+ * Parameters", Expert Specialization Analysis: the frequency of expert
+ * selection by spatial position, by image class and by denoising time step;
+ * "DiT-MoE" project hub page, section 4, analysis tools).  Adds the counts
+ * of one batch of B images x T tokens to caller-owned totals:
+ *
+ *   pos_counts[p][i] += number of (image b, slot k) with
+ *                       topk_idx[b*T + p][k] == i
+ *   tag_counts[g][i] += number of (token t, slot k) of the images b with
+ *                       image_tag[b] == g and topk_idx[t][k] == i
+ *
+ * Entries of topk_idx outside [0, E) (the -1 of an empty slot) count
+ * nowhere; an image whose tag lies outside [0, n_tags) counts only by
+ * position.  Counts are exact integers, independent of scheduling.  The
+ * caller zero-fills the totals before the first batch; the frequencies of
+ * the analysis are the totals divided by their sums.
+ *
+ *   topk_idx [B*T][Kmax] int32 device;  image_tag [B] int32 device or NULL
+ *   (then tag_counts is ignored);  pos_counts [T][E], tag_counts
+ *   [n_tags][E] int64 device, read and written
+ * Errors: INVALID_ARGUMENT for B < 0, T < 1, E < 1, Kmax < 1, a null
+ *   topk_idx (B > 0) or pos_counts, or image_tag given without n_tags >= 1
+ *   and tag_counts; UNSUPPORTED for E or Kmax > 64 or B*T*Kmax >= 2^31.
+ */
+moe_status moe_routing_histogram(const int32_t* topk_idx, int32_t B,
+                                 int32_t T, int32_t E, int32_t Kmax,
+                                 const int32_t* image_tag, int32_t n_tags,
+                                 int64_t* pos_counts, int64_t* tag_counts,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -249,4 +249,30 @@ moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                   fn);
 }
 
+moe_status moe_routing_histogram(const int32_t* topk_idx, int32_t B,
+                                 int32_t T, int32_t E, int32_t Kmax,
+                                 const int32_t* image_tag, int32_t n_tags,
+                                 int64_t* pos_counts, int64_t* tag_counts,
+                                 hipStream_t stream) {
+  const char* fn = "moe_routing_histogram";
+  if (B < 0 || T < 1 || E < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need B >= 0, T >= 1, E >= 1, Kmax >= 1", fn);
+  if (image_tag != nullptr && (n_tags < 1 || tag_counts == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: image_tag needs n_tags >= 1 and tag_counts", fn);
+  CHECK_PTR_IF(B > 0, topk_idx); CHECK_PTR(pos_counts);
+  if (E > kMaxE || Kmax > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d / Kmax=%d above %d", fn, E, Kmax,
+                kMaxE);
+  if (static_cast<int64_t>(B) * T * Kmax >= kI32Limit ||
+      static_cast<int64_t>(n_tags) * E >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: B*T*Kmax must stay below 2^31", fn);
+  return from_hip(moe::launch_routing_hist(topk_idx, B, T, E, Kmax, image_tag,
+                                           image_tag ? n_tags : 0, pos_counts,
+                                           image_tag ? tag_counts : nullptr,
+                                           stream),
+                  fn);
+}
+
 }  // extern "C"

@@ -58,4 +58,10 @@ hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int32_t* counts, float* psum, float* loss,
                           hipStream_t stream);
 
+// analytics.hip
+hipError_t launch_routing_hist(const int32_t* idx, int B, int T, int E,
+                               int Kmax, const int32_t* tags, int n_tags,
+                               int64_t* pos_counts, int64_t* tag_counts,
+                               hipStream_t stream);
+
 }  // namespace moe

@@ -91,3 +91,14 @@ def moe_balance_stats(probs, topk_idx, B: int, T: int, K: int, alpha: float,
     _lib.call("moe_balance_stats", _ptr(probs), _ptr(topk_idx), B, T, E, Kmax,
               K, alpha, mode, _ptr(counts), _ptr(prob_sums), _ptr(loss),
               _stream())
+
+
+def moe_routing_histogram(topk_idx, B: int, T: int, E: int, pos_counts,
+                          image_tag=None, tag_counts=None):
+    """Add one batch's expert-selection counts by position (and by image
+    tag) into the int64 totals pos_counts [T][E] (and tag_counts)."""
+    Kmax = topk_idx.shape[1]
+    n_tags = 0 if tag_counts is None else tag_counts.shape[0]
+    _lib.call("moe_routing_histogram", _ptr(topk_idx), B, T, E, Kmax,
+              _ptr(image_tag), n_tags, _ptr(pos_counts), _ptr(tag_counts),
+              _stream())

@@ -155,3 +155,29 @@ def test_binding_raises_on_error():
     with pytest.raises(_lib.MoEError, match="MOE_ERR_INVALID_ARGUMENT"):
         _lib.call("moe_gate_topk", None, 1, None, None, 1, 8, 8, 2, 0, None,
                   None, None, None, 0, None)
+
+
+def _hist(**kw):
+    a = dict(idx=FAKE, B=4, T=16, E=8, Kmax=2, tags=None, n_tags=0, pos=FAKE,
+             tag=None, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_routing_histogram", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(pos=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(Kmax=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(tags=FAKE, n_tags=0, tag=FAKE), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(tags=FAKE, n_tags=10, tag=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=65), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(Kmax=65), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(B=1 << 20, T=1 << 10, Kmax=2), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_routing_histogram_rejects(kw, status):
+    ensure_built()
+    assert _hist(**kw) == status
+    assert _lib.last_error()

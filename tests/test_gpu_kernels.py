@@ -334,3 +334,64 @@ def test_balance(B, T, E, K, race, mode):
     assert np.array_equal(to_np(counts), c_o)
     assert np.allclose(to_np(ps), p_o, rtol=1e-5, atol=1e-5)
     assert abs(float(to_np(loss)[0]) - l_o) <= 1e-5 * abs(l_o)
+
+
+# ------------------------------------------------------- routing analytics --
+
+def _run_hist(idx, B, T, E, tags, n_tags, calls=1):
+    _lib, ops = _ops()
+    pos = torch.zeros(T, E, dtype=torch.int64, device=DEV)
+    tag = None if tags is None else torch.zeros(n_tags, E, dtype=torch.int64,
+                                                device=DEV)
+    ti = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(DEV)
+    tg = None if tags is None else torch.from_numpy(
+        np.asarray(tags, dtype=np.int32)).to(DEV)
+    for _ in range(calls):
+        ops.moe_routing_histogram(ti, B, T, E, pos, tg, tag)
+    torch.cuda.synchronize()
+    return to_np(pos), None if tag is None else to_np(tag)
+
+
+@pytest.mark.parametrize("B,T,E,Kmax,kind,tagged", [
+    (1, 1, 1, 1, "topk", True), (3, 70, 8, 2, "topk", True),
+    (9, 129, 16, 2, "race", True), (32, 1024, 8, 2, "topk", True),
+    (5, 64, 64, 4, "random", True), (17, 33, 5, 3, "random", False),
+    (16, 1024, 16, 16, "race", True)])
+def test_routing_histogram(B, T, E, Kmax, kind, tagged):
+    """Bit-exact counts; random rows include -1 and indices >= E, and some
+    tags lie outside [0, n_tags)."""
+    rng = np.random.default_rng(B * 1000 + T + E)
+    N = B * T
+    if kind == "random":
+        idx = rng.integers(-1, E + 3, size=(N, Kmax))
+    else:
+        P = oracle.softmax(rng.standard_normal((N, E)) * 2.0)
+        if kind == "race":
+            idx, _, _ = oracle.race_select(P, Kmax if Kmax < E else 2)
+        else:
+            idx, _ = oracle.topk_select(P, Kmax)
+    n_tags = 7
+    tags = rng.integers(-1, n_tags + 1, size=B) if tagged else None
+    pos, tag = _run_hist(idx, B, T, E, tags, n_tags)
+    pos_o, tag_o = oracle.routing_histogram(idx, B, T, E, tags=tags,
+                                            n_tags=n_tags)
+    assert np.array_equal(pos, pos_o)
+    if tagged:
+        assert np.array_equal(tag, tag_o)
+
+
+def test_routing_histogram_accumulates():
+    """Two calls add: totals are twice one batch's counts."""
+    rng = np.random.default_rng(5)
+    B, T, E = 6, 200, 8
+    P = oracle.softmax(rng.standard_normal((B * T, E)))
+    idx, _ = oracle.topk_select(P, 2)
+    tags = np.arange(B) % 3
+    pos, tag = _run_hist(idx, B, T, E, tags, 3, calls=2)
+    pos_o, tag_o = oracle.routing_histogram(idx, B, T, E, tags=tags, n_tags=3)
+    assert np.array_equal(pos, 2 * pos_o) and np.array_equal(tag, 2 * tag_o)
+
+
+def test_routing_histogram_empty_batch():
+    pos, tag = _run_hist(np.zeros((0, 2), np.int32), 0, 16, 8, None, 0)
+    assert not pos.any()
