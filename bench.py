@@ -102,6 +102,8 @@ def kernel_work(cfg, gather: bool):
         "routed_down": ("flops", 2 * A * D * H),
         "shared_up": ("flops", 2 * N * D * H * n_s),
         "shared_down": ("flops", 2 * N * D * H * n_s),
+        # stage 2 of the shared experts with the combine in its epilogue
+        "shared_down_combine": ("flops", 2 * N * D * H * n_s),
         "combine": ("bytes", A * D * eb + (N * D * eb if n_s else 0) +
                     N * D * eb + N * Kmax * 8),
         "balance": ("bytes", N * E * 4 + N * Kmax * 4),
@@ -210,7 +212,7 @@ def main():
     x = layer._to_device(inp.x, dt, dev)
     wts = layer.LayerWeights.from_inputs(inp, dev)
     buf = layer.LayerBuffers(cfg, dev, gather=gather)
-    steps = [s for s in layer.STEPS if not (cfg.n_s == 0 and s[0].startswith("shared"))]
+    steps = list(layer.steps(cfg, buf))
 
     def one_step(evs=None):
         for i, (_, fn) in enumerate(steps):
@@ -255,7 +257,8 @@ def main():
     # dominant kernel: the grouped GEMM stage with the larger total time;
     # its two launches per step (routed, shared) carry equal FLOPs.
     up = [n for n in ("routed_up", "shared_up") if n in per_call]
-    down = [n for n in ("routed_down", "shared_down") if n in per_call]
+    down = [n for n in ("routed_down", "shared_down", "shared_down_combine")
+            if n in per_call]
     t_up = sum(per_call[n] for n in up)
     t_down = sum(per_call[n] for n in down)
     dom = up if t_up >= t_down else down

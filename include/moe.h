@@ -241,6 +241,33 @@ moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                              hipStream_t stream);
 
 /*
+ * Stage 2 of the shared experts fused with the weighted combine ("Scaling
+ * Diffusion Transformers to 16 Billion Parameters": eq. MLP for the shared
+ * experts, eq. MoE(x) for the routed ones, shared experts added with
+ * weight 1).  For every token t < N:
+ *
+ *   s[t] = bf16( h[t] . w2^T (+ b2) )                  (fp32 accumulation)
+ *   y[t] = sum over k < Kmax with slot_row[t][k] >= 0, in slot order, of
+ *            topk_w[t][k] * y_rows[slot_row[t][k]]  +  s[t]
+ * in fp32, rounded once to bf16: bit for bit what moe_grouped_ffn (stage 2
+ * of the shared experts, one group of all N tokens) followed by moe_combine
+ * produce, without writing or reading the shared output.
+ *
+ *   h [N][H] bf16 (stage-1 output of the shared experts, H = n_s * hidden);
+ *   w2 [D][H] bf16 (the shared experts' W2 side by side); b2 [D] fp32 or
+ *   NULL;  y_rows [*][D] bf16 routed outputs;  slot_row, topk_w [N][Kmax];
+ *   y [N][D] bf16 out
+ * Errors: INVALID_ARGUMENT for null pointers (N > 0), N < 0, D, H or
+ *   Kmax < 1; UNSUPPORTED for a dtype other than bf16, Kmax > 4, D or H
+ *   not multiples of 8, N*Kmax >= 2^31.
+ */
+moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
+                                int32_t D, int32_t H, const void* w2,
+                                const float* b2, const void* y_rows,
+                                const int32_t* slot_row, const float* topk_w,
+                                int32_t Kmax, void* y, hipStream_t stream);
+
+/*
  * Routing analytics ("Scaling Diffusion Transformers to 16 Billion
  * Parameters", Expert Specialization Analysis: the frequency of expert
  * selection by spatial position, by image class and by denoising time step;

@@ -249,6 +249,33 @@ moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                   fn);
 }
 
+moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
+                                int32_t D, int32_t H, const void* w2,
+                                const float* b2, const void* y_rows,
+                                const int32_t* slot_row, const float* topk_w,
+                                int32_t Kmax, void* y, hipStream_t stream) {
+  const char* fn = "moe_ffn_down_combine";
+  if (N < 0 || D < 1 || H < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need N >= 0, D >= 1, H >= 1, Kmax >= 1", fn);
+  const bool rows = N > 0;
+  CHECK_PTR_IF(rows, h); CHECK_PTR_IF(rows, w2); CHECK_PTR_IF(rows, y_rows);
+  CHECK_PTR_IF(rows, slot_row); CHECK_PTR_IF(rows, topk_w); CHECK_PTR_IF(rows, y);
+  if (dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (Kmax > 4)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: Kmax=%d above 4", fn, Kmax);
+  if (D % 8 != 0 || H % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
+                fn, D, H);
+  if (N >= kI32Limit || N * Kmax >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
+  return from_hip(moe::launch_ffn_down_combine(h, N, D, H, w2, b2, y_rows,
+                                               slot_row, topk_w, Kmax, y,
+                                               stream),
+                  fn);
+}
+
 moe_status moe_routing_histogram(const int32_t* topk_idx, int32_t B,
                                  int32_t T, int32_t E, int32_t Kmax,
                                  const int32_t* image_tag, int32_t n_tags,

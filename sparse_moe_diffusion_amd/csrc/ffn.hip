@@ -42,7 +42,12 @@ namespace moe {
 
 namespace {
 
-enum Epi { kEpiGelu = 0, kEpiStore = 1 };
+// kEpiCombine: the stage-2 store of the shared experts fused with the
+// weighted combine of the routed outputs (one group holding every token).
+enum Epi { kEpiGelu = 0, kEpiStore = 1, kEpiCombine = 2 };
+
+// Most slots per token the fused combine takes (top-K routing, K <= 4).
+constexpr int kCombineMaxSlots = 4;
 
 struct GemmParams {
   const void* a;           // activation rows [*][Kd]
@@ -50,9 +55,15 @@ struct GemmParams {
   const void* w;           // [G][Nd][Kd]
   const float* bias;       // [G][Nd] or null
   void* c;                 // [total][Nd]
-  const int64_t* offsets;  // [G+1], device
+  const int64_t* offsets;  // [G+1], device; null: one group of all rows
   int64_t total;
   int G, Nd, Kd;
+  // kEpiCombine only: c[t] = this GEMM's (bf16) output for token t plus, in
+  // slot order, cmb_w[t][k] * cmb_rows[cmb_slot[t][k]] for the slots >= 0.
+  const void* cmb_rows;      // [*][Nd] bf16 routed expert outputs
+  const int32_t* cmb_slot;   // [total][cmb_kmax]
+  const float* cmb_w;        // [total][cmb_kmax]
+  int cmb_kmax;              // 1..kCombineMaxSlots
 };
 
 struct TileLoc {
@@ -131,8 +142,8 @@ __device__ void build_group_table(const GemmParams& p, int32_t* tab, int wave,
       int64_t r0 = 0, r1 = 0;
       int tiles = 0;
       if (g < p.G) {
-        r0 = min(max(p.offsets[g], int64_t(0)), p.total);
-        r1 = min(max(p.offsets[g + 1], r0), p.total);
+        r0 = p.offsets ? min(max(p.offsets[g], int64_t(0)), p.total) : 0;
+        r1 = p.offsets ? min(max(p.offsets[g + 1], r0), p.total) : p.total;
         tiles = static_cast<int>((r1 - r0 + BM - 1) / BM) * ntn;
       }
       int inc = tiles;   // inclusive scan of tile counts over the wave
@@ -293,10 +304,16 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
   constexpr int kMainElems = (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2;
   constexpr int kPfElems = PF ? 256 : 0;
+  constexpr int kCmbInts = EPI == kEpiCombine ? 2 * BM * kCombineMaxSlots : 0;
+  static_assert(EPI != kEpiCombine || OUT_BF16, "the combine writes bf16");
   __shared__ __attribute__((aligned(1024)))
-  uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM)];
+  uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM + kCmbInts)];
   int32_t* const tab = reinterpret_cast<int32_t*>(lds + kMainElems + kPfElems);
   int32_t* const sidx = tab + kTabInts;   // 2 x BM gathered source rows
+  // kEpiCombine: the tile's slot rows and weights, [BM][cmb_kmax] each.
+  int32_t* const cslot = sidx + 2 * BM;
+  const float* const cwt =
+      reinterpret_cast<const float*>(cslot + BM * kCombineMaxSlots);
   uint16_t* const sA0 = lds;
   uint16_t* const sA1 = sA0 + BM * kBK;
   uint16_t* const sB0 = sA1 + BM * kBK;
@@ -307,6 +324,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const uint32_t bB0 = bA1 + BM * kBK * 2, bB1 = bB0 + BN * kBK * 2;
   const uint32_t bPf = lds0 + kMainElems * 2;
   const uint32_t bIdx = bPf + kPfElems * 2 + kTabInts * 4;
+  const uint32_t bCmb = bIdx + 2 * BM * 4;
 
   // Persistent: the grid is a multiple of 8 workgroups, about one per CU,
   // dealt round-robin to the 8 XCDs.  The pw workgroups of one XCD take
@@ -560,6 +578,27 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       MOE_FETCH_ROWS(nloc, (it + 1) & 1, lane);
   }
 
+  // kEpiCombine: the slot rows and weights of this tile's tokens, for the
+  // epilogue (rows past the end read zero and are never stored).
+  if constexpr (EPI == kEpiCombine) {
+    const int km = p.cmb_kmax;
+    const uint32_t nb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        min(static_cast<int>(loc.row_end - loc.row0), BM) * km * 4));
+    const __amdgpu_buffer_rsrc_t rsS = make_rsrc(
+        reinterpret_cast<const void*>(
+            uniform64(reinterpret_cast<int64_t>(p.cmb_slot + loc.row0 * km))),
+        nb);
+    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(
+        reinterpret_cast<const void*>(
+            uniform64(reinterpret_cast<int64_t>(p.cmb_w + loc.row0 * km))),
+        nb);
+    for (int q = wave; q < BM * km / 64; q += kWaves) {
+      const uint32_t o = static_cast<uint32_t>(q * 64 + lane) * 4u;
+      dma_untracked<4>(rsS, bCmb + q * 256, o);
+      dma_untracked<4>(rsW, bCmb + BM * kCombineMaxSlots * 4 + q * 256, o);
+    }
+  }
+
   MOE_ISSUE(0, bA0, bB0, 0, NQ);
   stage_barrier();
   MOE_FRAGS(fa0, fb0, sA0, sB0, 0);
@@ -613,6 +652,74 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     // the hint the write burst at the end of every tile allocates L2 lines).
     constexpr int kChunks = BN / 8;
     uint16_t* const c = static_cast<uint16_t*>(p.c);
+    if constexpr (EPI == kEpiCombine) {
+      // y[t] = sum over the slots >= 0, in slot order, of w * routed row,
+      // then plus the staged (bf16) shared output, in fp32, rounded once:
+      // the arithmetic of the separate combine kernel.  Chunks go in
+      // batches of kB whose routed-row loads are all issued before the
+      // first multiply-add.
+      constexpr int kIters = (BM * kChunks + 64 * kWaves - 1) / (64 * kWaves);
+      constexpr int kB = 6;
+      const uint16_t* const yr = static_cast<const uint16_t*>(p.cmb_rows);
+      const int km = p.cmb_kmax;
+      for (int i0 = 0; i0 < kIters; i0 += kB) {
+        uint4 v[kB][kCombineMaxSlots];
+        int32_t sl[kB][kCombineMaxSlots];
+        float wk[kB][kCombineMaxSlots];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = tid + (i0 + b) * 64 * kWaves;
+          const int r = idx / kChunks;
+          const int f = loc.n0 + (idx - r * kChunks) * 8;
+          const bool ok = idx < BM * kChunks && loc.row0 + r < loc.row_end &&
+                          f < p.Nd;
+#pragma unroll
+          for (int k = 0; k < kCombineMaxSlots; ++k) {
+            sl[b][k] = -1;
+            wk[b][k] = 0.0f;
+            v[b][k] = make_uint4(0, 0, 0, 0);
+            if (ok && k < km) {
+              sl[b][k] = cslot[r * km + k];
+              wk[b][k] = cwt[r * km + k];
+            }
+            if (sl[b][k] >= 0)
+              v[b][k] = *reinterpret_cast<const uint4*>(
+                  yr + static_cast<int64_t>(sl[b][k]) * p.Nd + f);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = tid + (i0 + b) * 64 * kWaves;
+          const int r = idx / kChunks;
+          const int f = loc.n0 + (idx - r * kChunks) * 8;
+          const int64_t row = loc.row0 + r;
+          if (idx >= BM * kChunks || row >= loc.row_end || f >= p.Nd) continue;
+          float a8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[j] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < kCombineMaxSlots; ++k) {
+            if (sl[b][k] < 0) continue;
+            float yv[8];
+            unpack8(v[b][k], yv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a8[j] = fmaf(wk[b][k], yv[j], a8[j]);
+          }
+          float sh[8];
+          unpack8(*reinterpret_cast<const uint4*>(
+                      &lds[r * kOutPitch + (f - loc.n0)]), sh);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[j] += sh[j];
+          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+          u32x4 o;
+          o[0] = pack_bf16x2(a8[0], a8[1]);
+          o[1] = pack_bf16x2(a8[2], a8[3]);
+          o[2] = pack_bf16x2(a8[4], a8[5]);
+          o[3] = pack_bf16x2(a8[6], a8[7]);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(c + row * p.Nd + f));
+        }
+      }
+    } else
     for (int idx = tid; idx < BM * kChunks; idx += 64 * kWaves) {
       const int r = idx / kChunks;
       const int f = loc.n0 + (idx - r * kChunks) * 8;
@@ -763,6 +870,21 @@ int persistent_grid(int tiles) {
 }
 
 }  // namespace
+
+hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
+                                  const void* w2, const float* b2,
+                                  const void* y_rows, const int32_t* slot_row,
+                                  const float* topk_w, int Kmax, void* y,
+                                  hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  GemmParams p{h,       nullptr, w2,       b2,     y, nullptr, N, 1, D, H,
+               y_rows, slot_row, topk_w, Kmax};
+  hipLaunchKernelGGL(
+      (gemm_bf16_kernel<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
+      dim3(persistent_grid(tile_grid(p, kDnBM, kDnBN))), dim3(64 * kDnWT * kDnWF),
+      0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
                       hipStream_t stream) {

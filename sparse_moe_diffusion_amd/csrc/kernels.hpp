@@ -45,6 +45,13 @@ struct FfnArgs {
   bool y_f32;               // output dtype
 };
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
+// Stage 2 of the shared experts (one group of all N tokens, bf16) fused with
+// the weighted combine of the routed outputs; Kmax <= 4.
+hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
+                                  const void* w2, const float* b2,
+                                  const void* y_rows, const int32_t* slot_row,
+                                  const float* topk_w, int Kmax, void* y,
+                                  hipStream_t stream);
 
 // combine.hip
 hipError_t launch_combine(const void* y_rows, bool y_bf16,

@@ -133,6 +133,20 @@ def shared_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
                             wts.w2s, None, buf.h_shared, buf.y_shared, stages)
 
 
+def fuses_combine(cfg, buf: LayerBuffers) -> bool:
+    """The shared experts' stage 2 and the combine run as one kernel for
+    bf16 layers with shared experts, bf16 routed outputs and at most 4 slots
+    per token."""
+    return (cfg.dtype == "bf16" and cfg.n_s > 0 and cfg.Kmax <= 4
+            and buf.y_rows.dtype == torch.bfloat16)
+
+
+def shared_down_combine(cfg, wts: LayerWeights, buf: LayerBuffers):
+    """Stage 2 of the shared experts fused with the weighted combine: y."""
+    ops.moe_ffn_down_combine(buf.h_shared, wts.w2s, None, buf.y_rows,
+                             buf.slot_row, buf.topk_w, buf.y)
+
+
 def combine(cfg, buf: LayerBuffers):
     ops.moe_combine(buf.y_rows, buf.slot_row, buf.topk_w, buf.y_shared, buf.y)
 
@@ -159,6 +173,22 @@ STEPS = (("gate", lambda c, x, w, b: gate(c, x, w, b)),
          ("combine", lambda c, x, w, b: combine(c, b)),
          ("balance", lambda c, x, w, b: balance(c, b)))
 
+# The same with the shared experts' stage 2 and the combine fused (what
+# forward() runs when fuses_combine(cfg, buf)): bit for bit the same y.
+FUSED_STEPS = tuple(
+    s for s in STEPS if s[0] not in ("shared_down", "combine")
+)[:-1] + (("shared_down_combine",
+           lambda c, x, w, b: shared_down_combine(c, w, b)),
+          STEPS[-1])
+
+
+def steps(cfg, buf: LayerBuffers):
+    """The calls forward() makes for this layer, in order."""
+    if fuses_combine(cfg, buf):
+        return FUSED_STEPS
+    return tuple(s for s in STEPS
+                 if not (cfg.n_s == 0 and s[0].startswith("shared")))
+
 
 def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
             balance_mode: str = "sequence") -> LayerBuffers:
@@ -168,7 +198,10 @@ def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
     routed_ffn(cfg, x, wts, buf, UP)
     shared_ffn(cfg, x, wts, buf, UP)
     routed_ffn(cfg, x, wts, buf, DOWN)
-    shared_ffn(cfg, x, wts, buf, DOWN)
-    combine(cfg, buf)
+    if fuses_combine(cfg, buf):
+        shared_down_combine(cfg, wts, buf)
+    else:
+        shared_ffn(cfg, x, wts, buf, DOWN)
+        combine(cfg, buf)
     balance(cfg, buf, balance_mode)
     return buf

@@ -68,7 +68,10 @@ def moe_permute(x, topk_idx, E: int, K: int, expert_counts, expert_offsets,
 
 def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
                     w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH):
-    G, H, D = w1.shape
+    if w1 is not None:
+        G, H, D = w1.shape
+    else:                      # stage 2 alone
+        G, D, H = w2.shape
     _lib.call("moe_grouped_ffn", _ptr(x_rows), _ptr(row_index),
               dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
               _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(y_rows),
@@ -102,3 +105,12 @@ def moe_routing_histogram(topk_idx, B: int, T: int, E: int, pos_counts,
     _lib.call("moe_routing_histogram", _ptr(topk_idx), B, T, E, Kmax,
               _ptr(image_tag), n_tags, _ptr(pos_counts), _ptr(tag_counts),
               _stream())
+
+
+def moe_ffn_down_combine(h, w2, b2, y_rows, slot_row, topk_w, y):
+    """Shared experts' stage 2 fused with the weighted combine: y [N][D]."""
+    N, H = h.shape
+    D = w2.shape[-2]
+    _lib.call("moe_ffn_down_combine", _ptr(h), dtype_code(h.dtype), N, D, H,
+              _ptr(w2), _ptr(b2), _ptr(y_rows), _ptr(slot_row), _ptr(topk_w),
+              slot_row.shape[1], _ptr(y), _stream())

@@ -181,3 +181,27 @@ def test_routing_histogram_rejects(kw, status):
     ensure_built()
     assert _hist(**kw) == status
     assert _lib.last_error()
+
+
+def _fdc(**kw):
+    a = dict(h=FAKE, dt=_lib.MOE_BF16, N=64, D=128, H=256, w2=FAKE, b2=None,
+             yr=FAKE, sr=FAKE, w=FAKE, Kmax=2, y=FAKE, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_ffn_down_combine", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(sr=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(y=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(Kmax=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(dt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(Kmax=5), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(N=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_ffn_down_combine_rejects(kw, status):
+    ensure_built()
+    assert _fdc(**kw) == status
+    assert _lib.last_error()

@@ -395,3 +395,58 @@ def test_routing_histogram_accumulates():
 def test_routing_histogram_empty_batch():
     pos, tag = _run_hist(np.zeros((0, 2), np.int32), 0, 16, 8, None, 0)
     assert not pos.any()
+
+
+# ------------------------------------------- shared stage 2 + combine, fused --
+
+@pytest.mark.parametrize("N,D,H,Kmax,empty,bias", [
+    (1, 64, 128, 1, 0.0, False), (300, 128, 256, 2, 0.1, True),
+    (1000, 384, 512, 4, 0.3, False), (2049, 1152, 384, 2, 0.0, True),
+    (777, 200, 136, 3, 0.5, True)])
+def test_ffn_down_combine_matches_separate(N, D, H, Kmax, empty, bias):
+    """The fused kernel gives the bits of stage 2 (one group of all tokens)
+    followed by the combine kernel, and both agree with the oracle."""
+    _lib, ops = _ops()
+    rng = np.random.default_rng(N + D + H + Kmax)
+    q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
+    h = q(rng.standard_normal((N, H)))
+    w2 = q(rng.standard_normal((1, D, H)) * 0.05)
+    b2 = (rng.standard_normal((1, D)) * 0.1).astype(np.float32) if bias else None
+    A = N * Kmax
+    yr = q(rng.standard_normal((A, D)))
+    sr = rng.permutation(A).reshape(N, Kmax).astype(np.int32)
+    sr[rng.random((N, Kmax)) < empty] = -1
+    w = rng.random((N, Kmax)).astype(np.float32)
+    bf = lambda a: _bits_tensor(a, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    th, tw2, tyr = bf(h), bf(w2), bf(yr)
+    tb2 = None if b2 is None else dev(b2)
+    tsr, tw = dev(sr), dev(w)
+    # separate: stage 2 of one group of all N tokens, then the combine
+    y_sh = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    offs = dev(np.array([0, N], np.int64))
+    ops.moe_grouped_ffn(None, None, N, offs, None, None, tw2, tb2, th, y_sh,
+                        _lib.MOE_FFN_DOWN)
+    y_sep = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    ops.moe_combine(tyr, tsr, tw, y_sh, y_sep)
+    y_fused = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    ops.moe_ffn_down_combine(th, tw2, tb2, tyr, tsr, tw, y_fused)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused.view(torch.int16), y_sep.view(torch.int16))
+    ref = h.astype(np.float64) @ w2[0].T.astype(np.float64)
+    if b2 is not None:
+        ref += b2[0]
+    for k in range(Kmax):
+        m = sr[:, k] >= 0
+        ref[m] += w[m, k, None].astype(np.float64) * yr[sr[m, k]]
+    assert_close(to_np(y_fused), ref, "bf16", "fused stage 2 + combine")
+
+
+def test_ffn_down_combine_empty():
+    _lib, ops = _ops()
+    z = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    w2 = torch.zeros(1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    sr = torch.empty(0, 2, dtype=torch.int32, device=DEV)
+    w = torch.empty(0, 2, dtype=torch.float32, device=DEV)
+    ops.moe_ffn_down_combine(z, w2, None, z, sr, w, z)
+    torch.cuda.synchronize()
