@@ -37,7 +37,11 @@ Readings where the pages are silent (each also listed in the design notes):
   * a token's slots are in descending-probability order for top-K;
   * the balance statistic is taken per image (T tokens) and averaged over
     the B images; a global variant pools all B*T tokens;
-  * no capacity limit: every selection is computed.
+  * no capacity limit: every selection is computed;
+  * backward (training, as the pages train with the balance loss added): the
+    gradient of <dy, y> + dloss * L_balance with the routing held fixed --
+    the selection itself has no gradient, the slot weights g(x)_i = P[t][i]
+    do, and the balance statistic's counts carry none.
 """
 from __future__ import annotations
 
@@ -236,6 +240,110 @@ def shared_output(x, w1s, w2s, tokens=None):
     for s in range(w1s.shape[0]):
         y += expert_mlp(x, w1s[s], w2s[s])
     return y
+
+
+def gelu_tanh_grad(u):
+    """Derivative of gelu_tanh: with z = sqrt(2/pi) (u + 0.044715 u^3),
+    d/du [0.5 u (1 + tanh z)] = 0.5 (1 + tanh z)
+                                + 0.5 u (1 - tanh^2 z) sqrt(2/pi) (1 + 3 0.044715 u^2)."""
+    u = _f64(u)
+    th = np.tanh(GELU_C * (u + GELU_A * u ** 3))
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * GELU_C * (
+        1.0 + 3.0 * GELU_A * u * u)
+
+
+def expert_mlp_backward(x_rows, w1, w2, dv, b1=None):
+    """Gradients of v = W2 gelu(W1 x (+ b1)) (+ b2), row by row, given dv =
+    dLoss/dv: returns (dx_rows, dW1 [H][D], dW2 [D][H], db1 [H], db2 [D])."""
+    x = _f64(x_rows)
+    u = x @ _f64(w1).T
+    if b1 is not None:
+        u = u + _f64(b1)
+    a = gelu_tanh(u)
+    dv = _f64(dv)
+    du = (dv @ _f64(w2)) * gelu_tanh_grad(u)
+    return du @ _f64(w1), du.T @ x, dv.T @ a, du.sum(axis=0), dv.sum(axis=0)
+
+
+def softmax_backward(P, dP):
+    """dLoss/dlogits of P = softmax(logits) per row: P (dP - sum_j P_j dP_j)."""
+    P = _f64(P)
+    dP = _f64(dP)
+    return P * (dP - (P * dP).sum(axis=1, keepdims=True))
+
+
+def balance_grad(idx, E, B, T, K, alpha, mode="sequence"):
+    """dL/dP[t][i] of the balance statistic with the counts held fixed (the
+    selection indicator has no gradient):
+      sequence: alpha / B * (n/(K T)) c[b][i] / T   for token t of image b
+      global:   alpha * (n/(K B T)) sum_b c[b][i] / (B T)"""
+    I = selection_indicator(idx, E)
+    counts = I.reshape(B, T, E).sum(axis=1).astype(np.float64)
+    if mode == "sequence":
+        g = alpha / B * (E / (K * T)) * counts / T          # [B][E]
+        return np.repeat(g, T, axis=0)
+    if mode == "global":
+        Tg = B * T
+        g = alpha * (E / (K * Tg)) * counts.sum(axis=0) / Tg
+        return np.broadcast_to(g, (Tg, E)).copy()
+    raise ValueError(mode)
+
+
+def layer_backward(inputs, idx, w, P, dy, dloss=0.0, balance_mode="sequence"):
+    """Gradients of  Loss = <dy, y> + dloss * L_balance  with the routing idx
+    held fixed (selection has no gradient; the slot weights w = P[idx] do):
+
+      routed slot (t,k) with expert e: dv = w[t][k] dy[t],
+        dw[t][k] = <dy[t], e(x_t)>, expert backward for dx, dW1[e], dW2[e]
+      shared expert s: dv = dy
+      dP[t][i] = sum_k [idx[t][k] == i] dw[t][k] + dloss * dL/dP[t][i]
+      dlogits = softmax_backward(P, dP);  dW_g = dlogits^T x;
+      dbias = sum_t dlogits;  dx = routed + shared + dlogits W_g.
+    Returns a dict of fp64 arrays."""
+    cfg = inputs.cfg
+    x = _f64(inputs.x)
+    dy = _f64(dy)
+    N, D = x.shape
+    E = cfg.E
+    Kmax = idx.shape[1]
+    dx = np.zeros((N, D))
+    dw = np.zeros((N, Kmax))
+    dw1 = np.zeros(_f64(inputs.w1).shape)
+    dw2 = np.zeros(_f64(inputs.w2).shape)
+    for e in range(E):
+        r, k = np.nonzero(idx == e)
+        if r.size == 0:
+            continue
+        v = expert_mlp(x[r], inputs.w1[e], inputs.w2[e])
+        dw[r, k] = (dy[r] * v).sum(axis=1)
+        dv = _f64(w)[r, k][:, None] * dy[r]
+        dxr, g1, g2, _, _ = expert_mlp_backward(x[r], inputs.w1[e],
+                                                inputs.w2[e], dv)
+        np.add.at(dx, r, dxr)
+        dw1[e] += g1
+        dw2[e] += g2
+    out = dict(dw=dw, dw1=dw1, dw2=dw2)
+    if cfg.n_s > 0:
+        dw1s = np.zeros(_f64(inputs.w1s).shape)
+        dw2s = np.zeros(_f64(inputs.w2s).shape)
+        for s_ in range(cfg.n_s):
+            dxs, g1, g2, _, _ = expert_mlp_backward(x, inputs.w1s[s_],
+                                                    inputs.w2s[s_], dy)
+            dx += dxs
+            dw1s[s_] = g1
+            dw2s[s_] = g2
+        out.update(dw1s=dw1s, dw2s=dw2s)
+    dP = np.zeros((N, E))
+    valid = idx >= 0
+    np.add.at(dP, (np.nonzero(valid)[0], idx[valid]), dw[valid])
+    if dloss:
+        dP += dloss * balance_grad(idx, E, cfg.B, cfg.T, cfg.K, cfg.alpha,
+                                   balance_mode)
+    dl = softmax_backward(P, dP)
+    dx += dl @ _f64(inputs.w_gate)
+    out.update(dP=dP, dlogits=dl, dw_gate=dl.T @ x, dbias=dl.sum(axis=0),
+               dx=dx)
+    return out
 
 
 # ------------------------------------------------------------- balance ----

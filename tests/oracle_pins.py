@@ -424,10 +424,125 @@ def check_routing_histogram_invariants():
     assert np.array_equal(zpos, expect)
 
 
+# --------------------------------------------------------------- backward --
+
+def check_gelu_grad():
+    u = np.linspace(-6.0, 6.0, 241)
+    h = 1e-5
+    fd = (om.gelu_tanh(u + h) - om.gelu_tanh(u - h)) / (2 * h)
+    assert np.abs(om.gelu_tanh_grad(u) - fd).max() < 1e-9
+    # gelu(u) - gelu(-u) = u exactly, so gelu'(u) + gelu'(-u) = 1
+    assert np.abs(om.gelu_tanh_grad(u) + om.gelu_tanh_grad(-u) - 1.0).max() < 1e-14
+    # torch's tanh GELU, differentiated by autograd
+    t = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    g, = torch.autograd.grad(F.gelu(t, approximate="tanh").sum(), t)
+    assert np.abs(om.gelu_tanh_grad(u) - g.numpy()).max() < 1e-14
+
+
+def _loss_fixed_routing(inp, idx, dy, dloss, mode):
+    """<dy, y> + dloss * L_balance at the inputs, routing held at idx; built
+    from the forward functions only."""
+    cfg = inp.cfg
+    P = om.softmax(om.gate_logits(inp.x, inp.w_gate, inp.bias))
+    w = om.slot_weights(P, idx)
+    y = om.layer_output(inp, idx, w)
+    _, _, L = om.balance_stats(P, idx, cfg.B, cfg.T, cfg.K, cfg.alpha, mode)
+    return float((dy * y).sum()) + dloss * L
+
+
+def _replace(inp, name, arr):
+    f = dict(x=inp.x, w_gate=inp.w_gate, bias=inp.bias, w1=inp.w1, w2=inp.w2,
+             w1s=inp.w1s, w2s=inp.w2s)
+    f[name] = arr
+    return synth.LayerInputs(inp.cfg, f["x"], f["w_gate"], f["bias"], f["w1"],
+                             f["w2"], f["w1s"], f["w2s"])
+
+
+def check_backward_finite_differences():
+    for mode, route in (("sequence", "topk"), ("global", "race")):
+        inp = _tiny_inputs(seed=31, B=2, T=4, D=6, H=8, E=3, K=2, n_s=1,
+                           bias=True, route=route)
+        cfg = inp.cfg
+        r = om.route(inp)
+        dy = _rng(32).standard_normal((cfg.N, cfg.D))
+        dloss = 3.0
+        g = om.layer_backward(inp, r["idx"], r["w"], r["P"], dy, dloss, mode)
+        keys = dict(x="dx", w_gate="dw_gate", bias="dbias", w1="dw1",
+                    w2="dw2", w1s="dw1s", w2s="dw2s")
+        pick = _rng(33)
+        h = 1e-6
+        for name, gk in keys.items():
+            base = np.array(getattr(inp, name), dtype=np.float64)
+            for _ in range(6):
+                j = tuple(int(pick.integers(0, n)) for n in base.shape)
+                plus, minus = base.copy(), base.copy()
+                plus[j] += h
+                minus[j] -= h
+                fd = (_loss_fixed_routing(_replace(inp, name, plus), r["idx"],
+                                          dy, dloss, mode)
+                      - _loss_fixed_routing(_replace(inp, name, minus),
+                                            r["idx"], dy, dloss, mode)) / (2 * h)
+                an = g[gk][j]
+                assert abs(an - fd) <= 1e-6 * max(1.0, abs(fd)), (mode, name, j, an, fd)
+
+
+def check_backward_autograd():
+    """torch autograd (fp64, CPU) of the same loss with the routing fixed."""
+    inp = _tiny_inputs(seed=34, B=3, T=5, D=7, H=9, E=4, K=2, n_s=2, bias=True)
+    cfg = inp.cfg
+    r = om.route(inp)
+    idx = r["idx"]
+    dy = _rng(35).standard_normal((cfg.N, cfg.D))
+    dloss = 0.7
+    T_ = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    x, wg, b = T_(inp.x), T_(inp.w_gate), T_(inp.bias)
+    w1, w2, w1s, w2s = T_(inp.w1), T_(inp.w2), T_(inp.w1s), T_(inp.w2s)
+    P = torch.softmax(x @ wg.T + b, dim=1)
+    mlp = lambda z, a1, a2: F.gelu(z @ a1.T, approximate="tanh") @ a2.T
+    y = torch.zeros(cfg.N, cfg.D, dtype=torch.float64)
+    for t in range(cfg.N):
+        for k in range(cfg.K):
+            e = int(idx[t, k])
+            y[t] = y[t] + P[t, e] * mlp(x[t:t + 1], w1[e], w2[e])[0]
+    for s_ in range(cfg.n_s):
+        y = y + mlp(x, w1s[s_], w2s[s_])
+    I = torch.tensor(om.selection_indicator(idx, cfg.E), dtype=torch.float64)
+    c = I.reshape(cfg.B, cfg.T, cfg.E).sum(1)
+    pbar = P.reshape(cfg.B, cfg.T, cfg.E).sum(1) / cfg.T
+    L = cfg.alpha * ((cfg.E / (cfg.K * cfg.T)) * c * pbar).sum(1).mean()
+    loss = (torch.tensor(dy) * y).sum() + dloss * L
+    grads = torch.autograd.grad(loss, [x, wg, b, w1, w2, w1s, w2s])
+    g = om.layer_backward(inp, idx, r["w"], r["P"], dy, dloss, "sequence")
+    for name, ref in zip(["dx", "dw_gate", "dbias", "dw1", "dw2", "dw1s", "dw2s"],
+                         grads):
+        assert np.abs(g[name] - ref.numpy()).max() < 1e-10, name
+
+
+def check_backward_dense_mlp():
+    """E = 1, K = 1, no shared expert: P = 1, the gate gets no gradient and
+    dx, dW1, dW2 are those of the plain MLP (torch autograd)."""
+    inp = _tiny_inputs(seed=36, B=2, T=6, D=5, H=7, E=1, K=1, n_s=0)
+    cfg = inp.cfg
+    r = om.route(inp)
+    dy = _rng(37).standard_normal((cfg.N, cfg.D))
+    g = om.layer_backward(inp, r["idx"], r["w"], r["P"], dy, 0.0)
+    x = torch.tensor(inp.x, requires_grad=True)
+    w1 = torch.tensor(inp.w1[0], requires_grad=True)
+    w2 = torch.tensor(inp.w2[0], requires_grad=True)
+    y = F.linear(F.gelu(F.linear(x, w1), approximate="tanh"), w2)
+    gx, g1, g2 = torch.autograd.grad((torch.tensor(dy) * y).sum(), [x, w1, w2])
+    assert np.abs(g["dx"] - gx.numpy()).max() < 1e-12
+    assert np.abs(g["dw1"][0] - g1.numpy()).max() < 1e-12
+    assert np.abs(g["dw2"][0] - g2.numpy()).max() < 1e-12
+    assert np.abs(g["dw_gate"]).max() == 0.0 and np.abs(g["dbias"]).max() == 0.0
+
+
 ALL_CHECKS = [check_gate_logits, check_softmax, check_topk, check_race,
               check_permute, check_gelu, check_expert_mlp, check_dense_mask,
               check_dense_mlp_special_case, check_full_mixture,
               check_one_hot_channels, check_balance_uniform_probs,
               check_balance_uniform_counts, check_balance_invariants,
               check_balance_golden, check_routing_histogram_golden,
-              check_routing_histogram_brute, check_routing_histogram_invariants]
+              check_routing_histogram_brute, check_routing_histogram_invariants,
+              check_gelu_grad, check_backward_finite_differences,
+              check_backward_autograd, check_backward_dense_mlp]

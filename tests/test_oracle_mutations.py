@@ -157,6 +157,33 @@ def _hist_tag_by_position(idx, B, T, E, tags=None, n_tags=0):
     return pos, out
 
 
+def _gelu_grad_no_cubic(u):
+    u = np.asarray(u, dtype=np.float64)
+    th = np.tanh(om.GELU_C * (u + om.GELU_A * u ** 3))
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * om.GELU_C
+
+
+def _softmax_backward_no_centering(P, dP):
+    return np.asarray(P, np.float64) * np.asarray(dP, np.float64)
+
+
+def _balance_grad_no_batch_mean(idx, E, B, T, K, alpha, mode="sequence"):
+    return _orig["balance_grad"](idx, E, B, T, K, alpha, mode) * B
+
+
+def _mlp_backward_w2_transposed(x_rows, w1, w2, dv, b1=None):
+    dx, g1, g2, db1, db2 = _orig["expert_mlp_backward"](x_rows, w1, w2, dv, b1)
+    return dx, g1, g2[::-1], db1, db2
+
+
+def _mlp_backward_no_gelu_grad(x_rows, w1, w2, dv, b1=None):
+    x = np.asarray(x_rows, np.float64)
+    u = x @ np.asarray(w1, np.float64).T
+    a = om.gelu_tanh(u)
+    du = np.asarray(dv, np.float64) @ np.asarray(w2, np.float64)
+    return du @ np.asarray(w1, np.float64), du.T @ x, np.asarray(dv).T @ a, du.sum(0), np.asarray(dv).sum(0)
+
+
 MUTATIONS = {
     "gelu_no_cubic": ("gelu_tanh", _gelu_no_cubic),
     "gelu_wrong_constant": ("gelu_tanh", _gelu_wrong_const),
@@ -180,6 +207,11 @@ MUTATIONS = {
     "histogram_counts_empty_slots": ("routing_histogram", _hist_wraps_empty),
     "histogram_position_by_image": ("routing_histogram", _hist_position_by_image),
     "histogram_tag_by_position": ("routing_histogram", _hist_tag_by_position),
+    "gelu_grad_drops_cubic_term": ("gelu_tanh_grad", _gelu_grad_no_cubic),
+    "softmax_backward_not_centred": ("softmax_backward", _softmax_backward_no_centering),
+    "balance_grad_not_averaged": ("balance_grad", _balance_grad_no_batch_mean),
+    "mlp_backward_w2_transposed": ("expert_mlp_backward", _mlp_backward_w2_transposed),
+    "mlp_backward_no_gelu_grad": ("expert_mlp_backward", _mlp_backward_no_gelu_grad),
 }
 
 
