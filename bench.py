@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes five "
                          "times (reference for the HBM byte counters)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward step, time the layer's "
+                         "backward pass (after one forward pass)")
     ap.add_argument("--analytics", action="store_true",
                     help="instead of the layer, time the routing histogram "
                          "(counts by patch position and by image tag) on the "
@@ -109,6 +112,77 @@ def kernel_work(cfg, gather: bool):
         "balance": ("bytes", N * E * 4 + N * Kmax * 4),
     }
     return w
+
+
+def backward_bench(args):
+    """Time the backward pass of the layer: gradients of <dy, y> + L_balance
+    for a seeded synthetic dy, after one forward pass (routing fixed)."""
+    import torch
+    import synth
+    from sparse_moe_diffusion_amd import _lib, layer
+
+    _lib.load()
+    cfg = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(cfg)
+    x = layer._to_device(inp.x, torch.bfloat16, "cuda")
+    wts = layer.LayerWeights.from_inputs(inp, "cuda")
+    buf = layer.LayerBuffers(cfg, "cuda", gather=True)
+    layer.forward(cfg, x, wts, buf)
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 77)
+    dy = torch.randn(cfg.N, cfg.D, device="cuda", generator=g).to(torch.bfloat16)
+    grads = layer.BackwardBuffers(cfg)
+    steps = layer.BACKWARD_STEPS
+
+    def one(evs=None):
+        for i, (_, fn) in enumerate(steps):
+            if evs is not None:
+                evs[i].record()
+            fn(cfg, x, wts, buf, grads, dy, 1.0)
+        if evs is not None:
+            evs[len(steps)].record()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+           for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        one(evs[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    per = {n: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)) / K
+           for i, (n, _) in enumerate(steps)}
+    # executed GEMM work of one grouped-MLP backward call: u recomputed,
+    # dgrad of both matrices, wgrad of both = 5 products of 2*M*D*H FLOPs
+    f_routed = 10.0 * cfg.A * cfg.D * cfg.H
+    f_shared = 10.0 * cfg.N * cfg.D * cfg.H * cfg.n_s
+    kern = {}
+    for n, t in per.items():
+        e = {"ms": round(t, 4)}
+        fl = {"routed_ffn_backward": f_routed, "shared_ffn_backward": f_shared}.get(n)
+        if fl:
+            tf = fl / (t * 1e-3) / 1e12
+            e.update(tflops=round(tf, 1), frac_mfma_peak=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+        kern[n] = e
+    ffn_ms = per["routed_ffn_backward"] + per["shared_ffn_backward"]
+    ach = (f_routed + f_shared) / (ffn_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "MoE-layer backward tokens/sec (gradients of <dy,y> + "
+                  "L_balance), XL/2-8E2A @512",
+        "value": round(cfg.N / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic (seeded dy)",
+        "config": {"workload": f"{cfg.name}: backward of the layer, B={cfg.B} x "
+                               f"T={cfg.T}, D={cfg.D}, E={cfg.E}, K={cfg.K}, "
+                               f"n_s={cfg.n_s}, H={cfg.H}"},
+        "roofline": {"kernel": "grouped expert MLP backward (5 GEMMs per call)",
+                     "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels": kern}), flush=True)
 
 
 def analytics_bench(args):
@@ -198,6 +272,9 @@ def main():
         return
     if args.analytics:
         analytics_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     import torch
     import synth

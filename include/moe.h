@@ -267,6 +267,100 @@ moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
                                 const int32_t* slot_row, const float* topk_w,
                                 int32_t Kmax, void* y, hipStream_t stream);
 
+/* ----------------------------------------------------------- backward ----
+ *
+ * Training ("Scaling Diffusion Transformers to 16 Billion Parameters",
+ * MoE-DiT: the layer is trained with the expert-level balance loss added to
+ * the task loss).  The three calls below give the gradients of
+ *
+ *   Loss = <dy, y> + dloss * L_balance
+ *
+ * for the routing the forward pass chose, held fixed: the selection has no
+ * gradient, the slot weights (gate probabilities) do, the balance counts do
+ * not.  Order: moe_combine_backward, moe_grouped_ffn_backward (routed
+ * experts, then shared experts with dy as their output gradient),
+ * moe_gate_backward.  Expert biases get no gradient here (the layer's
+ * experts have none).
+ */
+
+/*
+ * Backward of the weighted combine (eq. MoE(x)).  For every token t and
+ * slot k with r = slot_row[t][k] >= 0:
+ *   dy_rows[r]      = topk_w[t][k] * dy[t]           (y_dtype)
+ *   slot_grad[t][k] = <dy[t], y_rows[r]>             (fp32, fixed order)
+ * and slot_grad = 0 for empty slots.
+ *   dy [N][D] dy_dtype;  y_rows [*][D] y_dtype (the forward's expert rows);
+ *   dy_rows [*][D] y_dtype out;  slot_grad [N][Kmax] fp32 out
+ * Errors: INVALID_ARGUMENT for null pointers (N > 0), N < 0, D or
+ *   Kmax < 1; UNSUPPORTED for D % 8 != 0, Kmax > 64, unknown dtypes.
+ */
+moe_status moe_combine_backward(const void* dy, moe_dtype dy_dtype,
+                                const void* y_rows, moe_dtype y_dtype,
+                                const int32_t* slot_row, const float* topk_w,
+                                int64_t N, int32_t D, int32_t Kmax,
+                                void* dy_rows, float* slot_grad,
+                                hipStream_t stream);
+
+/* Bytes of workspace moe_grouped_ffn_backward needs (0 for bad sizes). */
+size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
+                                       int32_t D, int32_t H);
+
+/*
+ * Backward of the grouped expert MLPs (eq. MLP, tanh GELU), bf16.  With
+ * u = x_rows W1_g^T (+ b1_g), recomputed, and dy_rows the gradient of the
+ * expert outputs:
+ *   du      = (dy_rows W2_g) * gelu'(u)
+ *   dx_rows = du W1_g                                  (dx_dtype out)
+ *   dW1[g]  = sum over the group's rows of du^T x_rows  (fp32 out)
+ *   dW2[g]  = sum over the group's rows of dy_rows^T gelu(u)   (fp32 out)
+ * Rows, groups, row_index (gather) and weights are those of the forward
+ * moe_grouped_ffn call.  dW1 / dW2 are written whole (zero for empty
+ * groups).
+ *   dy_rows [total_rows][D] bf16;  dx_rows [total_rows][D];
+ *   dw1 [G][H][D], dw2 [G][D][H] fp32 out;  workspace of at least
+ *   moe_ffn_backward_workspace_size bytes (recomputed activations,
+ *   transposed weights, transposed token-padded operands)
+ * Errors: INVALID_ARGUMENT for null pointers or bad sizes;
+ *   UNSUPPORTED for non-bf16 inputs, G > 128, D or H not multiples of 8;
+ *   WORKSPACE_TOO_SMALL.
+ */
+moe_status moe_grouped_ffn_backward(
+    const void* x_rows, const int32_t* row_index, moe_dtype dtype,
+    int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
+    int32_t H, const void* w1, const float* b1, const void* w2,
+    const void* dy_rows, void* workspace, size_t workspace_bytes,
+    void* dx_rows, moe_dtype dx_dtype, float* dw1, float* dw2,
+    hipStream_t stream);
+
+/* Bytes of workspace moe_gate_backward needs (0 for bad sizes). */
+size_t moe_gate_backward_workspace_size(int64_t N, int32_t E, int32_t D);
+
+/*
+ * Backward of the gate and assembly of dx.  With P = probs, N = B*T:
+ *   dP[t][i]  = sum_k [topk_idx[t][k] == i] slot_grad[t][k]
+ *               + dloss * dL_balance/dP[t][i]   (counts from
+ *                 moe_balance_stats; sequence or global as in the forward)
+ *   dl[t]     = P[t] * (dP[t] - sum_j P[t][j] dP[t][j])     (softmax)
+ *   dw_gate   = sum_t dl[t]^T x[t]       [E][D] fp32 (fixed-order sums)
+ *   dbias     = sum_t dl[t]              [E] fp32 (may be NULL)
+ *   dx[t]     = sum_k dx_rows[slot_row[t][k]] + dx_shared[t] + dl[t] W_g
+ * in fp32, rounded once to dx_dtype; dx_rows / dx_shared may be NULL.
+ *   x [N][D] x_dtype;  w_gate [E][D] fp32;  topk_idx, slot_grad,
+ *   slot_row [N][Kmax];  counts [B][E] int32 (needed when dloss != 0);
+ *   dx_rows [*][D], dx_shared [N][D], dx [N][D] dx_dtype
+ * Errors: INVALID_ARGUMENT for null pointers or bad sizes, K outside
+ *   [1, E]; UNSUPPORTED for E or Kmax > 64, D % 8 != 0;
+ *   WORKSPACE_TOO_SMALL.
+ */
+moe_status moe_gate_backward(
+    const void* x, moe_dtype x_dtype, const float* w_gate, const float* probs,
+    const int32_t* topk_idx, const float* slot_grad, const int32_t* counts,
+    int32_t B, int32_t T, int32_t D, int32_t E, int32_t Kmax, int32_t K,
+    float alpha, float dloss, moe_balance_mode mode, const void* dx_rows,
+    const int32_t* slot_row, const void* dx_shared, moe_dtype dx_dtype,
+    void* dx, float* dw_gate, float* dbias, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Routing analytics ("Scaling Diffusion Transformers to 16 Billion
  * Parameters", Expert Specialization Analysis: the frequency of expert

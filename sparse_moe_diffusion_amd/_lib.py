@@ -52,6 +52,16 @@ SIGNATURES = {
                                _P, _P, _P]),
     "moe_ffn_down_combine": (_E, [_P, _E, _I64, _I32, _I32, _P, _P, _P, _P, _P,
                                   _I32, _P, _P]),
+    "moe_combine_backward": (_E, [_P, _E, _P, _E, _P, _P, _I64, _I32, _I32, _P,
+                                  _P, _P]),
+    "moe_ffn_backward_workspace_size": (_SZ, [_I64, _I32, _I32, _I32]),
+    "moe_grouped_ffn_backward": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32,
+                                      _P, _P, _P, _P, _P, _SZ, _P, _E, _P, _P,
+                                      _P]),
+    "moe_gate_backward_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "moe_gate_backward": (_E, [_P, _E, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                               _I32, _I32, _I32, _F, _F, _E, _P, _P, _P, _E,
+                               _P, _P, _P, _P, _SZ, _P]),
     "moe_routing_histogram": (_E, [_P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P,
                                    _P]),
 }

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["gate.hip", "permute.hip", "ffn.hip", "combine.hip", "balance.hip",
-           "analytics.hip", "abi.cpp"]
+           "analytics.hip", "backward.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -276,6 +276,127 @@ moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
                   fn);
 }
 
+moe_status moe_combine_backward(const void* dy, moe_dtype dy_dtype,
+                                const void* y_rows, moe_dtype y_dtype,
+                                const int32_t* slot_row, const float* topk_w,
+                                int64_t N, int32_t D, int32_t Kmax,
+                                void* dy_rows, float* slot_grad,
+                                hipStream_t stream) {
+  const char* fn = "moe_combine_backward";
+  if (N < 0 || D < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, Kmax >= 1",
+                fn);
+  const bool rows = N > 0;
+  CHECK_PTR_IF(rows, dy); CHECK_PTR_IF(rows, y_rows); CHECK_PTR_IF(rows, slot_row);
+  CHECK_PTR_IF(rows, topk_w); CHECK_PTR_IF(rows, dy_rows);
+  CHECK_PTR_IF(rows, slot_grad);
+  if (!valid_dtype(dy_dtype) || !valid_dtype(y_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (D % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
+  if (Kmax > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: Kmax=%d above %d", fn, Kmax, kMaxE);
+  if (N * Kmax >= kI32Limit || N * (D / 8) >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
+  return from_hip(moe::launch_combine_backward(dy, dy_dtype == MOE_BF16, y_rows,
+                                               y_dtype == MOE_BF16, slot_row,
+                                               topk_w, N, D, Kmax, dy_rows,
+                                               slot_grad, stream),
+                  fn);
+}
+
+size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G, int32_t D,
+                                       int32_t H) {
+  if (total_rows < 0 || G < 1 || D < 1 || H < 1) return 0;
+  return moe::ffn_backward_workspace_bytes(total_rows, G, D, H);
+}
+
+moe_status moe_grouped_ffn_backward(
+    const void* x_rows, const int32_t* row_index, moe_dtype dtype,
+    int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
+    int32_t H, const void* w1, const float* b1, const void* w2,
+    const void* dy_rows, void* workspace, size_t workspace_bytes,
+    void* dx_rows, moe_dtype dx_dtype, float* dw1, float* dw2,
+    hipStream_t stream) {
+  const char* fn = "moe_grouped_ffn_backward";
+  if (total_rows < 0 || G < 1 || D < 1 || H < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need total_rows >= 0, G >= 1, D >= 1, H >= 1", fn);
+  const bool rows = total_rows > 0;
+  CHECK_PTR(w1); CHECK_PTR(w2); CHECK_PTR(dw1); CHECK_PTR(dw2);
+  CHECK_PTR(workspace);
+  CHECK_PTR_IF(rows, x_rows); CHECK_PTR_IF(rows, group_offsets);
+  CHECK_PTR_IF(rows, dy_rows); CHECK_PTR_IF(rows, dx_rows);
+  if (dtype != MOE_BF16 || !valid_dtype(dx_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 inputs only", fn);
+  if (G > kMaxGroups)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d above %d", fn, G, kMaxGroups);
+  if (D % 8 != 0 || H % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
+                fn, D, H);
+  const int64_t Kt = moe::padded_columns(total_rows, G);
+  if (total_rows >= kI32Limit || Kt * 2 * 256 >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows=%lld too large", fn,
+                (long long)total_rows);
+  if (workspace_bytes < moe::ffn_backward_workspace_bytes(total_rows, G, D, H))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace below %zu bytes",
+                fn, moe::ffn_backward_workspace_bytes(total_rows, G, D, H));
+  moe::FfnBwdArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
+                    w1,     b1,        w2,         dy_rows,       workspace,
+                    dx_rows, dx_dtype == MOE_F32, dw1, dw2};
+  return from_hip(moe::launch_ffn_backward(a, stream), fn);
+}
+
+size_t moe_gate_backward_workspace_size(int64_t N, int32_t E, int32_t D) {
+  if (N < 0 || E < 1 || D < 1) return 0;
+  return moe::gate_backward_workspace_bytes(N, E, D);
+}
+
+moe_status moe_gate_backward(
+    const void* x, moe_dtype x_dtype, const float* w_gate, const float* probs,
+    const int32_t* topk_idx, const float* slot_grad, const int32_t* counts,
+    int32_t B, int32_t T, int32_t D, int32_t E, int32_t Kmax, int32_t K,
+    float alpha, float dloss, moe_balance_mode mode, const void* dx_rows,
+    const int32_t* slot_row, const void* dx_shared, moe_dtype dx_dtype,
+    void* dx, float* dw_gate, float* dbias, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_gate_backward";
+  if (B < 0 || T < 1 || D < 1 || E < 1 || Kmax < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need B >= 0, T >= 1, D >= 1, E >= 1, Kmax >= 1", fn);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: K=%d outside [1, E=%d]", fn, K, E);
+  if (mode != MOE_BAL_PER_SEQUENCE && mode != MOE_BAL_GLOBAL)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: unknown mode %d", fn, (int)mode);
+  if (dx_rows != nullptr && slot_row == nullptr)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: dx_rows needs slot_row", fn);
+  const bool rows = B > 0;
+  CHECK_PTR(w_gate); CHECK_PTR(dw_gate); CHECK_PTR(workspace);
+  CHECK_PTR_IF(rows, x); CHECK_PTR_IF(rows, probs); CHECK_PTR_IF(rows, topk_idx);
+  CHECK_PTR_IF(rows, slot_grad); CHECK_PTR_IF(rows, dx);
+  CHECK_PTR_IF(rows && dloss != 0.0f, counts);
+  if (!valid_dtype(x_dtype) || !valid_dtype(dx_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (E > kMaxE || Kmax > kMaxE)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d / Kmax=%d above %d", fn, E, Kmax,
+                kMaxE);
+  if (D % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
+  const int64_t N = static_cast<int64_t>(B) * T;
+  if (N * E >= kI32Limit || N * Kmax >= kI32Limit || N * (D / 8) >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: B*T*E must stay below 2^31", fn);
+  if (workspace_bytes < moe::gate_backward_workspace_bytes(N, E, D))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace below %zu bytes",
+                fn, moe::gate_backward_workspace_bytes(N, E, D));
+  return from_hip(moe::launch_gate_backward(
+                      x, x_dtype == MOE_BF16, w_gate, probs, topk_idx,
+                      slot_grad, counts, B, T, D, E, Kmax, K, alpha, dloss,
+                      mode == MOE_BAL_GLOBAL, dx_rows, slot_row, dx_shared,
+                      dx_dtype == MOE_BF16, dx, dw_gate, dbias, workspace,
+                      stream),
+                  fn);
+}
+
 moe_status moe_routing_histogram(const int32_t* topk_idx, int32_t B,
                                  int32_t T, int32_t E, int32_t Kmax,
                                  const int32_t* image_tag, int32_t n_tags,

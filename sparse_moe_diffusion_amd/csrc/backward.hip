@@ -1,0 +1,488 @@
+// Backward of the DiT-MoE layer: everything except the expert GEMMs.
+//
+// "Scaling Diffusion Transformers to 16 Billion Parameters", MoE-DiT: the
+// layer is trained with the expert-level balance loss added to the task
+// loss.  The gradients are those of the forward definitions (eq. MoE(x),
+// eq. MLP, eq. L_balance, the gate softmax of the "DiT-MoE" project hub
+// page, section 1) with the routing held fixed: the selection itself has no
+// gradient, the slot weights (gate probabilities) do.
+//
+// Kernels (gfx950):
+//  * transpose_kernel: [G][R][C] -> [G][C][R] bf16 through 64x64 LDS tiles
+//    (transposed copies of the expert weights for the data-gradient GEMMs).
+//  * tpad_kernel: activation rows grouped by expert -> [C][Kt] with group
+//    g's rows in columns [koff_g, koff_g + M_g) and zeros up to the next
+//    multiple of 64 (the operands of the K-grouped weight-gradient GEMM);
+//    optional row gather and GELU on the way.
+//  * combine_bwd_kernel: one wave per token; the routed rows' output
+//    gradients w * dy and the slot-weight gradients <dy, y_row>.
+//  * gate_bwd_token_kernel / gate_bwd_main_kernel / gate_bwd_reduce_kernel:
+//    dP -> dlogits per token, then dW_g and dbias partials per token chunk
+//    with dx assembled in the same pass, then a fixed-order sum.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ float gelu_fwd(float u) {
+  constexpr float kC1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
+  constexpr float kC2 = kC1 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(u * fmaf(kC2, u * u, kC1));
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ------------------------------------------------------------ transposes --
+
+constexpr int kTile = 64;
+
+__global__ __launch_bounds__(256) void transpose_kernel(
+    const uint16_t* __restrict__ src, int R, int C,
+    uint16_t* __restrict__ dst) {
+  __shared__ uint16_t t[kTile][kTile + 2];
+  const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
+  const int64_t g = blockIdx.z;
+  const uint16_t* s = src + g * R * C;
+  uint16_t* d = dst + g * R * C;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < kTile; r += 4) {
+    const int rr = r0 + r, cc = c0 + tx;
+    t[r][tx] = (rr < R && cc < C) ? s[static_cast<int64_t>(rr) * C + cc] : 0;
+  }
+  __syncthreads();
+  for (int c = ty; c < kTile; c += 4) {
+    const int cc = c0 + c, rr = r0 + tx;
+    if (cc < C && rr < R) d[static_cast<int64_t>(cc) * R + rr] = t[tx][c];
+  }
+}
+
+// Group g of rows [off_g, off_{g+1}) (clamped to [0, total]) occupies
+// columns [koff_g, koff_g + klen_g) of a padded operand, klen_g = M_g rounded
+// up to 64, so every 64-column block lies in one group's segment.  The block
+// table holds, per block, its first source row and how many of its 64
+// columns hold rows (the rest are zero padding, or past the last segment).
+__global__ __launch_bounds__(256) void kseg_kernel(
+    const int64_t* __restrict__ offsets, int G, int64_t total, int64_t nblk,
+    int64_t* __restrict__ blk_row, int32_t* __restrict__ blk_n) {
+  __shared__ int64_t r0s[kMaxFfnGroups], ms[kMaxFfnGroups], koffs[kMaxFfnGroups + 1];
+  if (threadIdx.x == 0) {
+    int64_t koff = 0;
+    for (int g = 0; g < G; ++g) {
+      const int64_t r0 = offsets ? min(max(offsets[g], int64_t(0)), total) : 0;
+      const int64_t r1 = offsets ? min(max(offsets[g + 1], r0), total) : total;
+      r0s[g] = r0;
+      ms[g] = r1 - r0;
+      koffs[g] = koff;
+      koff += (r1 - r0 + 63) / 64 * 64;
+    }
+    koffs[G] = koff;
+  }
+  __syncthreads();
+  for (int64_t kb = threadIdx.x; kb < nblk; kb += blockDim.x) {
+    const int64_t k0 = kb * kTile;
+    int64_t row = 0;
+    int n = 0;
+    for (int g = 0; g < G; ++g) {
+      if (k0 >= koffs[g] && k0 < koffs[g + 1]) {
+        const int64_t j0 = k0 - koffs[g];
+        row = r0s[g] + j0;
+        n = static_cast<int>(min<int64_t>(kTile, max<int64_t>(ms[g] - j0, 0)));
+        break;
+      }
+    }
+    blk_row[kb] = row;
+    blk_n[kb] = n;
+  }
+}
+
+// dst [C][Kt]: column block kb holds the blk_n[kb] source rows from
+// blk_row[kb] (through row_index when given), transposed, then zeros.
+template <bool GELU>
+__global__ __launch_bounds__(256) void tpad_kernel(
+    const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
+    const int64_t* __restrict__ blk_row, const int32_t* __restrict__ blk_n,
+    int C, int64_t Kt, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t t[kTile][kTile + 2];
+  const int c0 = blockIdx.x * kTile;
+  const int64_t kb = blockIdx.y;
+  const int64_t k0 = kb * kTile;
+  const int64_t row0 = blk_row[kb];
+  const int n = blk_n[kb];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int j = ty; j < kTile; j += 4) {
+    const int cc = c0 + tx;
+    uint16_t v = 0;
+    if (j < n && cc < C) {
+      const int64_t r = row0 + j;
+      const int64_t sr = row_index ? row_index[r] : r;
+      v = src[sr * C + cc];
+      if constexpr (GELU) v = f32_to_bf16_bits(gelu_fwd(bf16_bits_to_f32(v)));
+    }
+    t[j][tx] = v;
+  }
+  __syncthreads();
+  for (int c = ty; c < kTile; c += 4) {
+    const int cc = c0 + c;
+    if (cc < C) dst[static_cast<int64_t>(cc) * Kt + k0 + tx] = t[tx][c];
+  }
+}
+
+// --------------------------------------------------------------- combine --
+
+template <bool BF16>
+__device__ __forceinline__ void ld8(const void* base, int64_t row, int D, int c,
+                                    float* f) {
+  if constexpr (BF16) {
+    unpack8(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
+                                           row * D)[c], f);
+  } else {
+    const float4* p =
+        reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * D) + 2 * c;
+    const float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void st8(void* base, int64_t row, int D, int c,
+                                    const float* f) {
+  if constexpr (BF16) {
+    uint4 v;
+    v.x = pack_bf16x2(f[0], f[1]);
+    v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]);
+    v.w = pack_bf16x2(f[6], f[7]);
+    reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + row * D)[c] = v;
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + row * D) + 2 * c;
+    p[0] = make_float4(f[0], f[1], f[2], f[3]);
+    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+
+// Wave sum in a fixed order (xor butterfly): the same bits on every run.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+constexpr int kCbWaves = 4;
+
+// Token t: for each slot k with row r = slot_row[t][k] >= 0,
+//   dy_rows[r] = topk_w[t][k] * dy[t]   and   dw[t][k] = <dy[t], y_rows[r]>;
+// empty slots get dw = 0.
+template <bool DB, bool YB>
+__global__ __launch_bounds__(64 * kCbWaves) void combine_bwd_kernel(
+    const void* __restrict__ dy, const void* __restrict__ y_rows,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ w,
+    int64_t N, int D, int Kmax, void* __restrict__ dy_rows,
+    float* __restrict__ dw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCbWaves + (threadIdx.x >> 6);
+  if (t >= N) return;
+  const int nch = D / 8;
+  for (int k = 0; k < Kmax; ++k) {
+    const int32_t r = slot_row[t * Kmax + k];
+    if (r < 0) {
+      if (lane == 0) dw[t * Kmax + k] = 0.0f;
+      continue;
+    }
+    const float wk = w[t * Kmax + k];
+    float part = 0.0f;
+    for (int c = lane; c < nch; c += 64) {
+      float g[8], y[8], o[8];
+      ld8<DB>(dy, t, D, c, g);
+      ld8<YB>(y_rows, r, D, c, y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        part = fmaf(g[j], y[j], part);
+        o[j] = wk * g[j];
+      }
+      st8<YB>(dy_rows, r, D, c, o);
+    }
+    const float s = wave_sum(part);
+    if (lane == 0) dw[t * Kmax + k] = s;
+  }
+}
+
+// ------------------------------------------------------------------ gate --
+
+// Per token: dP[i] = sum_k [idx[t][k] == i] dw[t][k] + dloss * dL/dP[t][i],
+// dlogits = P (dP - sum_j P_j dP_j), written to dl [N][E].
+__global__ __launch_bounds__(256) void gate_bwd_token_kernel(
+    const float* __restrict__ probs, const int32_t* __restrict__ idx,
+    const float* __restrict__ dw, const int32_t* __restrict__ counts, int B,
+    int T, int E, int Kmax, int K, float alpha, float dloss, int global,
+    float* __restrict__ dl) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t N = static_cast<int64_t>(B) * T;
+  if (t >= N) return;
+  const int b = static_cast<int>(t / T);
+  float dP[kMaxExperts];
+  for (int i = 0; i < E; ++i) {
+    float g = 0.0f;
+    if (dloss != 0.0f) {
+      if (global) {
+        int64_t c = 0;
+        for (int bb = 0; bb < B; ++bb) c += counts[static_cast<int64_t>(bb) * E + i];
+        const float Tg = static_cast<float>(N);
+        g = alpha * (static_cast<float>(E) / (static_cast<float>(K) * Tg)) *
+            static_cast<float>(c) / Tg;
+      } else {
+        g = alpha / static_cast<float>(B) *
+            (static_cast<float>(E) / (static_cast<float>(K) * T)) *
+            static_cast<float>(counts[static_cast<int64_t>(b) * E + i]) /
+            static_cast<float>(T);
+      }
+      g *= dloss;
+    }
+    dP[i] = g;
+  }
+  for (int k = 0; k < Kmax; ++k) {
+    const int e = idx[t * Kmax + k];
+    if (e >= 0 && e < E) dP[e] += dw[t * Kmax + k];
+  }
+  float s = 0.0f;
+  for (int i = 0; i < E; ++i) s = fmaf(probs[t * E + i], dP[i], s);
+  for (int i = 0; i < E; ++i) {
+    const float p = probs[t * E + i];
+    dl[t * E + i] = p * (dP[i] - s);
+  }
+}
+
+constexpr int kGbTokens = 128;   // tokens per workgroup
+constexpr int kGbThreads = 256;
+
+// Workgroup = kGbTokens tokens; thread = 8 consecutive features (chunks
+// c = tid, tid + 256, ...).  Per chunk: the workgroup's dW_g partial
+// [E][8] for that chunk (experts in blocks of 8), and in the first block
+// pass, dx[t] = sum_k dx_rows[slot_row[t][k]] + dx_shared[t]
+//              + sum_i dl[t][i] W_g[i]   for each token, in fp32, rounded once.
+template <bool XB, bool OB>
+__global__ __launch_bounds__(kGbThreads) void gate_bwd_main_kernel(
+    const void* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ dl, int64_t N, int D, int E, int Kmax,
+    const void* __restrict__ dx_rows, const int32_t* __restrict__ slot_row,
+    const void* __restrict__ dx_shared, void* __restrict__ dx,
+    float* __restrict__ part_w, float* __restrict__ part_b) {
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGbTokens;
+  const int64_t t1 = min(N, t0 + kGbTokens);
+  const int nch = D / 8;
+  float* pw = part_w + static_cast<int64_t>(blockIdx.x) * E * D;
+  for (int c = threadIdx.x; c < nch; c += kGbThreads) {
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      float acc[8][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+      for (int64_t t = t0; t < t1; ++t) {
+        float xv[8];
+        ld8<XB>(x, t, D, c, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (e0 + i < E) {
+            const float d = dl[t * E + e0 + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xv[j], acc[i][j]);
+          }
+        }
+        if (e0 == 0 && dx != nullptr) {
+          float o[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+          if (slot_row != nullptr) {
+            for (int k = 0; k < Kmax; ++k) {
+              const int32_t r = slot_row[t * Kmax + k];
+              if (r < 0) continue;
+              float v[8];
+              ld8<OB>(dx_rows, r, D, c, v);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) o[j] += v[j];
+            }
+          }
+          if (dx_shared != nullptr) {
+            float v[8];
+            ld8<OB>(dx_shared, t, D, c, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] += v[j];
+          }
+          for (int i = 0; i < E; ++i) {
+            const float d = dl[t * E + i];
+            const float4* wp = reinterpret_cast<const float4*>(
+                wg + static_cast<int64_t>(i) * D) + 2 * c;
+            const float4 a = wp[0], b = wp[1];
+            o[0] = fmaf(d, a.x, o[0]); o[1] = fmaf(d, a.y, o[1]);
+            o[2] = fmaf(d, a.z, o[2]); o[3] = fmaf(d, a.w, o[3]);
+            o[4] = fmaf(d, b.x, o[4]); o[5] = fmaf(d, b.y, o[5]);
+            o[6] = fmaf(d, b.z, o[6]); o[7] = fmaf(d, b.w, o[7]);
+          }
+          st8<OB>(dx, t, D, c, o);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (e0 + i >= E) break;
+        float4* q = reinterpret_cast<float4*>(pw + static_cast<int64_t>(e0 + i) * D) + 2 * c;
+        q[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        q[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+      }
+    }
+  }
+  // dbias partial of the chunk: thread i < E sums its expert over the tokens
+  for (int i = threadIdx.x; i < E; i += kGbThreads) {
+    float s = 0.0f;
+    for (int64_t t = t0; t < t1; ++t) s += dl[t * E + i];
+    part_b[static_cast<int64_t>(blockIdx.x) * E + i] = s;
+  }
+}
+
+// Fixed-order sum of the chunk partials: dW_g [E][D] and dbias [E].
+__global__ __launch_bounds__(256) void gate_bwd_reduce_kernel(
+    const float* __restrict__ part_w, const float* __restrict__ part_b,
+    int nchunks, int E, int D, float* __restrict__ dw_gate,
+    float* __restrict__ dbias) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t ED = static_cast<int64_t>(E) * D;
+  if (i < ED) {
+    float s = 0.0f;
+    for (int c = 0; c < nchunks; ++c) s += part_w[c * ED + i];
+    dw_gate[i] = s;
+  }
+  if (i < E && dbias != nullptr) {
+    float s = 0.0f;
+    for (int c = 0; c < nchunks; ++c) s += part_b[static_cast<int64_t>(c) * E + i];
+    dbias[i] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
+                            hipStream_t stream) {
+  if (G == 0 || R == 0 || C == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(ceil_div(C, kTile)),
+                  static_cast<unsigned>(ceil_div(R, kTile)),
+                  static_cast<unsigned>(G));
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(src), R, C,
+                     static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+int64_t padded_columns(int64_t total, int G) {
+  return (total + 63) / 64 * 64 + 64 * static_cast<int64_t>(G);
+}
+
+hipError_t launch_kseg(const int64_t* offsets, int G, int64_t total,
+                       int64_t* blk_row, int32_t* blk_n, hipStream_t stream) {
+  if (total == 0) return hipSuccess;
+  const int64_t nblk = padded_columns(total, G) / kTile;
+  hipLaunchKernelGGL(kseg_kernel, dim3(1), dim3(256), 0, stream, offsets, G,
+                     total, nblk, blk_row, blk_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_tpad(const void* src, const int32_t* row_index,
+                       const int64_t* blk_row, const int32_t* blk_n, int G,
+                       int64_t total, int C, bool gelu, void* dst,
+                       hipStream_t stream) {
+  if (total == 0) return hipSuccess;
+  const int64_t Kt = padded_columns(total, G);
+  const dim3 grid(static_cast<unsigned>(ceil_div(C, kTile)),
+                  static_cast<unsigned>(Kt / kTile));
+  if (gelu)
+    hipLaunchKernelGGL(tpad_kernel<true>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), row_index, blk_row,
+                       blk_n, C, Kt, static_cast<uint16_t*>(dst));
+  else
+    hipLaunchKernelGGL(tpad_kernel<false>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), row_index, blk_row,
+                       blk_n, C, Kt, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const void* dy, bool dy_bf16,
+                                   const void* y_rows, bool y_bf16,
+                                   const int32_t* slot_row, const float* w,
+                                   int64_t N, int D, int Kmax, void* dy_rows,
+                                   float* dw, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, kCbWaves)));
+  const dim3 block(64 * kCbWaves);
+  if (dy_bf16 && y_bf16)
+    hipLaunchKernelGGL((combine_bwd_kernel<true, true>), grid, block, 0, stream,
+                       dy, y_rows, slot_row, w, N, D, Kmax, dy_rows, dw);
+  else if (dy_bf16)
+    hipLaunchKernelGGL((combine_bwd_kernel<true, false>), grid, block, 0, stream,
+                       dy, y_rows, slot_row, w, N, D, Kmax, dy_rows, dw);
+  else if (y_bf16)
+    hipLaunchKernelGGL((combine_bwd_kernel<false, true>), grid, block, 0, stream,
+                       dy, y_rows, slot_row, w, N, D, Kmax, dy_rows, dw);
+  else
+    hipLaunchKernelGGL((combine_bwd_kernel<false, false>), grid, block, 0, stream,
+                       dy, y_rows, slot_row, w, N, D, Kmax, dy_rows, dw);
+  return hipGetLastError();
+}
+
+// Workspace: dl [N][E], padded to 64 floats so that the 16-byte stores of
+// the partials stay aligned, then part_w [chunks][E][D], part_b [chunks][E].
+size_t gate_backward_workspace_bytes(int64_t N, int E, int D) {
+  const int64_t chunks = ceil_div(N, kGbTokens);
+  const int64_t dl = (N * E + 63) / 64 * 64;
+  return static_cast<size_t>(dl + chunks * E * D + chunks * E) * 4;
+}
+
+hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
+                                const float* probs, const int32_t* idx,
+                                const float* dw, const int32_t* counts, int B,
+                                int T, int D, int E, int Kmax, int K, float alpha,
+                                float dloss, bool global, const void* dx_rows,
+                                const int32_t* slot_row, const void* dx_shared,
+                                bool dx_bf16, void* dx, float* dw_gate,
+                                float* dbias, void* workspace,
+                                hipStream_t stream) {
+  const int64_t N = static_cast<int64_t>(B) * T;
+  const int64_t chunks = ceil_div(N, kGbTokens);
+  float* dl = static_cast<float*>(workspace);
+  float* part_w = dl + (N * E + 63) / 64 * 64;
+  float* part_b = part_w + chunks * E * D;
+  if (N > 0) {
+    hipLaunchKernelGGL(gate_bwd_token_kernel,
+                       dim3(static_cast<unsigned>(ceil_div(N, 256))), dim3(256),
+                       0, stream, probs, idx, dw, counts, B, T, E, Kmax, K,
+                       alpha, dloss, global ? 1 : 0, dl);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid(static_cast<unsigned>(chunks));
+    if (x_bf16 && dx_bf16)
+      hipLaunchKernelGGL((gate_bwd_main_kernel<true, true>), grid, dim3(kGbThreads),
+                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
+                         dx_shared, dx, part_w, part_b);
+    else if (x_bf16)
+      hipLaunchKernelGGL((gate_bwd_main_kernel<true, false>), grid, dim3(kGbThreads),
+                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
+                         dx_shared, dx, part_w, part_b);
+    else if (dx_bf16)
+      hipLaunchKernelGGL((gate_bwd_main_kernel<false, true>), grid, dim3(kGbThreads),
+                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
+                         dx_shared, dx, part_w, part_b);
+    else
+      hipLaunchKernelGGL((gate_bwd_main_kernel<false, false>), grid, dim3(kGbThreads),
+                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
+                         dx_shared, dx, part_w, part_b);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int64_t ED = static_cast<int64_t>(E) * D;
+  hipLaunchKernelGGL(gate_bwd_reduce_kernel,
+                     dim3(static_cast<unsigned>(ceil_div(ED, 256))), dim3(256),
+                     0, stream, part_w, part_b, static_cast<int>(chunks), E, D,
+                     dw_gate, dbias);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -44,7 +44,9 @@ namespace {
 
 // kEpiCombine: the stage-2 store of the shared experts fused with the
 // weighted combine of the routed outputs (one group holding every token).
-enum Epi { kEpiGelu = 0, kEpiStore = 1, kEpiCombine = 2 };
+// kEpiGeluGrad: the product times GELU'(u) at the same position, u read
+// from GemmParams::aux (backward of the first expert matrix).
+enum Epi { kEpiGelu = 0, kEpiStore = 1, kEpiCombine = 2, kEpiGeluGrad = 3 };
 
 // Most slots per token the fused combine takes (top-K routing, K <= 4).
 constexpr int kCombineMaxSlots = 4;
@@ -64,12 +66,19 @@ struct GemmParams {
   const int32_t* cmb_slot;   // [total][cmb_kmax]
   const float* cmb_w;        // [total][cmb_kmax]
   int cmb_kmax;              // 1..kCombineMaxSlots
+  // kEpiGeluGrad only: the pre-activations u [total][Nd] bf16.
+  const void* aux;
+  // K-grouped form (weight gradients): C[g] [mrows][Nd] fp32 = A[:, seg g]
+  // B[:, seg g]^T, A [mrows][ld] and B [Nd][ld] bf16, seg g = group g's
+  // token columns, padded to 64 (see the transposes).
+  int ld, mrows;
 };
 
 struct TileLoc {
   int g;
   int64_t row0, row_end;
   int n0;
+  int kofs, klen;   // K-grouped form: the group's token-column segment
 };
 
 // tanh-GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)),
@@ -203,10 +212,93 @@ __device__ __forceinline__ bool locate_tile_tab(const GemmParams& p,
   return true;
 }
 
-// Bias and activation of 4 consecutive output features f..f+3 of group g.
+// d/du of gelu_tanh: with s = 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)),
+// gelu'(u) = s + 2 sqrt(2/pi) u s (1 - s) (1 + 3 0.044715 u^2).
+__device__ __forceinline__ float gelu_tanh_grad(float u) {
+  constexpr float kC1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
+  constexpr float kC2 = kC1 * 0.044715f;
+  const float s = __builtin_amdgcn_rcpf(
+      1.0f + __builtin_amdgcn_exp2f(u * fmaf(kC2, u * u, kC1)));
+  return fmaf(2.0f * 0.7978845608028654f * u * s * (1.0f - s),
+              fmaf(3.0f * 0.044715f, u * u, 1.0f), s);
+}
+
+// K-grouped form: the group table holds each group's token-column segment
+// of the transposed operands, [kofs, kofs + klen), klen = the group's row
+// count rounded up to 64 (the transposes zero the padding).
+__device__ __forceinline__ void build_kseg_table(const GemmParams& p,
+                                                 int32_t* tab, int wave,
+                                                 int lane) {
+  if (wave == 0) {
+    int base = 0;
+    for (int c = 0; c < p.G; c += 64) {
+      const int g = c + lane;
+      int len = 0;
+      if (g < p.G) {
+        const int64_t r0 = p.offsets ? min(max(p.offsets[g], int64_t(0)), p.total) : 0;
+        const int64_t r1 = p.offsets ? min(max(p.offsets[g + 1], r0), p.total) : p.total;
+        len = static_cast<int>((r1 - r0 + 63) / 64 * 64);
+      }
+      int inc = len;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d);
+        if (lane >= d) inc += v;
+      }
+      if (g < p.G) {
+        tab[g] = base + inc - len;
+        tab[kTabCol + g] = len;
+      }
+      base += __shfl(inc, 63);
+    }
+  }
+  __syncthreads();
+}
+
+// Tile L of a K-grouped launch: group g = L / (row tiles x feature tiles),
+// bands of GM row tiles within it.  Output rows are g * mrows + row.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
+                                               const int32_t* tab, int L,
+                                               TileLoc& loc) {
+  const int mt = (p.mrows + BM - 1) / BM;
+  const int ntn = (p.Nd + BN - 1) / BN;
+  const int per = mt * ntn;
+  if (L >= p.G * per) return false;
+  const int g = L / per;
+  const int Lg = L - g * per;
+  const int band = Lg / (GM * ntn);
+  const int rem = Lg - band * GM * ntn;
+  const int m_first = band * GM;
+  const int gm = min(GM, mt - m_first);
+  const int64_t base = static_cast<int64_t>(g) * p.mrows;
+  loc.g = __builtin_amdgcn_readfirstlane(g);
+  loc.row0 = uniform64(base + static_cast<int64_t>(m_first + rem % gm) * BM);
+  loc.row_end = uniform64(base + p.mrows);
+  loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+  loc.kofs = __builtin_amdgcn_readfirstlane(tab[g]);
+  loc.klen = __builtin_amdgcn_readfirstlane(tab[kTabCol + g]);
+  return true;
+}
+
+template <bool KG, int BM, int BN, int GM>
+__device__ __forceinline__ bool locate_any(const GemmParams& p,
+                                           const int32_t* tab, int lane, int L,
+                                           TileLoc& loc) {
+  if constexpr (KG) {
+    return locate_tile_kg<BM, BN, GM>(p, tab, L, loc);
+  } else {
+    loc.kofs = 0;
+    loc.klen = 0;
+    return locate_tile_tab<BM, BN, GM>(p, tab, lane, L, loc);
+  }
+}
+
+// Bias and activation of 4 consecutive output features f..f+3 of group g,
+// output row `row`.
 template <int EPI>
-__device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g, int f,
-                                         f32x4 v) {
+__device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g,
+                                         int64_t row, int f, f32x4 v) {
   if (p.bias != nullptr) {
     const float* b = p.bias + static_cast<int64_t>(g) * p.Nd + f;
     v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
@@ -215,13 +307,19 @@ __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g, int f,
     v[0] = gelu_tanh(v[0]); v[1] = gelu_tanh(v[1]);
     v[2] = gelu_tanh(v[2]); v[3] = gelu_tanh(v[3]);
   }
+  if constexpr (EPI == kEpiGeluGrad) {
+    const uint2 u = *reinterpret_cast<const uint2*>(
+        static_cast<const uint16_t*>(p.aux) + row * p.Nd + f);
+    v[0] *= gelu_tanh_grad(bf16_lo(u.x)); v[1] *= gelu_tanh_grad(bf16_hi(u.x));
+    v[2] *= gelu_tanh_grad(bf16_lo(u.y)); v[3] *= gelu_tanh_grad(bf16_hi(u.y));
+  }
   return v;
 }
 
 template <int EPI, bool OUT_BF16>
 __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
                                        int f, f32x4 v) {
-  v = finish4<EPI>(p, g, f, v);
+  v = finish4<EPI>(p, g, row, f, v);
   if constexpr (OUT_BF16) {
     uint2 o;
     o.x = pack_bf16x2(v[0], v[1]);
@@ -287,8 +385,10 @@ __device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
-          bool PF>
+          bool PF, bool KG = false>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(!KG || (!OUT_BF16 && !PF && EPI == kEpiStore),
+                "the K-grouped form writes fp32 without prefetch");
   constexpr int kWaves = WT * WF;
   constexpr int TB = BM / WT / 32;   // token blocks per wave
   constexpr int FB = BN / WF / 32;   // feature blocks per wave
@@ -335,9 +435,12 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const int wt = wave % WT;   // token slice of the tile
   const int wf = wave / WT;   // feature slice of the tile
-  const int Kd = p.Kd;
-  const uint32_t row_bytes = static_cast<uint32_t>(Kd) * 2u;
-  build_group_table<BM, BN>(p, tab, wave, tid0 & 63);
+  const int Kd0 = p.Kd;
+  const uint32_t row_bytes0 = static_cast<uint32_t>(Kd0) * 2u;
+  if constexpr (KG)
+    build_kseg_table(p, tab, wave, tid0 & 63);
+  else
+    build_group_table<BM, BN>(p, tab, wave, tid0 & 63);
 
   // Token rows: gathered through a_index from the whole activation matrix,
   // or read in place from the tile's first row.  Rows past the group end
@@ -363,7 +466,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const int pj = blockIdx.x >> 3, pxcd = blockIdx.x & 7, pw = gridDim.x >> 3;
   int pc = pxcd, it = 0;
   TileLoc loc;
-  bool have = locate_tile_tab<BM, BN, GM>(p, tab, tid0 & 63, pc * pw + pj, loc);
+  bool have = locate_any<KG, BM, BN, GM>(p, tab, tid0 & 63, pc * pw + pj, loc);
   if (gather && have) MOE_FETCH_ROWS(loc, 0, tid0 & 63);
   stage_barrier();
   while (have) {
@@ -376,8 +479,17 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // The previous tile's readers of the LDS are done.
   __builtin_amdgcn_s_barrier();
 
-  const uint16_t* a_base = static_cast<const uint16_t*>(p.a) +
-                           (gather ? int64_t(0) : loc.row0 * Kd);
+  // Reduction length and operand row pitch of this tile: the group's padded
+  // token segment and the transposed operands' pitch in the K-grouped form.
+  const int Kd = KG ? loc.klen : Kd0;
+  const uint32_t row_bytes =
+      KG ? static_cast<uint32_t>(p.ld) * 2u : row_bytes0;
+  const uint16_t* a_base =
+      static_cast<const uint16_t*>(p.a) +
+      (gather ? int64_t(0)
+              : KG ? (loc.row0 - static_cast<int64_t>(loc.g) * p.mrows) * p.ld +
+                         loc.kofs
+                   : loc.row0 * Kd);
   const uint32_t a_bytes =
       gather ? kOutOfRange
              : static_cast<uint32_t>(min(static_cast<int>(loc.row_end - loc.row0), BM)) *
@@ -387,8 +499,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
                     uniform64(reinterpret_cast<int64_t>(a_base))),
                 __builtin_amdgcn_readfirstlane(a_bytes));
   // Weight rows of group g: features past Nd fall outside the descriptor.
-  const uint16_t* w_base = static_cast<const uint16_t*>(p.w) +
-                           (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd;
+  const uint16_t* w_base =
+      static_cast<const uint16_t*>(p.w) +
+      (KG ? static_cast<int64_t>(loc.n0) * p.ld + loc.kofs
+          : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
   const uint32_t w_bytes =
       static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsB =
@@ -574,7 +688,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // In gather mode, the source rows of this workgroup's next tile.
   if (gather) {
     TileLoc nloc;
-    if (locate_tile_tab<BM, BN, GM>(p, tab, lane, (pc + 8) * pw + pj, nloc))
+    if (locate_any<KG, BM, BN, GM>(p, tab, lane, (pc + 8) * pw + pj, nloc))
       MOE_FETCH_ROWS(nloc, (it + 1) & 1, lane);
   }
 
@@ -638,7 +752,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           v[1] = acc[i][j][4 * q + 1];
           v[2] = acc[i][j][4 * q + 2];
           v[3] = acc[i][j][4 * q + 3];
-          v = finish4<EPI>(p, loc.g, loc.n0 + fl, v);
+          v = finish4<EPI>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);
           uint2 o;
           o.x = pack_bf16x2(v[0], v[1]);
           o.y = pack_bf16x2(v[2], v[3]);
@@ -753,7 +867,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
   pc += 8;
   ++it;
-  have = locate_tile_tab<BM, BN, GM>(p, tab, lane, pc * pw + pj, loc);
+  have = locate_any<KG, BM, BN, GM>(p, tab, lane, pc * pw + pj, loc);
   }  // tile loop
 }
 
@@ -870,6 +984,129 @@ int persistent_grid(int tiles) {
 }
 
 }  // namespace
+
+namespace {
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct BwdLayout {
+  size_t u, du, w1t, w2t, dyT, aT, duT, xT, brow, bn, total;
+};
+
+BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
+  const int64_t Kt = padded_columns(total, G);
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  L.u = take(static_cast<size_t>(total) * H * 2);
+  L.du = take(static_cast<size_t>(total) * H * 2);
+  L.w1t = take(static_cast<size_t>(G) * D * H * 2);
+  L.w2t = take(static_cast<size_t>(G) * H * D * 2);
+  L.dyT = take(static_cast<size_t>(D) * Kt * 2);
+  L.aT = take(static_cast<size_t>(H) * Kt * 2);
+  L.duT = take(static_cast<size_t>(H) * Kt * 2);
+  L.xT = take(static_cast<size_t>(D) * Kt * 2);
+  L.brow = take(static_cast<size_t>(Kt / 64) * 8);
+  L.bn = take(static_cast<size_t>(Kt / 64) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H) {
+  return bwd_layout(total, G, D, H).total;
+}
+
+// Backward of the grouped expert MLPs, given dy_rows = dLoss/d(expert output):
+//   u       = x_rows W1^T (+ b1)                   (recomputed, bf16)
+//   du      = (dy_rows W2) * gelu'(u)              (W2 transposed once)
+//   dx_rows = du W1                                (W1 transposed once)
+//   dW2[g]  = dy_rows[g]^T gelu(u[g]),  dW1[g] = du[g]^T x_rows[g]
+// the last two as K-grouped GEMMs over token-padded transposed operands.
+hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(a.total_rows, a.G, a.D, a.H);
+  char* ws = static_cast<char*>(a.workspace);
+  void* u = ws + L.u;
+  void* du = ws + L.du;
+  void* w1t = ws + L.w1t;
+  void* w2t = ws + L.w2t;
+  void* dyT = ws + L.dyT;
+  void* aT = ws + L.aT;
+  void* duT = ws + L.duT;
+  void* xT = ws + L.xT;
+  int64_t* brow = reinterpret_cast<int64_t*>(ws + L.brow);
+  int32_t* bn = reinterpret_cast<int32_t*>(ws + L.bn);
+  const int64_t Kt = padded_columns(a.total_rows, a.G);
+  const int G = a.G, D = a.D, H = a.H;
+  hipError_t err;
+#define MOE_TRY(call)                      \
+  do {                                     \
+    err = (call);                          \
+    if (err != hipSuccess) return err;     \
+  } while (0)
+
+  // the weights' transposes are needed even without rows (dW = 0 then)
+  MOE_TRY(launch_transpose(a.w2, G, D, H, w2t, stream));
+  MOE_TRY(launch_transpose(a.w1, G, H, D, w1t, stream));
+  if (a.total_rows > 0) {
+    GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
+                  G, H, D};
+    hipLaunchKernelGGL(
+        (gemm_bf16_kernel<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
+        dim3(persistent_grid(tile_grid(pu, kUpBM, kUpBN))),
+        dim3(64 * kUpWT * kUpWF), 0, stream, pu);
+    MOE_TRY(hipGetLastError());
+    GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
+                  a.total_rows, G, H, D};
+    pd.aux = u;
+    hipLaunchKernelGGL(
+        (gemm_bf16_kernel<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
+        dim3(persistent_grid(tile_grid(pd, kUpBM, kUpBN))),
+        dim3(64 * kUpWT * kUpWF), 0, stream, pd);
+    MOE_TRY(hipGetLastError());
+    GemmParams px{du, nullptr, w1t, nullptr, a.dx_rows, a.offsets,
+                  a.total_rows, G, D, H};
+    if (a.dx_f32)
+      hipLaunchKernelGGL(
+          (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
+          dim3(persistent_grid(tile_grid(px, kDnBM, kDnBN))),
+          dim3(64 * kDnWT * kDnWF), 0, stream, px);
+    else
+      hipLaunchKernelGGL(
+          (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
+          dim3(persistent_grid(tile_grid(px, kDnBM, kDnBN))),
+          dim3(64 * kDnWT * kDnWF), 0, stream, px);
+    MOE_TRY(hipGetLastError());
+    MOE_TRY(launch_kseg(a.offsets, G, a.total_rows, brow, bn, stream));
+    MOE_TRY(launch_tpad(a.dy_rows, nullptr, brow, bn, G, a.total_rows, D, false, dyT, stream));
+    MOE_TRY(launch_tpad(u, nullptr, brow, bn, G, a.total_rows, H, true, aT, stream));
+    MOE_TRY(launch_tpad(du, nullptr, brow, bn, G, a.total_rows, H, false, duT, stream));
+    MOE_TRY(launch_tpad(a.x, a.row_index, brow, bn, G, a.total_rows, D, false, xT, stream));
+  }
+  // dW2[g] [D][H] = dyT[:, seg g] aT[:, seg g]^T;  dW1[g] [H][D] = duT xT^T.
+  // With no rows every segment is empty and the products are zero.
+  GemmParams pw2{dyT, nullptr, aT, nullptr, a.dw2, a.offsets, a.total_rows,
+                 G, H, 0};
+  pw2.ld = static_cast<int>(Kt);
+  pw2.mrows = D;
+  const int tiles2 = G * ((D + kUpBM - 1) / kUpBM) * ((H + kUpBN - 1) / kUpBN);
+  hipLaunchKernelGGL(
+      (gemm_bf16_kernel<kEpiStore, false, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false, true>),
+      dim3(persistent_grid(tiles2)), dim3(64 * kUpWT * kUpWF), 0, stream, pw2);
+  MOE_TRY(hipGetLastError());
+  GemmParams pw1{duT, nullptr, xT, nullptr, a.dw1, a.offsets, a.total_rows,
+                 G, D, 0};
+  pw1.ld = static_cast<int>(Kt);
+  pw1.mrows = H;
+  const int tiles1 = G * ((H + kUpBM - 1) / kUpBM) * ((D + kUpBN - 1) / kUpBN);
+  hipLaunchKernelGGL(
+      (gemm_bf16_kernel<kEpiStore, false, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false, true>),
+      dim3(persistent_grid(tiles1)), dim3(64 * kUpWT * kUpWF), 0, stream, pw1);
+  MOE_TRY(hipGetLastError());
+#undef MOE_TRY
+  return hipSuccess;
+}
 
 hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
                                   const void* w2, const float* b2,

@@ -65,6 +65,52 @@ hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int32_t* counts, float* psum, float* loss,
                           hipStream_t stream);
 
+// backward.hip
+int64_t padded_columns(int64_t total, int G);
+hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
+                            hipStream_t stream);
+hipError_t launch_kseg(const int64_t* offsets, int G, int64_t total,
+                       int64_t* blk_row, int32_t* blk_n, hipStream_t stream);
+hipError_t launch_tpad(const void* src, const int32_t* row_index,
+                       const int64_t* blk_row, const int32_t* blk_n, int G,
+                       int64_t total, int C, bool gelu, void* dst,
+                       hipStream_t stream);
+hipError_t launch_combine_backward(const void* dy, bool dy_bf16,
+                                   const void* y_rows, bool y_bf16,
+                                   const int32_t* slot_row, const float* w,
+                                   int64_t N, int D, int Kmax, void* dy_rows,
+                                   float* dw, hipStream_t stream);
+size_t gate_backward_workspace_bytes(int64_t N, int E, int D);
+hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
+                                const float* probs, const int32_t* idx,
+                                const float* dw, const int32_t* counts, int B,
+                                int T, int D, int E, int Kmax, int K, float alpha,
+                                float dloss, bool global, const void* dx_rows,
+                                const int32_t* slot_row, const void* dx_shared,
+                                bool dx_bf16, void* dx, float* dw_gate,
+                                float* dbias, void* workspace,
+                                hipStream_t stream);
+
+// ffn.hip, backward of the grouped expert MLPs (bf16)
+struct FfnBwdArgs {
+  const void* x;            // [*][D]
+  const int32_t* row_index; // [total] or null
+  int64_t total_rows;
+  const int64_t* offsets;   // [G+1] device
+  int G, D, H;
+  const void* w1;           // [G][H][D]
+  const float* b1;          // [G][H] or null
+  const void* w2;           // [G][D][H]
+  const void* dy_rows;      // [total][D] gradient of the expert outputs
+  void* workspace;
+  void* dx_rows;            // [total][D]
+  bool dx_f32;
+  float* dw1;               // [G][H][D]
+  float* dw2;               // [G][D][H]
+};
+size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H);
+hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream);
+
 // analytics.hip
 hipError_t launch_routing_hist(const int32_t* idx, int B, int T, int E,
                                int Kmax, const int32_t* tags, int n_tags,

@@ -205,3 +205,86 @@ def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
         combine(cfg, buf)
     balance(cfg, buf, balance_mode)
     return buf
+
+
+# ---------------------------------------------------------------- backward --
+
+class BackwardBuffers:
+    """Gradients and workspaces of one backward pass (bf16 layers)."""
+
+    def __init__(self, cfg, device="cuda"):
+        if cfg.dtype != "bf16":
+            raise ValueError("the backward pass takes bf16 layers")
+        dt, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+        N, D, H, E, Kmax, A, n_s = cfg.N, cfg.D, cfg.H, cfg.E, cfg.Kmax, cfg.A, cfg.n_s
+        dev = device
+        self.dy_rows = torch.empty(A, D, dtype=dt, device=dev)
+        self.slot_grad = torch.empty(N, Kmax, dtype=f32, device=dev)
+        self.dx_rows = torch.empty(A, D, dtype=dt, device=dev)
+        self.dw1 = torch.empty(E, H, D, dtype=f32, device=dev)
+        self.dw2 = torch.empty(E, D, H, dtype=f32, device=dev)
+        ws = ops.ffn_backward_workspace_size(A, E, D, H)
+        if n_s > 0:
+            self.dx_shared = torch.empty(N, D, dtype=dt, device=dev)
+            self.dw1s = torch.empty(1, n_s * H, D, dtype=f32, device=dev)
+            self.dw2s = torch.empty(1, D, n_s * H, dtype=f32, device=dev)
+            ws = max(ws, ops.ffn_backward_workspace_size(N, 1, D, n_s * H))
+        else:
+            self.dx_shared = self.dw1s = self.dw2s = None
+        self.ffn_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.dx = torch.empty(N, D, dtype=dt, device=dev)
+        self.dw_gate = torch.empty(E, D, dtype=f32, device=dev)
+        self.dbias = torch.empty(E, dtype=f32, device=dev)
+        gws = ops.gate_backward_workspace_size(N, E, D)
+        self.gate_ws = torch.empty(max(gws, 1), dtype=torch.uint8, device=dev)
+
+
+def combine_backward(cfg, buf, grads, dy):
+    ops.moe_combine_backward(dy, buf.y_rows, buf.slot_row, buf.topk_w,
+                             grads.dy_rows, grads.slot_grad)
+
+
+def routed_ffn_backward(cfg, x, wts, buf, grads):
+    x_rows, row_index = (x, buf.row_token) if buf.gather else (buf.x_perm, None)
+    ops.moe_grouped_ffn_backward(x_rows, row_index, cfg.A, buf.expert_offsets,
+                                 wts.w1, None, wts.w2, grads.dy_rows,
+                                 grads.ffn_ws, grads.dx_rows, grads.dw1,
+                                 grads.dw2)
+
+
+def shared_ffn_backward(cfg, x, wts, buf, grads, dy):
+    if cfg.n_s > 0:
+        ops.moe_grouped_ffn_backward(x, None, cfg.N, buf.shared_offsets,
+                                     wts.w1s, None, wts.w2s, dy, grads.ffn_ws,
+                                     grads.dx_shared, grads.dw1s, grads.dw2s)
+
+
+def gate_backward(cfg, x, wts, buf, grads, dloss, balance_mode="sequence"):
+    ops.moe_gate_backward(x, wts.w_gate, buf.probs, buf.topk_idx,
+                          grads.slot_grad, buf.bal_counts, cfg.B, cfg.T,
+                          cfg.K, cfg.alpha, dloss, BALANCE[balance_mode],
+                          grads.dx_rows, buf.slot_row, grads.dx_shared,
+                          grads.dx, grads.dw_gate, grads.dbias, grads.gate_ws)
+
+
+# The backward pass as named calls, in order (same work as backward()):
+# each takes (cfg, x, weights, forward buffers, gradients, dy, dloss).
+BACKWARD_STEPS = (
+    ("combine_backward", lambda c, x, w, b, g, dy, dl: combine_backward(c, b, g, dy)),
+    ("routed_ffn_backward", lambda c, x, w, b, g, dy, dl: routed_ffn_backward(c, x, w, b, g)),
+    ("shared_ffn_backward", lambda c, x, w, b, g, dy, dl: shared_ffn_backward(c, x, w, b, g, dy)),
+    ("gate_backward", lambda c, x, w, b, g, dy, dl: gate_backward(c, x, w, b, g, dl)),
+)
+
+
+def backward(cfg, x, wts: LayerWeights, buf: LayerBuffers,
+             grads: BackwardBuffers, dy: torch.Tensor, dloss: float = 1.0,
+             balance_mode: str = "sequence") -> BackwardBuffers:
+    """Gradients of <dy, y> + dloss * L_balance after forward() (same
+    buffers and balance mode): combine, routed experts, shared experts, gate
+    and dx."""
+    combine_backward(cfg, buf, grads, dy)
+    routed_ffn_backward(cfg, x, wts, buf, grads)
+    shared_ffn_backward(cfg, x, wts, buf, grads, dy)
+    gate_backward(cfg, x, wts, buf, grads, dloss, balance_mode)
+    return grads

@@ -114,3 +114,44 @@ def moe_ffn_down_combine(h, w2, b2, y_rows, slot_row, topk_w, y):
     _lib.call("moe_ffn_down_combine", _ptr(h), dtype_code(h.dtype), N, D, H,
               _ptr(w2), _ptr(b2), _ptr(y_rows), _ptr(slot_row), _ptr(topk_w),
               slot_row.shape[1], _ptr(y), _stream())
+
+
+# ---------------------------------------------------------------- backward --
+
+def moe_combine_backward(dy, y_rows, slot_row, topk_w, dy_rows, slot_grad):
+    N, D = dy.shape
+    _lib.call("moe_combine_backward", _ptr(dy), dtype_code(dy.dtype),
+              _ptr(y_rows), dtype_code(y_rows.dtype), _ptr(slot_row),
+              _ptr(topk_w), N, D, slot_row.shape[1], _ptr(dy_rows),
+              _ptr(slot_grad), _stream())
+
+
+def ffn_backward_workspace_size(total_rows: int, G: int, D: int, H: int) -> int:
+    return int(_lib.load().moe_ffn_backward_workspace_size(total_rows, G, D, H))
+
+
+def moe_grouped_ffn_backward(x_rows, row_index, total_rows: int, group_offsets,
+                             w1, b1, w2, dy_rows, workspace, dx_rows, dw1, dw2):
+    G, H, D = w1.shape
+    _lib.call("moe_grouped_ffn_backward", _ptr(x_rows), _ptr(row_index),
+              dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(dy_rows), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _ptr(dx_rows),
+              dtype_code(dx_rows.dtype), _ptr(dw1), _ptr(dw2), _stream())
+
+
+def gate_backward_workspace_size(N: int, E: int, D: int) -> int:
+    return int(_lib.load().moe_gate_backward_workspace_size(N, E, D))
+
+
+def moe_gate_backward(x, w_gate, probs, topk_idx, slot_grad, counts, B: int,
+                      T: int, K: int, alpha: float, dloss: float, mode: int,
+                      dx_rows, slot_row, dx_shared, dx, dw_gate, dbias,
+                      workspace):
+    E, D = w_gate.shape
+    _lib.call("moe_gate_backward", _ptr(x), dtype_code(x.dtype), _ptr(w_gate),
+              _ptr(probs), _ptr(topk_idx), _ptr(slot_grad), _ptr(counts), B, T,
+              D, E, topk_idx.shape[1], K, alpha, dloss, mode, _ptr(dx_rows),
+              _ptr(slot_row), _ptr(dx_shared), dtype_code(dx.dtype), _ptr(dx),
+              _ptr(dw_gate), _ptr(dbias), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream())

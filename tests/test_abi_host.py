@@ -205,3 +205,48 @@ def test_ffn_down_combine_rejects(kw, status):
     ensure_built()
     assert _fdc(**kw) == status
     assert _lib.last_error()
+
+
+def test_backward_entry_points_reject():
+    ensure_built()
+    lib = _lib.load()
+    assert lib.moe_ffn_backward_workspace_size(1000, 8, 128, 256) > 0
+    assert lib.moe_ffn_backward_workspace_size(-1, 8, 128, 256) == 0
+    assert lib.moe_gate_backward_workspace_size(1000, 8, 128) > 0
+    cb = dict(dy=FAKE, dydt=_lib.MOE_BF16, yr=FAKE, ydt=_lib.MOE_BF16, sr=FAKE,
+              w=FAKE, N=10, D=64, Kmax=2, dyr=FAKE, sg=FAKE, stream=None)
+    for kw, st in [(dict(dy=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(sg=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(Kmax=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(D=60), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(Kmax=65), _lib.MOE_ERR_UNSUPPORTED)]:
+        a = dict(cb); a.update(kw)
+        assert _lib.call_status("moe_combine_backward", *a.values()) == st
+    fb = dict(x=FAKE, ri=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
+              D=128, H=256, w1=FAKE, b1=None, w2=FAKE, dyr=FAKE, ws=FAKE,
+              wsb=1 << 40, dx=FAKE, dxdt=_lib.MOE_BF16, dw1=FAKE, dw2=FAKE,
+              stream=None)
+    for kw, st in [(dict(w1=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(dw2=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(G=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(dt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(H=100), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(wsb=16), _lib.MOE_ERR_WORKSPACE_TOO_SMALL)]:
+        a = dict(fb); a.update(kw)
+        assert _lib.call_status("moe_grouped_ffn_backward", *a.values()) == st
+    gb = dict(x=FAKE, xdt=_lib.MOE_BF16, wg=FAKE, P=FAKE, idx=FAKE, sg=FAKE,
+              counts=FAKE, B=2, T=16, D=64, E=8, Kmax=2, K=2, alpha=0.01,
+              dloss=1.0, mode=_lib.MOE_BAL_PER_SEQUENCE, dxr=None, sr=None,
+              dxs=None, dxdt=_lib.MOE_BF16, dx=FAKE, dwg=FAKE, db=None,
+              ws=FAKE, wsb=1 << 30, stream=None)
+    for kw, st in [(dict(wg=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(counts=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(K=9), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(mode=5), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(dxr=FAKE), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   (dict(E=65, K=2), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(D=60), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(wsb=8), _lib.MOE_ERR_WORKSPACE_TOO_SMALL)]:
+        a = dict(gb); a.update(kw)
+        assert _lib.call_status("moe_gate_backward", *a.values()) == st

@@ -1,0 +1,191 @@
+"""Backward pass through the C ABI against the CPU oracle's gradients
+(oracle.layer_backward, pinned by finite differences and autograd): the
+combine, grouped expert MLP and gate backward calls one by one, and the
+whole layer after a forward pass."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import GpuLayer, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _ops():
+    from sparse_moe_diffusion_amd import _lib, ops
+    return _lib, ops
+
+
+def q(a):
+    return synth.bf16_to_f32(synth.bf16_bits(np.asarray(a, np.float32)))
+
+
+def bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(DEV)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("N,D,Kmax,empty", [(1, 64, 1, 0.0), (500, 1152, 2, 0.1),
+                                            (333, 136, 4, 0.4)])
+def test_combine_backward(N, D, Kmax, empty):
+    _lib, ops = _ops()
+    rng = np.random.default_rng(N + D)
+    A = N * Kmax
+    dy = q(rng.standard_normal((N, D)))
+    yr = q(rng.standard_normal((A, D)))
+    sr = rng.permutation(A).reshape(N, Kmax).astype(np.int32)
+    sr[rng.random((N, Kmax)) < empty] = -1
+    w = rng.random((N, Kmax)).astype(np.float32)
+    dyr = torch.zeros(A, D, dtype=torch.bfloat16, device=DEV)
+    sg = torch.full((N, Kmax), 7.0, dtype=torch.float32, device=DEV)
+    ops.moe_combine_backward(bf(dy), bf(yr), dev(sr), dev(w), dyr, sg)
+    torch.cuda.synchronize()
+    got_rows = to_np(dyr)
+    ref_sg = np.zeros((N, Kmax))
+    ref_rows = np.zeros((A, D), np.float32)
+    for t in range(N):
+        for k in range(Kmax):
+            r = sr[t, k]
+            if r >= 0:
+                ref_rows[r] = q(np.float32(w[t, k]) * dy[t])   # one fp32 product, RNE
+                ref_sg[t, k] = float(dy[t].astype(np.float64) @ yr[r].astype(np.float64))
+    assert np.array_equal(got_rows, ref_rows)
+    assert np.abs(to_np(sg) - ref_sg).max() <= 1e-5 * max(1.0, np.abs(ref_sg).max())
+
+
+@pytest.mark.parametrize("sizes,D,H,gather", [
+    ([100, 0, 129, 1, 256], 128, 256, False), ([300, 70], 192, 384, True),
+    ([513], 1152, 512, False), ([0, 0, 5], 64, 128, True)])
+def test_grouped_ffn_backward(sizes, D, H, gather):
+    _lib, ops = _ops()
+    rng = np.random.default_rng(sum(sizes) + D + H)
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(offsets[-1])
+    nsrc = total + 9
+    xsrc = q(rng.standard_normal((nsrc, D)))
+    w1 = q(rng.standard_normal((G, H, D)) * 0.05)
+    w2 = q(rng.standard_normal((G, D, H)) * 0.05)
+    ri = rng.permutation(nsrc)[:total].astype(np.int32) if gather else None
+    rows = xsrc[ri] if gather else xsrc[:total]
+    dyr = q(rng.standard_normal((total, D)))
+    ws = torch.empty(ops.ffn_backward_workspace_size(total, G, D, H),
+                     dtype=torch.uint8, device=DEV)
+    dx = torch.empty(total, D, dtype=torch.bfloat16, device=DEV)
+    dw1 = torch.full((G, H, D), 5.0, dtype=torch.float32, device=DEV)
+    dw2 = torch.full((G, D, H), 5.0, dtype=torch.float32, device=DEV)
+    ops.moe_grouped_ffn_backward(bf(xsrc if gather else rows),
+                                 None if ri is None else dev(ri), total,
+                                 dev(offsets), bf(w1), None, bf(w2), bf(dyr),
+                                 ws, dx, dw1, dw2)
+    torch.cuda.synchronize()
+    ref_dx = np.zeros((total, D))
+    ref_dw1 = np.zeros((G, H, D))
+    ref_dw2 = np.zeros((G, D, H))
+    for g in range(G):
+        a, b = offsets[g], offsets[g + 1]
+        if b > a:
+            ref_dx[a:b], ref_dw1[g], ref_dw2[g], _, _ = oracle.expert_mlp_backward(
+                rows[a:b], w1[g], w2[g], dyr[a:b])
+    if total:
+        assert_close(to_np(dx), ref_dx, "bf16", "dx_rows")
+    for g in range(G):
+        if offsets[g + 1] == offsets[g]:
+            assert not to_np(dw1[g]).any() and not to_np(dw2[g]).any()
+    assert_close(to_np(dw1), ref_dw1, "bf16", "dW1")
+    assert_close(to_np(dw2), ref_dw2, "bf16", "dW2")
+
+
+@pytest.mark.parametrize("B,T,D,E,K,mode,with_rows", [
+    (2, 64, 128, 8, 2, "sequence", True), (3, 100, 64, 16, 2, "global", False),
+    (1, 37, 1152, 5, 3, "sequence", True)])
+def test_gate_backward(B, T, D, E, K, mode, with_rows):
+    _lib, ops = _ops()
+    rng = np.random.default_rng(B * T + E)
+    N = B * T
+    x = q(rng.standard_normal((N, D)))
+    wg = (rng.standard_normal((E, D)) * 0.05).astype(np.float32)
+    P = oracle.softmax(x @ wg.T.astype(np.float64)).astype(np.float32)
+    idx, _ = oracle.topk_select(P.astype(np.float64), K)
+    sg = rng.standard_normal((N, K)).astype(np.float32)
+    counts = oracle.selection_indicator(idx, E).reshape(B, T, E).sum(1).astype(np.int32)
+    A = N * K
+    sr = rng.permutation(A).reshape(N, K).astype(np.int32)
+    dxr = q(rng.standard_normal((A, D)))
+    dxs = q(rng.standard_normal((N, D)))
+    dloss, alpha = 2.5, 0.01
+    ws = torch.empty(ops.gate_backward_workspace_size(N, E, D), dtype=torch.uint8,
+                     device=DEV)
+    dx = torch.empty(N, D, dtype=torch.bfloat16, device=DEV)
+    dwg = torch.empty(E, D, dtype=torch.float32, device=DEV)
+    db = torch.empty(E, dtype=torch.float32, device=DEV)
+    bal = _lib.MOE_BAL_GLOBAL if mode == "global" else _lib.MOE_BAL_PER_SEQUENCE
+    ops.moe_gate_backward(bf(x), dev(wg), dev(P), dev(idx.astype(np.int32)),
+                          dev(sg), dev(counts), B, T, K, alpha, dloss, bal,
+                          bf(dxr) if with_rows else None,
+                          dev(sr) if with_rows else None,
+                          bf(dxs) if with_rows else None, dx, dwg, db, ws)
+    torch.cuda.synchronize()
+    dP = np.zeros((N, E))
+    np.add.at(dP, (np.repeat(np.arange(N), K), idx.ravel()), sg.ravel())
+    dP += dloss * oracle.balance_grad(idx, E, B, T, K, alpha, mode)
+    dl = oracle.softmax_backward(P, dP)
+    ref_dx = dl @ wg.astype(np.float64)
+    if with_rows:
+        for k in range(K):
+            ref_dx += dxr[sr[:, k]]
+        ref_dx += dxs
+    assert_close(to_np(dx), ref_dx, "bf16", "dx")
+    assert_close(to_np(dwg), dl.T @ x.astype(np.float64), "f32", "dW_g")
+    assert_close(to_np(db), dl.sum(0), "f32", "dbias")
+
+
+def _layer_backward(cfg, seed, dloss=1.0, mode="sequence"):
+    from sparse_moe_diffusion_amd import layer
+    inp = synth.make_inputs(cfg)
+    gl = GpuLayer(inp, gather=True).run(mode)
+    rng = np.random.default_rng(seed)
+    dy = q(rng.standard_normal((cfg.N, cfg.D)))
+    grads = layer.BackwardBuffers(cfg)
+    layer.backward(cfg, gl.x, gl.w, gl.buf, grads, bf(dy), dloss, mode)
+    torch.cuda.synchronize()
+    return inp, gl, dy, grads
+
+
+@pytest.mark.parametrize("name,mode", [("small", "sequence"), ("race", "global")])
+def test_layer_backward(name, mode):
+    cfg = synth.small_config(B=2, T=96, D=128, H=256, E=8, K=2, seed=41,
+                             route="race" if name == "race" else "topk")
+    inp, gl, dy, g = _layer_backward(cfg, 42, dloss=1.0, mode=mode)
+    idx = to_np(gl.buf.topk_idx)
+    r = oracle.route(inp)
+    P = r["P"]
+    w = oracle.slot_weights(P, idx)
+    ref = oracle.layer_backward(inp, idx, w, P, dy, 1.0, mode)
+    assert_close(to_np(g.dx), ref["dx"], "bf16", "dx")
+    assert_close(to_np(g.dw1), ref["dw1"], "bf16", "dW1")
+    assert_close(to_np(g.dw2), ref["dw2"], "bf16", "dW2")
+    n_s, H = cfg.n_s, cfg.H
+    dw1s = to_np(g.dw1s)[0].reshape(n_s, H, cfg.D)
+    dw2s = to_np(g.dw2s)[0].reshape(cfg.D, n_s, H).transpose(1, 0, 2)
+    assert_close(dw1s, ref["dw1s"], "bf16", "dW1s")
+    assert_close(dw2s, ref["dw2s"], "bf16", "dW2s")
+    assert_close(to_np(g.dw_gate), ref["dw_gate"], "bf16", "dW_g")
+    assert_close(to_np(g.dbias), ref["dbias"], "bf16", "dbias")
+
+
+def test_layer_backward_deterministic():
+    cfg = synth.small_config(B=2, T=80, D=128, H=256, E=8, K=2, seed=43)
+    _, _, _, g1 = _layer_backward(cfg, 44)
+    a = [to_np(t).copy() for t in (g1.dx, g1.dw1, g1.dw2, g1.dw_gate, g1.dbias)]
+    _, _, _, g2 = _layer_backward(cfg, 44)
+    b = [to_np(t) for t in (g2.dx, g2.dw1, g2.dw2, g2.dw_gate, g2.dbias)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
