@@ -16,9 +16,9 @@
 //    optional row gather and GELU on the way.
 //  * combine_bwd_kernel: one wave per token; the routed rows' output
 //    gradients w * dy and the slot-weight gradients <dy, y_row>.
-//  * gate_bwd_token_kernel / gate_bwd_main_kernel / gate_bwd_reduce_kernel:
-//    dP -> dlogits per token, then dW_g and dbias partials per token chunk
-//    with dx assembled in the same pass, then a fixed-order sum.
+//  * gate_bwd_token_kernel, gate_bwd_wgrad_kernel, gate_bwd_reduce_kernel,
+//    gate_bwd_dx_kernel: dP -> dlogits per token; dW_g and dbias partials
+//    per token chunk and their fixed-order sum; dx assembled per token.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,23 +37,47 @@ __device__ __forceinline__ float gelu_fwd(float u) {
 
 constexpr int kTile = 64;
 
+// 64 x 64 tile: 16-byte loads along the source rows, scattered 2-byte LDS
+// writes into the transposed tile, 16-byte LDS reads and 16-byte stores
+// along the destination rows (R and C are multiples of 8).
+constexpr int kTp = kTile + 8;   // LDS row pitch (elements), keeps 16 B rows
+
+__device__ __forceinline__ void tile_store_t(uint16_t (*t)[kTp], int j, int c8,
+                                             uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t[c8 + 2 * i][j] = static_cast<uint16_t>(w[i] & 0xffffu);
+    t[c8 + 2 * i + 1][j] = static_cast<uint16_t>(w[i] >> 16);
+  }
+}
+
 __global__ __launch_bounds__(256) void transpose_kernel(
     const uint16_t* __restrict__ src, int R, int C,
     uint16_t* __restrict__ dst) {
-  __shared__ uint16_t t[kTile][kTile + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t t[kTile][kTp];
   const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
   const int64_t g = blockIdx.z;
   const uint16_t* s = src + g * R * C;
   uint16_t* d = dst + g * R * C;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < kTile; r += 4) {
-    const int rr = r0 + r, cc = c0 + tx;
-    t[r][tx] = (rr < R && cc < C) ? s[static_cast<int64_t>(rr) * C + cc] : 0;
+  const int ch = threadIdx.x & 7, jr = threadIdx.x >> 3;   // 8 chunks x 32 rows
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = jr + 32 * h;
+    const int rr = r0 + j, cc = c0 + 8 * ch;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < R && cc < C)
+      v = *reinterpret_cast<const uint4*>(s + static_cast<int64_t>(rr) * C + cc);
+    tile_store_t(t, j, 8 * ch, v);
   }
   __syncthreads();
-  for (int c = ty; c < kTile; c += 4) {
-    const int cc = c0 + c, rr = r0 + tx;
-    if (cc < C && rr < R) d[static_cast<int64_t>(cc) * R + rr] = t[tx][c];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = jr + 32 * h;
+    const int cc = c0 + c, rr = r0 + 8 * ch;
+    if (cc < C && rr < R)
+      *reinterpret_cast<uint4*>(d + static_cast<int64_t>(cc) * R + rr) =
+          *reinterpret_cast<const uint4*>(&t[c][8 * ch]);
   }
 }
 
@@ -98,33 +122,47 @@ __global__ __launch_bounds__(256) void kseg_kernel(
 
 // dst [C][Kt]: column block kb holds the blk_n[kb] source rows from
 // blk_row[kb] (through row_index when given), transposed, then zeros.
+// Same 16-byte tile scheme as transpose_kernel (C a multiple of 8).
 template <bool GELU>
 __global__ __launch_bounds__(256) void tpad_kernel(
     const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
     const int64_t* __restrict__ blk_row, const int32_t* __restrict__ blk_n,
     int C, int64_t Kt, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t t[kTile][kTile + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t t[kTile][kTp];
   const int c0 = blockIdx.x * kTile;
   const int64_t kb = blockIdx.y;
   const int64_t k0 = kb * kTile;
   const int64_t row0 = blk_row[kb];
   const int n = blk_n[kb];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int j = ty; j < kTile; j += 4) {
-    const int cc = c0 + tx;
-    uint16_t v = 0;
+  const int ch = threadIdx.x & 7, jr = threadIdx.x >> 3;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = jr + 32 * h;
+    const int cc = c0 + 8 * ch;
+    uint4 v = make_uint4(0, 0, 0, 0);
     if (j < n && cc < C) {
       const int64_t r = row0 + j;
       const int64_t sr = row_index ? row_index[r] : r;
-      v = src[sr * C + cc];
-      if constexpr (GELU) v = f32_to_bf16_bits(gelu_fwd(bf16_bits_to_f32(v)));
+      v = *reinterpret_cast<const uint4*>(src + sr * C + cc);
+      if constexpr (GELU) {
+        float f[8];
+        unpack8(v, f);
+        v.x = pack_bf16x2(gelu_fwd(f[0]), gelu_fwd(f[1]));
+        v.y = pack_bf16x2(gelu_fwd(f[2]), gelu_fwd(f[3]));
+        v.z = pack_bf16x2(gelu_fwd(f[4]), gelu_fwd(f[5]));
+        v.w = pack_bf16x2(gelu_fwd(f[6]), gelu_fwd(f[7]));
+      }
     }
-    t[j][tx] = v;
+    tile_store_t(t, j, 8 * ch, v);
   }
   __syncthreads();
-  for (int c = ty; c < kTile; c += 4) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = jr + 32 * h;
     const int cc = c0 + c;
-    if (cc < C) dst[static_cast<int64_t>(cc) * Kt + k0 + tx] = t[tx][c];
+    if (cc < C)
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(cc) * Kt + k0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(&t[c][8 * ch]);
   }
 }
 
@@ -253,74 +291,104 @@ __global__ __launch_bounds__(256) void gate_bwd_token_kernel(
   }
 }
 
-constexpr int kGbTokens = 128;   // tokens per workgroup
-constexpr int kGbThreads = 256;
+constexpr int kGbTokens = 64;    // tokens per workgroup of the dW_g pass
+constexpr int kGbBatch = 8;      // x rows loaded ahead in that pass
 
-// Workgroup = kGbTokens tokens; thread = 8 consecutive features (chunks
-// c = tid, tid + 256, ...).  Per chunk: the workgroup's dW_g partial
-// [E][8] for that chunk (experts in blocks of 8), and in the first block
-// pass, dx[t] = sum_k dx_rows[slot_row[t][k]] + dx_shared[t]
-//              + sum_i dl[t][i] W_g[i]   for each token, in fp32, rounded once.
-template <bool XB, bool OB>
-__global__ __launch_bounds__(kGbThreads) void gate_bwd_main_kernel(
-    const void* __restrict__ x, const float* __restrict__ wg,
-    const float* __restrict__ dl, int64_t N, int D, int E, int Kmax,
-    const void* __restrict__ dx_rows, const int32_t* __restrict__ slot_row,
-    const void* __restrict__ dx_shared, void* __restrict__ dx,
-    float* __restrict__ part_w, float* __restrict__ part_b) {
+// dx[t] = sum_k dx_rows[slot_row[t][k]] + dx_shared[t] + sum_i dl[t][i] W_g[i]
+// in fp32, rounded once.  One thread per 8 features of a token; slot rows
+// in groups of 4, loaded before they are added (in slot order).
+template <bool OB>
+__global__ __launch_bounds__(256) void gate_bwd_dx_kernel(
+    const float* __restrict__ wg, const float* __restrict__ dl, int64_t N,
+    int D, int E, int Kmax, const void* __restrict__ dx_rows,
+    const int32_t* __restrict__ slot_row, const void* __restrict__ dx_shared,
+    void* __restrict__ dx) {
+  const uint32_t nch = static_cast<uint32_t>(D / 8);
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= static_cast<uint32_t>(N) * nch) return;
+  const uint32_t tq = i / nch;
+  const int64_t t = tq;
+  const int c = static_cast<int>(i - tq * nch);
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+  if (slot_row != nullptr) {
+    for (int k0 = 0; k0 < Kmax; k0 += 4) {
+      int32_t r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        r[q] = (k0 + q < Kmax) ? slot_row[t * Kmax + k0 + q] : -1;
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (r[q] >= 0) ld8<OB>(dx_rows, r[q], D, c, v[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (r[q] >= 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] += v[q][j];
+        }
+    }
+  }
+  if (dx_shared != nullptr) {
+    float v[8];
+    ld8<OB>(dx_shared, t, D, c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] += v[j];
+  }
+  for (int e = 0; e < E; ++e) {
+    const float d = dl[t * E + e];
+    const float4* wp =
+        reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * D) + 2 * c;
+    const float4 a = wp[0], b = wp[1];
+    o[0] = fmaf(d, a.x, o[0]); o[1] = fmaf(d, a.y, o[1]);
+    o[2] = fmaf(d, a.z, o[2]); o[3] = fmaf(d, a.w, o[3]);
+    o[4] = fmaf(d, b.x, o[4]); o[5] = fmaf(d, b.y, o[5]);
+    o[6] = fmaf(d, b.z, o[6]); o[7] = fmaf(d, b.w, o[7]);
+  }
+  st8<OB>(dx, t, D, c, o);
+}
+
+// Workgroup = kGbTokens tokens; their dl rows are staged in LDS.  Thread =
+// 8 consecutive features (chunk c); for experts in blocks of 8 it sums, over
+// the chunk's tokens, dl[t][i] x[t][c..c+8], loading kGbBatch x rows ahead,
+// and writes the chunk's partial [E][D].  Threads i < E also sum dl over
+// the chunk (the dbias partial).
+template <bool XB>
+__global__ __launch_bounds__(256) void gate_bwd_wgrad_kernel(
+    const void* __restrict__ x, const float* __restrict__ dl, int64_t N, int D,
+    int E, float* __restrict__ part_w, float* __restrict__ part_b) {
+  __shared__ float sdl[kGbTokens][kMaxExperts];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kGbTokens;
-  const int64_t t1 = min(N, t0 + kGbTokens);
+  const int nt = static_cast<int>(min<int64_t>(kGbTokens, N - t0));
+  for (int i = threadIdx.x; i < nt * E; i += blockDim.x)
+    sdl[i / E][i % E] = dl[t0 * E + i];
+  __syncthreads();
   const int nch = D / 8;
   float* pw = part_w + static_cast<int64_t>(blockIdx.x) * E * D;
-  for (int c = threadIdx.x; c < nch; c += kGbThreads) {
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
     for (int e0 = 0; e0 < E; e0 += 8) {
       float acc[8][8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-      for (int64_t t = t0; t < t1; ++t) {
-        float xv[8];
-        ld8<XB>(x, t, D, c, xv);
+      for (int tb = 0; tb < nt; tb += kGbBatch) {
+        float xv[kGbBatch][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (e0 + i < E) {
-            const float d = dl[t * E + e0 + i];
+        for (int b = 0; b < kGbBatch; ++b)
+          if (tb + b < nt) ld8<XB>(x, t0 + tb + b, D, c, xv[b]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xv[j], acc[i][j]);
-          }
-        }
-        if (e0 == 0 && dx != nullptr) {
-          float o[8];
+        for (int b = 0; b < kGbBatch; ++b) {
+          if (tb + b >= nt) break;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] = 0.0f;
-          if (slot_row != nullptr) {
-            for (int k = 0; k < Kmax; ++k) {
-              const int32_t r = slot_row[t * Kmax + k];
-              if (r < 0) continue;
-              float v[8];
-              ld8<OB>(dx_rows, r, D, c, v);
+          for (int i = 0; i < 8; ++i) {
+            if (e0 + i < E) {
+              const float d = sdl[tb + b][e0 + i];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) o[j] += v[j];
+              for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(d, xv[b][j], acc[i][j]);
             }
           }
-          if (dx_shared != nullptr) {
-            float v[8];
-            ld8<OB>(dx_shared, t, D, c, v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] += v[j];
-          }
-          for (int i = 0; i < E; ++i) {
-            const float d = dl[t * E + i];
-            const float4* wp = reinterpret_cast<const float4*>(
-                wg + static_cast<int64_t>(i) * D) + 2 * c;
-            const float4 a = wp[0], b = wp[1];
-            o[0] = fmaf(d, a.x, o[0]); o[1] = fmaf(d, a.y, o[1]);
-            o[2] = fmaf(d, a.z, o[2]); o[3] = fmaf(d, a.w, o[3]);
-            o[4] = fmaf(d, b.x, o[4]); o[5] = fmaf(d, b.y, o[5]);
-            o[6] = fmaf(d, b.z, o[6]); o[7] = fmaf(d, b.w, o[7]);
-          }
-          st8<OB>(dx, t, D, c, o);
         }
       }
 #pragma unroll
@@ -332,30 +400,56 @@ __global__ __launch_bounds__(kGbThreads) void gate_bwd_main_kernel(
       }
     }
   }
-  // dbias partial of the chunk: thread i < E sums its expert over the tokens
-  for (int i = threadIdx.x; i < E; i += kGbThreads) {
+  for (int i = threadIdx.x; i < E; i += blockDim.x) {
     float s = 0.0f;
-    for (int64_t t = t0; t < t1; ++t) s += dl[t * E + i];
+    for (int t = 0; t < nt; ++t) s += sdl[t][i];
     part_b[static_cast<int64_t>(blockIdx.x) * E + i] = s;
   }
 }
 
-// Fixed-order sum of the chunk partials: dW_g [E][D] and dbias [E].
+// Fixed-order sum of the chunk partials into dW_g [E][D] (entries
+// i < E*D) and dbias [E] (entries E*D + e).  A workgroup takes 32 entries;
+// its 8 groups of 32 threads each sum one eighth of the chunks in chunk
+// order (loads in batches of 8), and the 8 sums are added in group order:
+// a fixed association, the same bits on every run.
 __global__ __launch_bounds__(256) void gate_bwd_reduce_kernel(
     const float* __restrict__ part_w, const float* __restrict__ part_b,
     int nchunks, int E, int D, float* __restrict__ dw_gate,
     float* __restrict__ dbias) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  __shared__ float ps[8][32];
   const int64_t ED = static_cast<int64_t>(E) * D;
-  if (i < ED) {
-    float s = 0.0f;
-    for (int c = 0; c < nchunks; ++c) s += part_w[c * ED + i];
-    dw_gate[i] = s;
+  const int64_t nout = ED + (dbias != nullptr ? E : 0);
+  const int io = threadIdx.x & 31, seg = threadIdx.x >> 5;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 32 + io;
+  const int per = (nchunks + 7) / 8;
+  const int c_begin = seg * per, c_end = min(nchunks, c_begin + per);
+  float sum = 0.0f;
+  if (i < nout) {
+    for (int c0 = c_begin; c0 < c_end; c0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int c = c0 + b;
+        v[b] = 0.0f;
+        if (c < c_end)
+          v[b] = i < ED ? part_w[static_cast<int64_t>(c) * ED + i]
+                        : part_b[static_cast<int64_t>(c) * E + (i - ED)];
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (c0 + b < c_end) sum += v[b];
+    }
   }
-  if (i < E && dbias != nullptr) {
-    float s = 0.0f;
-    for (int c = 0; c < nchunks; ++c) s += part_b[static_cast<int64_t>(c) * E + i];
-    dbias[i] = s;
+  ps[seg][io] = sum;
+  __syncthreads();
+  if (seg == 0 && i < nout) {
+    float t = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) t += ps[g][io];
+    if (i < ED)
+      dw_gate[i] = t;
+    else
+      dbias[i - ED] = t;
   }
 }
 
@@ -457,29 +551,37 @@ hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
                        alpha, dloss, global ? 1 : 0, dl);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid(static_cast<unsigned>(chunks));
-    if (x_bf16 && dx_bf16)
-      hipLaunchKernelGGL((gate_bwd_main_kernel<true, true>), grid, dim3(kGbThreads),
-                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
-                         dx_shared, dx, part_w, part_b);
-    else if (x_bf16)
-      hipLaunchKernelGGL((gate_bwd_main_kernel<true, false>), grid, dim3(kGbThreads),
-                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
-                         dx_shared, dx, part_w, part_b);
-    else if (dx_bf16)
-      hipLaunchKernelGGL((gate_bwd_main_kernel<false, true>), grid, dim3(kGbThreads),
-                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
-                         dx_shared, dx, part_w, part_b);
+    // dW_g / dbias partials: threads = the feature chunks rounded up to
+    // whole waves, at most 256
+    const int nch = D / 8;
+    const int wthreads = min(256, (nch + 63) / 64 * 64);
+    if (x_bf16)
+      hipLaunchKernelGGL(gate_bwd_wgrad_kernel<true>,
+                         dim3(static_cast<unsigned>(chunks)), dim3(wthreads), 0,
+                         stream, x, dl, N, D, E, part_w, part_b);
     else
-      hipLaunchKernelGGL((gate_bwd_main_kernel<false, false>), grid, dim3(kGbThreads),
-                         0, stream, x, wg, dl, N, D, E, Kmax, dx_rows, slot_row,
-                         dx_shared, dx, part_w, part_b);
+      hipLaunchKernelGGL(gate_bwd_wgrad_kernel<false>,
+                         dim3(static_cast<unsigned>(chunks)), dim3(wthreads), 0,
+                         stream, x, dl, N, D, E, part_w, part_b);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (dx != nullptr) {
+      const dim3 g2(static_cast<unsigned>(ceil_div(N * nch, 256)));
+      if (dx_bf16)
+        hipLaunchKernelGGL(gate_bwd_dx_kernel<true>, g2, dim3(256), 0, stream,
+                           wg, dl, N, D, E, Kmax, dx_rows, slot_row, dx_shared,
+                           dx);
+      else
+        hipLaunchKernelGGL(gate_bwd_dx_kernel<false>, g2, dim3(256), 0, stream,
+                           wg, dl, N, D, E, Kmax, dx_rows, slot_row, dx_shared,
+                           dx);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
-  const int64_t ED = static_cast<int64_t>(E) * D;
+  const int64_t nout = static_cast<int64_t>(E) * D + (dbias != nullptr ? E : 0);
   hipLaunchKernelGGL(gate_bwd_reduce_kernel,
-                     dim3(static_cast<unsigned>(ceil_div(ED, 256))), dim3(256),
+                     dim3(static_cast<unsigned>(ceil_div(nout, 32))), dim3(256),
                      0, stream, part_w, part_b, static_cast<int>(chunks), E, D,
                      dw_gate, dbias);
   return hipGetLastError();

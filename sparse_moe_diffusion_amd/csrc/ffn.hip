@@ -44,8 +44,9 @@ namespace {
 
 // kEpiCombine: the stage-2 store of the shared experts fused with the
 // weighted combine of the routed outputs (one group holding every token).
-// kEpiGeluGrad: the product times GELU'(u) at the same position, u read
-// from GemmParams::aux (backward of the first expert matrix).
+// kEpiGeluGrad: the product (rounded to bf16 in the staged tile) times
+// GELU'(u) at the same position, u read from GemmParams::aux, rounded again
+// (backward of the first expert matrix).
 enum Epi { kEpiGelu = 0, kEpiStore = 1, kEpiCombine = 2, kEpiGeluGrad = 3 };
 
 // Most slots per token the fused combine takes (top-K routing, K <= 4).
@@ -308,10 +309,9 @@ __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g,
     v[2] = gelu_tanh(v[2]); v[3] = gelu_tanh(v[3]);
   }
   if constexpr (EPI == kEpiGeluGrad) {
-    const uint2 u = *reinterpret_cast<const uint2*>(
-        static_cast<const uint16_t*>(p.aux) + row * p.Nd + f);
-    v[0] *= gelu_tanh_grad(bf16_lo(u.x)); v[1] *= gelu_tanh_grad(bf16_hi(u.x));
-    v[2] *= gelu_tanh_grad(bf16_lo(u.y)); v[3] *= gelu_tanh_grad(bf16_hi(u.y));
+    // bf16 output only: the factor gelu'(u) is applied in the copy-out
+    // loop, where u is read row-contiguous.
+    (void)row;
   }
   return v;
 }
@@ -387,6 +387,7 @@ __device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
           bool PF, bool KG = false>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(EPI != kEpiGeluGrad || OUT_BF16, "gelu'(u) is applied on bf16 output");
   static_assert(!KG || (!OUT_BF16 && !PF && EPI == kEpiStore),
                 "the K-grouped form writes fp32 without prefetch");
   constexpr int kWaves = WT * WF;
@@ -824,6 +825,48 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
                       &lds[r * kOutPitch + (f - loc.n0)]), sh);
 #pragma unroll
           for (int j = 0; j < 8; ++j) a8[j] += sh[j];
+          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+          u32x4 o;
+          o[0] = pack_bf16x2(a8[0], a8[1]);
+          o[1] = pack_bf16x2(a8[2], a8[3]);
+          o[2] = pack_bf16x2(a8[4], a8[5]);
+          o[3] = pack_bf16x2(a8[6], a8[7]);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(c + row * p.Nd + f));
+        }
+      }
+    } else if constexpr (EPI == kEpiGeluGrad) {
+      // du = staged product * gelu'(u): u in batches of kB row-contiguous
+      // 16-byte chunks, all loaded before the first multiply.
+      constexpr int kIters = (BM * kChunks + 64 * kWaves - 1) / (64 * kWaves);
+      constexpr int kB = 8;
+      const uint16_t* const ua = static_cast<const uint16_t*>(p.aux);
+      for (int i0 = 0; i0 < kIters; i0 += kB) {
+        uint4 uv[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = tid + (i0 + b) * 64 * kWaves;
+          const int r = idx / kChunks;
+          const int f = loc.n0 + (idx - r * kChunks) * 8;
+          uv[b] = make_uint4(0, 0, 0, 0);
+          if (i0 + b < kIters && idx < BM * kChunks &&
+              loc.row0 + r < loc.row_end && f < p.Nd)
+            uv[b] = *reinterpret_cast<const uint4*>(ua + (loc.row0 + r) * p.Nd + f);
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          const int idx = tid + (i0 + b) * 64 * kWaves;
+          const int r = idx / kChunks;
+          const int f = loc.n0 + (idx - r * kChunks) * 8;
+          const int64_t row = loc.row0 + r;
+          if (i0 + b >= kIters || idx >= BM * kChunks || row >= loc.row_end ||
+              f >= p.Nd)
+            continue;
+          float a8[8], u8[8];
+          unpack8(*reinterpret_cast<const uint4*>(
+                      &lds[r * kOutPitch + (f - loc.n0)]), a8);
+          unpack8(uv[b], u8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[j] *= gelu_tanh_grad(u8[j]);
           typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
           u32x4 o;
           o[0] = pack_bf16x2(a8[0], a8[1]);
