@@ -110,6 +110,10 @@ def kernel_work(cfg, gather: bool):
         "combine": ("bytes", A * D * eb + (N * D * eb if n_s else 0) +
                     N * D * eb + N * Kmax * 8),
         "balance": ("bytes", N * E * 4 + N * Kmax * 4),
+        # the gate with the balance statistic reduced inside it: the gate's
+        # bytes plus the per-image counts and probability sums
+        "gate_balance": ("bytes", N * D * eb + E * D * 4 + N * E * 4 +
+                         N * Kmax * 8 + cfg.B * E * 8),
     }
     return w
 

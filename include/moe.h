@@ -227,6 +227,7 @@ moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
  *   prob_sums[b][i] = sum_t P(t,i)          (fp32 out, [B][E])
  * MOE_BAL_PER_SEQUENCE: loss = mean over b of L_b.
  * MOE_BAL_GLOBAL: loss = L over one pool of B*T tokens.
+ * B = 0 (no tokens): loss = 0 in both modes.
  * Sums use a fixed reduction order: repeated calls give identical bits.
  *
  *   probs [B*T][E] fp32;  topk_idx [B*T][Kmax] int32 (-1 = empty);
@@ -239,6 +240,41 @@ moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                              int32_t K, float alpha, moe_balance_mode mode,
                              int32_t* counts, float* prob_sums, float* loss,
                              hipStream_t stream);
+
+/* Bytes of device workspace moe_gate_topk_balance needs. */
+size_t moe_gate_balance_workspace_size(int32_t B, int32_t T, int32_t E);
+
+/*
+ * Top-K gate and the balance statistic in one call ("DiT-MoE" hub page,
+ * section 1: the gate returns the selected experts, their weights and the
+ * auxiliary loss; "Scaling Diffusion Transformers to 16 Billion
+ * Parameters", MoE-DiT, eq. L_balance).  Computes exactly what
+ * moe_gate_topk (MOE_ROUTE_TOPK) followed by moe_balance_stats (Kmax = K)
+ * compute, for N = B*T tokens, image b owning tokens [bT, (b+1)T).
+ *
+ * When x is bf16, T is a multiple of 16 and the gate weights fit the
+ * streaming gate kernel (E <= 16 and 3*ceil(D/32)*4*(8 or 16)*16 bytes
+ * <= 144 KiB), the gate kernel also reduces each 16-token group to partial
+ * sums in the workspace and one small kernel finishes counts, prob_sums and
+ * the loss; probs, topk_idx, topk_w and counts are then bit for bit those of
+ * the separate calls, and prob_sums and loss differ from them only by the
+ * order of the fp32 additions (16 tokens in order, then the groups in
+ * order).  Otherwise the separate kernels run.  Either way the result is
+ * deterministic.
+ *
+ *   arguments as moe_gate_topk and moe_balance_stats;
+ *   workspace  device scratch of at least moe_gate_balance_workspace_size()
+ *              bytes (contents need no initialisation)
+ * Errors: as moe_gate_topk and moe_balance_stats; WORKSPACE_TOO_SMALL.
+ */
+moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype,
+                                 const float* w_gate, const float* logit_bias,
+                                 int32_t B, int32_t T, int32_t D, int32_t E,
+                                 int32_t K, float alpha, moe_balance_mode mode,
+                                 float* probs, int32_t* topk_idx, float* topk_w,
+                                 int32_t* counts, float* prob_sums, float* loss,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Stage 2 of the shared experts fused with the weighted combine ("Scaling

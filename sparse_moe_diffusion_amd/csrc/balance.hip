@@ -12,6 +12,9 @@
 //    bits.
 //  * balance_loss_kernel: one workgroup turns counts and prob_sums into the
 //    loss, summing in a fixed order (per image, then over images).
+//  * balance_partials_kernel: when the gate kernel has already reduced each
+//    16-token group (partials [N/16][E]), one workgroup adds each image's
+//    T/16 partials in group order and then computes the loss as above.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -70,16 +73,33 @@ __global__ __launch_bounds__(kSeqThreads) void balance_seq_kernel(
   }
 }
 
-__global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
-    const int32_t* __restrict__ counts, const float* __restrict__ psum, int B,
-    int T, int E, int K, float alpha, int global, float* __restrict__ loss) {
+// part[0] = sum of part[0 .. kBalThreads), by a fixed pairwise tree (the
+// same association every call).  Every thread calls it; tid >= kBalThreads
+// only passes the barriers.
+__device__ __forceinline__ void tree_sum(float* part, int tid) {
+  for (int h = kBalThreads / 2; h > 0; h /= 2) {
+    if (tid < h) part[tid] += part[tid + h];
+    __syncthreads();
+  }
+}
+
+// The loss from counts and prob_sums.  Every thread of the workgroup calls
+// it (it holds barriers); threads kBalThreads and up only pass them.
+__device__ void balance_loss_body(const int32_t* __restrict__ counts,
+                                  const float* __restrict__ psum, int B, int T,
+                                  int E, int K, float alpha, int global,
+                                  float* __restrict__ loss) {
   __shared__ float part[kBalThreads];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x < kBalThreads ? threadIdx.x : kBalThreads;
+  if (B == 0) {   // no tokens: no load (uniform, so no thread skips a barrier)
+    if (tid == 0) loss[0] = 0.0f;
+    return;
+  }
   if (!global) {
     // L_b = alpha * sum_i (E/(K T)) c[b][i] * (S[b][i] / T); loss = mean_b.
     const float f = static_cast<float>(E) / (static_cast<float>(K) * T);
     float acc = 0.0f;
-    for (int b = tid; b < B; b += kBalThreads) {
+    for (int b = tid; tid < kBalThreads && b < B; b += kBalThreads) {
       float lb = 0.0f;
       for (int i = 0; i < E; ++i) {
         const int64_t o = static_cast<int64_t>(b) * E + i;
@@ -87,13 +107,10 @@ __global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
       }
       acc += alpha * lb;
     }
-    part[tid] = acc;
+    if (tid < kBalThreads) part[tid] = acc;
     __syncthreads();
-    if (tid == 0) {
-      float s = 0.0f;
-      for (int j = 0; j < kBalThreads; ++j) s += part[j];
-      loss[0] = (B > 0) ? s / static_cast<float>(B) : 0.0f;
-    }
+    tree_sum(part, tid);
+    if (tid == 0) loss[0] = part[0] / static_cast<float>(B);
   } else {
     // One pool of B*T tokens.
     const float Tg = static_cast<float>(B) * T;
@@ -108,17 +125,103 @@ __global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
       }
       term = (f * static_cast<float>(c)) * (s / Tg);
     }
-    part[tid] = term;
+    if (tid < kBalThreads) part[tid] = term;
     __syncthreads();
-    if (tid == 0) {
-      float s = 0.0f;
-      for (int j = 0; j < E; ++j) s += part[j];
-      loss[0] = alpha * s;
-    }
+    tree_sum(part, tid);
+    if (tid == 0) loss[0] = alpha * part[0];
   }
 }
 
+__global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
+    const int32_t* __restrict__ counts, const float* __restrict__ psum, int B,
+    int T, int E, int K, float alpha, int global, float* __restrict__ loss) {
+  balance_loss_body(counts, psum, B, T, E, K, alpha, global, loss);
+}
+
+// Partials of 16-token groups -> counts and prob_sums per image, then the
+// loss.  With B*E outputs of T/16 groups each, R = 1024 / (B*E) threads
+// (a power of two, at most 16) share an output: thread j of output (b, e)
+// adds groups j, j + R, ... of image b in order, and the R sums are then
+// added in j order.  Partial rows are E apart, so the threads of one j read
+// neighbouring words.  Fixed association throughout: same bits every call.
+__global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
+    int B, int T, int E, int K, float alpha, int global,
+    int32_t* __restrict__ counts, float* __restrict__ psum,
+    float* __restrict__ loss) {
+  __shared__ float sp[kSeqThreads];
+  __shared__ int32_t sc[kSeqThreads];
+  const int G = T / 16;
+  const int64_t outs = static_cast<int64_t>(B) * E;
+  int R = 1;
+  while (R < 16 && outs * (2 * R) <= kSeqThreads) R *= 2;
+  for (int64_t o0 = 0; o0 < outs; o0 += kSeqThreads / R) {
+    const int64_t o = o0 + threadIdx.x / R;
+    const int j = threadIdx.x % R;
+    float s = 0.0f;
+    int32_t c = 0;
+    if (o < outs) {
+      const int64_t b = o / E;
+      const int64_t base = b * G * E + (o - b * E);
+      int g = j;
+      for (; g + 7 * R < G; g += 8 * R) {
+        float q[8];
+        int32_t n[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          q[u] = part_p[base + static_cast<int64_t>(g + u * R) * E];
+          n[u] = part_c[base + static_cast<int64_t>(g + u * R) * E];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          s += q[u];
+          c += n[u];
+        }
+      }
+      for (; g < G; g += R) {
+        s += part_p[base + static_cast<int64_t>(g) * E];
+        c += part_c[base + static_cast<int64_t>(g) * E];
+      }
+    }
+    sp[threadIdx.x] = s;
+    sc[threadIdx.x] = c;
+    __syncthreads();
+    if (j == 0 && o < outs) {
+      for (int i = 1; i < R; ++i) {
+        s += sp[threadIdx.x + i];
+        c += sc[threadIdx.x + i];
+      }
+      psum[o] = s;
+      counts[o] = c;
+    }
+    __syncthreads();
+  }
+  // The loss reads what this workgroup just wrote: a workgroup barrier
+  // orders those global writes before the reads (the loop ended on one).
+  balance_loss_body(counts, psum, B, T, E, K, alpha, global, loss);
+}
+
 }  // namespace
+
+size_t balance_partials_bytes(int64_t N, int E) {
+  const size_t words = static_cast<size_t>((N + 15) / 16) * E;
+  const size_t half = (words * 4 + 255) / 256 * 256;
+  return 2 * half;
+}
+
+hipError_t launch_balance_from_partials(const void* partials, int B, int T,
+                                        int E, int K, float alpha, bool global,
+                                        int32_t* counts, float* psum,
+                                        float* loss, hipStream_t stream) {
+  const int64_t N = static_cast<int64_t>(B) * T;
+  const float* part_p = static_cast<const float*>(partials);
+  const int32_t* part_c = reinterpret_cast<const int32_t*>(
+      static_cast<const char*>(partials) + balance_partials_bytes(N, E) / 2);
+  hipLaunchKernelGGL(balance_partials_kernel, dim3(1), dim3(kSeqThreads), 0,
+                     stream, part_p, part_c, B, T, E, K, alpha, global ? 1 : 0,
+                     counts, psum, loss);
+  return hipGetLastError();
+}
 
 hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int E, int Kmax, int K, float alpha, bool global,

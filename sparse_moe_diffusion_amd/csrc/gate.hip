@@ -38,8 +38,10 @@ __device__ __forceinline__ float sel_key(float p) { return p == p ? p : -1.0f; }
 
 // Softmax over the E logits of one token (one lane) and, for top-K routing,
 // the K experts first in (probability descending, index ascending) order.
+// p is left holding the probabilities; the result has bit e set when expert
+// e was selected (0 without top-K routing).
 template <int EP>
-__device__ __forceinline__ void softmax_topk(float (&p)[EP], int64_t t, int E,
+__device__ __forceinline__ uint64_t softmax_topk(float (&p)[EP], int64_t t, int E,
                                              int K, bool topk,
                                              float* __restrict__ probs,
                                              int32_t* __restrict__ idx,
@@ -63,7 +65,7 @@ __device__ __forceinline__ void softmax_topk(float (&p)[EP], int64_t t, int E,
       probs[t * E + e] = p[e];
     }
   }
-  if (!topk) return;
+  if (!topk) return 0;
   uint64_t taken = 0;
   for (int k = 0; k < K; ++k) {
     int best = -1;
@@ -83,6 +85,7 @@ __device__ __forceinline__ void softmax_topk(float (&p)[EP], int64_t t, int E,
     idx[t * K + k] = best;
     wout[t * K + k] = bp;
   }
+  return taken;
 }
 
 // fp32 tokens: VALU dot products with fp64 accumulation.  One workgroup =
@@ -287,6 +290,12 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_mfma_kernel(
 // registers: no cross-wave sum.  Lane l's logits are token (l % 16),
 // experts 4 (l / 16) + 0..3; the wave passes them through LDS to lanes
 // 0..15, one token each, for the softmax and selection.
+//
+// With bal_p != nullptr (top-K routing, 16-token groups that never straddle
+// two images) each wave also writes the balance statistic's partial sums of
+// its 16 tokens: bal_p[g][e] = sum of P(t,e) over the group's tokens in
+// token order, bal_c[g][e] = how many of them selected e, for group
+// g = first token / 16.
 constexpr int kStreamWaves = 8;            // 16 tokens per wave
 constexpr int kRing = 12;                  // slices in flight per wave
 constexpr int kStreamLdsMax = 144 * 1024;  // split weights, bytes
@@ -300,10 +309,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gate_stream_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ wg,
     const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
     float* __restrict__ probs, int32_t* __restrict__ idx,
-    float* __restrict__ wout) {
+    float* __restrict__ wout, float* __restrict__ bal_p,
+    int32_t* __restrict__ bal_c) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   extern __shared__ u32x4 wsplit[];
   __shared__ float lg[kStreamWaves][16][17];
+  __shared__ uint32_t taken[kStreamWaves][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -422,11 +433,32 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gate_stream_kernel(
   }
   __syncthreads();
   const int64_t t = t0 + lane;
-  if (lane >= 16 || t >= N) return;
-  float p[16];
+  if (lane < 16 && t < N) {
+    float p[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) p[e] = lg[wave][lane][e];
-  softmax_topk<16>(p, t, E, K, topk != 0, probs, idx, wout);
+    for (int e = 0; e < 16; ++e) p[e] = lg[wave][lane][e];
+    const uint64_t sel = softmax_topk<16>(p, t, E, K, topk != 0, probs, idx, wout);
+    if (bal_p != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lg[wave][lane][e] = p[e];
+      taken[wave][lane] = static_cast<uint32_t>(sel);
+    }
+  }
+  if (bal_p == nullptr) return;
+  __syncthreads();
+  // Whole groups only: the host takes this path when N is a multiple of 16.
+  if (lane < E && t0 < N) {
+    float s = 0.0f;
+    int32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s += lg[wave][r][lane];
+      c += static_cast<int32_t>((taken[wave][r] >> lane) & 1u);
+    }
+    const int64_t o = (t0 / 16) * E + lane;
+    bal_p[o] = s;
+    bal_c[o] = c;
+  }
 }
 
 // Split weights of E experts over D features fit the streaming kernel's LDS.
@@ -438,6 +470,7 @@ template <int EC>
 hipError_t launch_gate_stream(const void* x, const float* wg, const float* bias,
                               int64_t N, int D, int E, int K, bool topk,
                               float* probs, int32_t* idx, float* w,
+                              float* bal_p, int32_t* bal_c,
                               hipStream_t stream) {
   static std::atomic<bool> lds_opt_in{false};
   if (!lds_opt_in.load(std::memory_order_acquire)) {
@@ -452,7 +485,7 @@ hipError_t launch_gate_stream(const void* x, const float* wg, const float* bias,
                      dim3(64 * kStreamWaves),
                      static_cast<unsigned>(stream_lds_bytes(D, EC)), stream,
                      static_cast<const uint16_t*>(x), wg, bias, N, D, E, K,
-                     topk ? 1 : 0, probs, idx, w);
+                     topk ? 1 : 0, probs, idx, w, bal_p, bal_c);
   return hipGetLastError();
 }
 
@@ -600,9 +633,11 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
   if (N == 0) return hipSuccess;
   if (x_bf16 && gate_stream_fits(D, E))
     return E <= 8 ? launch_gate_stream<8>(x, w_gate, bias, N, D, E, K, topk,
-                                          probs, idx, w, stream)
+                                          probs, idx, w, nullptr, nullptr,
+                                          stream)
                   : launch_gate_stream<16>(x, w_gate, bias, N, D, E, K, topk,
-                                           probs, idx, w, stream);
+                                           probs, idx, w, nullptr, nullptr,
+                                           stream);
   if (E <= 16)
     return launch_gate_eb<1>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
                              idx, w, stream);
@@ -611,6 +646,21 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
                              idx, w, stream);
   return launch_gate_eb<4>(x, x_bf16, w_gate, bias, N, D, E, K, topk, probs,
                            idx, w, stream);
+}
+
+bool gate_balance_fuses(bool x_bf16, int64_t N, int T, int D, int E) {
+  return x_bf16 && N > 0 && T % 16 == 0 && gate_stream_fits(D, E);
+}
+
+hipError_t launch_gate_balance_partials(const void* x, const float* w_gate,
+                                        const float* bias, int64_t N, int D,
+                                        int E, int K, float* probs,
+                                        int32_t* idx, float* w, float* bal_p,
+                                        int32_t* bal_c, hipStream_t stream) {
+  return E <= 8 ? launch_gate_stream<8>(x, w_gate, bias, N, D, E, K, true,
+                                        probs, idx, w, bal_p, bal_c, stream)
+                : launch_gate_stream<16>(x, w_gate, bias, N, D, E, K, true,
+                                         probs, idx, w, bal_p, bal_c, stream);
 }
 
 size_t race_workspace_bytes() { return 256; }

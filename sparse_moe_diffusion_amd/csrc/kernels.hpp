@@ -13,6 +13,15 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
                        const float* bias, int64_t N, int D, int E, int K,
                        bool topk, float* probs, int32_t* idx, float* w,
                        hipStream_t stream);
+// Top-K gate that also writes the balance statistic's per-16-token partial
+// sums (bal_p [N/16][E] fp32, bal_c [N/16][E] int32); fuses when x is bf16,
+// the streaming gate holds the weights and T is a multiple of 16.
+bool gate_balance_fuses(bool x_bf16, int64_t N, int T, int D, int E);
+hipError_t launch_gate_balance_partials(const void* x, const float* w_gate,
+                                        const float* bias, int64_t N, int D,
+                                        int E, int K, float* probs,
+                                        int32_t* idx, float* w, float* bal_p,
+                                        int32_t* bal_c, hipStream_t stream);
 size_t race_workspace_bytes();
 hipError_t launch_race(const float* probs, int64_t N, int E, int K,
                        int32_t* idx, float* w, void* workspace,
@@ -60,6 +69,12 @@ hipError_t launch_combine(const void* y_rows, bool y_bf16,
                           void* y, bool out_bf16, hipStream_t stream);
 
 // balance.hip
+// Bytes of the partial-sum buffer for N tokens (fp32 half, then int32 half).
+size_t balance_partials_bytes(int64_t N, int E);
+hipError_t launch_balance_from_partials(const void* partials, int B, int T,
+                                        int E, int K, float alpha, bool global,
+                                        int32_t* counts, float* psum,
+                                        float* loss, hipStream_t stream);
 hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int E, int Kmax, int K, float alpha, bool global,
                           int32_t* counts, float* psum, float* loss,

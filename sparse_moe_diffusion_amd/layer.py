@@ -100,6 +100,11 @@ class LayerBuffers:
         else:
             self.shared_offsets = self.h_shared = self.y_shared = None
         self.y = torch.empty(N, D, dtype=dt, device=dev)
+        self.gate_bal_ws = None
+        if route == ROUTES["topk"]:
+            bws = ops.gate_balance_workspace_size(cfg.B, cfg.T, E)
+            self.gate_bal_ws = torch.empty(max(bws, 1), dtype=torch.uint8,
+                                           device=dev)
         self.bal_counts = torch.empty(cfg.B, E, dtype=i32, device=dev)
         self.bal_psum = torch.empty(cfg.B, E, dtype=f32, device=dev)
         self.loss = torch.empty(1, dtype=f32, device=dev)
@@ -108,6 +113,20 @@ class LayerBuffers:
 def gate(cfg, x, wts: LayerWeights, buf: LayerBuffers):
     ops.moe_gate_topk(x, wts.w_gate, wts.bias, cfg.K, ROUTES[cfg.route],
                       buf.probs, buf.topk_idx, buf.topk_w, buf.gate_ws)
+
+
+def fuses_balance(cfg) -> bool:
+    """Top-K layers compute the balance statistic in the gate's call (its
+    kernel reduces each 16-token group where the shape allows)."""
+    return cfg.route == "topk"
+
+
+def gate_balance(cfg, x, wts: LayerWeights, buf: LayerBuffers,
+                 mode: str = "sequence"):
+    ops.moe_gate_topk_balance(x, wts.w_gate, wts.bias, cfg.B, cfg.T, cfg.K,
+                              cfg.alpha, BALANCE[mode], buf.probs,
+                              buf.topk_idx, buf.topk_w, buf.bal_counts,
+                              buf.bal_psum, buf.loss, buf.gate_bal_ws)
 
 
 def permute(cfg, x, buf: LayerBuffers):
@@ -173,27 +192,41 @@ STEPS = (("gate", lambda c, x, w, b: gate(c, x, w, b)),
          ("combine", lambda c, x, w, b: combine(c, b)),
          ("balance", lambda c, x, w, b: balance(c, b)))
 
-# The same with the shared experts' stage 2 and the combine fused (what
-# forward() runs when fuses_combine(cfg, buf)): bit for bit the same y.
-FUSED_STEPS = tuple(
-    s for s in STEPS if s[0] not in ("shared_down", "combine")
-)[:-1] + (("shared_down_combine",
-           lambda c, x, w, b: shared_down_combine(c, w, b)),
-          STEPS[-1])
+# The fused calls forward() makes instead: the gate with the balance
+# statistic (top-K routing), and the shared experts' stage 2 with the combine
+# (when fuses_combine(cfg, buf)): y bit for bit the same either way.
+GATE_BALANCE_STEP = ("gate_balance",
+                     lambda c, x, w, b: gate_balance(c, x, w, b))
+DOWN_COMBINE_STEP = ("shared_down_combine",
+                     lambda c, x, w, b: shared_down_combine(c, w, b))
 
 
 def steps(cfg, buf: LayerBuffers):
     """The calls forward() makes for this layer, in order."""
-    if fuses_combine(cfg, buf):
-        return FUSED_STEPS
-    return tuple(s for s in STEPS
-                 if not (cfg.n_s == 0 and s[0].startswith("shared")))
+    out = []
+    for s in STEPS:
+        name = s[0]
+        if cfg.n_s == 0 and name.startswith("shared"):
+            continue
+        if fuses_balance(cfg) and name == "balance":
+            continue
+        if fuses_combine(cfg, buf) and name == "combine":
+            continue
+        if fuses_balance(cfg) and name == "gate":
+            s = GATE_BALANCE_STEP
+        elif fuses_combine(cfg, buf) and name == "shared_down":
+            s = DOWN_COMBINE_STEP
+        out.append(s)
+    return tuple(out)
 
 
 def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
             balance_mode: str = "sequence") -> LayerBuffers:
     """One pass of the whole layer; results land in ``buf``."""
-    gate(cfg, x, wts, buf)
+    if fuses_balance(cfg):
+        gate_balance(cfg, x, wts, buf, balance_mode)
+    else:
+        gate(cfg, x, wts, buf)
     permute(cfg, x, buf)
     routed_ffn(cfg, x, wts, buf, UP)
     shared_ffn(cfg, x, wts, buf, UP)
@@ -203,7 +236,8 @@ def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
     else:
         shared_ffn(cfg, x, wts, buf, DOWN)
         combine(cfg, buf)
-    balance(cfg, buf, balance_mode)
+    if not fuses_balance(cfg):
+        balance(cfg, buf, balance_mode)
     return buf
 
 

@@ -96,6 +96,24 @@ def moe_balance_stats(probs, topk_idx, B: int, T: int, K: int, alpha: float,
               _stream())
 
 
+def gate_balance_workspace_size(B: int, T: int, E: int) -> int:
+    return _lib.load().moe_gate_balance_workspace_size(B, T, E)
+
+
+def moe_gate_topk_balance(x, w_gate, logit_bias, B: int, T: int, K: int,
+                          alpha: float, mode: int, probs, topk_idx, topk_w,
+                          counts, prob_sums, loss, workspace):
+    N, D = x.shape
+    if N != B * T:
+        raise ValueError(f"x has {N} rows, expected B*T = {B * T}")
+    E = w_gate.shape[0]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _lib.call("moe_gate_topk_balance", _ptr(x), dtype_code(x.dtype),
+              _ptr(w_gate), _ptr(logit_bias), B, T, D, E, K, alpha, mode,
+              _ptr(probs), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+              _ptr(prob_sums), _ptr(loss), _ptr(workspace), ws, _stream())
+
+
 def moe_routing_histogram(topk_idx, B: int, T: int, E: int, pos_counts,
                           image_tag=None, tag_counts=None):
     """Add one batch's expert-selection counts by position (and by image

@@ -150,6 +150,44 @@ def test_combine_and_balance_reject():
         assert _lib.call_status("moe_balance_stats", *a.values()) == st
 
 
+def _gate_balance(**kw):
+    a = dict(x=FAKE, dt=_lib.MOE_BF16, wg=FAKE, bias=None, B=4, T=16, D=128,
+             E=8, K=2, alpha=ctypes.c_float(0.01),
+             mode=_lib.MOE_BAL_PER_SEQUENCE, probs=FAKE, idx=FAKE, w=FAKE,
+             counts=FAKE, ps=FAKE, loss=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_gate_topk_balance", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(loss=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(counts=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=9), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(mode=2), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=65, K=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=5), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(wsb=0), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_gate_balance_rejects(kw, status):
+    ensure_built()
+    assert _gate_balance(**kw) == status
+    assert _lib.last_error()
+
+
+def test_gate_balance_workspace():
+    lib = ensure_built()
+    # 16-token groups x E partials, fp32 and int32 halves
+    assert lib.moe_gate_balance_workspace_size(32, 1024, 8) == 2 * 2048 * 8 * 4
+    assert lib.moe_gate_balance_workspace_size(0, 16, 8) == 0
+    assert lib.moe_gate_balance_workspace_size(3, 100, 8) >= 2 * 19 * 8 * 4
+
+
 def test_binding_raises_on_error():
     ensure_built()
     with pytest.raises(_lib.MoEError, match="MOE_ERR_INVALID_ARGUMENT"):

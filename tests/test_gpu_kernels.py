@@ -336,6 +336,70 @@ def test_balance(B, T, E, K, race, mode):
     assert abs(float(to_np(loss)[0]) - l_o) <= 1e-5 * abs(l_o)
 
 
+@pytest.mark.parametrize("B,T,D,E,K,dtype,mode,bias", [
+    (1, 16, 64, 1, 1, "bf16", "sequence", False),     # one group, E = 1
+    (4, 256, 1152, 8, 2, "bf16", "sequence", True),
+    (3, 112, 384, 16, 2, "bf16", "global", False),    # E = 16 columns
+    (5, 64, 200, 5, 3, "bf16", "sequence", True),     # unused expert columns
+    (3, 100, 256, 8, 2, "bf16", "sequence", False),   # T % 16 != 0: separate
+    (2, 64, 128, 8, 2, "f32", "global", False),       # fp32 x: separate
+    (2, 32, 2048, 16, 2, "bf16", "sequence", False),  # weights exceed LDS: separate
+    (32, 1024, 1152, 8, 2, "bf16", "sequence", False),  # the XL layer
+    (0, 16, 128, 8, 2, "bf16", "sequence", False),    # no tokens
+    (0, 16, 128, 8, 2, "bf16", "global", False),
+])
+def test_gate_balance_matches_separate(B, T, D, E, K, dtype, mode, bias):
+    """moe_gate_topk_balance against moe_gate_topk + moe_balance_stats on the
+    same inputs: routing and counts bit for bit, the probability sums and
+    the loss to fp32 summation-order accuracy; and against the oracle's
+    balance statistic on the routing the GPU chose."""
+    _lib, ops = _ops()
+    rng = np.random.default_rng(B * T + D + E)
+    N = B * T
+    x32 = rng.standard_normal((N, D)).astype(np.float32)
+    x = _bits_tensor(x32, dtype)
+    wg = torch.from_numpy((rng.standard_normal((E, D)) * 0.05).astype(np.float32)).to(DEV)
+    bt = (torch.from_numpy(rng.standard_normal(E).astype(np.float32)).to(DEV)
+          if bias else None)
+    mc = _lib.MOE_BAL_GLOBAL if mode == "global" else _lib.MOE_BAL_PER_SEQUENCE
+
+    def bufs():
+        f32, i32 = torch.float32, torch.int32
+        return (torch.full((N, E), -1.0, dtype=f32, device=DEV),
+                torch.full((N, K), -7, dtype=i32, device=DEV),
+                torch.full((N, K), -1.0, dtype=f32, device=DEV),
+                torch.full((B, E), -7, dtype=i32, device=DEV),
+                torch.full((B, E), -1.0, dtype=f32, device=DEV),
+                torch.full((1,), -1.0, dtype=f32, device=DEV))
+
+    sep = bufs()
+    ops.moe_gate_topk(x, wg, bt, K, _lib.MOE_ROUTE_TOPK, sep[0], sep[1], sep[2],
+                      None)
+    ops.moe_balance_stats(sep[0], sep[1], B, T, K, 0.01, mc, sep[3], sep[4],
+                          sep[5])
+    fus = bufs()
+    ws = torch.empty(max(ops.gate_balance_workspace_size(B, T, E), 1),
+                     dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)
+    for _ in range(2):   # the workspace needs no initialisation
+        ops.moe_gate_topk_balance(x, wg, bt, B, T, K, 0.01, mc, *fus, ws)
+    torch.cuda.synchronize()
+    s, f = [to_np(t) for t in sep], [to_np(t) for t in fus]
+    for i, name in enumerate(("probs", "idx", "w", "counts")):
+        assert np.array_equal(s[i], f[i]), name
+    assert np.allclose(f[4], s[4], rtol=2e-6, atol=1e-6)
+    if B == 0:
+        assert float(f[5][0]) == 0.0 and float(s[5][0]) == 0.0
+        return
+    c_o, p_o, l_o = oracle.balance_stats(f[0].astype(np.float64),
+                                         f[1].astype(np.int64), B, T, K, 0.01,
+                                         mode)
+    assert np.array_equal(f[3], c_o)
+    assert np.allclose(f[4], p_o, rtol=1e-5, atol=1e-5)
+    assert abs(float(f[5][0]) - l_o) <= 1e-5 * abs(l_o)
+    assert abs(float(f[5][0]) - float(s[5][0])) <= 1e-5 * abs(l_o)
+
+
 # ------------------------------------------------------- routing analytics --
 
 def _run_hist(idx, B, T, E, tags, n_tags, calls=1):
