@@ -926,6 +926,17 @@ constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
 // of h leaves HBM once.  Stage 1 (18+ feature tiles) keeps bands of 8.
 constexpr int kUpGM = 8, kDnGM = 1;
 constexpr bool kDnPF = true;
+// Small problems (short sequences, narrow layers): when the large tiles
+// would occupy fewer than 3/4 of the CUs, most of the chip idles.  Those
+// launches take 128 x 128 tiles (2 x 4 waves of 64 tokens x 32 features;
+// about 94 VGPRs and 64 KB of stages), two workgroups per CU.  Small tiles
+// run at about half the large tiles' rate per CU, so they only pay when
+// they bring that many more CUs in.  Measured on the S-sized layer (8192
+// tokens, D = 384): the shared experts' stage 2 with the combine (64 large
+// tiles) 89 -> 53 us, routed stage 2 (158 large tiles) 49 -> 42 us; the
+// 768-wide layer's shared stage 2 (256 large tiles, one full round) takes
+// 159 us with large tiles and 380 us with small ones.
+constexpr int kSmBM = 128, kSmBN = 128, kSmWT = 2, kSmWF = 4, kSmOcc = 2;
 
 // ---------------------------------------------------------- fp32 path ----
 // Plain fp32 FMA tiles (64 x 64 x 16, 4 x 4 outputs per thread) for fp32
@@ -1009,7 +1020,7 @@ int tile_grid(const GemmParams& p, int BM, int BN) {
 // Workgroups of a persistent launch: the CU count of the current device
 // (read once per device), rounded down to a multiple of 8, and no more than
 // the tile bound rounded up to a multiple of 8.
-int persistent_grid(int tiles) {
+int cu_count() {
   static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1021,9 +1032,31 @@ int persistent_grid(int tiles) {
       n = 8;
     cus[dev].store(n, std::memory_order_relaxed);
   }
-  const int cap = n / 8 * 8;
+  return n;
+}
+
+// occ workgroups per CU (the kernel's resources allow that many).
+int persistent_grid(int tiles, int occ = 1) {
+  const int cap = cu_count() / 8 * 8 * occ;
   const int want = (tiles + 7) / 8 * 8;
   return want < cap ? want : cap;
+}
+
+// Launch one forward GEMM stage: large tiles (BM x BN) or, for a problem
+// with fewer large tiles than 3/4 of the CUs, the small-tile form.
+template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM, bool PF>
+void launch_stage(const GemmParams& p, hipStream_t stream) {
+  const int big = tile_grid(p, BM, BN);
+  if (static_cast<int64_t>(big) * 4 < static_cast<int64_t>(cu_count()) * 3) {
+    hipLaunchKernelGGL(
+        (gemm_bf16_kernel<EPI, OUT_BF16, kSmBM, kSmBN, kSmWT, kSmWF, GM, PF>),
+        dim3(persistent_grid(tile_grid(p, kSmBM, kSmBN), kSmOcc)),
+        dim3(64 * kSmWT * kSmWF), 0, stream, p);
+    return;
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF>),
+                     dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream,
+                     p);
 }
 
 }  // namespace
@@ -1159,10 +1192,8 @@ hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
   if (N == 0) return hipSuccess;
   GemmParams p{h,       nullptr, w2,       b2,     y, nullptr, N, 1, D, H,
                y_rows, slot_row, topk_w, Kmax};
-  hipLaunchKernelGGL(
-      (gemm_bf16_kernel<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
-      dim3(persistent_grid(tile_grid(p, kDnBM, kDnBN))), dim3(64 * kDnWT * kDnWF),
-      0, stream, p);
+  launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+      p, stream);
   return hipGetLastError();
 }
 
@@ -1175,24 +1206,18 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
                 a.G, a.D, a.H};
   if (a.bf16) {
     if (up) {
-      hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
-          dim3(persistent_grid(tile_grid(p1, kUpBM, kUpBN))),
-          dim3(64 * kUpWT * kUpWF), 0, stream, p1);
+      launch_stage<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
+          p1, stream);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
     if (down) {
       if (a.y_f32)
-        hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
-            dim3(persistent_grid(tile_grid(p2, kDnBM, kDnBN))),
-            dim3(64 * kDnWT * kDnWF), 0, stream, p2);
+        launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+            p2, stream);
       else
-        hipLaunchKernelGGL(
-            (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
-            dim3(persistent_grid(tile_grid(p2, kDnBM, kDnBN))),
-            dim3(64 * kDnWT * kDnWF), 0, stream, p2);
+        launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+            p2, stream);
       return hipGetLastError();
     }
     return hipSuccess;

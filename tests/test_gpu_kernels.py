@@ -264,6 +264,43 @@ def test_grouped_ffn(sizes, D, H, dtype, gather, bias):
     assert_close(y, ref, dtype, "grouped ffn")
 
 
+@pytest.mark.parametrize("sizes,D,H,y_f32", [
+    # 288 / 216 large tiles in stages 1 / 2: both stages take the large tiles
+    ([3000, 2500, 0, 2700], 1152, 2048, False),
+    ([3000, 2500, 0, 2700], 1152, 2048, True),
+    # stage 1 large (288 tiles), stage 2 small (72 large tiles, under 3/4 of
+    # the CUs)
+    ([9000], 256, 2048, False),
+])
+def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
+    """Shapes on either side of the large/small tile switch, checked on a
+    sample of rows (group starts and ends, random ones)."""
+    rng = np.random.default_rng(sum(sizes) + D + H)
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)])
+    total = int(offsets[-1])
+    q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
+    nsrc = total + 5
+    xsrc = q(rng.standard_normal((nsrc, D)))
+    w1 = q(rng.standard_normal((G, H, D)) * 0.03)
+    w2 = q(rng.standard_normal((G, D, H)) * 0.03)
+    ri = rng.permutation(nsrc)[:total]
+    y = _run_ffn(xsrc, offsets, w1, w2, None, None, "bf16", row_index=ri,
+                 y_f32=y_f32)
+    assert not np.isnan(y).any()
+    picks = set(rng.choice(total, 40, replace=False).tolist())
+    for g in range(G):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        picks |= {r for r in (a, a + 1, b - 2, b - 1) if a <= r < b}
+    for g in range(G):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        rows = np.array(sorted(r for r in picks if a <= r < b), dtype=np.int64)
+        if rows.size == 0:
+            continue
+        ref = oracle.expert_mlp(xsrc[ri[rows]], w1[g], w2[g])
+        assert_close(y[rows], ref, "bf16", f"group {g}")
+
+
 def test_grouped_ffn_bf16_rows_fp32_out():
     rng = np.random.default_rng(3)
     q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
