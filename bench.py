@@ -46,6 +46,11 @@ def parse():
                     help="instead of the layer, time the routing histogram "
                          "(counts by patch position and by image tag) on the "
                          "layer's routing")
+    ap.add_argument("--mlp-fused", action="store_true",
+                    help="instead of the layer, time the one-kernel expert "
+                         "MLP against the two-stage grouped FFN on the "
+                         "configured layer's routed and shared experts at its "
+                         "own token count and at 4x")
     return ap.parse_args()
 
 
@@ -239,6 +244,70 @@ def analytics_bench(args):
                       "bound": "launch latency"}), flush=True)
 
 
+def mlp_fused_bench(args):
+    """moe_grouped_mlp_fused against moe_grouped_ffn (both stages) on the
+    routed experts (E groups of the balanced A/E rows, rows gathered from x)
+    and the shared experts (one group of N rows, hidden n_s*H) of a narrow
+    layer, at its token count and at 4x.  One JSON line, times in us."""
+    import torch
+    import synth
+    from sparse_moe_diffusion_amd import _lib, ops
+
+    _lib.load()
+    cfg = synth.CONFIGS[args.config]
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    rows = []
+    for scale in (1, 4):
+        N = cfg.N * scale
+        for kind, G, per, H, gather in (
+                ("routed", cfg.E, cfg.K * N // cfg.E, cfg.H, True),
+                ("shared", 1, N, cfg.n_s * cfg.H, False)):
+            total, D = G * per, cfg.D
+            x = torch.randn(N, D, device=dev, generator=gen).to(torch.bfloat16)
+            w1 = (torch.randn(G, H, D, device=dev, generator=gen) * 0.05).to(torch.bfloat16)
+            w2 = (torch.randn(G, D, H, device=dev, generator=gen) * 0.05).to(torch.bfloat16)
+            off = torch.arange(G + 1, device=dev, dtype=torch.int64) * per
+            ri = (torch.randint(0, N, (total,), device=dev, generator=gen,
+                                dtype=torch.int32) if gather else None)
+            h = torch.empty(total, H, dtype=torch.bfloat16, device=dev)
+            y2 = torch.empty(total, D, dtype=torch.bfloat16, device=dev)
+            y1 = torch.empty(total, D, dtype=torch.bfloat16, device=dev)
+            two = timed(lambda: ops.moe_grouped_ffn(x, ri, total, off, w1, None,
+                                                    w2, None, h, y2))
+            one = timed(lambda: ops.moe_grouped_mlp_fused(x, ri, total, off, w1,
+                                                          None, w2, None, y1))
+            same = bool(torch.equal(y1, y2))
+            flops = 4.0 * total * D * H
+            rows.append({"experts": kind, "tokens": N, "groups": G,
+                         "rows": total, "D": D, "H": H,
+                         "two_stage_us": round(two, 1),
+                         "fused_us": round(one, 1),
+                         "fused_tflops": round(flops / (one * 1e-6) / 1e12, 1),
+                         "same_bits": same})
+            del x, w1, w2, h, y1, y2
+    print(json.dumps({"metric": "one-kernel expert MLP vs two-stage grouped FFN",
+                      "unit": "us per call", "higher_is_better": False,
+                      "steps": args.steps, "warmup": args.warmup,
+                      "config": {"workload": cfg.name}, "cases": rows}),
+          flush=True)
+
+
 def cpu_baseline(cfg, inp, target_s):
     """The CPU oracle on whole images of the same workload until about
     ``target_s`` seconds of CPU work: tokens/s."""
@@ -279,6 +348,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.mlp_fused:
+        mlp_fused_bench(args)
         return
     import torch
     import synth

@@ -194,6 +194,28 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                            moe_ffn_stages stages, hipStream_t stream);
 
 /*
+ * The experts' MLPs of moe_grouped_ffn in one kernel, for narrow layers
+ * (same page and equations as moe_grouped_ffn): for each group g and row r,
+ *   y_rows[r] = W2[g] gelu_tanh(W1[g] a_r + b1[g]) + b2[g]
+ * with the hidden activation kept on chip (never written to memory).  The
+ * hidden values are rounded to bf16 and the sums run in the same order as
+ * in moe_grouped_ffn, so both calls give identical results.
+ *
+ *   arguments as moe_grouped_ffn, without h_ws and stages
+ * Errors: INVALID_ARGUMENT for null pointers or negative sizes;
+ *   UNSUPPORTED unless dtype is MOE_BF16 (y_dtype MOE_BF16 or MOE_F32),
+ *   D is 128, 256 or 384 and H is a multiple of 64, G <= 128,
+ *   total_rows < 2^31.
+ */
+moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
+                                 moe_dtype dtype, int64_t total_rows,
+                                 const int64_t* group_offsets, int32_t G,
+                                 int32_t D, int32_t H, const void* w1,
+                                 const float* b1, const void* w2,
+                                 const float* b2, void* y_rows,
+                                 moe_dtype y_dtype, hipStream_t stream);
+
+/*
  * Weighted combine ("Scaling Diffusion Transformers to 16 Billion
  * Parameters": eq. MoE(x) with g(x)_i the gate probability; shared experts
  * added with weight 1):

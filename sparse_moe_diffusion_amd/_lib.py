@@ -47,6 +47,8 @@ SIGNATURES = {
                          _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32, _P, _P, _P,
                              _P, _P, _P, _E, _E, _P]),
+    "moe_grouped_mlp_fused": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32, _P,
+                                   _P, _P, _P, _P, _E, _P]),
     "moe_combine": (_E, [_P, _E, _P, _P, _I64, _I32, _I32, _P, _E, _P, _E, _P]),
     "moe_balance_stats": (_E, [_P, _P, _I32, _I32, _I32, _I32, _I32, _F, _E, _P,
                                _P, _P, _P]),

@@ -194,6 +194,38 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
   return from_hip(moe::launch_ffn(a, up, down, stream), fn);
 }
 
+moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
+                                 moe_dtype dtype, int64_t total_rows,
+                                 const int64_t* group_offsets, int32_t G,
+                                 int32_t D, int32_t H, const void* w1,
+                                 const float* b1, const void* w2,
+                                 const float* b2, void* y_rows,
+                                 moe_dtype y_dtype, hipStream_t stream) {
+  const char* fn = "moe_grouped_mlp_fused";
+  if (total_rows < 0 || G < 1 || D < 1 || H < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need total_rows >= 0, G >= 1, D >= 1, H >= 1", fn);
+  const bool rows = total_rows > 0;
+  CHECK_PTR(w1); CHECK_PTR(w2);
+  CHECK_PTR_IF(rows, x_rows); CHECK_PTR_IF(rows, group_offsets);
+  CHECK_PTR_IF(rows, y_rows);
+  if (dtype != MOE_BF16 || (y_dtype != MOE_BF16 && y_dtype != MOE_F32))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: needs bf16 inputs and a bf16 or fp32 output", fn);
+  if (G > kMaxGroups)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d above %d", fn, G, kMaxGroups);
+  if (!moe::mlp_fused_supported(D, H))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: needs D in {128, 256, 384} and H a multiple of 64 "
+                "(D=%d, H=%d)", fn, D, H);
+  if (total_rows >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows must stay below 2^31", fn);
+  moe::FfnArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
+                 w1,     b1,        w2,         b2,            nullptr, y_rows,
+                 true,   y_dtype == MOE_F32};
+  return from_hip(moe::launch_mlp_fused(a, stream), fn);
+}
+
 moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
                        const int32_t* slot_row, const float* topk_w, int64_t N,
                        int32_t D, int32_t Kmax, const void* y_shared,

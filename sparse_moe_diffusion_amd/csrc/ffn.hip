@@ -914,6 +914,217 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }  // tile loop
 }
 
+// ------------------------------------------- single-kernel expert MLP ----
+// Both matrices of an expert MLP in one kernel, for narrow layers (D = 128,
+// 256 or 384): the hidden activation never leaves the CU.  A workgroup of
+// 8 waves owns 128 token rows of one group and walks the hidden width in
+// chunks of 64:
+//   phase A:  hc = gelu(W1[chunk] x^T + b1[chunk])   -> LDS (bf16, 128 x 64)
+//   phase B:  y^T += W2[:, chunk] hc^T               -> registers (fp32)
+// Wave w owns tokens 32 (w % 4) .. +32; in phase A hidden rows 32 (w / 4)
+// .. +32 of the chunk, in phase B output features (w / 4) D/2 .. +D/2.  Its
+// token rows stay in registers as MFMA operands for the whole tile.  The
+// weights of the chunk reach LDS by buffer_load ... lds: W2's while phase A
+// runs, the next chunk's W1 while phase B runs.  LDS rows are 64 k (128
+// bytes) with the 16-byte chunks swizzled as in the GEMMs.  Rounding and
+// summation order are those of the two-stage path (h rounded to bf16 once,
+// y summed over the hidden width in the same order), so both give the same
+// bits.
+constexpr int kMlpBM = 128, kMlpHC = 64, kMlpWaves = 8;
+
+template <int DT>   // D = 128 DT
+__global__ __launch_bounds__(64 * kMlpWaves, 1) void mlp_fused_kernel(
+    GemmParams p, const void* __restrict__ w2, const float* __restrict__ b2,
+    int H, int y_f32) {
+  constexpr int D = 128 * DT;
+  constexpr int KS = D / 16;          // phase-A k steps (16 wide)
+  constexpr int FBY = D / 64;         // phase-B output blocks of 32 per wave
+  constexpr int NT = D / 8;           // 1 KB transfers per weight chunk
+  constexpr int NTW = NT / kMlpWaves; // ... per wave
+  static_assert(NT % kMlpWaves == 0, "whole transfers per wave");
+  constexpr int kW1Bytes = kMlpHC * D * 2;   // [D/64 slices][64 rows][128 B]
+  constexpr int kW2Bytes = D * 128;          // [D rows][128 B]
+  constexpr int kHBytes = kMlpBM * 128;      // [128 tokens][128 B]
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[kW1Bytes + kW2Bytes + kHBytes + kTabInts * 4];
+  int32_t* const tab = reinterpret_cast<int32_t*>(lds + kW1Bytes + kW2Bytes + kHBytes);
+  const uint16_t* const sW1 = reinterpret_cast<const uint16_t*>(lds);
+  const uint16_t* const sW2 = reinterpret_cast<const uint16_t*>(lds + kW1Bytes);
+  uint8_t* const sH = lds + kW1Bytes + kW2Bytes;
+  const uint32_t bW1 = lds_addr(lds), bW2 = bW1 + kW1Bytes;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = wave & 3, fh = wave >> 2;
+  const int khalf = lane >> 5;
+  build_group_table<kMlpBM, D>(p, tab, wave, lane);
+  TileLoc loc;
+  if (!locate_tile_tab<kMlpBM, D, 1>(p, tab, lane,
+                                     xcd_remap(blockIdx.x, gridDim.x), loc))
+    return;
+  const int g = loc.g;
+  const uint16_t* const w1g =
+      static_cast<const uint16_t*>(p.w) + static_cast<int64_t>(g) * H * D;
+  const uint16_t* const w2g =
+      static_cast<const uint16_t*>(w2) + static_cast<int64_t>(g) * D * H;
+
+  // Transfer q of this wave for a weight chunk: rows r0 .. r0 + 7; lane l
+  // fetches chunk (l % 8) ^ swz(row) of row r0 + l / 8 into slot l % 8.
+  // W1 chunk (hidden rows hc0 .. hc0 + 63, all D k): transfer t covers
+  // slice t / 8 (k 64 (t / 8) ..), rows 8 (t % 8) ..; W2 chunk (all D
+  // output rows, hidden k hc0 .. hc0 + 63): transfer t covers rows 8 t ...
+  // Lane-dependent offsets are recomputed from an opaque copy of the lane
+  // index in every chunk (a few VALU operations), instead of being hoisted
+  // into registers that would stay live through the MFMA loops next to the
+  // token fragments and accumulators.
+#define MOE_MLP_ISSUE_W1(HC0)                                                \
+  do {                                                                       \
+    const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(                            \
+        reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(   \
+            w1g + static_cast<int64_t>(HC0) * D))),                          \
+        static_cast<uint32_t>(kW1Bytes));                                    \
+    _Pragma("unroll") for (int q = 0; q < NTW; ++q) {                        \
+      const int t_ = wave + kMlpWaves * q;                                   \
+      const int r_ = (t_ % 8) * 8 + (ol >> 3);                               \
+      const uint32_t o_ = static_cast<uint32_t>(r_) * (D * 2) +              \
+                          (t_ / 8) * 128 + (((ol & 7) ^ swz(r_)) * 16);      \
+      dma_untracked<16>(rs_, bW1 + (t_ / 8) * (kMlpHC * 128) + (t_ % 8) * 1024, o_); \
+    }                                                                        \
+  } while (0)
+#define MOE_MLP_ISSUE_W2(HC0)                                                \
+  do {                                                                       \
+    const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(                            \
+        reinterpret_cast<const void*>(                                       \
+            uniform64(reinterpret_cast<int64_t>(w2g + (HC0)))),              \
+        static_cast<uint32_t>((D - 1) * H * 2 + kMlpHC * 2));                \
+    _Pragma("unroll") for (int q = 0; q < NTW; ++q) {                        \
+      const int t_ = wave + kMlpWaves * q;                                   \
+      const int r_ = t_ * 8 + (ol >> 3);                                     \
+      const uint32_t o_ = static_cast<uint32_t>(r_) * static_cast<uint32_t>(H * 2) + \
+                          (((ol & 7) ^ swz(r_)) * 16);                       \
+      dma_untracked<16>(rs_, bW2 + t_ * 1024, o_);                           \
+    }                                                                        \
+  } while (0)
+
+  {
+    const int ol = lane;
+    MOE_MLP_ISSUE_W1(0);
+  }
+  // This lane's token row as phase A's B operand: k 16 s + 8 khalf .. + 8
+  // of step s.  Rows past the group end re-read the tile's first row (never
+  // stored).
+  bf16x8 xf[KS];
+  {
+    const int64_t row = loc.row0 + tb * 32 + (lane & 31);
+    const int64_t r = row < loc.row_end ? row : loc.row0;
+    const int64_t src = p.a_index != nullptr ? p.a_index[r] : r;
+    const uint16_t* const xr = static_cast<const uint16_t*>(p.a) + src * D + 8 * khalf;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
+  }
+  f32x16 acc[FBY];
+#pragma unroll
+  for (int i = 0; i < FBY; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+  stage_barrier();
+
+  // LDS element offsets.  Phase A: W1 row 32 fh + (lane & 31) of the
+  // chunk, k step s -> slice s / 4, chunk 2 (s % 4) + khalf.  Phase B: W2
+  // row (output feature) fh D/2 + 32 i + (lane & 31); h row (token)
+  // 32 tb + (lane & 31); k step s -> chunk 2 s + khalf.
+  const int nc = H / kMlpHC;
+  for (int c = 0; c < nc; ++c) {
+    int ol = lane;
+    asm volatile("" : "+v"(ol));
+    const int kh = ol >> 5;
+    const int ra = fh * 32 + (ol & 31);
+    const int rt = tb * 32 + (ol & 31);
+    const int hc0 = c * kMlpHC;
+    MOE_MLP_ISSUE_W2(hc0);
+    // phase A
+    f32x16 ah;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ah[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int ck = 2 * (s % 4) + kh;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          &sW1[(s / 4) * kMlpHC * 64 + ra * 64 + ((ck ^ swz(ra)) * 8)]);
+      ah = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[s], ah, 0, 0, 0);
+    }
+    // bias, GELU, bf16 into hc: register 4 q + j holds hidden feature
+    // 32 fh + 8 q + 4 khalf + j of token rt.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int hf = fh * 32 + 8 * q + 4 * kh;
+      f32x4 v;
+      v[0] = ah[4 * q + 0]; v[1] = ah[4 * q + 1];
+      v[2] = ah[4 * q + 2]; v[3] = ah[4 * q + 3];
+      if (p.bias != nullptr) {
+        const float* b = p.bias + static_cast<int64_t>(g) * H + hc0 + hf;
+        v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+      }
+      uint2 o;
+      o.x = pack_bf16x2(gelu_tanh(v[0]), gelu_tanh(v[1]));
+      o.y = pack_bf16x2(gelu_tanh(v[2]), gelu_tanh(v[3]));
+      const int ch = hf >> 3;
+      *reinterpret_cast<uint2*>(sH + rt * 128 + ((ch ^ swz(rt)) * 16) + kh * 8) = o;
+    }
+    stage_barrier();   // hc written, W2 chunk landed, W1 chunk read by all
+    if (c + 1 < nc) MOE_MLP_ISSUE_W1(hc0 + kMlpHC);
+    // phase B, k step outermost: one h fragment live at a time.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 hb = *reinterpret_cast<const bf16x8*>(
+          sH + rt * 128 + (((2 * s + kh) ^ swz(rt)) * 16));
+#pragma unroll
+      for (int i = 0; i < FBY; ++i) {
+        const int ro = fh * (D / 2) + 32 * i + (ol & 31);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            &sW2[ro * 64 + (((2 * s + kh) ^ swz(ro)) * 8)]);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, hb, acc[i], 0, 0, 0);
+      }
+    }
+    stage_barrier();   // next W1 chunk landed; W2 chunk and hc read by all
+  }
+
+  // y row rt: register 4 q + j of block i is output feature
+  // fh D/2 + 32 i + 8 q + 4 khalf + j.
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int rt = tb * 32 + (el & 31);
+  const int64_t row = loc.row0 + rt;
+  if (row >= loc.row_end) return;
+#pragma unroll
+  for (int i = 0; i < FBY; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = fh * (D / 2) + 32 * i + 8 * q + 4 * (el >> 5);
+      f32x4 v;
+      v[0] = acc[i][4 * q + 0]; v[1] = acc[i][4 * q + 1];
+      v[2] = acc[i][4 * q + 2]; v[3] = acc[i][4 * q + 3];
+      if (b2 != nullptr) {
+        const float* b = b2 + static_cast<int64_t>(g) * D + f;
+        v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+      }
+      if (y_f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.c) + row * D + f) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        uint2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + row * D + f) = o;
+      }
+    }
+  }
+#undef MOE_MLP_ISSUE_W1
+#undef MOE_MLP_ISSUE_W2
+}
+
 // Tile shapes: the up-projection (N = H, a multiple of 256 in every DiT-MoE
 // shape) uses 256 x 256 tiles, 2 x 4 waves of 128 tokens x 64 features; the
 // down-projection (N = D, e.g. 1152 = 6 x 192) uses 256 x 192 tiles, 4 x 2
@@ -1194,6 +1405,33 @@ hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
                y_rows, slot_row, topk_w, Kmax};
   launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
       p, stream);
+  return hipGetLastError();
+}
+
+bool mlp_fused_supported(int D, int H) {
+  return (D == 128 || D == 256 || D == 384) && H > 0 && H % kMlpHC == 0;
+}
+
+hipError_t launch_mlp_fused(const FfnArgs& a, hipStream_t stream) {
+  if (a.total_rows == 0) return hipSuccess;
+  GemmParams p{a.x, a.row_index, a.w1, a.b1, a.y, a.offsets, a.total_rows,
+               a.G, a.D, a.D};
+  const int tiles = tile_grid(p, kMlpBM, a.D);
+  const dim3 grid(static_cast<unsigned>(tiles)), block(64 * kMlpWaves);
+  const int yf = a.y_f32 ? 1 : 0;
+  switch (a.D) {
+    case 128:
+      hipLaunchKernelGGL((mlp_fused_kernel<1>), grid, block, 0, stream, p,
+                         a.w2, a.b2, a.H, yf);
+      break;
+    case 256:
+      hipLaunchKernelGGL((mlp_fused_kernel<2>), grid, block, 0, stream, p,
+                         a.w2, a.b2, a.H, yf);
+      break;
+    default:
+      hipLaunchKernelGGL((mlp_fused_kernel<3>), grid, block, 0, stream, p,
+                         a.w2, a.b2, a.H, yf);
+  }
   return hipGetLastError();
 }
 

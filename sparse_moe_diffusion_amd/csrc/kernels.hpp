@@ -54,6 +54,10 @@ struct FfnArgs {
   bool y_f32;               // output dtype
 };
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
+// Both stages in one kernel (bf16, D in {128, 256, 384}, H % 64 == 0); h is
+// not used.
+bool mlp_fused_supported(int D, int H);
+hipError_t launch_mlp_fused(const FfnArgs& a, hipStream_t stream);
 // Stage 2 of the shared experts (one group of all N tokens, bf16) fused with
 // the weighted combine of the routed outputs; Kmax <= 4.
 hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,

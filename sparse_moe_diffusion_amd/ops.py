@@ -78,6 +78,15 @@ def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
               dtype_code(y_rows.dtype), stages, _stream())
 
 
+def moe_grouped_mlp_fused(x_rows, row_index, total_rows: int, group_offsets,
+                          w1, b1, w2, b2, y_rows):
+    G, H, D = w1.shape
+    _lib.call("moe_grouped_mlp_fused", _ptr(x_rows), _ptr(row_index),
+              dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y_rows),
+              dtype_code(y_rows.dtype), _stream())
+
+
 def moe_combine(y_rows, slot_row, topk_w, y_shared, y):
     N, D = y.shape
     Kmax = slot_row.shape[1]

@@ -150,6 +150,33 @@ def test_combine_and_balance_reject():
         assert _lib.call_status("moe_balance_stats", *a.values()) == st
 
 
+def _mlp_fused(**kw):
+    a = dict(x=FAKE, ri=None, dt=_lib.MOE_BF16, total=256, off=FAKE, G=2,
+             D=384, H=1536, w1=FAKE, b1=None, w2=FAKE, b2=None, y=FAKE,
+             ydt=_lib.MOE_BF16, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_grouped_mlp_fused", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(w2=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(off=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(total=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(G=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(D=1152), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=320), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(H=1000), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(ydt=7), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_mlp_fused_rejects(kw, status):
+    ensure_built()
+    assert _mlp_fused(**kw) == status
+    assert _lib.last_error()
+
+
 def _gate_balance(**kw):
     a = dict(x=FAKE, dt=_lib.MOE_BF16, wg=FAKE, bias=None, B=4, T=16, D=128,
              E=8, K=2, alpha=ctypes.c_float(0.01),

@@ -301,6 +301,65 @@ def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
         assert_close(y[rows], ref, "bf16", f"group {g}")
 
 
+@pytest.mark.parametrize("sizes,D,H,gather,bias,y_f32", [
+    ([100, 0, 129, 1, 256, 0, 0, 300], 128, 256, False, False, False),
+    ([100, 0, 129, 1, 256, 0, 0, 300], 256, 512, True, True, False),
+    ([513], 384, 64, False, True, True),
+    ([77, 3, 200], 384, 1536, True, False, False),
+    ([(i * 37) % 23 * 3 for i in range(64)], 128, 192, True, False, True),
+    ([0, 0, 0], 128, 256, False, False, False),
+    # the S layer's routed experts: 16 groups of about 1024 rows
+    ([1024 + (i * 97) % 200 - 100 for i in range(16)], 384, 1536, True, False,
+     False),
+])
+def test_grouped_mlp_fused(sizes, D, H, gather, bias, y_f32):
+    """The one-kernel MLP against the two-stage grouped FFN on the same
+    inputs (same bits) and against the oracle (rows sampled when large)."""
+    _, ops = _ops()
+    rng = np.random.default_rng(sum(sizes) + D + H)
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    total = int(offsets[-1])
+    q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
+    nsrc = total + 9
+    xsrc = q(rng.standard_normal((nsrc, D)))
+    w1 = q(rng.standard_normal((G, H, D)) * 0.05)
+    w2 = q(rng.standard_normal((G, D, H)) * 0.05)
+    b1 = (rng.standard_normal((G, H)) * 0.1).astype(np.float32) if bias else None
+    b2 = (rng.standard_normal((G, D)) * 0.1).astype(np.float32) if bias else None
+    ri = rng.permutation(nsrc)[:total] if gather else None
+    xs = xsrc if gather else xsrc[:total]
+    y_two = _run_ffn(xs, offsets, w1, w2, b1, b2, "bf16", row_index=ri,
+                     y_f32=y_f32)
+    x = _bits_tensor(xs, "bf16")
+    rit = None if ri is None else torch.from_numpy(ri.astype(np.int32)).to(DEV)
+    ydt = torch.float32 if y_f32 else torch.bfloat16
+    y = torch.full((total, D), float("nan"), dtype=ydt, device=DEV)
+    b1t = None if b1 is None else torch.from_numpy(b1).to(DEV)
+    b2t = None if b2 is None else torch.from_numpy(b2).to(DEV)
+    ops.moe_grouped_mlp_fused(x, rit, total, torch.from_numpy(offsets).to(DEV),
+                              _bits_tensor(w1, "bf16"), b1t,
+                              _bits_tensor(w2, "bf16"), b2t, y)
+    torch.cuda.synchronize()
+    yf = to_np(y)
+    if total == 0:
+        return
+    assert np.array_equal(yf, y_two), np.abs(yf - y_two).max()
+    rows_all = xsrc[ri] if gather else xsrc[:total]
+    pick = (np.arange(total) if total <= 3000 else
+            np.unique(np.concatenate([rng.choice(total, 64, replace=False),
+                                      offsets[1:-1] - 1, offsets[1:-1]])))
+    pick = pick[pick < total]
+    grp = np.searchsorted(offsets, pick, side="right") - 1
+    ref = np.zeros((pick.size, D))
+    for g in np.unique(grp):
+        m = grp == g
+        ref[m] = oracle.expert_mlp(rows_all[pick[m]], w1[g], w2[g],
+                                   None if b1 is None else b1[g],
+                                   None if b2 is None else b2[g])
+    assert_close(yf[pick], ref, "bf16", "fused mlp")
+
+
 def test_grouped_ffn_bf16_rows_fp32_out():
     rng = np.random.default_rng(3)
     q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
