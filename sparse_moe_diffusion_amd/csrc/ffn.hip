@@ -736,31 +736,38 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
   // feature block i, token (lane & 31) of token block j.
   if constexpr (OUT_BF16) {
-    // Every wave is done with the stages: stage the tile in LDS.
+    // Every wave is done with the stages: stage the tile in LDS.  Rows past
+    // the group end are staged too (finite values from the zero or re-read
+    // operand rows; the copy-out skips them).  Features past Nd are skipped
+    // (their bias would lie outside the array); a tile that holds none takes
+    // the branch-free form.
     stage_barrier();
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      const int t = wt * (BM / WT) + j * 32 + (lane & 31);
-      if (loc.row0 + t >= loc.row_end) continue;
-#pragma unroll
-      for (int i = 0; i < FB; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int fl = wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
-          if (loc.n0 + fl >= p.Nd) continue;
-          f32x4 v;
-          v[0] = acc[i][j][4 * q + 0];
-          v[1] = acc[i][j][4 * q + 1];
-          v[2] = acc[i][j][4 * q + 2];
-          v[3] = acc[i][j][4 * q + 3];
-          v = finish4<EPI>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(&lds[t * kOutPitch + fl]) = o;
-        }
-      }
+#define MOE_STAGE_OUT(CHECK)                                                 \
+    _Pragma("unroll") for (int j = 0; j < TB; ++j) {                         \
+      const int t = wt * (BM / WT) + j * 32 + (lane & 31);                   \
+      _Pragma("unroll") for (int i = 0; i < FB; ++i) {                       \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                      \
+          const int fl = wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;        \
+          if ((CHECK) && loc.n0 + fl >= p.Nd) continue;                      \
+          f32x4 v;                                                           \
+          v[0] = acc[i][j][4 * q + 0];                                       \
+          v[1] = acc[i][j][4 * q + 1];                                       \
+          v[2] = acc[i][j][4 * q + 2];                                       \
+          v[3] = acc[i][j][4 * q + 3];                                       \
+          v = finish4<EPI>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);          \
+          uint2 o;                                                           \
+          o.x = pack_bf16x2(v[0], v[1]);                                     \
+          o.y = pack_bf16x2(v[2], v[3]);                                     \
+          *reinterpret_cast<uint2*>(&lds[t * kOutPitch + fl]) = o;           \
+        }                                                                    \
+      }                                                                      \
     }
+    if (loc.n0 + BN <= p.Nd) {
+      MOE_STAGE_OUT(false)
+    } else {
+      MOE_STAGE_OUT(true)
+    }
+#undef MOE_STAGE_OUT
     stage_barrier();
     // Copy out: 16 bytes per lane, consecutive lanes along a row, as
     // non-temporal stores (the tile is not read again by this kernel; without
