@@ -46,6 +46,9 @@ def parse():
                     help="instead of the layer, time the routing histogram "
                          "(counts by patch position and by image tag) on the "
                          "layer's routing")
+    ap.add_argument("--recompute-u", action="store_true",
+                    help="with --backward: the forward keeps no "
+                         "pre-activations and the backward recomputes them")
     ap.add_argument("--mlp-fused", action="store_true",
                     help="instead of the layer, time the one-kernel expert "
                          "MLP against the two-stage grouped FFN on the "
@@ -125,7 +128,10 @@ def kernel_work(cfg, gather: bool):
 
 def backward_bench(args):
     """Time the backward pass of the layer: gradients of <dy, y> + L_balance
-    for a seeded synthetic dy, after one forward pass (routing fixed)."""
+    for a seeded synthetic dy, after one forward pass (routing fixed).  By
+    default the forward is a training forward that keeps the expert MLPs'
+    pre-activations (no recomputation in the backward); the forward's own
+    time is reported beside it."""
     import torch
     import synth
     from sparse_moe_diffusion_amd import _lib, layer
@@ -135,7 +141,8 @@ def backward_bench(args):
     inp = synth.make_inputs(cfg)
     x = layer._to_device(inp.x, torch.bfloat16, "cuda")
     wts = layer.LayerWeights.from_inputs(inp, "cuda")
-    buf = layer.LayerBuffers(cfg, "cuda", gather=True)
+    save_u = not args.recompute_u
+    buf = layer.LayerBuffers(cfg, "cuda", gather=True, save_u=save_u)
     layer.forward(cfg, x, wts, buf)
     g = torch.Generator(device="cuda").manual_seed(cfg.seed + 77)
     dy = torch.randn(cfg.N, cfg.D, device="cuda", generator=g).to(torch.bfloat16)
@@ -163,10 +170,18 @@ def backward_bench(args):
     ms = (time.perf_counter() - t0) * 1e3 / K
     per = {n: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)) / K
            for i, (n, _) in enumerate(steps)}
-    # executed GEMM work of one grouped-MLP backward call: u recomputed,
-    # dgrad of both matrices, wgrad of both = 5 products of 2*M*D*H FLOPs
-    f_routed = 10.0 * cfg.A * cfg.D * cfg.H
-    f_shared = 10.0 * cfg.N * cfg.D * cfg.H * cfg.n_s
+    # the forward that feeds it (same buffers), timed alone
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        layer.forward(cfg, x, wts, buf)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) * 1e3 / K
+    # executed GEMM work of one grouped-MLP backward call: dgrad of both
+    # matrices and wgrad of both (plus u when recomputed), 2*M*D*H FLOPs each
+    prods = 4.0 if save_u else 5.0
+    f_routed = 2.0 * prods * cfg.A * cfg.D * cfg.H
+    f_shared = 2.0 * prods * cfg.N * cfg.D * cfg.H * cfg.n_s
     kern = {}
     for n, t in per.items():
         e = {"ms": round(t, 4)}
@@ -186,8 +201,12 @@ def backward_bench(args):
         "dtype": "bf16", "data": "synthetic (seeded dy)",
         "config": {"workload": f"{cfg.name}: backward of the layer, B={cfg.B} x "
                                f"T={cfg.T}, D={cfg.D}, E={cfg.E}, K={cfg.K}, "
-                               f"n_s={cfg.n_s}, H={cfg.H}"},
-        "roofline": {"kernel": "grouped expert MLP backward (5 GEMMs per call)",
+                               f"n_s={cfg.n_s}, H={cfg.H}",
+                   "pre_activations": "kept by the forward" if save_u
+                                      else "recomputed"},
+        "forward_ms": round(fwd_ms, 4),
+        "train_step_ms": round(fwd_ms + ms, 4),
+        "roofline": {"kernel": f"grouped expert MLP backward ({int(prods)} GEMMs per call)",
                      "bound": "mfma", "achieved": round(ach, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)},

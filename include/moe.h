@@ -172,6 +172,11 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
  *                  total_rows (total_rows is also passed by value)
  *   w1 [G][H][D], w2 [G][D][H] dtype;  b1 [G][H], b2 [G][D] fp32 or NULL
  *   h_ws           [total_rows][H] dtype scratch (caller-owned)
+ *   u_ws           [total_rows][H] bf16 out, or NULL: with stage 1, the
+ *                  pre-activations u[r] = W1[g] a_r + b1[g] rounded once to
+ *                  bf16 (what the training backward needs; passing them to
+ *                  moe_grouped_ffn_backward skips its recomputation).  bf16
+ *                  inputs only.
  *   y_rows         [total_rows][D] y_dtype out (MOE_F32, or MOE_BF16 when
  *                  dtype is MOE_BF16)
  *   stages         MOE_FFN_BOTH, or one stage alone (MOE_FFN_UP writes h_ws;
@@ -190,7 +195,7 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                            const int64_t* group_offsets, int32_t G, int32_t D,
                            int32_t H, const void* w1, const float* b1,
                            const void* w2, const float* b2, void* h_ws,
-                           void* y_rows, moe_dtype y_dtype,
+                           void* u_ws, void* y_rows, moe_dtype y_dtype,
                            moe_ffn_stages stages, hipStream_t stream);
 
 /*
@@ -365,15 +370,20 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
 
 /*
  * Backward of the grouped expert MLPs (eq. MLP, tanh GELU), bf16.  With
- * u = x_rows W1_g^T (+ b1_g), recomputed, and dy_rows the gradient of the
- * expert outputs:
+ * u = x_rows W1_g^T (+ b1_g) (bf16), h = gelu(u) (bf16) and dy_rows the
+ * gradient of the expert outputs:
  *   du      = (dy_rows W2_g) * gelu'(u)
  *   dx_rows = du W1_g                                  (dx_dtype out)
  *   dW1[g]  = sum over the group's rows of du^T x_rows  (fp32 out)
- *   dW2[g]  = sum over the group's rows of dy_rows^T gelu(u)   (fp32 out)
+ *   dW2[g]  = sum over the group's rows of dy_rows^T h  (fp32 out)
  * Rows, groups, row_index (gather) and weights are those of the forward
  * moe_grouped_ffn call.  dW1 / dW2 are written whole (zero for empty
  * groups).
+ *   u_rows  [total_rows][H] bf16: the forward's u_ws, or NULL to recompute
+ *           u here (the same bits);
+ *   h_rows  [total_rows][H] bf16: the forward's h_ws, or NULL to use
+ *           gelu(u) of the bf16 u instead (it can differ from the
+ *           forward's h by one bf16 rounding);
  *   dy_rows [total_rows][D] bf16;  dx_rows [total_rows][D];
  *   dw1 [G][H][D], dw2 [G][D][H] fp32 out;  workspace of at least
  *   moe_ffn_backward_workspace_size bytes (recomputed activations,
@@ -386,9 +396,9 @@ moe_status moe_grouped_ffn_backward(
     const void* x_rows, const int32_t* row_index, moe_dtype dtype,
     int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
     int32_t H, const void* w1, const float* b1, const void* w2,
-    const void* dy_rows, void* workspace, size_t workspace_bytes,
-    void* dx_rows, moe_dtype dx_dtype, float* dw1, float* dw2,
-    hipStream_t stream);
+    const void* dy_rows, const void* u_rows, const void* h_rows,
+    void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype,
+    float* dw1, float* dw2, hipStream_t stream);
 
 /* Bytes of workspace moe_gate_backward needs (0 for bad sizes). */
 size_t moe_gate_backward_workspace_size(int64_t N, int32_t E, int32_t D);

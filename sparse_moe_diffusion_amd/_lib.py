@@ -46,7 +46,7 @@ SIGNATURES = {
     "moe_permute": (_E, [_P, _E, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
                          _P, _P, _P, _SZ, _P]),
     "moe_grouped_ffn": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32, _P, _P, _P,
-                             _P, _P, _P, _E, _E, _P]),
+                             _P, _P, _P, _P, _E, _E, _P]),
     "moe_grouped_mlp_fused": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32, _P,
                                    _P, _P, _P, _P, _E, _P]),
     "moe_combine": (_E, [_P, _E, _P, _P, _I64, _I32, _I32, _P, _E, _P, _E, _P]),
@@ -62,8 +62,8 @@ SIGNATURES = {
                                   _P, _P]),
     "moe_ffn_backward_workspace_size": (_SZ, [_I64, _I32, _I32, _I32]),
     "moe_grouped_ffn_backward": (_E, [_P, _P, _E, _I64, _P, _I32, _I32, _I32,
-                                      _P, _P, _P, _P, _P, _SZ, _P, _E, _P, _P,
-                                      _P]),
+                                      _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _E,
+                                      _P, _P, _P]),
     "moe_gate_backward_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_gate_backward": (_E, [_P, _E, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                _I32, _I32, _I32, _F, _F, _E, _P, _P, _P, _E,

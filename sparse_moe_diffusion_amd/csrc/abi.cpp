@@ -163,7 +163,7 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                            const int64_t* group_offsets, int32_t G, int32_t D,
                            int32_t H, const void* w1, const float* b1,
                            const void* w2, const float* b2, void* h_ws,
-                           void* y_rows, moe_dtype y_dtype,
+                           void* u_ws, void* y_rows, moe_dtype y_dtype,
                            moe_ffn_stages stages, hipStream_t stream) {
   const char* fn = "moe_grouped_ffn";
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
@@ -181,6 +181,8 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
   if (dtype == MOE_F32 && y_dtype != MOE_F32)
     return fail(MOE_ERR_UNSUPPORTED, "%s: fp32 inputs need fp32 outputs", fn);
+  if (u_ws != nullptr && dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: u_ws needs bf16 inputs", fn);
   if (G > kMaxGroups)
     return fail(MOE_ERR_UNSUPPORTED, "%s: G=%d above %d", fn, G, kMaxGroups);
   if (D % 8 != 0 || H % 8 != 0)
@@ -191,6 +193,7 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
   moe::FfnArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
                  w1,     b1,        w2,         b2,            h_ws, y_rows,
                  dtype == MOE_BF16,  y_dtype == MOE_F32};
+  a.u = up ? u_ws : nullptr;
   return from_hip(moe::launch_ffn(a, up, down, stream), fn);
 }
 
@@ -409,9 +412,9 @@ moe_status moe_grouped_ffn_backward(
     const void* x_rows, const int32_t* row_index, moe_dtype dtype,
     int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
     int32_t H, const void* w1, const float* b1, const void* w2,
-    const void* dy_rows, void* workspace, size_t workspace_bytes,
-    void* dx_rows, moe_dtype dx_dtype, float* dw1, float* dw2,
-    hipStream_t stream) {
+    const void* dy_rows, const void* u_rows, const void* h_rows,
+    void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype,
+    float* dw1, float* dw2, hipStream_t stream) {
   const char* fn = "moe_grouped_ffn_backward";
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -438,6 +441,8 @@ moe_status moe_grouped_ffn_backward(
   moe::FfnBwdArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
                     w1,     b1,        w2,         dy_rows,       workspace,
                     dx_rows, dx_dtype == MOE_F32, dw1, dw2};
+  a.u_saved = u_rows;
+  a.h_saved = h_rows;
   return from_hip(moe::launch_ffn_backward(a, stream), fn);
 }
 

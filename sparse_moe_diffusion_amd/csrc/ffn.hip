@@ -73,6 +73,9 @@ struct GemmParams {
   // B[:, seg g]^T, A [mrows][ld] and B [Nd][ld] bf16, seg g = group g's
   // token columns, padded to 64 (see the transposes).
   int ld, mrows;
+  // kEpiGelu with bf16 output: if set, also the pre-activations u = A W^T
+  // + bias, [total][Nd] bf16 (kept by a training forward for the backward).
+  void* u_out;
 };
 
 struct TileLoc {
@@ -742,7 +745,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     // (their bias would lie outside the array); a tile that holds none takes
     // the branch-free form.
     stage_barrier();
-#define MOE_STAGE_OUT(CHECK)                                                 \
+#define MOE_STAGE_OUT(CHECK, E_)                                             \
     _Pragma("unroll") for (int j = 0; j < TB; ++j) {                         \
       const int t = wt * (BM / WT) + j * 32 + (lane & 31);                   \
       _Pragma("unroll") for (int i = 0; i < FB; ++i) {                       \
@@ -754,7 +757,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           v[1] = acc[i][j][4 * q + 1];                                       \
           v[2] = acc[i][j][4 * q + 2];                                       \
           v[3] = acc[i][j][4 * q + 3];                                       \
-          v = finish4<EPI>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);          \
+          v = finish4<E_>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);           \
           uint2 o;                                                           \
           o.x = pack_bf16x2(v[0], v[1]);                                     \
           o.y = pack_bf16x2(v[2], v[3]);                                     \
@@ -762,18 +765,45 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
         }                                                                    \
       }                                                                      \
     }
-    if (loc.n0 + BN <= p.Nd) {
-      MOE_STAGE_OUT(false)
+    constexpr int kChunks = BN / 8;
+    uint16_t* const c = static_cast<uint16_t*>(p.c);
+    const bool full_n = loc.n0 + BN <= p.Nd;
+    // Copy out the staged tile to `dst`: 16 bytes per lane, consecutive
+    // lanes along a row, as non-temporal stores (the tile is not read again
+    // by this kernel; without the hint the write burst at the end of every
+    // tile allocates L2 lines).
+#define MOE_COPY_OUT(DST)                                                    \
+    for (int idx = tid; idx < BM * kChunks; idx += 64 * kWaves) {            \
+      const int r = idx / kChunks;                                           \
+      const int f = loc.n0 + (idx - r * kChunks) * 8;                        \
+      const int64_t row = loc.row0 + r;                                      \
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));        \
+      if (row < loc.row_end && f < p.Nd)                                     \
+        __builtin_nontemporal_store(                                         \
+            *reinterpret_cast<const u32x4*>(&lds[r * kOutPitch + (f - loc.n0)]), \
+            reinterpret_cast<u32x4*>((DST) + row * p.Nd + f));               \
+    }
+    if constexpr (EPI == kEpiGelu) {
+      // Training forward: the pre-activations first, through the same
+      // staging area, then the activations below.
+      if (p.u_out != nullptr) {
+        if (full_n) {
+          MOE_STAGE_OUT(false, kEpiStore)
+        } else {
+          MOE_STAGE_OUT(true, kEpiStore)
+        }
+        stage_barrier();
+        MOE_COPY_OUT(static_cast<uint16_t*>(p.u_out))
+        stage_barrier();
+      }
+    }
+    if (full_n) {
+      MOE_STAGE_OUT(false, EPI)
     } else {
-      MOE_STAGE_OUT(true)
+      MOE_STAGE_OUT(true, EPI)
     }
 #undef MOE_STAGE_OUT
     stage_barrier();
-    // Copy out: 16 bytes per lane, consecutive lanes along a row, as
-    // non-temporal stores (the tile is not read again by this kernel; without
-    // the hint the write burst at the end of every tile allocates L2 lines).
-    constexpr int kChunks = BN / 8;
-    uint16_t* const c = static_cast<uint16_t*>(p.c);
     if constexpr (EPI == kEpiCombine) {
       // y[t] = sum over the slots >= 0, in slot order, of w * routed row,
       // then plus the staged (bf16) shared output, in fp32, rounded once:
@@ -883,17 +913,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(c + row * p.Nd + f));
         }
       }
-    } else
-    for (int idx = tid; idx < BM * kChunks; idx += 64 * kWaves) {
-      const int r = idx / kChunks;
-      const int f = loc.n0 + (idx - r * kChunks) * 8;
-      const int64_t row = loc.row0 + r;
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      if (row < loc.row_end && f < p.Nd)
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4*>(&lds[r * kOutPitch + (f - loc.n0)]),
-            reinterpret_cast<u32x4*>(c + row * p.Nd + f));
+    } else {
+      MOE_COPY_OUT(c)
     }
+#undef MOE_COPY_OUT
   } else {
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
@@ -1344,16 +1367,21 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   MOE_TRY(launch_transpose(a.w2, G, D, H, w2t, stream));
   MOE_TRY(launch_transpose(a.w1, G, H, D, w1t, stream));
   if (a.total_rows > 0) {
-    GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
-                  G, H, D};
-    hipLaunchKernelGGL(
-        (gemm_bf16_kernel<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
-        dim3(persistent_grid(tile_grid(pu, kUpBM, kUpBN))),
-        dim3(64 * kUpWT * kUpWF), 0, stream, pu);
-    MOE_TRY(hipGetLastError());
+    // u: the forward's saved pre-activations, or recomputed.
+    const void* uu = a.u_saved;
+    if (uu == nullptr) {
+      GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
+                    G, H, D};
+      hipLaunchKernelGGL(
+          (gemm_bf16_kernel<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
+          dim3(persistent_grid(tile_grid(pu, kUpBM, kUpBN))),
+          dim3(64 * kUpWT * kUpWF), 0, stream, pu);
+      MOE_TRY(hipGetLastError());
+      uu = u;
+    }
     GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
                   a.total_rows, G, H, D};
-    pd.aux = u;
+    pd.aux = uu;
     hipLaunchKernelGGL(
         (gemm_bf16_kernel<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
         dim3(persistent_grid(tile_grid(pd, kUpBM, kUpBN))),
@@ -1374,7 +1402,11 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
     MOE_TRY(hipGetLastError());
     MOE_TRY(launch_kseg(a.offsets, G, a.total_rows, brow, bn, stream));
     MOE_TRY(launch_tpad(a.dy_rows, nullptr, brow, bn, G, a.total_rows, D, false, dyT, stream));
-    MOE_TRY(launch_tpad(u, nullptr, brow, bn, G, a.total_rows, H, true, aT, stream));
+    // a = gelu(u): the forward's saved activations, or gelu of u.
+    if (a.h_saved != nullptr)
+      MOE_TRY(launch_tpad(a.h_saved, nullptr, brow, bn, G, a.total_rows, H, false, aT, stream));
+    else
+      MOE_TRY(launch_tpad(uu, nullptr, brow, bn, G, a.total_rows, H, true, aT, stream));
     MOE_TRY(launch_tpad(du, nullptr, brow, bn, G, a.total_rows, H, false, duT, stream));
     MOE_TRY(launch_tpad(a.x, a.row_index, brow, bn, G, a.total_rows, D, false, xT, stream));
   }
@@ -1447,6 +1479,7 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
   if (a.total_rows == 0) return hipSuccess;
   GemmParams p1{a.x, a.row_index, a.w1, a.b1, a.h, a.offsets, a.total_rows,
                 a.G, a.H, a.D};
+  p1.u_out = a.u;
   GemmParams p2{a.h, nullptr, a.w2, a.b2, a.y, a.offsets, a.total_rows,
                 a.G, a.D, a.H};
   if (a.bf16) {

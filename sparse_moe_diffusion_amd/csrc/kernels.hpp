@@ -52,6 +52,7 @@ struct FfnArgs {
   void* y;                  // [total][D]
   bool bf16;                // input / weight / h dtype
   bool y_f32;               // output dtype
+  void* u = nullptr;        // [total][H] bf16 pre-activations out, or null
 };
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
 // Both stages in one kernel (bf16, D in {128, 256, 384}, H % 64 == 0); h is
@@ -126,6 +127,8 @@ struct FfnBwdArgs {
   bool dx_f32;
   float* dw1;               // [G][H][D]
   float* dw2;               // [G][D][H]
+  const void* u_saved = nullptr;  // [total][H] forward pre-activations, or null
+  const void* h_saved = nullptr;  // [total][H] forward activations, or null
 };
 size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H);
 hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream);

@@ -67,10 +67,12 @@ class LayerWeights:
 
 class LayerBuffers:
     """Every intermediate and output tensor of one forward pass, allocated
-    once for a fixed token count."""
+    once for a fixed token count.  With save_u (training, bf16 layers) the
+    expert MLPs' pre-activations are kept too, so that the backward pass
+    does not recompute them."""
 
     def __init__(self, cfg, device="cuda", gather: bool = False,
-                 y_rows_f32: bool = False):
+                 y_rows_f32: bool = False, save_u: bool = False):
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         N, D, H, E, K, n_s = cfg.N, cfg.D, cfg.H, cfg.E, cfg.K, cfg.n_s
         Kmax, A = cfg.Kmax, cfg.A
@@ -91,14 +93,20 @@ class LayerBuffers:
         pws = ops.permute_workspace_size(N, E, Kmax)
         self.perm_ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
         self.h = torch.empty(A, H, dtype=dt, device=dev)
+        if save_u and dt != torch.bfloat16:
+            raise ValueError("saved pre-activations need a bf16 layer")
+        self.u = torch.empty(A, H, dtype=dt, device=dev) if save_u else None
         ydt = f32 if (y_rows_f32 or dt == f32) else dt
         self.y_rows = torch.empty(A, D, dtype=ydt, device=dev)
         if n_s > 0:
             self.shared_offsets = torch.tensor([0, N], dtype=i64, device=dev)
             self.h_shared = torch.empty(N, n_s * H, dtype=dt, device=dev)
+            self.u_shared = (torch.empty(N, n_s * H, dtype=dt, device=dev)
+                             if save_u else None)
             self.y_shared = torch.empty(N, D, dtype=dt, device=dev)
         else:
             self.shared_offsets = self.h_shared = self.y_shared = None
+            self.u_shared = None
         self.y = torch.empty(N, D, dtype=dt, device=dev)
         self.gate_bal_ws = None
         if route == ROUTES["topk"]:
@@ -139,17 +147,20 @@ def routed_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
                stages: int = _lib.MOE_FFN_BOTH):
     if buf.gather:
         ops.moe_grouped_ffn(x, buf.row_token, cfg.A, buf.expert_offsets, wts.w1,
-                            None, wts.w2, None, buf.h, buf.y_rows, stages)
+                            None, wts.w2, None, buf.h, buf.y_rows, stages,
+                            buf.u)
     else:
         ops.moe_grouped_ffn(buf.x_perm, None, cfg.A, buf.expert_offsets, wts.w1,
-                            None, wts.w2, None, buf.h, buf.y_rows, stages)
+                            None, wts.w2, None, buf.h, buf.y_rows, stages,
+                            buf.u)
 
 
 def shared_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
                stages: int = _lib.MOE_FFN_BOTH):
     if cfg.n_s > 0:
         ops.moe_grouped_ffn(x, None, cfg.N, buf.shared_offsets, wts.w1s, None,
-                            wts.w2s, None, buf.h_shared, buf.y_shared, stages)
+                            wts.w2s, None, buf.h_shared, buf.y_shared, stages,
+                            buf.u_shared)
 
 
 def fuses_combine(cfg, buf: LayerBuffers) -> bool:
@@ -280,17 +291,21 @@ def combine_backward(cfg, buf, grads, dy):
 
 def routed_ffn_backward(cfg, x, wts, buf, grads):
     x_rows, row_index = (x, buf.row_token) if buf.gather else (buf.x_perm, None)
+    saved = buf.u is not None
     ops.moe_grouped_ffn_backward(x_rows, row_index, cfg.A, buf.expert_offsets,
                                  wts.w1, None, wts.w2, grads.dy_rows,
                                  grads.ffn_ws, grads.dx_rows, grads.dw1,
-                                 grads.dw2)
+                                 grads.dw2, buf.u, buf.h if saved else None)
 
 
 def shared_ffn_backward(cfg, x, wts, buf, grads, dy):
     if cfg.n_s > 0:
+        saved = buf.u_shared is not None
         ops.moe_grouped_ffn_backward(x, None, cfg.N, buf.shared_offsets,
                                      wts.w1s, None, wts.w2s, dy, grads.ffn_ws,
-                                     grads.dx_shared, grads.dw1s, grads.dw2s)
+                                     grads.dx_shared, grads.dw1s, grads.dw2s,
+                                     buf.u_shared,
+                                     buf.h_shared if saved else None)
 
 
 def gate_backward(cfg, x, wts, buf, grads, dloss, balance_mode="sequence"):
@@ -316,7 +331,8 @@ def backward(cfg, x, wts: LayerWeights, buf: LayerBuffers,
              balance_mode: str = "sequence") -> BackwardBuffers:
     """Gradients of <dy, y> + dloss * L_balance after forward() (same
     buffers and balance mode): combine, routed experts, shared experts, gate
-    and dx."""
+    and dx.  Buffers made with save_u give the expert MLPs the forward's
+    pre-activations and activations (no recomputation)."""
     combine_backward(cfg, buf, grads, dy)
     routed_ffn_backward(cfg, x, wts, buf, grads)
     shared_ffn_backward(cfg, x, wts, buf, grads, dy)

@@ -67,15 +67,18 @@ def moe_permute(x, topk_idx, E: int, K: int, expert_counts, expert_offsets,
 
 
 def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
-                    w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH):
+                    w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH,
+                    u_ws=None):
     if w1 is not None:
         G, H, D = w1.shape
     else:                      # stage 2 alone
         G, D, H = w2.shape
     _lib.call("moe_grouped_ffn", _ptr(x_rows), _ptr(row_index),
               dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
-              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(y_rows),
-              dtype_code(y_rows.dtype), stages, _stream())
+              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(u_ws),
+              _ptr(y_rows),
+              dtype_code(y_rows.dtype if y_rows is not None else h_ws.dtype),
+              stages, _stream())
 
 
 def moe_grouped_mlp_fused(x_rows, row_index, total_rows: int, group_offsets,
@@ -158,11 +161,13 @@ def ffn_backward_workspace_size(total_rows: int, G: int, D: int, H: int) -> int:
 
 
 def moe_grouped_ffn_backward(x_rows, row_index, total_rows: int, group_offsets,
-                             w1, b1, w2, dy_rows, workspace, dx_rows, dw1, dw2):
+                             w1, b1, w2, dy_rows, workspace, dx_rows, dw1, dw2,
+                             u_rows=None, h_rows=None):
     G, H, D = w1.shape
     _lib.call("moe_grouped_ffn_backward", _ptr(x_rows), _ptr(row_index),
               dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
-              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(dy_rows), _ptr(workspace),
+              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(dy_rows), _ptr(u_rows),
+              _ptr(h_rows), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _ptr(dx_rows),
               dtype_code(dx_rows.dtype), _ptr(dw1), _ptr(dw2), _stream())
 

@@ -111,7 +111,8 @@ def reconcile_race(P, K, idx_o, idx_g, tau):
 class GpuLayer:
     """Upload one layer's inputs, run the library, fetch the results."""
 
-    def __init__(self, inp, gather=False, y_rows_f32=False, device="cuda"):
+    def __init__(self, inp, gather=False, y_rows_f32=False, device="cuda",
+                 save_u=False):
         from sparse_moe_diffusion_amd import layer
         self.layer = layer
         self.inp = inp
@@ -120,7 +121,7 @@ class GpuLayer:
         self.x = layer._to_device(inp.x, dt, device)
         self.w = layer.LayerWeights.from_inputs(inp, device)
         self.buf = layer.LayerBuffers(self.cfg, device, gather=gather,
-                                      y_rows_f32=y_rows_f32)
+                                      y_rows_f32=y_rows_f32, save_u=save_u)
 
     def run(self, balance_mode="sequence"):
         self.layer.forward(self.cfg, self.x, self.w, self.buf, balance_mode)

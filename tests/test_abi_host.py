@@ -101,8 +101,8 @@ def test_permute_rejects(kw, status):
 
 def _ffn(**kw):
     a = dict(x=FAKE, idx=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
-             D=128, H=512, w1=FAKE, b1=None, w2=FAKE, b2=None, h=FAKE, y=FAKE,
-             ydt=_lib.MOE_BF16, stages=_lib.MOE_FFN_BOTH, stream=None)
+             D=128, H=512, w1=FAKE, b1=None, w2=FAKE, b2=None, h=FAKE, u=None,
+             y=FAKE, ydt=_lib.MOE_BF16, stages=_lib.MOE_FFN_BOTH, stream=None)
     a.update(kw)
     return _lib.call_status("moe_grouped_ffn", *a.values())
 
@@ -120,6 +120,7 @@ def _ffn(**kw):
     (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
     (dict(H=100), _lib.MOE_ERR_UNSUPPORTED),
     (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_BF16), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_F32, u=FAKE), _lib.MOE_ERR_UNSUPPORTED),
     (dict(total=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_ffn_rejects(kw, status):
@@ -288,9 +289,9 @@ def test_backward_entry_points_reject():
         a = dict(cb); a.update(kw)
         assert _lib.call_status("moe_combine_backward", *a.values()) == st
     fb = dict(x=FAKE, ri=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
-              D=128, H=256, w1=FAKE, b1=None, w2=FAKE, dyr=FAKE, ws=FAKE,
-              wsb=1 << 40, dx=FAKE, dxdt=_lib.MOE_BF16, dw1=FAKE, dw2=FAKE,
-              stream=None)
+              D=128, H=256, w1=FAKE, b1=None, w2=FAKE, dyr=FAKE, u=None,
+              h=None, ws=FAKE, wsb=1 << 40, dx=FAKE, dxdt=_lib.MOE_BF16,
+              dw1=FAKE, dw2=FAKE, stream=None)
     for kw, st in [(dict(w1=None), _lib.MOE_ERR_INVALID_ARGUMENT),
                    (dict(dw2=None), _lib.MOE_ERR_INVALID_ARGUMENT),
                    (dict(G=0), _lib.MOE_ERR_INVALID_ARGUMENT),

@@ -147,10 +147,10 @@ def test_gate_backward(B, T, D, E, K, mode, with_rows):
     assert_close(to_np(db), dl.sum(0), "f32", "dbias")
 
 
-def _layer_backward(cfg, seed, dloss=1.0, mode="sequence"):
+def _layer_backward(cfg, seed, dloss=1.0, mode="sequence", save_u=False):
     from sparse_moe_diffusion_amd import layer
     inp = synth.make_inputs(cfg)
-    gl = GpuLayer(inp, gather=True).run(mode)
+    gl = GpuLayer(inp, gather=True, save_u=save_u).run(mode)
     rng = np.random.default_rng(seed)
     dy = q(rng.standard_normal((cfg.N, cfg.D)))
     grads = layer.BackwardBuffers(cfg)
@@ -159,11 +159,14 @@ def _layer_backward(cfg, seed, dloss=1.0, mode="sequence"):
     return inp, gl, dy, grads
 
 
-@pytest.mark.parametrize("name,mode", [("small", "sequence"), ("race", "global")])
-def test_layer_backward(name, mode):
+@pytest.mark.parametrize("name,mode,save_u", [
+    ("small", "sequence", False), ("race", "global", False),
+    ("small", "sequence", True), ("race", "global", True)])
+def test_layer_backward(name, mode, save_u):
     cfg = synth.small_config(B=2, T=96, D=128, H=256, E=8, K=2, seed=41,
                              route="race" if name == "race" else "topk")
-    inp, gl, dy, g = _layer_backward(cfg, 42, dloss=1.0, mode=mode)
+    inp, gl, dy, g = _layer_backward(cfg, 42, dloss=1.0, mode=mode,
+                                     save_u=save_u)
     idx = to_np(gl.buf.topk_idx)
     r = oracle.route(inp)
     P = r["P"]
@@ -189,3 +192,42 @@ def test_layer_backward_deterministic():
     b = [to_np(t) for t in (g2.dx, g2.dw1, g2.dw2, g2.dw_gate, g2.dbias)]
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("cfg", [
+    synth.small_config(B=2, T=96, D=128, H=256, E=8, K=2, seed=45),
+    synth.small_config(B=3, T=200, D=384, H=1536, E=16, K=2, seed=46),
+], ids=["small", "s_like"])
+def test_saved_preactivations(cfg):
+    """A training forward (save_u) writes y and h bit for bit as the plain
+    forward, and u equal to the backward's own recomputation: the backward
+    with the saved u gives dx and dW1 bit for bit as with recomputation;
+    dW2, which then uses the forward's own h instead of gelu of the bf16 u,
+    stays within the oracle's tolerance."""
+    inp, gl0, dy, g0 = _layer_backward(cfg, 47)
+    _, gl1, _, g1 = _layer_backward(cfg, 47, save_u=True)
+    b0, b1 = gl0.buf, gl1.buf
+    for k in ("y", "h", "h_shared", "y_rows"):
+        assert torch.equal(getattr(b0, k).view(torch.int16),
+                           getattr(b1, k).view(torch.int16)), k
+    # u against the oracle's pre-activations on sampled rows
+    rows = to_np(b1.row_token)[:cfg.A]
+    offs = to_np(b1.expert_offsets)
+    pick = np.unique(np.concatenate([[0, cfg.A - 1],
+                                     np.random.default_rng(1).integers(0, cfg.A, 30)]))
+    grp = np.searchsorted(offs, pick, side="right") - 1
+    u = to_np(b1.u)
+    x = inp.x.astype(np.float64)
+    for r, gidx in zip(pick, grp):
+        ref = x[rows[r]] @ inp.w1[gidx].astype(np.float64).T
+        assert_close(u[r:r + 1], ref[None], "bf16", "u")
+    for k in ("dx", "dw1", "dw1s", "dx_rows"):
+        assert torch.equal(getattr(g0, k), getattr(g1, k)), k
+    idx = to_np(b1.topk_idx)
+    P = oracle.route(inp)["P"]
+    ref = oracle.layer_backward(inp, idx, oracle.slot_weights(P, idx), P, dy,
+                                1.0)
+    assert_close(to_np(g1.dw2), ref["dw2"], "bf16", "dW2")
+    n_s, H = cfg.n_s, cfg.H
+    dw2s = to_np(g1.dw2s)[0].reshape(cfg.D, n_s, H).transpose(1, 0, 2)
+    assert_close(dw2s, ref["dw2s"], "bf16", "dW2s")
