@@ -123,24 +123,31 @@ __global__ __launch_bounds__(256) void kseg_kernel(
 // dst [C][Kt]: column block kb holds the blk_n[kb] source rows from
 // blk_row[kb] (through row_index when given), transposed, then zeros.
 // Same 16-byte tile scheme as transpose_kernel (C a multiple of 8).
+// Lane (a, b) of a wave owns tokens 8a .. 8a + 7 of a 64-token block and
+// features 8b .. 8b + 7 of a 64-feature slice: eight 16-byte row loads (the
+// eight lanes of one a read 128 contiguous bytes of a row), an 8 x 8
+// transpose in registers (v_perm_b32 picks the 16-bit halves), eight
+// 16-byte stores (the eight lanes of one b write 128 contiguous bytes of an
+// output row).  No LDS and no barrier.  A workgroup's four waves take four
+// consecutive 64-feature slices of the same token block.
 template <bool GELU>
 __global__ __launch_bounds__(256) void tpad_kernel(
     const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
     const int64_t* __restrict__ blk_row, const int32_t* __restrict__ blk_n,
     int C, int64_t Kt, uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[kTile][kTp];
-  const int c0 = blockIdx.x * kTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int a = lane >> 3, b = lane & 7;
   const int64_t kb = blockIdx.y;
-  const int64_t k0 = kb * kTile;
   const int64_t row0 = blk_row[kb];
   const int n = blk_n[kb];
-  const int ch = threadIdx.x & 7, jr = threadIdx.x >> 3;
+  const int cc = blockIdx.x * (4 * kTile) + wave * kTile + 8 * b;
+  if (cc >= C) return;
+  uint32_t w[8][4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = jr + 32 * h;
-    const int cc = c0 + 8 * ch;
+  for (int t = 0; t < 8; ++t) {
+    const int j = 8 * a + t;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < n && cc < C) {
+    if (j < n) {
       const int64_t r = row0 + j;
       const int64_t sr = row_index ? row_index[r] : r;
       v = *reinterpret_cast<const uint4*>(src + sr * C + cc);
@@ -153,16 +160,21 @@ __global__ __launch_bounds__(256) void tpad_kernel(
         v.w = pack_bf16x2(gelu_fwd(f[6]), gelu_fwd(f[7]));
       }
     }
-    tile_store_t(t, j, 8 * ch, v);
+    w[t][0] = v.x; w[t][1] = v.y; w[t][2] = v.z; w[t][3] = v.w;
   }
-  __syncthreads();
+  // Output row cc + i holds tokens 8a .. 8a + 7: dword k = (token 2k,
+  // token 2k + 1) of feature i, i.e. half (i % 2) of dword i / 2 of the
+  // loads of tokens 2k and 2k + 1.
+  const int64_t k0 = kb * kTile + 8 * a;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = jr + 32 * h;
-    const int cc = c0 + c;
-    if (cc < C)
-      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(cc) * Kt + k0 + 8 * ch) =
-          *reinterpret_cast<const uint4*>(&t[c][8 * ch]);
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(w[1][i / 2], w[0][i / 2], sel);
+    o.y = __builtin_amdgcn_perm(w[3][i / 2], w[2][i / 2], sel);
+    o.z = __builtin_amdgcn_perm(w[5][i / 2], w[4][i / 2], sel);
+    o.w = __builtin_amdgcn_perm(w[7][i / 2], w[6][i / 2], sel);
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(cc + i) * Kt + k0) = o;
   }
 }
 
@@ -486,7 +498,7 @@ hipError_t launch_tpad(const void* src, const int32_t* row_index,
                        hipStream_t stream) {
   if (total == 0) return hipSuccess;
   const int64_t Kt = padded_columns(total, G);
-  const dim3 grid(static_cast<unsigned>(ceil_div(C, kTile)),
+  const dim3 grid(static_cast<unsigned>(ceil_div(C, 4 * kTile)),
                   static_cast<unsigned>(Kt / kTile));
   if (gelu)
     hipLaunchKernelGGL(tpad_kernel<true>, grid, dim3(256), 0, stream,
