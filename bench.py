@@ -46,6 +46,10 @@ def parse():
                     help="instead of the layer, time the routing histogram "
                          "(counts by patch position and by image tag) on the "
                          "layer's routing")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager calls instead of replays of "
+                         "one captured HIP graph (the default; per-call "
+                         "times always come from an eager pass)")
     ap.add_argument("--recompute-u", action="store_true",
                     help="with --backward: the forward keeps no "
                          "pre-activations and the backward recomputes them")
@@ -409,6 +413,25 @@ def main():
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / K
+    if not args.eager:
+        # the same step captured once, then K replays on the same stream
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / K
     per_call = {}
     for i, (name, _) in enumerate(steps):
         per_call[name] = sum(evs[k][i].elapsed_time(evs[k][i + 1])
@@ -464,7 +487,8 @@ def main():
                                f"B={cfg.B} images x T={cfg.T} tokens, D={cfg.D}, "
                                f"E={cfg.E}, K={cfg.K}, n_s={cfg.n_s}, H={cfg.H}, "
                                f"{cfg.route} routing",
-                   "tokens": N, "gather_rows_in_gemm": gather},
+                   "tokens": N, "gather_rows_in_gemm": gather,
+                   "launch": "eager" if args.eager else "hip_graph"},
         "layer_tflops": round(layer_tflops, 1),
         "layer_frac_mfma_peak": round(layer_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "expert_gemm_tflops": round(gemm_tflops, 1),

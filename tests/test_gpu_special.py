@@ -100,3 +100,56 @@ def test_empty_layer():
     g = gl.result()
     assert g["expert_counts"].sum() == 0 and np.all(g["offsets"] == 0)
     assert g["loss"] == 0.0
+
+
+@pytest.mark.parametrize("route,save_u", [("topk", False), ("race", False),
+                                          ("topk", True)])
+def test_layer_in_hip_graph(route, save_u):
+    """The whole forward (and, for bf16 top-K, the backward) captured in one
+    HIP graph and replayed three times, with eager work and synchronisation
+    between the replays: every replay gives the eager pass's bits (no call
+    allocates, synchronises or clears memory with hipMemsetAsync)."""
+    from sparse_moe_diffusion_amd import layer
+    cfg = synth.small_config(B=2, T=96, D=128, H=256, E=8, K=2, n_s=2,
+                             route=route, seed=61)
+    inp = synth.make_inputs(cfg)
+    gl = GpuLayer(inp, gather=True, save_u=save_u)
+    backward = route == "topk"
+    dy = torch.randn(cfg.N, cfg.D, device="cuda",
+                     generator=torch.Generator(device="cuda").manual_seed(3)
+                     ).to(torch.bfloat16)
+    grads = layer.BackwardBuffers(cfg) if backward else None
+
+    def step():
+        layer.forward(cfg, gl.x, gl.w, gl.buf)
+        if backward:
+            layer.backward(cfg, gl.x, gl.w, gl.buf, grads, dy, 1.0)
+
+    names = ["probs", "topk_idx", "topk_w", "slot_row", "y", "bal_psum", "loss"]
+    gnames = ["dx", "dw1", "dw2", "dw_gate"] if backward else []
+
+    def snapshot():
+        torch.cuda.synchronize()
+        out = [getattr(gl.buf, n).clone() for n in names]
+        out += [getattr(grads, n).clone() for n in gnames]
+        return out
+
+    step()
+    ref = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in [getattr(gl.buf, n) for n in names]:
+            t.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot()
+        for n, a, b in zip(names + gnames, ref, got):
+            assert torch.equal(a, b), (rep, n)
