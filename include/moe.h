@@ -334,7 +334,7 @@ moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
  *
  * Training ("Scaling Diffusion Transformers to 16 Billion Parameters",
  * MoE-DiT: the layer is trained with the expert-level balance loss added to
- * the task loss).  The three calls below give the gradients of
+ * the denoising loss).  The three calls below give the gradients of
  *
  *   Loss = <dy, y> + dloss * L_balance
  *

@@ -1,8 +1,8 @@
 // Backward of the DiT-MoE layer: everything except the expert GEMMs.
 //
 // "Scaling Diffusion Transformers to 16 Billion Parameters", MoE-DiT: the
-// layer is trained with the expert-level balance loss added to the task
-// loss.  The gradients are those of the forward definitions (eq. MoE(x),
+// layer is trained with the expert-level balance loss added to the
+// denoising loss.  The gradients are those of the forward definitions (eq. MoE(x),
 // eq. MLP, eq. L_balance, the gate softmax of the "DiT-MoE" project hub
 // page, section 1) with the routing held fixed: the selection itself has no
 // gradient, the slot weights (gate probabilities) do.
