@@ -13,10 +13,11 @@
 //    logits from VALU fp64 FMAs.  Both leave 64 tokens' logits in LDS after
 //    a fixed-order sum over 4 waves, and wave 0 runs the fp32 softmax and the
 //    top-K selection in registers, one token per lane (ties: lower index).
-//  * race_select_kernel: one 1024-thread workgroup finds the exact K*N-th
-//    largest probability key by an MSB-first radix select (4 passes of 8
-//    bits, per-wave LDS histograms) and the flat index of the last kept
-//    entry among keys equal to it.
+//  * race_hist_kernel / race_digit_kernel / race_cut_kernel: the exact
+//    K*N-th largest probability key by an MSB-first radix select (4 passes
+//    of 8 bits; each pass a histogram over 256 workgroups and a one-
+//    workgroup digit choice), then the flat index of the last kept entry
+//    among keys equal to it.
 //  * race_emit_kernel: one thread per token writes its kept experts in
 //    ascending order.
 #include <atomic>
@@ -500,61 +501,147 @@ __device__ __forceinline__ uint32_t race_key(float p) {
   return (p > 0.0f) ? __float_as_uint(p) : 0u;
 }
 
-// out[0] = threshold key tau, out[1] = flat index of the last kept entry
-// whose key equals tau.  Entries with key > tau, or key == tau and flat
-// index <= out[1], are kept: exactly A of them.
-__global__ __launch_bounds__(kRaceThreads) void race_select_kernel(
-    const float* __restrict__ probs, int64_t total, int64_t A,
-    uint32_t* __restrict__ out) {
-  __shared__ uint32_t hist[kRaceWaves][256];
+// The global top-A of the N*E probabilities as a threshold: tau (a key)
+// and the flat index `cut` of the last kept entry equal to tau.  Entries
+// with key > tau, or key == tau and flat index <= cut, are kept: exactly A.
+//
+// Four 8-bit radix passes, most significant digit first.  Each pass is two
+// launches: race_hist_kernel, where kRaceBlocks workgroups each count the
+// digits of their slice of the keys that still match the prefix in an LDS
+// histogram and write it out, and race_digit_kernel, where one workgroup
+// adds the kRaceBlocks histograms bin by bin in workgroup order (integer
+// counts: exact in any order) and narrows the prefix.  The state after pass
+// p (prefix, mask, how many of the matching entries are still needed) is
+// RaceState p + 1 in the workspace; the state before pass 0 (no prefix,
+// A needed) is implicit.  Probabilities share their sign and high
+// exponent bits, so in the first pass most keys of a wave fall in a few
+// bins: the wave counts each distinct digit with one ballot and one LDS
+// atomic instead of 64 colliding atomics.
+constexpr int kRaceBlocks = 256;
+constexpr int kRaceHistThreads = 256;
+static_assert(kRaceBlocks % 64 == 0, "whole batches of 16 per quarter");
+
+struct RaceState {
+  uint32_t prefix, mask, need, all;
+};
+
+size_t race_hist_offset() { return 256; }   // RaceState[5] first
+
+__global__ __launch_bounds__(kRaceHistThreads) void race_hist_kernel(
+    const float* __restrict__ probs, int64_t total, int pass,
+    const RaceState* __restrict__ st, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[256];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  h[tid] = 0;
+  __syncthreads();
+  // pass 0 matches every key (st[0] is never written)
+  const uint32_t prefix = pass == 0 ? 0u : st[pass].prefix;
+  const uint32_t mask = pass == 0 ? 0u : st[pass].mask;
+  const int shift = 24 - 8 * pass;
+  const int64_t per = (total + kRaceBlocks - 1) / kRaceBlocks;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t b1 = min(total, b0 + per);
+  for (int64_t i0 = b0; i0 < b1; i0 += kRaceHistThreads) {
+    const int64_t i = i0 + tid;
+    const uint32_t k = i < b1 ? race_key(probs[i]) : 0u;
+    bool live = i < b1 && (k & mask) == prefix;
+    const uint32_t d = (k >> shift) & 255u;
+    if (pass == 0) {
+      // one round per distinct digit among the wave's live lanes
+      uint64_t left = __ballot(live);
+      while (left != 0) {
+        const int leader = __builtin_ctzll(left);
+        const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+        const uint64_t same = __ballot(live && d == dl);
+        if (lane == leader) atomicAdd(&h[dl], static_cast<uint32_t>(__popcll(same)));
+        if (d == dl) live = false;
+        left = __ballot(live);
+      }
+    } else if (live) {
+      atomicAdd(&h[d], 1u);
+    }
+  }
+  __syncthreads();
+  hist[static_cast<int64_t>(blockIdx.x) * 256 + tid] = h[tid];
+}
+
+// One workgroup: the pass's digit.  Thread (q, d) adds bin d over the
+// q-th quarter of the histogram workgroups (16 loads in flight), the four
+// quarter sums are added in order, and thread 0 walks the digits from the
+// top.
+__global__ __launch_bounds__(1024) void race_digit_kernel(
+    const uint32_t* __restrict__ hist, int pass, uint32_t a_first,
+    RaceState* __restrict__ st) {
+  __shared__ uint32_t part[4][256];
   __shared__ uint32_t tot[256];
-  __shared__ uint32_t s_prefix, s_mask, s_need;
+  const int tid = threadIdx.x;
+  const int d = tid & 255, q = tid >> 8;
+  constexpr int kQuarter = kRaceBlocks / 4;
+  uint32_t c = 0;
+  for (int b0 = q * kQuarter; b0 < (q + 1) * kQuarter; b0 += 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = hist[static_cast<int64_t>(b0 + u) * 256 + d];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c += v[u];
+  }
+  part[q][d] = c;
+  __syncthreads();
+  // above[d] = entries in bins above d (a suffix sum: 8 doubling steps)
+  __shared__ uint32_t above[2][256];
+  if (tid < 256) {
+    tot[tid] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    above[0][tid] = tot[tid];
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int h = 1; h < 256; h *= 2) {
+    if (tid < 256)
+      above[cur ^ 1][tid] = above[cur][tid] + (tid + h < 256 ? above[cur][tid + h] : 0u);
+    __syncthreads();
+    cur ^= 1;
+  }
+  if (tid < 256) {
+    // inclusive suffix sum -> exclusive
+    const uint32_t ab = above[cur][tid] - tot[tid];
+    const RaceState in = pass == 0 ? RaceState{0u, 0u, a_first, 0u} : st[pass];
+    // The bins' ranges [ab, ab + tot) partition the matching entries from
+    // the top: exactly one digit holds the need-th (bin 0 takes the
+    // remainder if the counts fall short, as the serial walk would).
+    const bool hit = ab < in.need && (ab + tot[tid] >= in.need || tid == 0);
+    if (hit) {
+      const int shift = 24 - 8 * pass;
+      RaceState out;
+      out.prefix = in.prefix | (static_cast<uint32_t>(tid) << shift);
+      out.mask = in.mask | (255u << shift);
+      out.need = in.need - ab;
+      // after the last pass tot[digit] counts the entries equal to tau
+      out.all = (pass == 3 && out.need == tot[tid]) ? 1u : 0u;
+      st[pass + 1] = out;
+    }
+  }
+}
+
+// sel[0] = tau, sel[1] = cut.  When every entry equal to tau is kept (no
+// tie straddles the cut: the usual case) cut is the last flat index;
+// otherwise one workgroup finds the need-th entry equal to tau in flat
+// order, in tiles of 1024 entries.
+__global__ __launch_bounds__(kRaceThreads) void race_cut_kernel(
+    const float* __restrict__ probs, int64_t total,
+    const RaceState* __restrict__ st4, uint32_t* __restrict__ sel) {
   __shared__ uint32_t wcnt[kRaceWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  if (tid == 0) {
-    s_prefix = 0;
-    s_mask = 0;
-    s_need = static_cast<uint32_t>(A);
-  }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kRaceWaves * 256; i += kRaceThreads)
-      (&hist[0][0])[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int64_t i = tid; i < total; i += kRaceThreads) {
-      const uint32_t k = race_key(probs[i]);
-      if ((k & mask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-      for (int w = 0; w < kRaceWaves; ++w) c += hist[w][tid];
-      tot[tid] = c;
-    }
-    __syncthreads();
+  const uint32_t tau = st4->prefix;
+  const uint32_t need = st4->need;
+  if (st4->all != 0) {
     if (tid == 0) {
-      uint32_t need = s_need, above = 0;
-      int digit = 0;
-      for (int d = 255; d >= 0; --d) {
-        if (above + tot[d] >= need) {
-          digit = d;
-          break;
-        }
-        above += tot[d];
-      }
-      s_need = need - above;
-      s_prefix = prefix | (static_cast<uint32_t>(digit) << shift);
-      s_mask = mask | (255u << shift);
+      sel[0] = tau;
+      sel[1] = static_cast<uint32_t>(total - 1);
     }
-    __syncthreads();
+    return;
   }
-  // The s_need-th (1-based) entry equal to tau in flat order is the last
-  // one kept.  Walk the keys in tiles of 1024 flat entries.
-  const uint32_t tau = s_prefix;
-  const uint32_t need = s_need;
   uint32_t running = 0;
   for (int64_t base = 0; base < total; base += kRaceThreads) {
     const int64_t i = base + tid;
@@ -570,8 +657,8 @@ __global__ __launch_bounds__(kRaceThreads) void race_select_kernel(
     if (running + tile >= need) {
       const uint32_t rank = running + before + lanes_below(bal);
       if (eq && rank + 1 == need) {
-        out[0] = tau;
-        out[1] = static_cast<uint32_t>(i);
+        sel[0] = tau;
+        sel[1] = static_cast<uint32_t>(i);
       }
       return;
     }
@@ -663,16 +750,37 @@ hipError_t launch_gate_balance_partials(const void* x, const float* w_gate,
                                          probs, idx, w, bal_p, bal_c, stream);
 }
 
-size_t race_workspace_bytes() { return 256; }
+// [0, 80): RaceState[5]; [96, 104): sel; [256, ...): 4 passes of
+// kRaceBlocks x 256 histogram words.
+size_t race_workspace_bytes() {
+  return race_hist_offset() + static_cast<size_t>(4) * kRaceBlocks * 256 * 4;
+}
 
 hipError_t launch_race(const float* probs, int64_t N, int E, int K,
                        int32_t* idx, float* w, void* workspace,
                        hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  uint32_t* sel = static_cast<uint32_t*>(workspace);
-  hipLaunchKernelGGL(race_select_kernel, dim3(1), dim3(kRaceThreads), 0,
-                     stream, probs, N * E, static_cast<int64_t>(K) * N, sel);
-  hipError_t err = hipGetLastError();
+  char* ws = static_cast<char*>(workspace);
+  RaceState* st = reinterpret_cast<RaceState*>(ws);
+  uint32_t* sel = reinterpret_cast<uint32_t*>(ws + 96);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + race_hist_offset());
+  const int64_t total = N * E;
+  hipError_t err;
+  for (int pass = 0; pass < 4; ++pass) {
+    uint32_t* hp = hist + static_cast<size_t>(pass) * kRaceBlocks * 256;
+    hipLaunchKernelGGL(race_hist_kernel, dim3(kRaceBlocks),
+                       dim3(kRaceHistThreads), 0, stream, probs, total, pass,
+                       st, hp);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(race_digit_kernel, dim3(1), dim3(1024), 0, stream, hp,
+                       pass, static_cast<uint32_t>(K * N), st);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(race_cut_kernel, dim3(1), dim3(kRaceThreads), 0, stream,
+                     probs, total, st + 4, sel);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(race_emit_kernel,
                      dim3(static_cast<unsigned>(ceil_div(N, 256))), dim3(256),
