@@ -30,31 +30,53 @@ __global__ __launch_bounds__(kSeqThreads) void balance_seq_kernel(
     int E, int Kmax, int32_t* __restrict__ counts, float* __restrict__ psum) {
   __shared__ float sp[kSeqThreads];
   __shared__ int32_t sc[kSeqThreads];
+  // Each chunk of kSeqThreads tokens: every thread first turns one token's
+  // Kmax slots into a bit mask of its experts, so the (r, e) threads read
+  // a mask per token instead of Kmax slots.
+  __shared__ uint64_t tmask[kSeqThreads];
   const int R = kSeqThreads / E;
   const int r = threadIdx.x / E;
   const int e = threadIdx.x - r * E;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * T;
   float p = 0.0f;
   int32_t c = 0;
-  if (r < R) {
-    // tokens r, r + R, ...; unrolled so that several loads are in flight
-    int t = r;
-    for (; t + 3 * R < T; t += 4 * R) {
-      float q[4];
+  // Token t of the image is summed by thread (t % R, e), in ascending t:
+  // chunks of R * (kSeqThreads / R) tokens keep that order.
+  const int chunk = R * (kSeqThreads / R);
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    {
+      const int t = c0 + static_cast<int>(threadIdx.x);
+      uint64_t m = 0;
+      if (threadIdx.x < chunk && t < T) {
+        const int32_t* s = idx + (t0 + t) * Kmax;
+        for (int k = 0; k < Kmax; ++k) {
+          const int v = s[k];
+          if (v >= 0 && v < 64) m |= 1ull << v;
+        }
+      }
+      tmask[threadIdx.x] = m;
+    }
+    __syncthreads();
+    if (r < R) {
+      const int c1 = min(T, c0 + chunk);
+      // tokens c0 + r, c0 + r + R, ...; four loads in flight
+      int t = c0 + r;
+      for (; t + 3 * R < c1; t += 4 * R) {
+        float q[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = probs[(t0 + t + u * R) * E + e];
+        for (int u = 0; u < 4; ++u) q[u] = probs[(t0 + t + u * R) * E + e];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p += q[u];
-        const int64_t tt = t0 + t + u * R;
-        for (int k = 0; k < Kmax; ++k) c += (idx[tt * Kmax + k] == e) ? 1 : 0;
+        for (int u = 0; u < 4; ++u) {
+          p += q[u];
+          c += static_cast<int32_t>((tmask[t + u * R - c0] >> e) & 1ull);
+        }
+      }
+      for (; t < c1; t += R) {
+        p += probs[(t0 + t) * E + e];
+        c += static_cast<int32_t>((tmask[t - c0] >> e) & 1ull);
       }
     }
-    for (; t < T; t += R) {
-      const int64_t tt = t0 + t;
-      p += probs[tt * E + e];
-      for (int k = 0; k < Kmax; ++k) c += (idx[tt * Kmax + k] == e) ? 1 : 0;
-    }
+    __syncthreads();
   }
   sp[threadIdx.x] = p;
   sc[threadIdx.x] = c;

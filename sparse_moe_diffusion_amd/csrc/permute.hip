@@ -13,11 +13,11 @@
 //  2. permute_scan_kernel: one 1024-thread workgroup scans the block counts
 //     (chunks of blocks x experts, then a scan over chunks and experts):
 //     expert counts, exclusive offsets and block bases.
-//  3. permute_scatter_kernel: repeats the ballots, so a selection's row is
-//     block base + earlier waves' count + set lanes below it; writes slot_row
-//     and row_token, then copies each token row once from HBM to its K
-//     destination rows with 16-byte lanes (row copy skipped when x_perm is
-//     null).
+//  3. permute_scatter_kernel: repeats the ballots (one per expert), so a
+//     selection's row is block base + earlier waves' count + set lanes below
+//     it; writes row_token, the block's slot_row (coalesced, from LDS), then
+//     copies each token row once from HBM to its K destination rows with
+//     16-byte lanes (row copy skipped when x_perm is null).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -128,27 +128,34 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
   }
   __syncthreads();
   const int64_t* base = block_base + static_cast<int64_t>(blockIdx.x) * E;
+  // The token's slots, then one ballot per expert (taken by the whole
+  // wave): a lane holding expert ee finds its rank and writes it into the
+  // slot that names ee.  Slots naming no valid expert keep -1.
+  int32_t* const my = s_rows + threadIdx.x * Kmax;
   for (int k = 0; k < Kmax; ++k) {
-    const int e = valid ? idx[t * Kmax + k] : -1;
-    int32_t row = -1;
-    // The ballot for expert e must be taken by the whole wave: loop over
-    // every expert and keep the rank of the one this slot names.
-    for (int ee = 0; ee < E; ++ee) {
-      const uint64_t b = __ballot((m >> ee) & 1ull);
-      if (ee == e) {
-        int64_t r = base[ee] + lanes_below(b);
-        for (int w = 0; w < wave; ++w) r += wc[w][ee];
-        row = (r < A) ? static_cast<int32_t>(r) : -1;
-      }
-    }
-    if (valid) {
-      slot_row[t * Kmax + k] = row;
+    const int v = valid ? idx[t * Kmax + k] : -1;
+    my[k] = (v >= 0 && v < E) ? v : -1;   // contents outside [0, E): empty
+  }
+  for (int ee = 0; ee < E; ++ee) {
+    const bool has = (m >> ee) & 1ull;
+    const uint64_t b = __ballot(has);
+    if (has) {
+      int64_t r = base[ee] + lanes_below(b);
+      for (int w = 0; w < wave; ++w) r += wc[w][ee];
+      const int32_t row = (r < A) ? static_cast<int32_t>(r) : -1;
+      for (int k = 0; k < Kmax; ++k)
+        if (my[k] == ee) my[k] = -2 - row;   // marked: no longer an expert
       if (row >= 0) row_token[row] = static_cast<int32_t>(t);
     }
-    s_rows[threadIdx.x * Kmax + k] = row;
   }
-  if (x_perm == nullptr) return;
+  // Marked slots hold -2 - row; the rest (empty or invalid) become -1.
+  for (int k = 0; k < Kmax; ++k) my[k] = my[k] <= -2 ? -2 - my[k] : -1;
   __syncthreads();
+  // slot_row of the block's tokens, coalesced.
+  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
+  for (int i = threadIdx.x; i < ntok * Kmax; i += kPermTokens)
+    slot_row[t0 * Kmax + i] = s_rows[i];
+  if (x_perm == nullptr) return;
 
   // Row copy: each wave takes tokens wave, wave+4, ...; lanes cover the row
   // in VEC_BYTES pieces.
@@ -157,7 +164,6 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
   const int nvec = row_bytes / VEC_BYTES;
   const char* xb = static_cast<const char*>(x);
   char* pb = static_cast<char*>(x_perm);
-  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
   for (int tl = wave; tl < ntok; tl += kPermWaves) {
     const vec_t* src = reinterpret_cast<const vec_t*>(xb + (t0 + tl) * row_bytes);
     for (int c = lane; c < nvec; c += kWave) {
