@@ -1372,33 +1372,25 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
     if (uu == nullptr) {
       GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
                     G, H, D};
-      hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
-          dim3(persistent_grid(tile_grid(pu, kUpBM, kUpBN))),
-          dim3(64 * kUpWT * kUpWF), 0, stream, pu);
+      launch_stage<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
+          pu, stream);
       MOE_TRY(hipGetLastError());
       uu = u;
     }
     GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
                   a.total_rows, G, H, D};
     pd.aux = uu;
-    hipLaunchKernelGGL(
-        (gemm_bf16_kernel<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>),
-        dim3(persistent_grid(tile_grid(pd, kUpBM, kUpBN))),
-        dim3(64 * kUpWT * kUpWF), 0, stream, pd);
+    launch_stage<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
+        pd, stream);
     MOE_TRY(hipGetLastError());
     GemmParams px{du, nullptr, w1t, nullptr, a.dx_rows, a.offsets,
                   a.total_rows, G, D, H};
     if (a.dx_f32)
-      hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
-          dim3(persistent_grid(tile_grid(px, kDnBM, kDnBN))),
-          dim3(64 * kDnWT * kDnWF), 0, stream, px);
+      launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+          px, stream);
     else
-      hipLaunchKernelGGL(
-          (gemm_bf16_kernel<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>),
-          dim3(persistent_grid(tile_grid(px, kDnBM, kDnBN))),
-          dim3(64 * kDnWT * kDnWF), 0, stream, px);
+      launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+          px, stream);
     MOE_TRY(hipGetLastError());
     MOE_TRY(launch_kseg(a.offsets, G, a.total_rows, brow, bn, stream));
     MOE_TRY(launch_tpad(a.dy_rows, nullptr, brow, bn, G, a.total_rows, D, false, dyT, stream));
