@@ -362,10 +362,10 @@ __global__ __launch_bounds__(256) void gate_bwd_dx_kernel(
 }
 
 // Workgroup = kGbTokens tokens; their dl rows are staged in LDS.  Thread =
-// 8 consecutive features (chunk c); for experts in blocks of 8 it sums, over
+// one (8 consecutive features c, block of 8 experts) pair: it sums, over
 // the chunk's tokens, dl[t][i] x[t][c..c+8], loading kGbBatch x rows ahead,
-// and writes the chunk's partial [E][D].  Threads i < E also sum dl over
-// the chunk (the dbias partial).
+// and writes its part of the chunk's partial [E][D].  Threads i < E also sum
+// dl over the chunk (the dbias partial).
 template <bool XB>
 __global__ __launch_bounds__(256) void gate_bwd_wgrad_kernel(
     const void* __restrict__ x, const float* __restrict__ dl, int64_t N, int D,
@@ -377,9 +377,12 @@ __global__ __launch_bounds__(256) void gate_bwd_wgrad_kernel(
     sdl[i / E][i % E] = dl[t0 * E + i];
   __syncthreads();
   const int nch = D / 8;
+  const int neb = (E + 7) / 8;
   float* pw = part_w + static_cast<int64_t>(blockIdx.x) * E * D;
-  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
-    for (int e0 = 0; e0 < E; e0 += 8) {
+  for (int pr = threadIdx.x; pr < nch * neb; pr += blockDim.x) {
+    const int c = pr % nch;
+    {
+      const int e0 = 8 * (pr / nch);
       float acc[8][8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -566,7 +569,7 @@ hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
     // dW_g / dbias partials: threads = the feature chunks rounded up to
     // whole waves, at most 256
     const int nch = D / 8;
-    const int wthreads = min(256, (nch + 63) / 64 * 64);
+    const int wthreads = min(256, (nch * ((E + 7) / 8) + 63) / 64 * 64);
     if (x_bf16)
       hipLaunchKernelGGL(gate_bwd_wgrad_kernel<true>,
                          dim3(static_cast<unsigned>(chunks)), dim3(wthreads), 0,

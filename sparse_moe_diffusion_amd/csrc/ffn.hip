@@ -33,6 +33,7 @@
 // XCD walk chunks of consecutive tiles; within a group, tiles go in bands of
 // GM row-tiles, feature-tile major, so tiles running at once share both
 // their token rows and their weight rows in the XCD's L2.
+#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -73,6 +74,10 @@ struct GemmParams {
   // B[:, seg g]^T, A [mrows][ld] and B [Nd][ld] bf16, seg g = group g's
   // token columns, padded to 64 (see the transposes).
   int ld, mrows;
+  // K-grouped form split over the reduction: each group's segment is cut
+  // into ksplit pieces (multiples of 64 columns) whose products go to
+  // separate fp32 partials, C [ksplit][G][mrows][Nd] (0 or 1: no split).
+  int ksplit;
   // kEpiGelu with bf16 output: if set, also the pre-activations u = A W^T
   // + bias, [total][Nd] bf16 (kept by a training forward for the backward).
   void* u_out;
@@ -259,8 +264,9 @@ __device__ __forceinline__ void build_kseg_table(const GemmParams& p,
   __syncthreads();
 }
 
-// Tile L of a K-grouped launch: group g = L / (row tiles x feature tiles),
-// bands of GM row tiles within it.  Output rows are g * mrows + row.
+// Tile L of a K-grouped launch: virtual group v = L / (row tiles x feature
+// tiles) is split v / G of group g = v % G, bands of GM row tiles within
+// it.  Output rows are v * mrows + row (the split's partial).
 template <int BM, int BN, int GM>
 __device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
                                                const int32_t* tab, int L,
@@ -268,20 +274,27 @@ __device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
   const int mt = (p.mrows + BM - 1) / BM;
   const int ntn = (p.Nd + BN - 1) / BN;
   const int per = mt * ntn;
-  if (L >= p.G * per) return false;
-  const int g = L / per;
-  const int Lg = L - g * per;
+  const int S = p.ksplit > 1 ? p.ksplit : 1;
+  if (L >= S * p.G * per) return false;
+  const int v = L / per;
+  const int g = v % p.G, sp = v / p.G;
+  const int Lg = L - v * per;
   const int band = Lg / (GM * ntn);
   const int rem = Lg - band * GM * ntn;
   const int m_first = band * GM;
   const int gm = min(GM, mt - m_first);
-  const int64_t base = static_cast<int64_t>(g) * p.mrows;
-  loc.g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t base = static_cast<int64_t>(v) * p.mrows;
+  loc.g = __builtin_amdgcn_readfirstlane(v);
   loc.row0 = uniform64(base + static_cast<int64_t>(m_first + rem % gm) * BM);
   loc.row_end = uniform64(base + p.mrows);
   loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
-  loc.kofs = __builtin_amdgcn_readfirstlane(tab[g]);
-  loc.klen = __builtin_amdgcn_readfirstlane(tab[kTabCol + g]);
+  // the split's piece of the group's segment (its length a multiple of 64,
+  // possibly empty: the partial is then zero)
+  const int kofs = __builtin_amdgcn_readfirstlane(tab[g]);
+  const int klen = __builtin_amdgcn_readfirstlane(tab[kTabCol + g]);
+  const int cs = (klen / 64 + S - 1) / S * 64;
+  loc.kofs = kofs + sp * cs;
+  loc.klen = max(0, min(cs, klen - sp * cs));
   return true;
 }
 
@@ -1306,8 +1319,43 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Reduction splits of the K-grouped weight-gradient GEMMs ([G][M][N] out,
+// 256 x 256 tiles, `total` token rows over G groups): the largest S <= 8
+// whose S x tiles still fit one round of the chip (assumed 256 CUs, so the
+// choice and the workspace depend on the shape alone) and whose pieces keep
+// at least 2048 tokens of an average group.  Measured: the shared experts'
+// weight gradients of the S layer (24 tiles, 8192 tokens) take 0.28 instead
+// of 0.46 ms per backward call with S = 4; splits past one round, or into
+// short pieces, were slower (a tile's fixed cost is several k stages, and
+// fewer busy CUs run at a higher clock).
+int choose_ksplit(int G, int M, int N, int64_t total) {
+  const int64_t tiles = static_cast<int64_t>(G) * ((M + kUpBM - 1) / kUpBM) *
+                        ((N + kUpBN - 1) / kUpBN);
+  constexpr int64_t kCus = 256, kMinTokens = 2048;
+  const int64_t per_group = G > 0 ? total / G : 0;
+  int S = 1;
+  while (S < 8 && tiles * (S + 1) <= kCus && per_group / (S + 1) >= kMinTokens)
+    ++S;
+  return S;
+}
+
+// out[i] = part[0][i] + part[1][i] + ... in split order (same bits every
+// call), four floats per thread.
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(
+    const float4* __restrict__ part, int S, int64_t n4, float4* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 a = part[i];
+    for (int s = 1; s < S; ++s) {
+      const float4 b = part[static_cast<int64_t>(s) * n4 + i];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    out[i] = a;
+  }
+}
+
 struct BwdLayout {
-  size_t u, du, w1t, w2t, dyT, aT, duT, xT, brow, bn, total;
+  size_t u, du, w1t, w2t, dyT, aT, duT, xT, brow, bn, part, total;
 };
 
 BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
@@ -1325,6 +1373,8 @@ BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
   L.xT = take(static_cast<size_t>(D) * Kt * 2);
   L.brow = take(static_cast<size_t>(Kt / 64) * 8);
   L.bn = take(static_cast<size_t>(Kt / 64) * 4);
+  const int S = choose_ksplit(G, D, H, total);
+  L.part = take(S > 1 ? static_cast<size_t>(S) * G * D * H * 4 : 0);
   L.total = o;
   return L;
 }
@@ -1404,24 +1454,47 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   }
   // dW2[g] [D][H] = dyT[:, seg g] aT[:, seg g]^T;  dW1[g] [H][D] = duT xT^T.
   // With no rows every segment is empty and the products are zero.
-  GemmParams pw2{dyT, nullptr, aT, nullptr, a.dw2, a.offsets, a.total_rows,
-                 G, H, 0};
+  // When the tiles would not fill the chip, the reduction is split and the
+  // partials are added in split order afterwards.
+  const int S = choose_ksplit(G, D, H, a.total_rows);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const int64_t n4 = static_cast<int64_t>(G) * D * H / 4;
+  const unsigned rgrid =
+      static_cast<unsigned>(std::min<int64_t>((n4 + 255) / 256, 4096));
+  GemmParams pw2{dyT, nullptr, aT, nullptr, S > 1 ? part : a.dw2, a.offsets,
+                 a.total_rows, G, H, 0};
   pw2.ld = static_cast<int>(Kt);
   pw2.mrows = D;
-  const int tiles2 = G * ((D + kUpBM - 1) / kUpBM) * ((H + kUpBN - 1) / kUpBN);
+  pw2.ksplit = S;
+  const int tiles2 =
+      S * G * ((D + kUpBM - 1) / kUpBM) * ((H + kUpBN - 1) / kUpBN);
   hipLaunchKernelGGL(
       (gemm_bf16_kernel<kEpiStore, false, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false, true>),
       dim3(persistent_grid(tiles2)), dim3(64 * kUpWT * kUpWF), 0, stream, pw2);
   MOE_TRY(hipGetLastError());
-  GemmParams pw1{duT, nullptr, xT, nullptr, a.dw1, a.offsets, a.total_rows,
-                 G, D, 0};
+  if (S > 1) {
+    hipLaunchKernelGGL(ksplit_reduce_kernel, dim3(rgrid), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(part), S, n4,
+                       reinterpret_cast<float4*>(a.dw2));
+    MOE_TRY(hipGetLastError());
+  }
+  GemmParams pw1{duT, nullptr, xT, nullptr, S > 1 ? part : a.dw1, a.offsets,
+                 a.total_rows, G, D, 0};
   pw1.ld = static_cast<int>(Kt);
   pw1.mrows = H;
-  const int tiles1 = G * ((H + kUpBM - 1) / kUpBM) * ((D + kUpBN - 1) / kUpBN);
+  pw1.ksplit = S;
+  const int tiles1 =
+      S * G * ((H + kUpBM - 1) / kUpBM) * ((D + kUpBN - 1) / kUpBN);
   hipLaunchKernelGGL(
       (gemm_bf16_kernel<kEpiStore, false, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false, true>),
       dim3(persistent_grid(tiles1)), dim3(64 * kUpWT * kUpWF), 0, stream, pw1);
   MOE_TRY(hipGetLastError());
+  if (S > 1) {
+    hipLaunchKernelGGL(ksplit_reduce_kernel, dim3(rgrid), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(part), S, n4,
+                       reinterpret_cast<float4*>(a.dw1));
+    MOE_TRY(hipGetLastError());
+  }
 #undef MOE_TRY
   return hipSuccess;
 }

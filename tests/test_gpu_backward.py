@@ -62,7 +62,12 @@ def test_combine_backward(N, D, Kmax, empty):
 
 @pytest.mark.parametrize("sizes,D,H,gather", [
     ([100, 0, 129, 1, 256], 128, 256, False), ([300, 70], 192, 384, True),
-    ([513], 1152, 512, False), ([0, 0, 5], 64, 128, True)])
+    ([513], 1152, 512, False), ([0, 0, 5], 64, 128, True),
+    # 16 x 2 x 8 = 256 tiles, a full round
+    ([120 + 7 * i for i in range(16)], 512, 2048, True),
+    # few weight-gradient tiles over long token segments: the reduction is
+    # split in 4, and in 2 with an empty piece for the short group
+    ([8192], 128, 256, False), ([12000, 64], 128, 256, True)])
 def test_grouped_ffn_backward(sizes, D, H, gather):
     _lib, ops = _ops()
     rng = np.random.default_rng(sum(sizes) + D + H)
