@@ -81,7 +81,10 @@ const char* moe_status_string(moe_status status);
 /* Detail of the last failed call on this host thread ("" if none). */
 const char* moe_last_error(void);
 
-/* Bytes of device workspace moe_gate_topk needs (0 for top-K routing). */
+/* Bytes of device workspace moe_gate_topk needs: 0 for top-K routing; for
+ * Expert Race a fixed ~1 MiB (the radix passes' per-workgroup histograms
+ * and the threshold), whatever N and E.  The contents need no
+ * initialisation. */
 size_t moe_gate_workspace_size(int64_t N, int32_t E, int32_t K, moe_route route);
 
 /*
@@ -387,7 +390,10 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
  *   dy_rows [total_rows][D] bf16;  dx_rows [total_rows][D];
  *   dw1 [G][H][D], dw2 [G][D][H] fp32 out;  workspace of at least
  *   moe_ffn_backward_workspace_size bytes (recomputed activations,
- *   transposed weights, transposed token-padded operands)
+ *   transposed weights, transposed token-padded operands and, when few
+ *   weight-gradient tiles meet long token segments, the fp32 partials of a
+ *   split reduction, added in a fixed order); contents need no
+ *   initialisation
  * Errors: INVALID_ARGUMENT for null pointers or bad sizes;
  *   UNSUPPORTED for non-bf16 inputs, G > 128, D or H not multiples of 8;
  *   WORKSPACE_TOO_SMALL.
