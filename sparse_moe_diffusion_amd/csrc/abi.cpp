@@ -432,7 +432,10 @@ moe_status moe_grouped_ffn_backward(
     return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
                 fn, D, H);
   const int64_t Kt = moe::padded_columns(total_rows, G);
-  if (total_rows >= kI32Limit || Kt * 2 * 256 >= (int64_t(1) << 32))
+  // the token-blocked transposed operands ([max(D, H)][Kt] bf16) are
+  // addressed with 32-bit byte offsets
+  if (total_rows >= kI32Limit ||
+      Kt * static_cast<int64_t>(D > H ? D : H) * 2 >= (int64_t(1) << 32))
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows=%lld too large", fn,
                 (long long)total_rows);
   if (workspace_bytes < moe::ffn_backward_workspace_bytes(total_rows, G, D, H))

@@ -10,9 +10,11 @@
 // Kernels (gfx950):
 //  * transpose_kernel: [G][R][C] -> [G][C][R] bf16 through 64x64 LDS tiles
 //    (transposed copies of the expert weights for the data-gradient GEMMs).
-//  * tpad_kernel: activation rows grouped by expert -> [C][Kt] with group
-//    g's rows in columns [koff_g, koff_g + M_g) and zeros up to the next
-//    multiple of 64 (the operands of the K-grouped weight-gradient GEMM);
+//  * tpad_kernel: activation rows grouped by expert -> a transposed [C][Kt]
+//    operand with group g's rows in columns [koff_g, koff_g + M_g) and
+//    zeros up to the next multiple of 64, stored token-blocked: columns
+//    64j .. 64j + 63 form the contiguous [C][64] slab j (the operands of the
+//    K-grouped weight-gradient GEMM, which reads one slab per k stage);
 //    optional row gather and GELU on the way.
 //  * combine_bwd_kernel: one wave per token; the routed rows' output
 //    gradients w * dy and the slot-weight gradients <dy, y_row>.
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(256) void tpad_kernel(
     const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
     const int64_t* __restrict__ blk_row, const int32_t* __restrict__ blk_n,
     int C, int64_t Kt, uint16_t* __restrict__ dst) {
+  (void)Kt;   // the slabs are addressed by block, not by row pitch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int a = lane >> 3, b = lane & 7;
   const int64_t kb = blockIdx.y;
@@ -164,8 +167,9 @@ __global__ __launch_bounds__(256) void tpad_kernel(
   }
   // Output row cc + i holds tokens 8a .. 8a + 7: dword k = (token 2k,
   // token 2k + 1) of feature i, i.e. half (i % 2) of dword i / 2 of the
-  // loads of tokens 2k and 2k + 1.
-  const int64_t k0 = kb * kTile + 8 * a;
+  // loads of tokens 2k and 2k + 1.  Token block kb is the [C][64] slab
+  // starting at element kb * C * 64.
+  uint16_t* const slab = dst + kb * C * static_cast<int64_t>(kTile) + 8 * a;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(256) void tpad_kernel(
     o.y = __builtin_amdgcn_perm(w[3][i / 2], w[2][i / 2], sel);
     o.z = __builtin_amdgcn_perm(w[5][i / 2], w[4][i / 2], sel);
     o.w = __builtin_amdgcn_perm(w[7][i / 2], w[6][i / 2], sel);
-    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(cc + i) * Kt + k0) = o;
+    *reinterpret_cast<uint4*>(slab + static_cast<int64_t>(cc + i) * kTile) = o;
   }
 }
 

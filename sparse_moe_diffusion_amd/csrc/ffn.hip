@@ -499,16 +499,27 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // Reduction length and operand row pitch of this tile: the group's padded
   // token segment and the transposed operands' pitch in the K-grouped form.
   const int Kd = KG ? loc.klen : Kd0;
-  const uint32_t row_bytes =
-      KG ? static_cast<uint32_t>(p.ld) * 2u : row_bytes0;
+  // The K-grouped operands are token-blocked: token block j (64 columns) of
+  // a [C][Kt] operand is a contiguous [C][64] slab, so rows are 128 bytes
+  // apart and one k stage is one slab further (C x 128 bytes).  The other
+  // forms have k-contiguous rows.
+  const uint32_t row_bytes = KG ? 128u : row_bytes0;
+  const uint32_t kstep_a = KG ? static_cast<uint32_t>(p.mrows) * 128u : kBK * 2u;
+  const uint32_t kstep_b = KG ? static_cast<uint32_t>(p.Nd) * 128u : kBK * 2u;
+  const int64_t kg_m = KG ? loc.row0 - static_cast<int64_t>(loc.g) * p.mrows : 0;
   const uint16_t* a_base =
       static_cast<const uint16_t*>(p.a) +
       (gather ? int64_t(0)
-              : KG ? (loc.row0 - static_cast<int64_t>(loc.g) * p.mrows) * p.ld +
-                         loc.kofs
+              : KG ? (static_cast<int64_t>(loc.kofs / 64) * p.mrows + kg_m) * 64
                    : loc.row0 * Kd);
+  // KG: from the tile's first row to the end of the segment's last slab.
+  // Tile rows past the operand's C read the next slab's rows (finite
+  // values, or zeros past the segment); they only reach output rows and
+  // features that are not stored.
+  const int64_t kg_a = KG ? (static_cast<int64_t>(loc.klen / 64) * p.mrows - kg_m) * 128 : 0;
   const uint32_t a_bytes =
       gather ? kOutOfRange
+      : KG   ? static_cast<uint32_t>(kg_a > 0 ? kg_a : 0)
              : static_cast<uint32_t>(min(static_cast<int>(loc.row_end - loc.row0), BM)) *
                    row_bytes;
   const __amdgpu_buffer_rsrc_t rsA =
@@ -518,10 +529,12 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // Weight rows of group g: features past Nd fall outside the descriptor.
   const uint16_t* w_base =
       static_cast<const uint16_t*>(p.w) +
-      (KG ? static_cast<int64_t>(loc.n0) * p.ld + loc.kofs
+      (KG ? (static_cast<int64_t>(loc.kofs / 64) * p.Nd + loc.n0) * 64
           : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
+  const int64_t kg_w = KG ? (static_cast<int64_t>(loc.klen / 64) * p.Nd - loc.n0) * 128 : 0;
   const uint32_t w_bytes =
-      static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
+      KG ? static_cast<uint32_t>(kg_w > 0 ? kg_w : 0)
+         : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(w_base))),
@@ -596,7 +609,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     const bool full_ = (ikt_ + 1) * kBK <= Kd;                               \
     _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                    \
       const bool isA_ = q < QA;                                              \
-      uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);     \
+      uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (isA_ ? kstep_a : kstep_b); \
       if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;            \
       dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
     }                                                                        \
