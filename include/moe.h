@@ -384,19 +384,20 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
  * groups).
  *   u_rows  [total_rows][H] bf16: the forward's u_ws, or NULL to recompute
  *           u here (the same bits);
- *   h_rows  [total_rows][H] bf16: the forward's h_ws, or NULL to use
- *           gelu(u) of the bf16 u instead (it can differ from the
- *           forward's h by one bf16 rounding);
+ *   h_rows  [total_rows][H] bf16: the forward's h_ws, or NULL: recomputed
+ *           with u (the same bits) when u_rows is NULL too, else gelu of
+ *           the bf16 u (it can differ from the forward's h by one bf16
+ *           rounding);
  *   dy_rows [total_rows][D] bf16;  dx_rows [total_rows][D];
  *   dw1 [G][H][D], dw2 [G][D][H] fp32 out;  workspace of at least
  *   moe_ffn_backward_workspace_size bytes (recomputed activations,
- *   transposed weights, transposed token-padded operands and, when few
+ *   transposed weights, the gathered input rows and, when few
  *   weight-gradient tiles meet long token segments, the fp32 partials of a
  *   split reduction, added in a fixed order); contents need no
  *   initialisation
  * Errors: INVALID_ARGUMENT for null pointers or bad sizes;
- *   UNSUPPORTED for non-bf16 inputs, G > 128, D or H not multiples of 8;
- *   WORKSPACE_TOO_SMALL.
+ *   UNSUPPORTED for non-bf16 inputs, G > 128, D or H not multiples of 8,
+ *   (total_rows + 64) * max(D, H) * 2 >= 2^32; WORKSPACE_TOO_SMALL.
  */
 moe_status moe_grouped_ffn_backward(
     const void* x_rows, const int32_t* row_index, moe_dtype dtype,

@@ -431,11 +431,12 @@ moe_status moe_grouped_ffn_backward(
   if (D % 8 != 0 || H % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
                 fn, D, H);
-  const int64_t Kt = moe::padded_columns(total_rows, G);
-  // the token-blocked transposed operands ([max(D, H)][Kt] bf16) are
-  // addressed with 32-bit byte offsets
+  // the weight-gradient GEMMs address a group's rows of the row-major
+  // operands (up to [total_rows + 64][max(D, H)] bf16) with 32-bit byte
+  // offsets
   if (total_rows >= kI32Limit ||
-      Kt * static_cast<int64_t>(D > H ? D : H) * 2 >= (int64_t(1) << 32))
+      (total_rows + 64) * static_cast<int64_t>(D > H ? D : H) * 2 >=
+          (int64_t(1) << 32))
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows=%lld too large", fn,
                 (long long)total_rows);
   if (workspace_bytes < moe::ffn_backward_workspace_bytes(total_rows, G, D, H))

@@ -10,17 +10,16 @@
 // Kernels (gfx950):
 //  * transpose_kernel: [G][R][C] -> [G][C][R] bf16 through 64x64 LDS tiles
 //    (transposed copies of the expert weights for the data-gradient GEMMs).
-//  * tpad_kernel: activation rows grouped by expert -> a transposed [C][Kt]
-//    operand with group g's rows in columns [koff_g, koff_g + M_g) and
-//    zeros up to the next multiple of 64, stored token-blocked: columns
-//    64j .. 64j + 63 form the contiguous [C][64] slab j (the operands of the
-//    K-grouped weight-gradient GEMM, which reads one slab per k stage);
-//    optional row gather and GELU on the way.
+//  * rows_kernel: a row copy, optionally gathered through a row index and
+//    optionally through GELU (the row-major operands of the K-grouped
+//    weight-gradient GEMM when they are not already in HBM).
 //  * combine_bwd_kernel: one wave per token; the routed rows' output
 //    gradients w * dy and the slot-weight gradients <dy, y_row>.
 //  * gate_bwd_token_kernel, gate_bwd_wgrad_kernel, gate_bwd_reduce_kernel,
 //    gate_bwd_dx_kernel: dP -> dlogits per token; dW_g and dbias partials
 //    per token chunk and their fixed-order sum; dx assembled per token.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -83,106 +82,32 @@ __global__ __launch_bounds__(256) void transpose_kernel(
   }
 }
 
-// Group g of rows [off_g, off_{g+1}) (clamped to [0, total]) occupies
-// columns [koff_g, koff_g + klen_g) of a padded operand, klen_g = M_g rounded
-// up to 64, so every 64-column block lies in one group's segment.  The block
-// table holds, per block, its first source row and how many of its 64
-// columns hold rows (the rest are zero padding, or past the last segment).
-__global__ __launch_bounds__(256) void kseg_kernel(
-    const int64_t* __restrict__ offsets, int G, int64_t total, int64_t nblk,
-    int64_t* __restrict__ blk_row, int32_t* __restrict__ blk_n) {
-  __shared__ int64_t r0s[kMaxFfnGroups], ms[kMaxFfnGroups], koffs[kMaxFfnGroups + 1];
-  if (threadIdx.x == 0) {
-    int64_t koff = 0;
-    for (int g = 0; g < G; ++g) {
-      const int64_t r0 = offsets ? min(max(offsets[g], int64_t(0)), total) : 0;
-      const int64_t r1 = offsets ? min(max(offsets[g + 1], r0), total) : total;
-      r0s[g] = r0;
-      ms[g] = r1 - r0;
-      koffs[g] = koff;
-      koff += (r1 - r0 + 63) / 64 * 64;
-    }
-    koffs[G] = koff;
-  }
-  __syncthreads();
-  for (int64_t kb = threadIdx.x; kb < nblk; kb += blockDim.x) {
-    const int64_t k0 = kb * kTile;
-    int64_t row = 0;
-    int n = 0;
-    for (int g = 0; g < G; ++g) {
-      if (k0 >= koffs[g] && k0 < koffs[g + 1]) {
-        const int64_t j0 = k0 - koffs[g];
-        row = r0s[g] + j0;
-        n = static_cast<int>(min<int64_t>(kTile, max<int64_t>(ms[g] - j0, 0)));
-        break;
-      }
-    }
-    blk_row[kb] = row;
-    blk_n[kb] = n;
-  }
-}
-
-// dst [C][Kt]: column block kb holds the blk_n[kb] source rows from
-// blk_row[kb] (through row_index when given), transposed, then zeros.
-// Same 16-byte tile scheme as transpose_kernel (C a multiple of 8).
-// Lane (a, b) of a wave owns tokens 8a .. 8a + 7 of a 64-token block and
-// features 8b .. 8b + 7 of a 64-feature slice: eight 16-byte row loads (the
-// eight lanes of one a read 128 contiguous bytes of a row), an 8 x 8
-// transpose in registers (v_perm_b32 picks the 16-bit halves), eight
-// 16-byte stores (the eight lanes of one b write 128 contiguous bytes of an
-// output row).  No LDS and no barrier.  A workgroup's four waves take four
-// consecutive 64-feature slices of the same token block.
+// dst [total][C] = f(src rows): row r is source row row_index[r] (or r),
+// with GELU applied when asked.  One 16-byte chunk per thread (C a multiple
+// of 8); consecutive threads along a row.
 template <bool GELU>
-__global__ __launch_bounds__(256) void tpad_kernel(
+__global__ __launch_bounds__(256) void rows_kernel(
     const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
-    const int64_t* __restrict__ blk_row, const int32_t* __restrict__ blk_n,
-    int C, int64_t Kt, uint16_t* __restrict__ dst) {
-  (void)Kt;   // the slabs are addressed by block, not by row pitch
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int a = lane >> 3, b = lane & 7;
-  const int64_t kb = blockIdx.y;
-  const int64_t row0 = blk_row[kb];
-  const int n = blk_n[kb];
-  const int cc = blockIdx.x * (4 * kTile) + wave * kTile + 8 * b;
-  if (cc >= C) return;
-  uint32_t w[8][4];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int j = 8 * a + t;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (j < n) {
-      const int64_t r = row0 + j;
-      const int64_t sr = row_index ? row_index[r] : r;
-      v = *reinterpret_cast<const uint4*>(src + sr * C + cc);
-      if constexpr (GELU) {
-        float f[8];
-        unpack8(v, f);
-        v.x = pack_bf16x2(gelu_fwd(f[0]), gelu_fwd(f[1]));
-        v.y = pack_bf16x2(gelu_fwd(f[2]), gelu_fwd(f[3]));
-        v.z = pack_bf16x2(gelu_fwd(f[4]), gelu_fwd(f[5]));
-        v.w = pack_bf16x2(gelu_fwd(f[6]), gelu_fwd(f[7]));
-      }
+    int64_t total, int C, uint16_t* __restrict__ dst) {
+  const int cpr = C / 8;
+  const int64_t n = total * cpr;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+       i < n; i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = i / cpr;
+    const int c = static_cast<int>(i - r * cpr) * 8;
+    const int64_t sr = row_index ? row_index[r] : r;
+    uint4 v = *reinterpret_cast<const uint4*>(src + sr * C + c);
+    if constexpr (GELU) {
+      float f[8];
+      unpack8(v, f);
+      v.x = pack_bf16x2(gelu_fwd(f[0]), gelu_fwd(f[1]));
+      v.y = pack_bf16x2(gelu_fwd(f[2]), gelu_fwd(f[3]));
+      v.z = pack_bf16x2(gelu_fwd(f[4]), gelu_fwd(f[5]));
+      v.w = pack_bf16x2(gelu_fwd(f[6]), gelu_fwd(f[7]));
     }
-    w[t][0] = v.x; w[t][1] = v.y; w[t][2] = v.z; w[t][3] = v.w;
-  }
-  // Output row cc + i holds tokens 8a .. 8a + 7: dword k = (token 2k,
-  // token 2k + 1) of feature i, i.e. half (i % 2) of dword i / 2 of the
-  // loads of tokens 2k and 2k + 1.  Token block kb is the [C][64] slab
-  // starting at element kb * C * 64.
-  uint16_t* const slab = dst + kb * C * static_cast<int64_t>(kTile) + 8 * a;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(w[1][i / 2], w[0][i / 2], sel);
-    o.y = __builtin_amdgcn_perm(w[3][i / 2], w[2][i / 2], sel);
-    o.z = __builtin_amdgcn_perm(w[5][i / 2], w[4][i / 2], sel);
-    o.w = __builtin_amdgcn_perm(w[7][i / 2], w[6][i / 2], sel);
-    *reinterpret_cast<uint4*>(slab + static_cast<int64_t>(cc + i) * kTile) = o;
+    *reinterpret_cast<uint4*>(dst + r * C + c) = v;
   }
 }
-
-// --------------------------------------------------------------- combine --
 
 template <bool BF16>
 __device__ __forceinline__ void ld8(const void* base, int64_t row, int D, int c,
@@ -486,35 +411,21 @@ hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
   return hipGetLastError();
 }
 
-int64_t padded_columns(int64_t total, int G) {
-  return (total + 63) / 64 * 64 + 64 * static_cast<int64_t>(G);
-}
-
-hipError_t launch_kseg(const int64_t* offsets, int G, int64_t total,
-                       int64_t* blk_row, int32_t* blk_n, hipStream_t stream) {
-  if (total == 0) return hipSuccess;
-  const int64_t nblk = padded_columns(total, G) / kTile;
-  hipLaunchKernelGGL(kseg_kernel, dim3(1), dim3(256), 0, stream, offsets, G,
-                     total, nblk, blk_row, blk_n);
-  return hipGetLastError();
-}
-
-hipError_t launch_tpad(const void* src, const int32_t* row_index,
-                       const int64_t* blk_row, const int32_t* blk_n, int G,
+hipError_t launch_rows(const void* src, const int32_t* row_index,
                        int64_t total, int C, bool gelu, void* dst,
                        hipStream_t stream) {
-  if (total == 0) return hipSuccess;
-  const int64_t Kt = padded_columns(total, G);
-  const dim3 grid(static_cast<unsigned>(ceil_div(C, 4 * kTile)),
-                  static_cast<unsigned>(Kt / kTile));
+  if (total == 0 || C == 0) return hipSuccess;
+  const int64_t n = total * (C / 8);
+  const unsigned grid =
+      static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 8192));
   if (gelu)
-    hipLaunchKernelGGL(tpad_kernel<true>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), row_index, blk_row,
-                       blk_n, C, Kt, static_cast<uint16_t*>(dst));
+    hipLaunchKernelGGL(rows_kernel<true>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), row_index, total, C,
+                       static_cast<uint16_t*>(dst));
   else
-    hipLaunchKernelGGL(tpad_kernel<false>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), row_index, blk_row,
-                       blk_n, C, Kt, static_cast<uint16_t*>(dst));
+    hipLaunchKernelGGL(rows_kernel<false>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), row_index, total, C,
+                       static_cast<uint16_t*>(dst));
   return hipGetLastError();
 }
 

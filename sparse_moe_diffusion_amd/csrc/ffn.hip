@@ -70,13 +70,14 @@ struct GemmParams {
   int cmb_kmax;              // 1..kCombineMaxSlots
   // kEpiGeluGrad only: the pre-activations u [total][Nd] bf16.
   const void* aux;
-  // K-grouped form (weight gradients): C[g] [mrows][Nd] fp32 = A[:, seg g]
-  // B[:, seg g]^T, A [mrows][ld] and B [Nd][ld] bf16, seg g = group g's
-  // token columns, padded to 64 (see the transposes).
-  int ld, mrows;
-  // K-grouped form split over the reduction: each group's segment is cut
-  // into ksplit pieces (multiples of 64 columns) whose products go to
-  // separate fp32 partials, C [ksplit][G][mrows][Nd] (0 or 1: no split).
+  // K-grouped form (weight gradients): C[g] [mrows][Nd] fp32 = A[rows g]^T
+  // B[rows g], A [total][mrows] and B (in w) [total][Nd] bf16 row-major,
+  // rows g = group g's token rows.
+  int mrows;
+  // K-grouped form split over the reduction: each group's rows are cut
+  // into ksplit pieces (multiples of 64 rows but the last) whose products
+  // go to separate fp32 partials, C [ksplit][G][mrows][Nd] (0 or 1: no
+  // split).
   int ksplit;
   // kEpiGelu with bf16 output: if set, also the pre-activations u = A W^T
   // + bias, [total][Nd] bf16 (kept by a training forward for the backward).
@@ -232,33 +233,20 @@ __device__ __forceinline__ float gelu_tanh_grad(float u) {
               fmaf(3.0f * 0.044715f, u * u, 1.0f), s);
 }
 
-// K-grouped form: the group table holds each group's token-column segment
-// of the transposed operands, [kofs, kofs + klen), klen = the group's row
-// count rounded up to 64 (the transposes zero the padding).
+// K-grouped form: the group table holds each group's token rows of the
+// row-major operands, [kofs, kofs + klen) (offsets clamped to [0, total]).
 __device__ __forceinline__ void build_kseg_table(const GemmParams& p,
                                                  int32_t* tab, int wave,
                                                  int lane) {
   if (wave == 0) {
-    int base = 0;
     for (int c = 0; c < p.G; c += 64) {
       const int g = c + lane;
-      int len = 0;
       if (g < p.G) {
         const int64_t r0 = p.offsets ? min(max(p.offsets[g], int64_t(0)), p.total) : 0;
         const int64_t r1 = p.offsets ? min(max(p.offsets[g + 1], r0), p.total) : p.total;
-        len = static_cast<int>((r1 - r0 + 63) / 64 * 64);
+        tab[g] = static_cast<int>(r0);
+        tab[kTabCol + g] = static_cast<int>(r1 - r0);
       }
-      int inc = len;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(inc, d);
-        if (lane >= d) inc += v;
-      }
-      if (g < p.G) {
-        tab[g] = base + inc - len;
-        tab[kTabCol + g] = len;
-      }
-      base += __shfl(inc, 63);
     }
   }
   __syncthreads();
@@ -288,11 +276,11 @@ __device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
   loc.row0 = uniform64(base + static_cast<int64_t>(m_first + rem % gm) * BM);
   loc.row_end = uniform64(base + p.mrows);
   loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
-  // the split's piece of the group's segment (its length a multiple of 64,
-  // possibly empty: the partial is then zero)
+  // the split's piece of the group's rows (a multiple of 64 rows except
+  // the last piece, possibly empty: the partial is then zero)
   const int kofs = __builtin_amdgcn_readfirstlane(tab[g]);
   const int klen = __builtin_amdgcn_readfirstlane(tab[kTabCol + g]);
-  const int cs = (klen / 64 + S - 1) / S * 64;
+  const int cs = ((klen + 63) / 64 + S - 1) / S * 64;
   loc.kofs = kofs + sp * cs;
   loc.klen = max(0, min(cs, klen - sp * cs));
   return true;
@@ -372,6 +360,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((lds_void*)(const_cast<void*>(p))));
 }
 
+// MFMA fragment of a [k][rows] LDS tile (rows contiguous within each k row,
+// row pitch PITCH bytes): 8 consecutive k values of one row, from two
+// transpose reads of 4 k rows each.  In every 16-lane group the transpose
+// read hands lane j element y of the 8-byte piece addressed by lane
+// 4y + j/4, position j % 4; the caller's per-lane address makes that piece
+// (k row 4y.., rows 4(j/4)..) so lane j ends up with row j's k values.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int PITCH>
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint16_t* base, int off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  char* b = const_cast<char*>(reinterpret_cast<const char*>(base)) + off;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + 4 * PITCH));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
+                                                            4, 5, 6, 7));
+}
+
 // SZ bytes per lane (16 or 4) from global memory straight into LDS: lane l
 // of the wave writes bytes [SZ l, SZ l + SZ) of the block at LDS byte
 // address `dst`.  The destination reaches the instruction as a plain
@@ -392,6 +398,32 @@ __device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, a, 4, off, 0, 0, 0);
 }
 
+// The same 16-byte transfer, written out (for the K-grouped form): the
+// compiler waits for every outstanding transfer before each LDS transpose
+// read that follows a transfer it can see, which would stall the pipeline
+// at every k step.  The descriptor is rebuilt from a uniform base and byte
+// count (stride 0, the flags make_rsrc uses); offsets at or past the count
+// read zero.  The transfer writes no register, and the kernel orders it
+// against its readers itself (vmcnt wait, then workgroup barrier).  One
+// wait state between the M0 write and the transfer that reads it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
+                                          uint32_t dst, uint32_t off) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(b));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(off), "s"(r)
+      : "memory", "m0");
+}
+
 // Tile of BM token rows x BN output features; waves form a WT x WF grid, each
 // owning (BM/WT) tokens x (BN/WF) features as (BN/WF/32) x (BM/WT/32)
 // v_mfma_f32_32x32x16_bf16 tiles.  LDS holds two k-stages of both operands
@@ -406,6 +438,8 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   static_assert(EPI != kEpiGeluGrad || OUT_BF16, "gelu'(u) is applied on bf16 output");
   static_assert(!KG || (!OUT_BF16 && !PF && EPI == kEpiStore),
                 "the K-grouped form writes fp32 without prefetch");
+  static_assert(!KG || (BM == 256 && BN == 256),
+                "the K-grouped stage tiles are two 512-byte k rows per transfer");
   constexpr int kWaves = WT * WF;
   constexpr int TB = BM / WT / 32;   // token blocks per wave
   constexpr int FB = BN / WF / 32;   // feature blocks per wave
@@ -496,27 +530,26 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // The previous tile's readers of the LDS are done.
   __builtin_amdgcn_s_barrier();
 
-  // Reduction length and operand row pitch of this tile: the group's padded
-  // token segment and the transposed operands' pitch in the K-grouped form.
+  // Reduction length of this tile: the feature width, or in the K-grouped
+  // form this split's piece of the group's token rows.  The K-grouped
+  // operands are row-major [rows][C] (C = mrows for A, Nd for W): a k stage
+  // is 64 token rows, kept in LDS as [64][BM] and [64][BN] tiles.
   const int Kd = KG ? loc.klen : Kd0;
-  // The K-grouped operands are token-blocked: token block j (64 columns) of
-  // a [C][Kt] operand is a contiguous [C][64] slab, so rows are 128 bytes
-  // apart and one k stage is one slab further (C x 128 bytes).  The other
-  // forms have k-contiguous rows.
-  const uint32_t row_bytes = KG ? 128u : row_bytes0;
-  const uint32_t kstep_a = KG ? static_cast<uint32_t>(p.mrows) * 128u : kBK * 2u;
-  const uint32_t kstep_b = KG ? static_cast<uint32_t>(p.Nd) * 128u : kBK * 2u;
+  const uint32_t row_bytes = row_bytes0;
+  const uint32_t kstep_a = static_cast<uint32_t>(p.mrows) * 128u;   // KG only
+  const uint32_t kstep_b = static_cast<uint32_t>(p.Nd) * 128u;
   const int64_t kg_m = KG ? loc.row0 - static_cast<int64_t>(loc.g) * p.mrows : 0;
   const uint16_t* a_base =
       static_cast<const uint16_t*>(p.a) +
       (gather ? int64_t(0)
-              : KG ? (static_cast<int64_t>(loc.kofs / 64) * p.mrows + kg_m) * 64
+              : KG ? static_cast<int64_t>(loc.kofs) * p.mrows + kg_m
                    : loc.row0 * Kd);
-  // KG: from the tile's first row to the end of the segment's last slab.
-  // Tile rows past the operand's C read the next slab's rows (finite
-  // values, or zeros past the segment); they only reach output rows and
-  // features that are not stored.
-  const int64_t kg_a = KG ? (static_cast<int64_t>(loc.klen / 64) * p.mrows - kg_m) * 128 : 0;
+  // KG: from the tile's first feature of the piece's first row to the end
+  // of its last row.  Rows past the piece read zero; tile features past the
+  // operand's C read the next row's (finite) values, which only reach
+  // output rows and features that are not stored.
+  const int64_t kg_a =
+      KG ? (static_cast<int64_t>(loc.klen) * p.mrows - kg_m) * 2 : 0;
   const uint32_t a_bytes =
       gather ? kOutOfRange
       : KG   ? static_cast<uint32_t>(kg_a > 0 ? kg_a : 0)
@@ -529,9 +562,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // Weight rows of group g: features past Nd fall outside the descriptor.
   const uint16_t* w_base =
       static_cast<const uint16_t*>(p.w) +
-      (KG ? (static_cast<int64_t>(loc.kofs / 64) * p.Nd + loc.n0) * 64
+      (KG ? static_cast<int64_t>(loc.kofs) * p.Nd + loc.n0
           : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
-  const int64_t kg_w = KG ? (static_cast<int64_t>(loc.klen / 64) * p.Nd - loc.n0) * 128 : 0;
+  const int64_t kg_w =
+      KG ? (static_cast<int64_t>(loc.klen) * p.Nd - loc.n0) * 2 : 0;
   const uint32_t w_bytes =
       KG ? static_cast<uint32_t>(kg_w > 0 ? kg_w : 0)
          : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
@@ -539,6 +573,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(w_base))),
                 __builtin_amdgcn_readfirstlane(w_bytes));
+  const char* const kg_abase =
+      reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(a_base)));
+  const char* const kg_wbase =
+      reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(w_base)));
 
   // Per DMA transfer q of this wave: byte offset of this lane's chunk at
   // k = 0, the chunk's k index, and the LDS destination (elements).
@@ -549,6 +587,23 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   for (int q = 0; q < NQ; ++q) {
     const int t = wave + kWaves * q;          // transfer index in the stage
     const bool isA = q < QA;                  // uniform across the wave
+    if constexpr (KG) {
+      // 1 KB of the operand's [64][R] stage tile per transfer: lane l lands
+      // at byte 16 l of it, i.e. k row kr, 16-byte slot pc, which holds
+      // chunk pc ^ 4 (kr % 4) of that token row (so the transpose reads of
+      // four consecutive k rows hit four different bank quarters).
+      const int ta = isA ? t : t - BM / 8;
+      const int rb = (isA ? BM : BN) * 2;
+      const int byte = ta * 1024 + lane * 16;
+      const int kr = byte / rb;
+      const int pc = (byte - kr * rb) / 16;
+      const int lc = pc ^ (4 * (kr & 3));
+      gk[q] = kr;
+      ldst[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ta * 1024));
+      goff[q] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(isA ? p.mrows : p.Nd) * 2u +
+                static_cast<uint32_t>(lc) * 16u;
+      continue;
+    }
     const int r0 = (isA ? t : t - BM / 8) * 8;
     const int r = r0 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
@@ -603,15 +658,31 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 
 // DMA transfers Q0 <= q < Q1 of k-stage KT into the LDS buffers at byte
 // addresses DA / DB.
+// K-grouped form: the descriptors' base moves to the stage's first token
+// row and their range shrinks with it, so rows past the piece read zero and
+// the per-lane offsets stay fixed (held in registers for the whole tile).
 #define MOE_ISSUE(KT, DA, DB, Q0, Q1)                                        \
   do {                                                                       \
     const int ikt_ = (KT);                                                   \
-    const bool full_ = (ikt_ + 1) * kBK <= Kd;                               \
-    _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                    \
-      const bool isA_ = q < QA;                                              \
-      uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (isA_ ? kstep_a : kstep_b); \
-      if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;            \
-      dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
+    if constexpr (KG) {                                                      \
+      const uint32_t sa_ = static_cast<uint32_t>(ikt_) * kstep_a;            \
+      const uint32_t sb_ = static_cast<uint32_t>(ikt_) * kstep_b;            \
+      _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
+        if (q < QA)                                                          \
+          dma16_raw(kg_abase + sa_, a_bytes > sa_ ? a_bytes - sa_ : 0u,      \
+                    (DA) + ldst[q], goff[q]);                                \
+        else                                                                 \
+          dma16_raw(kg_wbase + sb_, w_bytes > sb_ ? w_bytes - sb_ : 0u,      \
+                    (DB) + ldst[q], goff[q]);                                \
+      }                                                                      \
+    } else {                                                                 \
+      const bool full_ = (ikt_ + 1) * kBK <= Kd;                             \
+      _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
+        const bool isA_ = q < QA;                                            \
+        uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);   \
+        if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;          \
+        dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
+      }                                                                      \
     }                                                                        \
   } while (0)
 
@@ -620,6 +691,26 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // kc ^ swz(row).  Element offsets for all four k steps are precomputed.
   const int khalf = lane >> 5;
   int oa[FB][4], ob[TB][4];
+  if constexpr (KG) {
+    // Transposed fragments (byte offsets at k step 0): lane l addresses k
+    // row 8 (l / 32) + (l / 4) % 4 and the 8-byte piece of features
+    // 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 of its 32-row block, in the
+    // swizzled slot of that k row (see the transfers).
+    const int kr = 8 * khalf + ((lane >> 2) & 3);
+    const int sw = 4 * ((lane >> 2) & 3);
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int hb = (lane & 1) * 8;
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+      const int c0 = (wf * (BN / WF) + i * 32) / 8;
+      oa[i][0] = kr * BN * 2 + ((c0 + cl) ^ sw) * 16 + hb;
+    }
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int c0 = (wt * (BM / WT) + j * 32) / 8;
+      ob[j][0] = kr * BM * 2 + ((c0 + cl) ^ sw) * 16 + hb;
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < FB; ++i) {
     const int row = wf * (BN / WF) + i * 32 + (lane & 31);
@@ -633,6 +724,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       ob[j][ks] = row * kBK + (((2 * ks + khalf) ^ swz(row)) * 8);
+  }
   }
 
   f32x16 acc[FB][TB];
@@ -649,10 +741,17 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 
 #define MOE_FRAGS(FA, FB_, SA, SB, KS)                                       \
   do {                                                                       \
-    _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                   \
-        *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][KS]]);                  \
-    _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                  \
-        *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][KS]]);                  \
+    if constexpr (KG) {                                                      \
+      _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                 \
+          lds_frag_tr<BN * 2>((SB), oa[i][0] + (KS) * 16 * BN * 2);          \
+      _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                \
+          lds_frag_tr<BM * 2>((SA), ob[j][0] + (KS) * 16 * BM * 2);          \
+    } else {                                                                 \
+      _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                 \
+          *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][KS]]);                \
+      _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                \
+          *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][KS]]);                \
+    }                                                                        \
   } while (0)
 
 #define MOE_MFMAS(FA, FB_, I0, I1)                                           \
@@ -1368,24 +1467,19 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(
 }
 
 struct BwdLayout {
-  size_t u, du, w1t, w2t, dyT, aT, duT, xT, brow, bn, part, total;
+  size_t u, h, du, w1t, w2t, xr, part, total;
 };
 
 BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
-  const int64_t Kt = padded_columns(total, G);
   BwdLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
   L.u = take(static_cast<size_t>(total) * H * 2);
+  L.h = take(static_cast<size_t>(total) * H * 2);
   L.du = take(static_cast<size_t>(total) * H * 2);
   L.w1t = take(static_cast<size_t>(G) * D * H * 2);
   L.w2t = take(static_cast<size_t>(G) * H * D * 2);
-  L.dyT = take(static_cast<size_t>(D) * Kt * 2);
-  L.aT = take(static_cast<size_t>(H) * Kt * 2);
-  L.duT = take(static_cast<size_t>(H) * Kt * 2);
-  L.xT = take(static_cast<size_t>(D) * Kt * 2);
-  L.brow = take(static_cast<size_t>(Kt / 64) * 8);
-  L.bn = take(static_cast<size_t>(Kt / 64) * 4);
+  L.xr = take(static_cast<size_t>(total) * D * 2);
   const int S = choose_ksplit(G, D, H, total);
   L.part = take(S > 1 ? static_cast<size_t>(S) * G * D * H * 4 : 0);
   L.total = o;
@@ -1403,7 +1497,8 @@ size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H) {
 //   du      = (dy_rows W2) * gelu'(u)              (W2 transposed once)
 //   dx_rows = du W1                                (W1 transposed once)
 //   dW2[g]  = dy_rows[g]^T gelu(u[g]),  dW1[g] = du[g]^T x_rows[g]
-// the last two as K-grouped GEMMs over token-padded transposed operands.
+// the last two as K-grouped GEMMs that read the row-major operands and
+// transpose them on the way from LDS.
 hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   const BwdLayout L = bwd_layout(a.total_rows, a.G, a.D, a.H);
   char* ws = static_cast<char*>(a.workspace);
@@ -1411,13 +1506,10 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   void* du = ws + L.du;
   void* w1t = ws + L.w1t;
   void* w2t = ws + L.w2t;
-  void* dyT = ws + L.dyT;
-  void* aT = ws + L.aT;
-  void* duT = ws + L.duT;
-  void* xT = ws + L.xT;
-  int64_t* brow = reinterpret_cast<int64_t*>(ws + L.brow);
-  int32_t* bn = reinterpret_cast<int32_t*>(ws + L.bn);
-  const int64_t Kt = padded_columns(a.total_rows, a.G);
+  // a = gelu(u) and the expert's input rows, row-major, for the weight
+  // gradients: the forward's, or formed here.
+  const void* hh = a.h_saved != nullptr ? a.h_saved : ws + L.h;
+  const void* xr = a.row_index != nullptr ? ws + L.xr : a.x;
   const int G = a.G, D = a.D, H = a.H;
   hipError_t err;
 #define MOE_TRY(call)                      \
@@ -1430,15 +1522,25 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   MOE_TRY(launch_transpose(a.w2, G, D, H, w2t, stream));
   MOE_TRY(launch_transpose(a.w1, G, H, D, w1t, stream));
   if (a.total_rows > 0) {
-    // u: the forward's saved pre-activations, or recomputed.
+    // u: the forward's saved pre-activations, or recomputed (with
+    // h = gelu(u) beside it when h was not kept either).
     const void* uu = a.u_saved;
     if (uu == nullptr) {
       GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
                     G, H, D};
-      launch_stage<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
-          pu, stream);
+      if (a.h_saved == nullptr) {
+        pu.c = ws + L.h;
+        pu.u_out = u;
+        launch_stage<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
+            pu, stream);
+      } else {
+        launch_stage<kEpiStore, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
+            pu, stream);
+      }
       MOE_TRY(hipGetLastError());
       uu = u;
+    } else if (a.h_saved == nullptr) {
+      MOE_TRY(launch_rows(uu, nullptr, a.total_rows, H, true, ws + L.h, stream));
     }
     GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
                   a.total_rows, G, H, D};
@@ -1455,17 +1557,10 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
       launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
           px, stream);
     MOE_TRY(hipGetLastError());
-    MOE_TRY(launch_kseg(a.offsets, G, a.total_rows, brow, bn, stream));
-    MOE_TRY(launch_tpad(a.dy_rows, nullptr, brow, bn, G, a.total_rows, D, false, dyT, stream));
-    // a = gelu(u): the forward's saved activations, or gelu of u.
-    if (a.h_saved != nullptr)
-      MOE_TRY(launch_tpad(a.h_saved, nullptr, brow, bn, G, a.total_rows, H, false, aT, stream));
-    else
-      MOE_TRY(launch_tpad(uu, nullptr, brow, bn, G, a.total_rows, H, true, aT, stream));
-    MOE_TRY(launch_tpad(du, nullptr, brow, bn, G, a.total_rows, H, false, duT, stream));
-    MOE_TRY(launch_tpad(a.x, a.row_index, brow, bn, G, a.total_rows, D, false, xT, stream));
+    if (a.row_index != nullptr)
+      MOE_TRY(launch_rows(a.x, a.row_index, a.total_rows, D, false, ws + L.xr, stream));
   }
-  // dW2[g] [D][H] = dyT[:, seg g] aT[:, seg g]^T;  dW1[g] [H][D] = duT xT^T.
+  // dW2[g] [D][H] = dy_rows[g]^T h[g];  dW1[g] [H][D] = du[g]^T x_rows[g].
   // With no rows every segment is empty and the products are zero.
   // When the tiles would not fill the chip, the reduction is split and the
   // partials are added in split order afterwards.
@@ -1474,9 +1569,8 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   const int64_t n4 = static_cast<int64_t>(G) * D * H / 4;
   const unsigned rgrid =
       static_cast<unsigned>(std::min<int64_t>((n4 + 255) / 256, 4096));
-  GemmParams pw2{dyT, nullptr, aT, nullptr, S > 1 ? part : a.dw2, a.offsets,
-                 a.total_rows, G, H, 0};
-  pw2.ld = static_cast<int>(Kt);
+  GemmParams pw2{a.dy_rows, nullptr, hh, nullptr, S > 1 ? part : a.dw2,
+                 a.offsets, a.total_rows, G, H, 0};
   pw2.mrows = D;
   pw2.ksplit = S;
   const int tiles2 =
@@ -1491,9 +1585,8 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
                        reinterpret_cast<float4*>(a.dw2));
     MOE_TRY(hipGetLastError());
   }
-  GemmParams pw1{duT, nullptr, xT, nullptr, S > 1 ? part : a.dw1, a.offsets,
+  GemmParams pw1{du, nullptr, xr, nullptr, S > 1 ? part : a.dw1, a.offsets,
                  a.total_rows, G, D, 0};
-  pw1.ld = static_cast<int>(Kt);
   pw1.mrows = H;
   pw1.ksplit = S;
   const int tiles1 =

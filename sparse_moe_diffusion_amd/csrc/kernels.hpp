@@ -86,13 +86,9 @@ hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           hipStream_t stream);
 
 // backward.hip
-int64_t padded_columns(int64_t total, int G);
 hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
                             hipStream_t stream);
-hipError_t launch_kseg(const int64_t* offsets, int G, int64_t total,
-                       int64_t* blk_row, int32_t* blk_n, hipStream_t stream);
-hipError_t launch_tpad(const void* src, const int32_t* row_index,
-                       const int64_t* blk_row, const int32_t* blk_n, int G,
+hipError_t launch_rows(const void* src, const int32_t* row_index,
                        int64_t total, int C, bool gelu, void* dst,
                        hipStream_t stream);
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16,

@@ -60,15 +60,20 @@ def test_combine_backward(N, D, Kmax, empty):
     assert np.abs(to_np(sg) - ref_sg).max() <= 1e-5 * max(1.0, np.abs(ref_sg).max())
 
 
-@pytest.mark.parametrize("sizes,D,H,gather", [
-    ([100, 0, 129, 1, 256], 128, 256, False), ([300, 70], 192, 384, True),
-    ([513], 1152, 512, False), ([0, 0, 5], 64, 128, True),
+@pytest.mark.parametrize("sizes,D,H,gather,saved", [
+    ([100, 0, 129, 1, 256], 128, 256, False, None),
+    ([300, 70], 192, 384, True, None),
+    ([513], 1152, 512, False, None), ([0, 0, 5], 64, 128, True, None),
     # 16 x 2 x 8 = 256 tiles, a full round
-    ([120 + 7 * i for i in range(16)], 512, 2048, True),
+    ([120 + 7 * i for i in range(16)], 512, 2048, True, None),
     # few weight-gradient tiles over long token segments: the reduction is
     # split in 4, and in 2 with an empty piece for the short group
-    ([8192], 128, 256, False), ([12000, 64], 128, 256, True)])
-def test_grouped_ffn_backward(sizes, D, H, gather):
+    ([8192], 128, 256, False, None), ([12000, 64], 128, 256, True, None),
+    # pre-activations given (h = gelu of them here), or activations given
+    # (u recomputed alone)
+    ([300, 70], 192, 384, True, "u"), ([8192], 128, 256, False, "u"),
+    ([100, 0, 129, 1, 256], 128, 256, False, "h")])
+def test_grouped_ffn_backward(sizes, D, H, gather, saved):
     _lib, ops = _ops()
     rng = np.random.default_rng(sum(sizes) + D + H)
     G = len(sizes)
@@ -86,10 +91,20 @@ def test_grouped_ffn_backward(sizes, D, H, gather):
     dx = torch.empty(total, D, dtype=torch.bfloat16, device=DEV)
     dw1 = torch.full((G, H, D), 5.0, dtype=torch.float32, device=DEV)
     dw2 = torch.full((G, D, H), 5.0, dtype=torch.float32, device=DEV)
+    # the given u / h: the exact products rounded to bf16 (h = gelu of the
+    # bf16 u), as a forward would have kept them
+    u_in = np.zeros((total, H))
+    for g in range(G):
+        a, b = offsets[g], offsets[g + 1]
+        u_in[a:b] = rows[a:b].astype(np.float64) @ w1[g].astype(np.float64).T
+    u_in = q(u_in)
+    h_in = q(oracle.gelu_tanh(u_in.astype(np.float64)))
     ops.moe_grouped_ffn_backward(bf(xsrc if gather else rows),
                                  None if ri is None else dev(ri), total,
                                  dev(offsets), bf(w1), None, bf(w2), bf(dyr),
-                                 ws, dx, dw1, dw2)
+                                 ws, dx, dw1, dw2,
+                                 u_rows=bf(u_in) if saved == "u" else None,
+                                 h_rows=bf(h_in) if saved == "h" else None)
     torch.cuda.synchronize()
     ref_dx = np.zeros((total, D))
     ref_dw1 = np.zeros((G, H, D))
@@ -205,10 +220,9 @@ def test_layer_backward_deterministic():
 ], ids=["small", "s_like"])
 def test_saved_preactivations(cfg):
     """A training forward (save_u) writes y and h bit for bit as the plain
-    forward, and u equal to the backward's own recomputation: the backward
-    with the saved u gives dx and dW1 bit for bit as with recomputation;
-    dW2, which then uses the forward's own h instead of gelu of the bf16 u,
-    stays within the oracle's tolerance."""
+    forward, and u and h equal to the backward's own recomputation: the
+    backward with the saved u and h gives every gradient bit for bit as
+    with recomputation, and dW2 stays within the oracle's tolerance."""
     inp, gl0, dy, g0 = _layer_backward(cfg, 47)
     _, gl1, _, g1 = _layer_backward(cfg, 47, save_u=True)
     b0, b1 = gl0.buf, gl1.buf
@@ -226,7 +240,7 @@ def test_saved_preactivations(cfg):
     for r, gidx in zip(pick, grp):
         ref = x[rows[r]] @ inp.w1[gidx].astype(np.float64).T
         assert_close(u[r:r + 1], ref[None], "bf16", "u")
-    for k in ("dx", "dw1", "dw1s", "dx_rows"):
+    for k in ("dx", "dw1", "dw1s", "dx_rows", "dw2", "dw2s"):
         assert torch.equal(getattr(g0, k), getattr(g1, k)), k
     idx = to_np(b1.topk_idx)
     P = oracle.route(inp)["P"]
