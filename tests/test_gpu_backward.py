@@ -250,3 +250,111 @@ def test_saved_preactivations(cfg):
     n_s, H = cfg.n_s, cfg.H
     dw2s = to_np(g1.dw2s)[0].reshape(cfg.D, n_s, H).transpose(1, 0, 2)
     assert_close(dw2s, ref["dw2s"], "bf16", "dW2s")
+
+
+def _full_size_reference(inp, rec, P, dy, dloss, mode, tokens, cols, feats,
+                         experts):
+    """Oracle backward of a full-size layer on a sample: dx on ``tokens``;
+    dW1[e][j][d] and dW2[e][d][j] for e in ``experts``, j in ``cols`` and d
+    in ``feats`` (and the same for the shared experts); dW_g, dbias and the
+    slot gradients in full.  Each piece is the oracle's definition applied to
+    the rows it needs."""
+    cfg = inp.cfg
+    x = inp.x.astype(np.float64)
+    w = oracle.slot_weights(P, rec)
+    # slot gradients <dy[t], expert_e(x_t)> of every routed slot
+    dws = np.zeros(rec.shape)
+    for e in range(cfg.E):
+        r, k = np.nonzero(rec == e)
+        for c in range(0, r.size, 8192):
+            rr, kk = r[c:c + 8192], k[c:c + 8192]
+            v = oracle.expert_mlp(x[rr], inp.w1[e], inp.w2[e])
+            dws[rr, kk] = (dy[rr] * v).sum(axis=1)
+    dP = np.zeros((cfg.N, cfg.E))
+    valid = rec >= 0
+    np.add.at(dP, (np.nonzero(valid)[0], rec[valid]), dws[valid])
+    dP += dloss * oracle.balance_grad(rec, cfg.E, cfg.B, cfg.T, cfg.K,
+                                      cfg.alpha, mode)
+    dl = oracle.softmax_backward(P, dP)
+    ref = dict(slot_grad=dws, dw_gate=dl.T @ x, dbias=dl.sum(axis=0))
+    # dx on the sampled tokens
+    dx = dl[tokens] @ inp.w_gate.astype(np.float64)
+    for i, t in enumerate(tokens):
+        for k in range(rec.shape[1]):
+            e = rec[t, k]
+            if e >= 0:
+                dx[i] += oracle.expert_mlp_backward(
+                    x[t:t + 1], inp.w1[e], inp.w2[e], w[t, k] * dy[t:t + 1])[0][0]
+        for s in range(cfg.n_s):
+            dx[i] += oracle.expert_mlp_backward(
+                x[t:t + 1], inp.w1s[s], inp.w2s[s], dy[t:t + 1])[0][0]
+    ref["dx"] = dx
+
+    def sampled(X, dv, w1, w2):
+        # dW1[j][d] = sum_r du[r][j] X[r][d];  dW2[d][j] = sum_r dv[r][d] a[r][j]
+        u = X @ w1[cols].astype(np.float64).T
+        du = (dv @ w2[:, cols].astype(np.float64)) * oracle.gelu_tanh_grad(u)
+        return du.T @ X[:, feats], dv[:, feats].T @ oracle.gelu_tanh(u)
+
+    for e in experts:
+        r, k = np.nonzero(rec == e)
+        ref[("dw", e)] = sampled(x[r], w[r, k][:, None] * dy[r], inp.w1[e],
+                                 inp.w2[e])
+    for s in range(cfg.n_s):
+        ref[("dws", s)] = sampled(x, dy, inp.w1s[s], inp.w2s[s])
+    return ref
+
+
+@pytest.mark.parametrize("name,mode,save_u", [
+    ("xl_8e2a_512", "sequence", True), ("race_16e", "global", False)])
+def test_full_size_backward(name, mode, save_u):
+    """The backward at a full-size workload, in the launch configuration the
+    benchmark times: routing reconciled as in the forward checks, then dx on
+    sampled tokens, sampled dW1 / dW2 elements of three routed experts and
+    of the shared experts, and the slot gradients, dW_g and dbias in full."""
+    from parity import reconcile_race, reconcile_topk, sample_tokens
+    cfg = synth.CONFIGS[name]
+    print(f"[full-size backward] {name} N={cfg.N} D={cfg.D} H={cfg.H} "
+          f"E={cfg.E} save_u={save_u}", flush=True)
+    inp, gl, dy, g = _layer_backward(cfg, 51, dloss=1.0, mode=mode,
+                                     save_u=save_u)
+    idx = to_np(gl.buf.topk_idx)
+    got = {k: to_np(getattr(g, k)) for k in
+           ("dx", "slot_grad", "dw_gate", "dbias")}
+    counts = to_np(gl.buf.expert_counts)
+    rng = np.random.default_rng(7)
+    cols = np.sort(rng.choice(cfg.H, 8, replace=False))
+    feats = np.sort(rng.choice(cfg.D, 8, replace=False))
+    experts = sorted({0, cfg.E - 1, int(np.argmax(counts))})
+    dw1 = {e: to_np(g.dw1[e])[np.ix_(cols, feats)] for e in experts}
+    dw2 = {e: to_np(g.dw2[e])[np.ix_(feats, cols)] for e in experts}
+    H = cfg.H
+    dw1s = {s: to_np(g.dw1s[0, s * H + cols])[:, feats] for s in range(cfg.n_s)}
+    dw2s = {s: to_np(g.dw2s[0][:, s * H + cols])[feats] for s in range(cfg.n_s)}
+    del gl, g
+    torch.cuda.empty_cache()
+
+    r = oracle.route(inp)
+    P = r["P"]
+    if cfg.route == "race":
+        rec, bad = reconcile_race(P, cfg.K, r["idx"], idx, r["tau"])
+    else:
+        rec, bad, _ = reconcile_topk(P, r["idx"], idx)
+    assert not bad, f"routing differs on non-tie tokens {bad[:10]}"
+    assert np.array_equal(rec, idx)
+    tokens = sample_tokens(cfg, 32)
+    ref = _full_size_reference(inp, rec, P, dy.astype(np.float64), 1.0, mode,
+                               tokens, cols, feats, experts)
+    assert_close(got["dx"][tokens], ref["dx"], "bf16", "dx")
+    valid = rec >= 0
+    assert_close(got["slot_grad"][valid], ref["slot_grad"][valid], "bf16",
+                 "slot_grad")
+    assert_close(got["dw_gate"], ref["dw_gate"], "bf16", "dW_g")
+    assert_close(got["dbias"], ref["dbias"], "bf16", "dbias")
+    for e in experts:
+        assert_close(dw1[e], ref[("dw", e)][0], "bf16", f"dW1[{e}]")
+        assert_close(dw2[e], ref[("dw", e)][1], "bf16", f"dW2[{e}]")
+    for s in range(cfg.n_s):
+        assert_close(dw1s[s], ref[("dws", s)][0], "bf16", f"dW1s[{s}]")
+        assert_close(dw2s[s], ref[("dws", s)][1], "bf16", f"dW2s[{s}]")
+    print(name, "ok", flush=True)
