@@ -24,6 +24,11 @@
 // branches.  With bf16 output the finished tile goes through LDS and leaves
 // in row-contiguous 16-byte stores.
 //
+// The weight gradients of the backward run the same kernel in a K-grouped
+// form: the reduction runs down the token rows of row-major operands, which
+// land in LDS as [64 tokens][256 features] stage tiles and reach the matrix
+// cores through LDS transpose reads (ds_read_b64_tr_b16).
+//
 // The MFMA computes out^T: weight rows are the 32-row "A" operand and token
 // rows the "B" operand, so each lane ends up holding 4 consecutive output
 // features of one token and stores 8 (bf16) or 16 (fp32) bytes at a time.
@@ -88,7 +93,7 @@ struct TileLoc {
   int g;
   int64_t row0, row_end;
   int n0;
-  int kofs, klen;   // K-grouped form: the group's token-column segment
+  int kofs, klen;   // K-grouped form: the split's first token row and row count
 };
 
 // tanh-GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2z)),
