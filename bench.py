@@ -360,7 +360,7 @@ def cpu_baseline(cfg, inp, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
+        print(json.dumps({"error": "the layer benchmark runs on one GPU only; "
                           "--gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
