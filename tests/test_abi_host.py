@@ -298,6 +298,12 @@ def test_backward_entry_points_reject():
                    (dict(dt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
                    (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
                    (dict(H=100), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(total=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
+                   # the weight-gradient GEMMs' 32-bit byte offsets:
+                   # (total + 64) * max(D, H) * 2 must stay below 2^32
+                   (dict(total=(1 << 23) - 64), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(total=(1 << 23) - 65, wsb=16),
+                    _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
                    (dict(wsb=16), _lib.MOE_ERR_WORKSPACE_TOO_SMALL)]:
         a = dict(fb); a.update(kw)
         assert _lib.call_status("moe_grouped_ffn_backward", *a.values()) == st
