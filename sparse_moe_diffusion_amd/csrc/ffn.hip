@@ -409,8 +409,12 @@ __device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
 // at every k step.  The descriptor is rebuilt from a uniform base and byte
 // count (stride 0, the flags make_rsrc uses); offsets at or past the count
 // read zero.  The transfer writes no register, and the kernel orders it
-// against its readers itself (vmcnt wait, then workgroup barrier).  One
-// wait state between the M0 write and the transfer that reads it.
+// against its readers itself (vmcnt wait, then workgroup barrier).  The
+// compiler's hazard checks do not see into the block, so it carries its own
+// wait states: the descriptor's SGPRs may come straight from
+// v_readfirstlane, and a VMEM instruction needs 5 wait states after a VALU
+// write of an SGPR it reads (the M0 write needs 1).  The M0 write and
+// s_nop 4 give 6.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
                                           uint32_t dst, uint32_t off) {
@@ -422,7 +426,7 @@ __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
   r[3] = 0x00020000;
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
       : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(off), "s"(r)
