@@ -35,9 +35,11 @@
  *     nothing; moe_last_error() then describes the failure (thread-local).
  *     MOE_ERR_HIP reports a launch error from the HIP runtime.  Device data
  *     are not validated: NaN/Inf inputs are outside the contract, and every
- *     kernel stays in bounds on any input values, except that row indices
- *     passed in (moe_grouped_ffn's row_index, moe_combine's slot_row) must
- *     name rows of the matrix they index, or be -1 where documented.
+ *     kernel stays in bounds on any input values, except that the slot rows
+ *     passed to moe_combine, moe_ffn_down_combine and moe_combine_backward
+ *     must name rows of y_rows, or be -1.  Row indices of the expert MLPs
+ *     (row_index) come with the row count of the matrix they index: an
+ *     entry outside it reads a zero row.
  *   - The library keeps no state between calls and is thread-safe.
  *   - Supported ranges: 1 <= E <= 64, 1 <= K <= E, D and H multiples of 8,
  *     N * Kmax < 2^31, every row count < 2^31.
@@ -168,9 +170,13 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
  * n_s*H (W1 rows concatenated, W2 columns concatenated) -- their outputs
  * sum with weight 1, which is exactly that wider MLP.
  *
- *   x_rows         [*][D] dtype;  row_index [total_rows] int32 or NULL
- *                  (row_index entries must be rows of x_rows, and x_rows
- *                  must span less than 4 GiB when row_index is used)
+ *   x_rows         [src_rows][D] dtype with row_index, else [total_rows][D]
+ *   row_index      [total_rows] int32 or NULL; an entry outside
+ *                  [0, src_rows) reads a zero row (never memory outside
+ *                  x_rows)
+ *   src_rows       rows of x_rows, read only with row_index (then >= 1 when
+ *                  stage 1 runs on rows, and (src_rows + 1) * D * element
+ *                  bytes + 256 <= 2^32)
  *   group_offsets  [G+1] int64 DEVICE array, non-decreasing, from 0 to
  *                  total_rows (total_rows is also passed by value)
  *   w1 [G][H][D], w2 [G][D][H] dtype;  b1 [G][H], b2 [G][D] fp32 or NULL
@@ -189,12 +195,14 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
  *                  read; with MOE_FFN_UP alone w2 and y_rows are not.
  * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation; h and bf16
  *   outputs are rounded to nearest even.  fp32 inputs compute in fp32.
- * Errors: INVALID_ARGUMENT for null pointers, negative sizes or stages
- *   outside 1..3; UNSUPPORTED for G > 128, D or H not multiples of 8, an unsupported dtype
- *   pair or total_rows >= 2^31.
+ * Errors: INVALID_ARGUMENT for null pointers, negative sizes, stages
+ *   outside 1..3 or src_rows < 1 with row_index; UNSUPPORTED for G > 128,
+ *   D or H not multiples of 8, an unsupported dtype pair, total_rows >=
+ *   2^31 or a gathered x_rows past the 4 GiB range above.
  */
 moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
-                           moe_dtype dtype, int64_t total_rows,
+                           int64_t src_rows, moe_dtype dtype,
+                           int64_t total_rows,
                            const int64_t* group_offsets, int32_t G, int32_t D,
                            int32_t H, const void* w1, const float* b1,
                            const void* w2, const float* b2, void* h_ws,
@@ -210,13 +218,15 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
  * in moe_grouped_ffn, so both calls give identical results.
  *
  *   arguments as moe_grouped_ffn, without h_ws and stages
- * Errors: INVALID_ARGUMENT for null pointers or negative sizes;
- *   UNSUPPORTED unless dtype is MOE_BF16 (y_dtype MOE_BF16 or MOE_F32),
- *   D is 128, 256 or 384 and H is a multiple of 64, G <= 128,
- *   total_rows < 2^31.
+ * Errors: INVALID_ARGUMENT for null pointers, negative sizes or src_rows
+ *   < 1 with row_index; UNSUPPORTED unless dtype is MOE_BF16 (y_dtype
+ *   MOE_BF16 or MOE_F32), D is 128, 256 or 384 and H is a multiple of 64,
+ *   G <= 128, total_rows < 2^31 and a gathered x_rows fits the 4 GiB range
+ *   of moe_grouped_ffn.
  */
 moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
-                                 moe_dtype dtype, int64_t total_rows,
+                                 int64_t src_rows, moe_dtype dtype,
+                                 int64_t total_rows,
                                  const int64_t* group_offsets, int32_t G,
                                  int32_t D, int32_t H, const void* w1,
                                  const float* b1, const void* w2,
@@ -367,7 +377,10 @@ moe_status moe_combine_backward(const void* dy, moe_dtype dy_dtype,
                                 void* dy_rows, float* slot_grad,
                                 hipStream_t stream);
 
-/* Bytes of workspace moe_grouped_ffn_backward needs (0 for bad sizes). */
+/* Bytes of workspace moe_grouped_ffn_backward needs (0 for bad sizes).  The
+ * size depends on the shape and on the compute-unit count of the current
+ * device (it holds the partials of a split reduction sized to fill that
+ * device): query it with the device current that the call will run on. */
 size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
                                        int32_t D, int32_t H);
 
@@ -379,8 +392,9 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
  *   dx_rows = du W1_g                                  (dx_dtype out)
  *   dW1[g]  = sum over the group's rows of du^T x_rows  (fp32 out)
  *   dW2[g]  = sum over the group's rows of dy_rows^T h  (fp32 out)
- * Rows, groups, row_index (gather) and weights are those of the forward
- * moe_grouped_ffn call.  dW1 / dW2 are written whole (zero for empty
+ * Rows, groups, row_index and src_rows (gather) and weights are those of
+ * the forward moe_grouped_ffn call (an index entry outside [0, src_rows)
+ * reads a zero row).  dW1 / dW2 are written whole (zero for empty
  * groups).
  *   u_rows  [total_rows][H] bf16: the forward's u_ws, or NULL to recompute
  *           u here (the same bits);
@@ -395,13 +409,14 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
  *   weight-gradient tiles meet long token segments, the fp32 partials of a
  *   split reduction, added in a fixed order); contents need no
  *   initialisation
- * Errors: INVALID_ARGUMENT for null pointers or bad sizes;
- *   UNSUPPORTED for non-bf16 inputs, G > 128, D or H not multiples of 8,
- *   (total_rows + 64) * max(D, H) * 2 >= 2^32; WORKSPACE_TOO_SMALL.
+ * Errors: INVALID_ARGUMENT for null pointers, bad sizes or src_rows < 1
+ *   with row_index; UNSUPPORTED for non-bf16 inputs, G > 128, D or H not
+ *   multiples of 8, (total_rows + 64) * max(D, H) * 2 >= 2^32, a gathered
+ *   x_rows past the 4 GiB range of moe_grouped_ffn; WORKSPACE_TOO_SMALL.
  */
 moe_status moe_grouped_ffn_backward(
-    const void* x_rows, const int32_t* row_index, moe_dtype dtype,
-    int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
+    const void* x_rows, const int32_t* row_index, int64_t src_rows,
+    moe_dtype dtype, int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
     int32_t H, const void* w1, const float* b1, const void* w2,
     const void* dy_rows, const void* u_rows, const void* h_rows,
     void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype,

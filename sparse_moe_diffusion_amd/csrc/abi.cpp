@@ -7,6 +7,7 @@
 
 #include <string>
 
+#include "gather.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -50,6 +51,24 @@ constexpr int kMaxGroups = moe::kMaxFfnGroups;
   do {                                                                     \
     if ((cond) && (p) == nullptr)                                          \
       return fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s is null", fn, #p);     \
+  } while (0)
+
+// Rows gathered through a row index: the source matrix needs at least one
+// row, and its bytes must stay addressable by the kernels' 32-bit buffer
+// offsets (index entries outside [0, src_rows) then read zero rows).
+#define CHECK_GATHER(rows, row_index, src_rows, row_bytes)                 \
+  do {                                                                     \
+    if ((rows) && (row_index) != nullptr) {                                \
+      if ((src_rows) < 1)                                                  \
+        return fail(MOE_ERR_INVALID_ARGUMENT,                              \
+                    "%s: src_rows=%lld, need >= 1 with row_index", fn,     \
+                    (long long)(src_rows));                                \
+      if (!moe::gather_fits((src_rows), (row_bytes)))                      \
+        return fail(MOE_ERR_UNSUPPORTED,                                   \
+                    "%s: src_rows=%lld rows of %lld bytes exceed the "     \
+                    "4 GiB gather range",                                  \
+                    fn, (long long)(src_rows), (long long)(row_bytes));    \
+    }                                                                      \
   } while (0)
 
 }  // namespace
@@ -159,7 +178,8 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
 }
 
 moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
-                           moe_dtype dtype, int64_t total_rows,
+                           int64_t src_rows, moe_dtype dtype,
+                           int64_t total_rows,
                            const int64_t* group_offsets, int32_t G, int32_t D,
                            int32_t H, const void* w1, const float* b1,
                            const void* w2, const float* b2, void* h_ws,
@@ -190,15 +210,19 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                 fn, D, H);
   if (total_rows >= kI32Limit)
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows must stay below 2^31", fn);
+  CHECK_GATHER(rows && up, row_index, src_rows,
+               static_cast<int64_t>(D) * (dtype == MOE_BF16 ? 2 : 4));
   moe::FfnArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
                  w1,     b1,        w2,         b2,            h_ws, y_rows,
                  dtype == MOE_BF16,  y_dtype == MOE_F32};
   a.u = up ? u_ws : nullptr;
+  a.src_rows = src_rows;
   return from_hip(moe::launch_ffn(a, up, down, stream), fn);
 }
 
 moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
-                                 moe_dtype dtype, int64_t total_rows,
+                                 int64_t src_rows, moe_dtype dtype,
+                                 int64_t total_rows,
                                  const int64_t* group_offsets, int32_t G,
                                  int32_t D, int32_t H, const void* w1,
                                  const float* b1, const void* w2,
@@ -223,9 +247,11 @@ moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
                 "(D=%d, H=%d)", fn, D, H);
   if (total_rows >= kI32Limit)
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows must stay below 2^31", fn);
+  CHECK_GATHER(rows, row_index, src_rows, static_cast<int64_t>(D) * 2);
   moe::FfnArgs a{x_rows, row_index, total_rows, group_offsets, G, D, H,
                  w1,     b1,        w2,         b2,            nullptr, y_rows,
                  true,   y_dtype == MOE_F32};
+  a.src_rows = src_rows;
   return from_hip(moe::launch_mlp_fused(a, stream), fn);
 }
 
@@ -409,8 +435,8 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G, int32_t D,
 }
 
 moe_status moe_grouped_ffn_backward(
-    const void* x_rows, const int32_t* row_index, moe_dtype dtype,
-    int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
+    const void* x_rows, const int32_t* row_index, int64_t src_rows,
+    moe_dtype dtype, int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
     int32_t H, const void* w1, const float* b1, const void* w2,
     const void* dy_rows, const void* u_rows, const void* h_rows,
     void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype,
@@ -439,6 +465,7 @@ moe_status moe_grouped_ffn_backward(
           (int64_t(1) << 32))
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows=%lld too large", fn,
                 (long long)total_rows);
+  CHECK_GATHER(rows, row_index, src_rows, static_cast<int64_t>(D) * 2);
   if (workspace_bytes < moe::ffn_backward_workspace_bytes(total_rows, G, D, H))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace below %zu bytes",
                 fn, moe::ffn_backward_workspace_bytes(total_rows, G, D, H));
@@ -447,6 +474,7 @@ moe_status moe_grouped_ffn_backward(
                     dx_rows, dx_dtype == MOE_F32, dw1, dw2};
   a.u_saved = u_rows;
   a.h_saved = h_rows;
+  a.src_rows = src_rows;
   return from_hip(moe::launch_ffn_backward(a, stream), fn);
 }
 

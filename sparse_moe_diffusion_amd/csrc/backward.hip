@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "gather.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(
 template <bool GELU>
 __global__ __launch_bounds__(256) void rows_kernel(
     const uint16_t* __restrict__ src, const int32_t* __restrict__ row_index,
-    int64_t total, int C, uint16_t* __restrict__ dst) {
+    int64_t src_rows, int64_t total, int C, uint16_t* __restrict__ dst) {
   const int cpr = C / 8;
   const int64_t n = total * cpr;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
@@ -96,7 +97,10 @@ __global__ __launch_bounds__(256) void rows_kernel(
     const int64_t r = i / cpr;
     const int c = static_cast<int>(i - r * cpr) * 8;
     const int64_t sr = row_index ? row_index[r] : r;
-    uint4 v = *reinterpret_cast<const uint4*>(src + sr * C + c);
+    // an index entry outside [0, src_rows) gives a zero row
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row_index == nullptr || gather_row_valid(sr, src_rows))
+      v = *reinterpret_cast<const uint4*>(src + sr * C + c);
     if constexpr (GELU) {
       float f[8];
       unpack8(v, f);
@@ -412,20 +416,20 @@ hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
 }
 
 hipError_t launch_rows(const void* src, const int32_t* row_index,
-                       int64_t total, int C, bool gelu, void* dst,
-                       hipStream_t stream) {
+                       int64_t src_rows, int64_t total, int C, bool gelu,
+                       void* dst, hipStream_t stream) {
   if (total == 0 || C == 0) return hipSuccess;
   const int64_t n = total * (C / 8);
   const unsigned grid =
       static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 8192));
   if (gelu)
     hipLaunchKernelGGL(rows_kernel<true>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), row_index, total, C,
-                       static_cast<uint16_t*>(dst));
+                       static_cast<const uint16_t*>(src), row_index, src_rows,
+                       total, C, static_cast<uint16_t*>(dst));
   else
     hipLaunchKernelGGL(rows_kernel<false>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), row_index, total, C,
-                       static_cast<uint16_t*>(dst));
+                       static_cast<const uint16_t*>(src), row_index, src_rows,
+                       total, C, static_cast<uint16_t*>(dst));
   return hipGetLastError();
 }
 

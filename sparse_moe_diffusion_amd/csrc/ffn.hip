@@ -42,6 +42,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "gather.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -87,6 +88,9 @@ struct GemmParams {
   // kEpiGelu with bf16 output: if set, also the pre-activations u = A W^T
   // + bias, [total][Nd] bf16 (kept by a training forward for the backward).
   void* u_out;
+  // With a_index: the rows of a.  Index entries outside [0, a_rows) read
+  // zero rows (the gathered rows' descriptor spans exactly a_rows rows).
+  int64_t a_rows;
 };
 
 struct TileLoc {
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const int64_t kg_a =
       KG ? (static_cast<int64_t>(loc.klen) * p.mrows - kg_m) * 2 : 0;
   const uint32_t a_bytes =
-      gather ? kOutOfRange
+      gather ? static_cast<uint32_t>(p.a_rows) * row_bytes
       : KG   ? static_cast<uint32_t>(kg_a > 0 ? kg_a : 0)
              : static_cast<uint32_t>(min(static_cast<int>(loc.row_end - loc.row0), BM)) *
                    row_bytes;
@@ -620,10 +624,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     ldst[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r0 * kBK * 2));
     if (isA) {
       const bool valid = loc.row0 + r < loc.row_end;
-      const uint32_t src =
-          gather ? static_cast<uint32_t>(sidx[(it & 1) * BM + r])
-                 : static_cast<uint32_t>(valid ? r : 0);
-      goff[q] = src * row_bytes + c * 16u;
+      goff[q] = gather ? gather_row_offset(sidx[(it & 1) * BM + r],
+                                           static_cast<uint32_t>(p.a_rows),
+                                           row_bytes, c * 16u)
+                       : static_cast<uint32_t>(valid ? r : 0) * row_bytes +
+                             c * 16u;
     } else {
       goff[q] = static_cast<uint32_t>(r) * row_bytes + c * 16u;
     }
@@ -1178,15 +1183,21 @@ __global__ __launch_bounds__(64 * kMlpWaves, 1) void mlp_fused_kernel(
   // This lane's token row as phase A's B operand: k 16 s + 8 khalf .. + 8
   // of step s.  Rows past the group end re-read the tile's first row (never
   // stored).
+  // An index entry outside [0, a_rows) gives a zero row.
   bf16x8 xf[KS];
   {
     const int64_t row = loc.row0 + tb * 32 + (lane & 31);
     const int64_t r = row < loc.row_end ? row : loc.row0;
     const int64_t src = p.a_index != nullptr ? p.a_index[r] : r;
-    const uint16_t* const xr = static_cast<const uint16_t*>(p.a) + src * D + 8 * khalf;
+    const bool ok = p.a_index == nullptr || gather_row_valid(src, p.a_rows);
+    const uint16_t* const xr =
+        static_cast<const uint16_t*>(p.a) + (ok ? src : 0) * D + 8 * khalf;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = ok ? *reinterpret_cast<const uint4*>(xr + 16 * s)
+                         : make_uint4(0, 0, 0, 0);
+      xf[s] = __builtin_bit_cast(bf16x8, v);
+    }
   }
   f32x16 acc[FBY];
 #pragma unroll
@@ -1336,9 +1347,14 @@ __global__ __launch_bounds__(kF32Threads) void gemm_f32_kernel(GemmParams p) {
   // loads: row tid >> 2 (0..63), k quad (tid & 3) * 4
   const int lrow = tid >> 2, lk = (tid & 3) * 4;
   const int64_t grow = loc.row0 + lrow;
-  const bool a_ok = grow < loc.row_end;
+  bool a_ok = grow < loc.row_end;
   int64_t src = 0;
   if (a_ok) src = (p.a_index != nullptr) ? p.a_index[grow] : grow;
+  // an index entry outside [0, a_rows) gives a zero row
+  if (a_ok && p.a_index != nullptr && !gather_row_valid(src, p.a_rows)) {
+    a_ok = false;
+    src = 0;
+  }
   const float* a_src = A + src * Kd + lk;
   const int f = loc.n0 + lrow;
   const bool b_ok = f < p.Nd;
@@ -1442,8 +1458,9 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Reduction splits of the K-grouped weight-gradient GEMMs ([G][M][N] out,
 // 256 x 256 tiles, `total` token rows over G groups): the largest S <= 8
-// whose S x tiles still fit one round of the chip (assumed 256 CUs, so the
-// choice and the workspace depend on the shape alone) and whose pieces keep
+// whose S x tiles still fit one round of the chip (the current device's CU
+// count, as the persistent grids use; the workspace query and the launch
+// take the same count, so the partials always fit) and whose pieces keep
 // at least 2048 tokens of an average group.  Measured: the shared experts'
 // weight gradients of the S layer (24 tiles, 8192 tokens) take 0.28 instead
 // of 0.46 ms per backward call with S = 4; splits past one round, or into
@@ -1452,10 +1469,11 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 int choose_ksplit(int G, int M, int N, int64_t total) {
   const int64_t tiles = static_cast<int64_t>(G) * ((M + kUpBM - 1) / kUpBM) *
                         ((N + kUpBN - 1) / kUpBN);
-  constexpr int64_t kCus = 256, kMinTokens = 2048;
+  constexpr int64_t kMinTokens = 2048;
+  const int64_t cus = cu_count();
   const int64_t per_group = G > 0 ? total / G : 0;
   int S = 1;
-  while (S < 8 && tiles * (S + 1) <= kCus && per_group / (S + 1) >= kMinTokens)
+  while (S < 8 && tiles * (S + 1) <= cus && per_group / (S + 1) >= kMinTokens)
     ++S;
   return S;
 }
@@ -1537,6 +1555,7 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
     if (uu == nullptr) {
       GemmParams pu{a.x, a.row_index, a.w1, a.b1, u, a.offsets, a.total_rows,
                     G, H, D};
+      pu.a_rows = a.src_rows;
       if (a.h_saved == nullptr) {
         pu.c = ws + L.h;
         pu.u_out = u;
@@ -1549,7 +1568,8 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
       MOE_TRY(hipGetLastError());
       uu = u;
     } else if (a.h_saved == nullptr) {
-      MOE_TRY(launch_rows(uu, nullptr, a.total_rows, H, true, ws + L.h, stream));
+      MOE_TRY(launch_rows(uu, nullptr, 0, a.total_rows, H, true, ws + L.h,
+                          stream));
     }
     GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
                   a.total_rows, G, H, D};
@@ -1567,7 +1587,8 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
           px, stream);
     MOE_TRY(hipGetLastError());
     if (a.row_index != nullptr)
-      MOE_TRY(launch_rows(a.x, a.row_index, a.total_rows, D, false, ws + L.xr, stream));
+      MOE_TRY(launch_rows(a.x, a.row_index, a.src_rows, a.total_rows, D, false,
+                          ws + L.xr, stream));
   }
   // dW2[g] [D][H] = dy_rows[g]^T h[g];  dW1[g] [H][D] = du[g]^T x_rows[g].
   // With no rows every segment is empty and the products are zero.
@@ -1635,6 +1656,7 @@ hipError_t launch_mlp_fused(const FfnArgs& a, hipStream_t stream) {
   if (a.total_rows == 0) return hipSuccess;
   GemmParams p{a.x, a.row_index, a.w1, a.b1, a.y, a.offsets, a.total_rows,
                a.G, a.D, a.D};
+  p.a_rows = a.src_rows;
   const int tiles = tile_grid(p, kMlpBM, a.D);
   const dim3 grid(static_cast<unsigned>(tiles)), block(64 * kMlpWaves);
   const int yf = a.y_f32 ? 1 : 0;
@@ -1660,6 +1682,7 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
   GemmParams p1{a.x, a.row_index, a.w1, a.b1, a.h, a.offsets, a.total_rows,
                 a.G, a.H, a.D};
   p1.u_out = a.u;
+  p1.a_rows = a.src_rows;
   GemmParams p2{a.h, nullptr, a.w2, a.b2, a.y, a.offsets, a.total_rows,
                 a.G, a.D, a.H};
   if (a.bf16) {

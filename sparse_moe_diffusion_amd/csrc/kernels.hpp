@@ -53,6 +53,7 @@ struct FfnArgs {
   bool bf16;                // input / weight / h dtype
   bool y_f32;               // output dtype
   void* u = nullptr;        // [total][H] bf16 pre-activations out, or null
+  int64_t src_rows = 0;     // rows of x when row_index is given
 };
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
 // Both stages in one kernel (bf16, D in {128, 256, 384}, H % 64 == 0); h is
@@ -88,9 +89,11 @@ hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
 // backward.hip
 hipError_t launch_transpose(const void* src, int G, int R, int C, void* dst,
                             hipStream_t stream);
+// dst[r] = src[row_index[r]] (or src[r]), optionally through GELU; index
+// entries outside [0, src_rows) give zero rows.
 hipError_t launch_rows(const void* src, const int32_t* row_index,
-                       int64_t total, int C, bool gelu, void* dst,
-                       hipStream_t stream);
+                       int64_t src_rows, int64_t total, int C, bool gelu,
+                       void* dst, hipStream_t stream);
 hipError_t launch_combine_backward(const void* dy, bool dy_bf16,
                                    const void* y_rows, bool y_bf16,
                                    const int32_t* slot_row, const float* w,
@@ -125,6 +128,7 @@ struct FfnBwdArgs {
   float* dw2;               // [G][D][H]
   const void* u_saved = nullptr;  // [total][H] forward pre-activations, or null
   const void* h_saved = nullptr;  // [total][H] forward activations, or null
+  int64_t src_rows = 0;           // rows of x when row_index is given
 };
 size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H);
 hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream);

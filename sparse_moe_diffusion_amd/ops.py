@@ -33,6 +33,11 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _src_rows(x_rows) -> int:
+    """Row count of a matrix the expert MLPs gather rows from."""
+    return 0 if x_rows is None else int(x_rows.shape[0])
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -74,7 +79,7 @@ def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
     else:                      # stage 2 alone
         G, D, H = w2.shape
     _lib.call("moe_grouped_ffn", _ptr(x_rows), _ptr(row_index),
-              dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _src_rows(x_rows), dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
               _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(u_ws),
               _ptr(y_rows),
               dtype_code(y_rows.dtype if y_rows is not None else h_ws.dtype),
@@ -85,7 +90,7 @@ def moe_grouped_mlp_fused(x_rows, row_index, total_rows: int, group_offsets,
                           w1, b1, w2, b2, y_rows):
     G, H, D = w1.shape
     _lib.call("moe_grouped_mlp_fused", _ptr(x_rows), _ptr(row_index),
-              dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _src_rows(x_rows), dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
               _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y_rows),
               dtype_code(y_rows.dtype), _stream())
 
@@ -165,7 +170,7 @@ def moe_grouped_ffn_backward(x_rows, row_index, total_rows: int, group_offsets,
                              u_rows=None, h_rows=None):
     G, H, D = w1.shape
     _lib.call("moe_grouped_ffn_backward", _ptr(x_rows), _ptr(row_index),
-              dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
+              _src_rows(x_rows), dtype_code(w1.dtype), total_rows, _ptr(group_offsets), G, D, H,
               _ptr(w1), _ptr(b1), _ptr(w2), _ptr(dy_rows), _ptr(u_rows),
               _ptr(h_rows), _ptr(workspace),
               workspace.numel() * workspace.element_size(), _ptr(dx_rows),

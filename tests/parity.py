@@ -8,8 +8,12 @@ the oracle evaluated on that reconciled routing.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle
 import synth
@@ -174,7 +178,7 @@ def check_layer(inp, g, sample_tokens=None, balance_mode="sequence",
     assert np.array_equal(g["slot_row"], slot_row)
     # outputs
     tokens = np.arange(cfg.N) if sample_tokens is None else np.asarray(sample_tokens)
-    yo = oracle.layer_output(inp, rec, wo, tokens)
+    yo = oracle_layer_output(inp, rec, wo, tokens)
     rep["y_max_rel"], rep["y_mean_rel"] = assert_close(g["y"][tokens], yo,
                                                        cfg.dtype, "y")
     # balance statistic
@@ -185,6 +189,39 @@ def check_layer(inp, g, sample_tokens=None, balance_mode="sequence",
     rep["loss"], rep["loss_ref"] = g["loss"], loss
     assert abs(g["loss"] - loss) <= LOSS_RTOL * abs(loss), (g["loss"], loss)
     return rep
+
+
+def workers() -> int:
+    """Host threads for the oracle's chunked runs: the CPUs this process may
+    use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def pmap(fn, items):
+    """[fn(i) for i in items] on a thread pool, BLAS held to one thread per
+    call.  numpy's elementwise passes and matrix products release the GIL,
+    so oracle calls on disjoint row chunks run side by side; each result is
+    the oracle's own call on its chunk."""
+    items = list(items)
+    with threadpool_limits(1), ThreadPoolExecutor(workers()) as ex:
+        return list(ex.map(fn, items))
+
+
+def chunks(rows, size=1024):
+    rows = np.asarray(rows)
+    return [rows[i:i + size] for i in range(0, rows.size, size)]
+
+
+def oracle_layer_output(inp, idx, w, tokens=None):
+    """oracle.layer_output on every token (or on ``tokens``), evaluated as
+    the oracle's calls on chunks of 1024 tokens in parallel."""
+    tokens = np.arange(inp.cfg.N) if tokens is None else np.asarray(tokens)
+    parts = pmap(lambda t: oracle.layer_output(inp, idx, w, t), chunks(tokens))
+    return np.concatenate(parts) if parts else np.zeros((0, inp.cfg.D))
 
 
 def sample_tokens(cfg, n=48, seed=0):

@@ -100,7 +100,8 @@ def test_permute_rejects(kw, status):
 
 
 def _ffn(**kw):
-    a = dict(x=FAKE, idx=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
+    a = dict(x=FAKE, idx=None, src=0, dt=_lib.MOE_BF16, total=100, offs=FAKE,
+             G=8,
              D=128, H=512, w1=FAKE, b1=None, w2=FAKE, b2=None, h=FAKE, u=None,
              y=FAKE, ydt=_lib.MOE_BF16, stages=_lib.MOE_FFN_BOTH, stream=None)
     a.update(kw)
@@ -122,6 +123,14 @@ def _ffn(**kw):
     (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_BF16), _lib.MOE_ERR_UNSUPPORTED),
     (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_F32, u=FAKE), _lib.MOE_ERR_UNSUPPORTED),
     (dict(total=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
+    # gathered rows: the source matrix's row count bounds the index
+    (dict(idx=FAKE, src=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(idx=FAKE, src=-3), _lib.MOE_ERR_INVALID_ARGUMENT),
+    # (src + 1) * D * 2 + 256 must stay within 2^32 (D = 128: src <= 2^24 - 2)
+    (dict(idx=FAKE, src=(1 << 24) - 1), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(idx=FAKE, src=1 << 40), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(idx=FAKE, src=(1 << 23), dt=_lib.MOE_F32, ydt=_lib.MOE_F32),
+     _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_ffn_rejects(kw, status):
     ensure_built()
@@ -152,8 +161,8 @@ def test_combine_and_balance_reject():
 
 
 def _mlp_fused(**kw):
-    a = dict(x=FAKE, ri=None, dt=_lib.MOE_BF16, total=256, off=FAKE, G=2,
-             D=384, H=1536, w1=FAKE, b1=None, w2=FAKE, b2=None, y=FAKE,
+    a = dict(x=FAKE, ri=None, src=0, dt=_lib.MOE_BF16, total=256, off=FAKE,
+             G=2, D=384, H=1536, w1=FAKE, b1=None, w2=FAKE, b2=None, y=FAKE,
              ydt=_lib.MOE_BF16, stream=None)
     a.update(kw)
     return _lib.call_status("moe_grouped_mlp_fused", *a.values())
@@ -171,6 +180,8 @@ def _mlp_fused(**kw):
     (dict(dt=_lib.MOE_F32, ydt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
     (dict(ydt=7), _lib.MOE_ERR_UNSUPPORTED),
     (dict(G=129), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(ri=FAKE, src=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(ri=FAKE, src=1 << 23), _lib.MOE_ERR_UNSUPPORTED),
 ])
 def test_mlp_fused_rejects(kw, status):
     ensure_built()
@@ -288,7 +299,8 @@ def test_backward_entry_points_reject():
                    (dict(Kmax=65), _lib.MOE_ERR_UNSUPPORTED)]:
         a = dict(cb); a.update(kw)
         assert _lib.call_status("moe_combine_backward", *a.values()) == st
-    fb = dict(x=FAKE, ri=None, dt=_lib.MOE_BF16, total=100, offs=FAKE, G=8,
+    fb = dict(x=FAKE, ri=None, src=0, dt=_lib.MOE_BF16, total=100, offs=FAKE,
+              G=8,
               D=128, H=256, w1=FAKE, b1=None, w2=FAKE, dyr=FAKE, u=None,
               h=None, ws=FAKE, wsb=1 << 40, dx=FAKE, dxdt=_lib.MOE_BF16,
               dw1=FAKE, dw2=FAKE, stream=None)
@@ -304,7 +316,14 @@ def test_backward_entry_points_reject():
                    (dict(total=(1 << 23) - 64), _lib.MOE_ERR_UNSUPPORTED),
                    (dict(total=(1 << 23) - 65, wsb=16),
                     _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
-                   (dict(wsb=16), _lib.MOE_ERR_WORKSPACE_TOO_SMALL)]:
+                   (dict(wsb=16), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+                   (dict(ri=FAKE, src=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+                   # D = 128: src <= 2^24 - 2 passes the gather check and
+                   # reaches the workspace check
+                   (dict(ri=FAKE, src=(1 << 24) - 1),
+                    _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(ri=FAKE, src=(1 << 24) - 2, wsb=16),
+                    _lib.MOE_ERR_WORKSPACE_TOO_SMALL)]:
         a = dict(fb); a.update(kw)
         assert _lib.call_status("moe_grouped_ffn_backward", *a.values()) == st
     gb = dict(x=FAKE, xdt=_lib.MOE_BF16, wg=FAKE, P=FAKE, idx=FAKE, sg=FAKE,

@@ -1,13 +1,13 @@
 """Whole-layer parity: the HIP path through the C ABI against the CPU oracle.
 
-Small layers are compared on every token; the full-size workloads compare
-routing, permutation and balance on every token and outputs on a sample.
+Every layer, the full-size workloads included, is compared on every token:
+routing, permutation, outputs and the balance statistic.
 """
 import numpy as np
 import pytest
 
 import synth
-from parity import GpuLayer, check_layer, sample_tokens
+from parity import GpuLayer, check_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,12 @@ def test_balance_modes(mode):
     check_layer(inp, g, balance_mode=mode)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", list(synth.CONFIGS))
 def test_full_size_workload(name):
+    """The benchmark's workloads at their full sizes, in the launch
+    configuration it times (gathered rows, fused gate+balance and
+    stage-2+combine where the layer fuses them): y on all N tokens."""
     cfg = synth.CONFIGS[name]
     print(f"[full-size] {name} N={cfg.N} D={cfg.D} H={cfg.H} E={cfg.E}",
           flush=True)
@@ -68,7 +72,7 @@ def test_full_size_workload(name):
     gl = GpuLayer(inp, gather=True).run()
     g = gl.result()
     del gl
-    rep = check_layer(inp, g, sample_tokens=sample_tokens(cfg, 48))
+    rep = check_layer(inp, g)
     counts = g["expert_counts"]
     print(name, rep, "expert rows", counts.tolist(), flush=True)
     assert counts.sum() == cfg.A
