@@ -153,6 +153,34 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* Bytes of the static scratch moe_permute_noalloc works in. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as moe_permute,
+ * minus the workspace: its block counts and bases live in a static device
+ * array of MOE_PERMUTE_NOALLOC_SCRATCH_BYTES bytes, one per device, held
+ * until the process ends.  The call allocates nothing.
+ *
+ * Limit: moe_permute_workspace_size(N, E, Kmax) must not exceed the scratch
+ *   (about N * E <= 22 million, e.g. N <= 2.7 million tokens at E = 8);
+ *   larger inputs return MOE_ERR_UNSUPPORTED.
+ * Concurrency: every call on a device shares that device's scratch.  Calls
+ *   that may overlap on one device (different streams, or several host
+ *   threads) race and give wrong results; order them, e.g. on one stream.
+ *   Nothing in the scratch needs to start at zero.
+ * The first call on a device looks up the scratch's address on that
+ *   device (hipGetSymbolAddress); a failure there returns MOE_ERR_HIP.
+ */
+moe_status moe_permute_noalloc(const void* x, moe_dtype dtype,
+                               const int32_t* topk_idx, int64_t N, int32_t D,
+                               int32_t E, int32_t Kmax, int32_t K,
+                               int32_t* expert_counts, int64_t* expert_offsets,
+                               int32_t* row_token, int32_t* slot_row,
+                               void* x_perm, hipStream_t stream);
+
 /*
  * The experts' MLPs over row groups ("Scaling Diffusion Transformers to 16
  * Billion Parameters", MoE-DiT eq. MLP; "Scalable Diffusion Models with

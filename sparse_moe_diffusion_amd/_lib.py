@@ -45,6 +45,8 @@ SIGNATURES = {
     "moe_permute_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_permute": (_E, [_P, _E, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P,
                          _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc": (_E, [_P, _E, _P, _I64, _I32, _I32, _I32, _I32, _P,
+                                 _P, _P, _P, _P, _P]),
     "moe_grouped_ffn": (_E, [_P, _P, _I64, _E, _I64, _P, _I32, _I32, _I32, _P,
                              _P, _P, _P, _P, _P, _P, _E, _E, _P]),
     "moe_grouped_mlp_fused": (_E, [_P, _P, _I64, _E, _I64, _P, _I32, _I32,

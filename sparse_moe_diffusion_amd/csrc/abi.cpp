@@ -139,13 +139,18 @@ size_t moe_permute_workspace_size(int64_t N, int32_t E, int32_t Kmax) {
   return moe::permute_workspace_bytes(N, E);
 }
 
-moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
-                       int64_t N, int32_t D, int32_t E, int32_t Kmax, int32_t K,
-                       int32_t* expert_counts, int64_t* expert_offsets,
-                       int32_t* row_token, int32_t* slot_row, void* x_perm,
-                       void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
-  const char* fn = "moe_permute";
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by moe_permute and moe_permute_noalloc.
+moe_status check_permute(const char* fn, const void* x, moe_dtype dtype,
+                         const int32_t* topk_idx, int64_t N, int32_t D,
+                         int32_t E, int32_t Kmax, int32_t K,
+                         const int32_t* expert_counts,
+                         const int64_t* expert_offsets,
+                         const int32_t* row_token, const int32_t* slot_row,
+                         const void* x_perm) {
   if (N < 0 || D < 1 || E < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, E >= 1", fn);
   if (K < 1 || K > E)
@@ -164,6 +169,24 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
     return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d not a multiple of 8", fn, D);
   if (N * Kmax >= kI32Limit)
     return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
+                       int64_t N, int32_t D, int32_t E, int32_t Kmax, int32_t K,
+                       int32_t* expert_counts, int64_t* expert_offsets,
+                       int32_t* row_token, int32_t* slot_row, void* x_perm,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const char* fn = "moe_permute";
+  const moe_status st =
+      check_permute(fn, x, dtype, topk_idx, N, D, E, Kmax, K, expert_counts,
+                    expert_offsets, row_token, slot_row, x_perm);
+  if (st != MOE_OK) return st;
   const size_t need = moe_permute_workspace_size(N, E, Kmax);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
@@ -173,6 +196,35 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
   return from_hip(moe::launch_permute(x, dtype == MOE_BF16, topk_idx, N, D, E,
                                       Kmax, A, expert_counts, expert_offsets,
                                       row_token, slot_row, x_perm, workspace,
+                                      stream),
+                  fn);
+}
+
+moe_status moe_permute_noalloc(const void* x, moe_dtype dtype,
+                               const int32_t* topk_idx, int64_t N, int32_t D,
+                               int32_t E, int32_t Kmax, int32_t K,
+                               int32_t* expert_counts, int64_t* expert_offsets,
+                               int32_t* row_token, int32_t* slot_row,
+                               void* x_perm, hipStream_t stream) {
+  const char* fn = "moe_permute_noalloc";
+  const moe_status st =
+      check_permute(fn, x, dtype, topk_idx, N, D, E, Kmax, K, expert_counts,
+                    expert_offsets, row_token, slot_row, x_perm);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_permute_workspace_size(N, E, Kmax);
+  if (need > moe::permute_scratch_bytes())
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: N=%lld, E=%d need %zu bytes of scratch, above the %zu "
+                "bytes of the static scratch (use moe_permute with a "
+                "workspace)",
+                fn, (long long)N, E, need, moe::permute_scratch_bytes());
+  void* scratch = nullptr;
+  const hipError_t err = moe::permute_scratch(&scratch);
+  if (err != hipSuccess) return from_hip(err, fn);
+  const int64_t A = static_cast<int64_t>(K) * N;
+  return from_hip(moe::launch_permute(x, dtype == MOE_BF16, topk_idx, N, D, E,
+                                      Kmax, A, expert_counts, expert_offsets,
+                                      row_token, slot_row, x_perm, scratch,
                                       stream),
                   fn);
 }

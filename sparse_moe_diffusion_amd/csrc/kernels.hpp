@@ -29,6 +29,10 @@ hipError_t launch_race(const float* probs, int64_t N, int E, int K,
 
 // permute.hip
 size_t permute_workspace_bytes(int64_t N, int E);
+// The allocation-free variant's static scratch: its size, and its address on
+// the current device (looked up once per device).
+size_t permute_scratch_bytes();
+hipError_t permute_scratch(void** ptr);
 hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                           int64_t N, int D, int E, int Kmax, int64_t A,
                           int32_t* counts, int64_t* offsets, int32_t* row_token,

@@ -18,6 +18,8 @@
 //     it; writes row_token, the block's slot_row (coalesced, from LDS), then
 //     copies each token row once from HBM to its K destination rows with
 //     16-byte lanes (row copy skipped when x_perm is null).
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -184,6 +186,37 @@ size_t permute_workspace_bytes(int64_t N, int E) {
   // block_counts (int32) + block_base (int64), each [nb][E], 256-B aligned
   const size_t a = ((nb * E * sizeof(int32_t)) + 255) / 256 * 256;
   return a + nb * E * sizeof(int64_t) + 256;
+}
+
+// ------------------------------------------------ allocation-free variant --
+// moe_permute_noalloc keeps the block counts and block bases in this array
+// instead of a caller's workspace.  Each device holds its own copy for the
+// life of the process.  On the host the array's name only stands in for the
+// device copies and is never passed to a kernel: permute_scratch() returns
+// the current device's address, looked up once per device.
+constexpr size_t kPermScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kPermScratchBytes];
+
+size_t permute_scratch_bytes() { return kPermScratchBytes; }
+
+hipError_t permute_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,

@@ -71,6 +71,17 @@ def moe_permute(x, topk_idx, E: int, K: int, expert_counts, expert_offsets,
               ws, _stream())
 
 
+def moe_permute_noalloc(x, topk_idx, E: int, K: int, expert_counts,
+                        expert_offsets, row_token, slot_row, x_perm):
+    """moe_permute on the library's static scratch (no workspace)."""
+    N, D = x.shape
+    Kmax = topk_idx.shape[1]
+    _lib.call("moe_permute_noalloc", _ptr(x), dtype_code(x.dtype),
+              _ptr(topk_idx), N, D, E, Kmax, K, _ptr(expert_counts),
+              _ptr(expert_offsets), _ptr(row_token), _ptr(slot_row),
+              _ptr(x_perm), _stream())
+
+
 def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
                     w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH,
                     u_ws=None):

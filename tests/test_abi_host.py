@@ -99,6 +99,44 @@ def test_permute_rejects(kw, status):
     assert _permute(**kw) == status
 
 
+def _permute_noalloc(**kw):
+    a = dict(x=FAKE, dt=_lib.MOE_BF16, idx=FAKE, N=64, D=128, E=8, Kmax=2, K=2,
+             counts=FAKE, offs=FAKE, rt=FAKE, sr=FAKE, xp=None, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_permute_noalloc", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(counts=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(idx=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(Kmax=3), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(xp=FAKE, x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=65), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    # the static scratch holds moe_permute's workspace up to 1 MiB
+    (dict(N=1 << 24, E=64, Kmax=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(N=3 << 20, E=8, Kmax=2), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_permute_noalloc_rejects(kw, status):
+    ensure_built()
+    assert _permute_noalloc(**kw) == status
+    assert "moe_permute_noalloc" in _lib.last_error()
+
+
+def test_permute_noalloc_limit_matches_workspace_size():
+    """The static scratch's size is the header's constant, and the sizes the
+    call accepts are those whose moe_permute workspace fits it."""
+    lib = ensure_built()
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES \(1u << (\d+)\)",
+                  text)
+    limit = 1 << int(m.group(1))
+    assert lib.moe_permute_workspace_size(2_700_000, 8, 2) <= limit
+    assert lib.moe_permute_workspace_size(3 << 20, 8, 2) > limit
+
+
 def _ffn(**kw):
     a = dict(x=FAKE, idx=None, src=0, dt=_lib.MOE_BF16, total=100, offs=FAKE,
              G=8,
