@@ -53,6 +53,12 @@ def parse():
     ap.add_argument("--recompute-u", action="store_true",
                     help="with --backward: the forward keeps no "
                          "pre-activations and the backward recomputes them")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="repetitions of each HBM-bound call timed after a "
+                         "1 GiB cache flush (0: skip)")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="instead of the layer, time the CPU oracle on a "
+                         "bounded sample of every configured workload")
     ap.add_argument("--mlp-fused", action="store_true",
                     help="instead of the layer, time the one-kernel expert "
                          "MLP against the two-stage grouped FFN on the "
@@ -331,14 +337,47 @@ def mlp_fused_bench(args):
           flush=True)
 
 
+def host_info():
+    """The host the CPU baseline runs on: logical CPUs, the ones this
+    process may use, CPU model, sockets, cores and threads per core."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        pass
+    try:
+        text = open("/proc/cpuinfo").read()
+    except OSError:
+        return info
+    blocks = [b for b in text.split("\n\n") if b.strip()]
+    fields = [dict((k.strip(), v.strip()) for k, v in
+                   (l.split(":", 1) for l in b.splitlines() if ":" in l))
+              for b in blocks]
+    if fields:
+        f0 = fields[0]
+        info["model"] = f0.get("model name", "")
+        sockets = {f.get("physical id") for f in fields if "physical id" in f}
+        info["sockets"] = len(sockets) or 1
+        cores = int(f0.get("cpu cores", 0) or 0)
+        sib = int(f0.get("siblings", 0) or 0)
+        if cores:
+            info["cores_per_socket"] = cores
+            info["threads_per_core"] = sib // cores if sib else 1
+    return info
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+
+
 def cpu_baseline(cfg, inp, target_s):
     """The CPU oracle on whole images of the same workload until about
-    ``target_s`` seconds of CPU work: tokens/s."""
-    import numpy as np
+    ``target_s`` seconds of CPU work (at least one image, or the first
+    ``T`` tokens' worth of a shorter slice for very wide layers): tokens/s
+    and GFLOP/s of the layer's algorithmic work."""
     import oracle
     import synth
-    from threadpoolctl import threadpool_info
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     done_tokens, elapsed, images = 0, 0.0, 0
     while elapsed < target_s and images < cfg.B:
         b = images
@@ -351,10 +390,87 @@ def cpu_baseline(cfg, inp, target_s):
         elapsed += time.perf_counter() - t0
         done_tokens += cfg.T
         images += 1
-    return {"value": done_tokens / elapsed, "unit": "tokens/s",
-            "cores": int(threads), "kind": "oracle",
+    tps = done_tokens / elapsed
+    return {"value": tps, "unit": "tokens/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "gflops": round(tps * cfg.flops_per_token() / 1e9, 2),
+            "host": host_info(),
             "sample": f"{images} image(s) x {cfg.T} tokens of {cfg.name} "
                       f"(whole layer in float64 numpy, {elapsed:.1f} s)"}
+
+
+def cpu_baseline_all(args):
+    """The oracle on a bounded sample of every configured workload (whole
+    images, about --cpu-seconds each), beside the host description: one JSON
+    line.  A reported baseline, not a target."""
+    import synth
+    rows = []
+    for name, cfg in synth.CONFIGS.items():
+        inp = synth.make_inputs(cfg)
+        r = cpu_baseline(cfg, inp, args.cpu_seconds)
+        rows.append({"workload": name, "tokens_per_s": round(r["value"], 1),
+                     "gflops": r["gflops"], "sample": r["sample"]})
+        print(json.dumps({"progress": name, **rows[-1]}), flush=True)
+        del inp
+    print(json.dumps({"metric": "CPU oracle throughput per workload",
+                      "kind": "oracle", "threads": blas_threads(),
+                      "host": host_info(), "workloads": rows}), flush=True)
+
+
+def cold_timings(cfg, x, wts, buf, steps, reps):
+    """The HBM-bound calls of the step, each timed ``reps`` times right after
+    a 1 GiB write that evicts the 256 MB memory-side cache and the L2s (so
+    their inputs come from HBM), plus two measured-only forms: the permute
+    that also copies the rows to x_perm, and the separate combine kernel
+    where the layer fuses it.  Median ms, GB/s of algorithmic bytes and the
+    fraction of the HBM peak."""
+    import torch
+    import numpy as np
+    from sparse_moe_diffusion_amd import layer
+    import copy
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    work = kernel_work(cfg, buf.gather)
+    calls = [(n, f) for n, f in steps
+             if n in ("gate", "gate_balance", "permute", "combine", "balance")]
+    extra = {}
+    if cfg.dtype == "bf16":
+        eb = 2
+        xp = torch.empty(cfg.A, cfg.D, dtype=x.dtype, device="cuda")
+        bx = copy.copy(buf)
+        bx.x_perm = xp
+        calls.append(("permute_x_perm", lambda c, x_, w, b: layer.permute(c, x_, bx)))
+        extra["permute_x_perm"] = (cfg.N * cfg.D * eb + cfg.A * cfg.D * eb +
+                                   cfg.N * cfg.Kmax * 8 + cfg.A * 4)
+        if not any(n == "combine" for n, _ in steps) and cfg.n_s > 0:
+            # the separate combine on the step's routed rows and a shared
+            # output from the unfused stage 2
+            layer.shared_ffn(cfg, x, wts, buf, layer.DOWN)
+            yc = torch.empty_like(buf.y)
+            by = copy.copy(buf)
+            by.y = yc
+            calls.append(("combine_separate", lambda c, x_, w, b: layer.combine(c, by)))
+            extra["combine_separate"] = work["combine"][1]
+    out = {}
+    for name, fn in calls:
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(cfg, x, wts, buf)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        nbytes = extra.get(name, work.get(name, ("bytes", 0))[1])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "bytes": int(nbytes),
+                     "gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    del flush
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -374,6 +490,9 @@ def main():
         return
     if args.mlp_fused:
         mlp_fused_bench(args)
+        return
+    if args.cpu_baseline_all:
+        cpu_baseline_all(args)
         return
     import torch
     import synth
@@ -504,6 +623,9 @@ def main():
                                  else None)},
         "kernels": kernels,
     }
+    if args.cold_reps > 0:
+        out["kernels_cache_cold"] = cold_timings(cfg, x, wts, buf, steps,
+                                                 args.cold_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -320,15 +320,14 @@ size_t moe_gate_balance_workspace_size(int32_t B, int32_t T, int32_t E);
  * moe_gate_topk (MOE_ROUTE_TOPK) followed by moe_balance_stats (Kmax = K)
  * compute, for N = B*T tokens, image b owning tokens [bT, (b+1)T).
  *
- * When x is bf16, T is a multiple of 16 and the gate weights fit the
- * streaming gate kernel (E <= 16 and 3*ceil(D/32)*4*(8 or 16)*16 bytes
- * <= 144 KiB), the gate kernel also reduces each 16-token group to partial
+ * When x is bf16, T is a multiple of 16 and E <= 16 (the streaming gate
+ * kernel), the gate kernel also reduces each 16-token group to partial
  * sums in the workspace and one small kernel finishes counts, prob_sums and
  * the loss; probs, topk_idx, topk_w and counts are then bit for bit those of
  * the separate calls, and prob_sums and loss differ from them only by the
- * order of the fp32 additions (16 tokens in order, then the groups in
- * order).  Otherwise the separate kernels run.  Either way the result is
- * deterministic.
+ * order of the fp32 additions (pairwise over each 16-token group, then the
+ * groups in order).  Otherwise the separate kernels run.  Either way the
+ * result is deterministic.
  *
  *   arguments as moe_gate_topk and moe_balance_stats;
  *   workspace  device scratch of at least moe_gate_balance_workspace_size()

@@ -163,9 +163,15 @@ __global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
 // Partials of 16-token groups -> counts and prob_sums per image, then the
 // loss.  With B*E outputs of T/16 groups each, R = 1024 / (B*E) threads
 // (a power of two, at most 16) share an output: thread j of output (b, e)
-// adds groups j, j + R, ... of image b in order, and the R sums are then
-// added in j order.  Partial rows are E apart, so the threads of one j read
-// neighbouring words.  Fixed association throughout: same bits every call.
+// adds groups j, j + R, ... of image b in order, all its loads issued
+// before the first addition (up to kPartBatch per round), and the R sums
+// are then added in j order.  Partial rows are E apart, so the threads of
+// one j read neighbouring words.  The results also stay in LDS (up to
+// kPartLds outputs), where the loss reads them.  Fixed association
+// throughout: same bits every call.
+constexpr int kPartBatch = 16;
+constexpr int kPartLds = 2048;
+
 __global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
     int B, int T, int E, int K, float alpha, int global,
@@ -173,6 +179,8 @@ __global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
     float* __restrict__ loss) {
   __shared__ float sp[kSeqThreads];
   __shared__ int32_t sc[kSeqThreads];
+  __shared__ float lps[kPartLds];
+  __shared__ int32_t lcn[kPartLds];
   const int G = T / 16;
   const int64_t outs = static_cast<int64_t>(B) * E;
   int R = 1;
@@ -185,24 +193,22 @@ __global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
     if (o < outs) {
       const int64_t b = o / E;
       const int64_t base = b * G * E + (o - b * E);
-      int g = j;
-      for (; g + 7 * R < G; g += 8 * R) {
-        float q[8];
-        int32_t n[8];
+      for (int g0 = j; g0 < G; g0 += kPartBatch * R) {
+        float q[kPartBatch];
+        int32_t n[kPartBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          q[u] = part_p[base + static_cast<int64_t>(g + u * R) * E];
-          n[u] = part_c[base + static_cast<int64_t>(g + u * R) * E];
+        for (int u = 0; u < kPartBatch; ++u) {
+          const int g = g0 + u * R;
+          q[u] = g < G ? part_p[base + static_cast<int64_t>(g) * E] : 0.0f;
+          n[u] = g < G ? part_c[base + static_cast<int64_t>(g) * E] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          s += q[u];
-          c += n[u];
+        for (int u = 0; u < kPartBatch; ++u) {
+          if (g0 + u * R < G) {
+            s += q[u];
+            c += n[u];
+          }
         }
-      }
-      for (; g < G; g += R) {
-        s += part_p[base + static_cast<int64_t>(g) * E];
-        c += part_c[base + static_cast<int64_t>(g) * E];
       }
     }
     sp[threadIdx.x] = s;
@@ -215,12 +221,20 @@ __global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
       }
       psum[o] = s;
       counts[o] = c;
+      if (o < kPartLds) {
+        lps[o] = s;
+        lcn[o] = c;
+      }
     }
     __syncthreads();
   }
-  // The loss reads what this workgroup just wrote: a workgroup barrier
-  // orders those global writes before the reads (the loop ended on one).
-  balance_loss_body(counts, psum, B, T, E, K, alpha, global, loss);
+  // The loss from the LDS copies when they hold every output; otherwise it
+  // reads what this workgroup just wrote to global memory (a workgroup
+  // barrier orders those writes before the reads; the loop ended on one).
+  if (outs <= kPartLds)
+    balance_loss_body(lcn, lps, B, T, E, K, alpha, global, loss);
+  else
+    balance_loss_body(counts, psum, B, T, E, K, alpha, global, loss);
 }
 
 }  // namespace

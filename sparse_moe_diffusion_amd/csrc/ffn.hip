@@ -309,11 +309,13 @@ __device__ __forceinline__ bool locate_any(const GemmParams& p,
 }
 
 // Bias and activation of 4 consecutive output features f..f+3 of group g,
-// output row `row`.
-template <int EPI>
+// output row `row`.  BIAS: whether p.bias is set, decided once per tile by
+// the caller, so that the loops over a tile's outputs hold no branch (the
+// activations of consecutive groups of 4 can then be interleaved).
+template <int EPI, bool BIAS>
 __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g,
                                          int64_t row, int f, f32x4 v) {
-  if (p.bias != nullptr) {
+  if constexpr (BIAS) {
     const float* b = p.bias + static_cast<int64_t>(g) * p.Nd + f;
     v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
   }
@@ -332,7 +334,8 @@ __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g,
 template <int EPI, bool OUT_BF16>
 __device__ __forceinline__ void store4(const GemmParams& p, int g, int64_t row,
                                        int f, f32x4 v) {
-  v = finish4<EPI>(p, g, row, f, v);
+  v = p.bias != nullptr ? finish4<EPI, true>(p, g, row, f, v)
+                        : finish4<EPI, false>(p, g, row, f, v);
   if constexpr (OUT_BF16) {
     uint2 o;
     o.x = pack_bf16x2(v[0], v[1]);
@@ -594,7 +597,6 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // Per DMA transfer q of this wave: byte offset of this lane's chunk at
   // k = 0, the chunk's k index, and the LDS destination (elements).
   uint32_t goff[NQ];
-  int gk[NQ];
   uint32_t ldst[NQ];   // LDS byte offset of the transfer in its stage
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -611,7 +613,6 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       const int kr = byte / rb;
       const int pc = (byte - kr * rb) / 16;
       const int lc = pc ^ (4 * (kr & 3));
-      gk[q] = kr;
       ldst[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ta * 1024));
       goff[q] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(isA ? p.mrows : p.Nd) * 2u +
                 static_cast<uint32_t>(lc) * 16u;
@@ -620,7 +621,6 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     const int r0 = (isA ? t : t - BM / 8) * 8;
     const int r = r0 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
-    gk[q] = c * 8;
     ldst[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r0 * kBK * 2));
     if (isA) {
       const bool valid = loc.row0 + r < loc.row_end;
@@ -694,7 +694,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
         const bool isA_ = q < QA;                                            \
         uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);   \
-        if (!full_ && ikt_ * kBK + gk[q] >= Kd) off_ = kOutOfRange;          \
+        if (!full_) {                                                        \
+          /* this lane's chunk of the transfer: row r, k index 8 c */        \
+          const int t_ = wave + kWaves * q;                                  \
+          const int r_ = (isA_ ? t_ : t_ - BM / 8) * 8 + (lane >> 3);        \
+          const int c_ = (lane & 7) ^ swz(r_);                               \
+          if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;                 \
+        }                                                                    \
         dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
       }                                                                      \
     }                                                                        \
@@ -704,7 +710,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // stage the lane reads chunk kc = 2 ks + (lane >> 5), stored at slot
   // kc ^ swz(row).  Element offsets for all four k steps are precomputed.
   const int khalf = lane >> 5;
-  int oa[FB][4], ob[TB][4];
+  // Non-K-grouped form: oa[i][0] / ob[j][0] hold row * 64 + 8 (khalf ^
+  // swz(row)), the chunk of k step 0; step ks reads chunk (2 ks + khalf) ^
+  // swz(row), i.e. that offset XOR 16 ks (the row part has its low 6 bits
+  // clear), so one register per fragment serves all four steps.
+  int oa[FB][1], ob[TB][1];
   if constexpr (KG) {
     // Transposed fragments (byte offsets at k step 0): lane l addresses k
     // row 8 (l / 32) + (l / 4) % 4 and the 8-byte piece of features
@@ -728,16 +738,12 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 #pragma unroll
   for (int i = 0; i < FB; ++i) {
     const int row = wf * (BN / WF) + i * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      oa[i][ks] = row * kBK + (((2 * ks + khalf) ^ swz(row)) * 8);
+    oa[i][0] = row * kBK + ((khalf ^ swz(row)) * 8);
   }
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int row = wt * (BM / WT) + j * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      ob[j][ks] = row * kBK + (((2 * ks + khalf) ^ swz(row)) * 8);
+    ob[j][0] = row * kBK + ((khalf ^ swz(row)) * 8);
   }
   }
 
@@ -762,9 +768,9 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           lds_frag_tr<BM * 2>((SA), ob[j][0] + (KS) * 16 * BM * 2);          \
     } else {                                                                 \
       _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                 \
-          *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][KS]]);                \
+          *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][0] ^ (16 * (KS))]);   \
       _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                \
-          *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][KS]]);                \
+          *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][0] ^ (16 * (KS))]);   \
     }                                                                        \
   } while (0)
 
@@ -884,7 +890,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     // (their bias would lie outside the array); a tile that holds none takes
     // the branch-free form.
     stage_barrier();
-#define MOE_STAGE_OUT(CHECK, E_)                                             \
+#define MOE_STAGE_OUT_B(CHECK, E_, B_)                                       \
     _Pragma("unroll") for (int j = 0; j < TB; ++j) {                         \
       const int t = wt * (BM / WT) + j * 32 + (lane & 31);                   \
       _Pragma("unroll") for (int i = 0; i < FB; ++i) {                       \
@@ -896,13 +902,19 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           v[1] = acc[i][j][4 * q + 1];                                       \
           v[2] = acc[i][j][4 * q + 2];                                       \
           v[3] = acc[i][j][4 * q + 3];                                       \
-          v = finish4<E_>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);           \
+          v = finish4<E_, B_>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);       \
           uint2 o;                                                           \
           o.x = pack_bf16x2(v[0], v[1]);                                     \
           o.y = pack_bf16x2(v[2], v[3]);                                     \
           *reinterpret_cast<uint2*>(&lds[t * kOutPitch + fl]) = o;           \
         }                                                                    \
       }                                                                      \
+    }
+#define MOE_STAGE_OUT(CHECK, E_)                                             \
+    if (p.bias != nullptr) {                                                 \
+      MOE_STAGE_OUT_B(CHECK, E_, true)                                       \
+    } else {                                                                 \
+      MOE_STAGE_OUT_B(CHECK, E_, false)                                      \
     }
     constexpr int kChunks = BN / 8;
     uint16_t* const c = static_cast<uint16_t*>(p.c);
@@ -942,6 +954,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       MOE_STAGE_OUT(true, EPI)
     }
 #undef MOE_STAGE_OUT
+#undef MOE_STAGE_OUT_B
     stage_barrier();
     if constexpr (EPI == kEpiCombine) {
       // y[t] = sum over the slots >= 0, in slot order, of w * routed row,
@@ -1408,9 +1421,9 @@ int tile_grid(const GemmParams& p, int BM, int BN) {
   return static_cast<int>(mt * ((p.Nd + BN - 1) / BN));
 }
 
-// Workgroups of a persistent launch: the CU count of the current device
-// (read once per device), rounded down to a multiple of 8, and no more than
-// the tile bound rounded up to a multiple of 8.
+}  // namespace
+
+// The CU count of the current device, read once per device.
 int cu_count() {
   static std::atomic<int> cus[64];
   int dev = 0;
@@ -1426,6 +1439,11 @@ int cu_count() {
   return n;
 }
 
+namespace {
+
+// Workgroups of a persistent launch: the CU count of the current device,
+// rounded down to a multiple of 8, and no more than the tile bound rounded
+// up to a multiple of 8.
 // occ workgroups per CU (the kernel's resources allow that many).
 int persistent_grid(int tiles, int occ = 1) {
   const int cap = cu_count() / 8 * 8 * occ;

@@ -280,29 +280,45 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_mfma_kernel(
 // per 32-wide slice on the exact split of the gate weight, slice sums added
 // in fp64 in slice order, one rounding to fp32.
 //
-// Each workgroup first splits the fp32 gate weight into its three bf16
-// parts once, into LDS; chunk ((part * nsteps + s) * 4 + kq) * EC + e holds
-// the 8 bf16 of part `part` (hi, mid, lo) of expert e for features
-// 32 s + 8 kq .. 32 s + 8 kq + 7, so the lanes of a wave read one slice's
-// operand as consecutive 16-byte chunks.  Each wave then streams the
-// features of its own 16 tokens with kRing 32-wide slices in flight (a ring
-// of register loads refilled as each slice is consumed), so HBM sees a
-// steady stream instead of bursts, and keeps its tokens' logits in
-// registers: no cross-wave sum.  Lane l's logits are token (l % 16),
-// experts 4 (l / 16) + 0..3; the wave passes them through LDS to lanes
-// 0..15, one token each, for the softmax and selection.
+// A workgroup of W waves (8, 4 or 2: enough workgroups to occupy every CU)
+// owns 16 W tokens; each wave streams the features of its own 16 tokens
+// with kRing 32-wide slices in flight (a ring of register loads refilled as
+// each slice is consumed), so HBM sees a steady stream, and keeps its
+// tokens' logits in registers: no cross-wave sum.  Lane l's logits are
+// token (l % 16), experts 4 (l / 16) + 0..3.
 //
-// With bal_p != nullptr (top-K routing, 16-token groups that never straddle
-// two images) each wave also writes the balance statistic's partial sums of
-// its 16 tokens: bal_p[g][e] = sum of P(t,e) over the group's tokens in
-// token order, bal_c[g][e] = how many of them selected e, for group
-// g = first token / 16.
-constexpr int kStreamWaves = 8;            // 16 tokens per wave
+// The split weights live in LDS, P slices at a time (a phase; P is all the
+// slices when they fit, else a multiple of kRing): chunk
+// ((part * P + s) * 4 + kq) * EC + e holds the 8 bf16 of part `part` (hi,
+// mid, lo) of expert e for features 32 s + 8 kq .. + 7 of the phase, so the
+// lanes of a wave read one slice's operand as consecutive 16-byte chunks.
+// The first phase's fp32 weights are loaded before the token ring (loads
+// return in order, so they are not queued behind it) and split while the
+// ring's slices are in flight; a later phase is split when every wave has
+// finished the previous one, the ring still loading tokens.
+//
+// The softmax and the selection run on all 64 lanes: the four lanes of a
+// token combine their maxima, sums and candidates with cross-lane swaps
+// (the same bits on all four).  With bal_p != nullptr (top-K routing,
+// 16-token groups that never straddle two images) each wave also writes
+// the balance statistic's partial sums of its 16 tokens, added as a
+// pairwise tree over the tokens: bal_p[g][e] (probabilities) and
+// bal_c[g][e] (selections), for group g = first token / 16.
+constexpr int kStreamWaves = 8;            // most waves per workgroup
 constexpr int kRing = 12;                  // slices in flight per wave
 constexpr int kStreamLdsMax = 144 * 1024;  // split weights, bytes
+constexpr int kSplitBatch = 6;             // weight chunks loaded per thread at once
+
+// Slices per phase of the split weights: all of them if they fit the LDS
+// budget, else the largest multiple of kRing that does.
+__host__ __device__ constexpr int stream_phase_slices(int D, int EC) {
+  const int nsteps = (D + 31) / 32;
+  const int fit = kStreamLdsMax / (3 * 4 * EC * 16);
+  return nsteps <= fit ? nsteps : fit / kRing * kRing;
+}
 
 __host__ __device__ constexpr size_t stream_lds_bytes(int D, int EC) {
-  return static_cast<size_t>(3) * ((D + 31) / 32) * 4 * EC * 16;
+  return static_cast<size_t>(3) * stream_phase_slices(D, EC) * 4 * EC * 16;
 }
 
 template <int EC>
@@ -311,22 +327,23 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gate_stream_kernel(
     const float* __restrict__ bias, int64_t N, int D, int E, int K, int topk,
     float* __restrict__ probs, int32_t* __restrict__ idx,
     float* __restrict__ wout, float* __restrict__ bal_p,
-    int32_t* __restrict__ bal_c) {
+    int32_t* __restrict__ bal_c, int P) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   extern __shared__ u32x4 wsplit[];
-  __shared__ float lg[kStreamWaves][16][17];
-  __shared__ uint32_t taken[kStreamWaves][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
+  const int waves = static_cast<int>(blockDim.x) / kWave;
+  const int nthreads = static_cast<int>(blockDim.x);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 15;
   const int kq = lane >> 4;
   const int nsteps = (D + 31) / 32;
-  const int stride = nsteps * 4 * EC;   // chunks per part
+  const int stride = P * 4 * EC;        // chunks per part
+  const int nchunks = EC * P * 4;       // weight chunks of one phase
 
   // This wave's 16 token rows; rows past N read zero.
   const int64_t t0 =
-      static_cast<int64_t>(blockIdx.x) * (16 * kStreamWaves) + 16 * wave;
+      static_cast<int64_t>(blockIdx.x) * (16 * waves) + 16 * wave;
   const int64_t left = N - t0;
   const int nrows = left <= 0 ? 0 : (left >= 16 ? 16 : static_cast<int>(left));
   const uint32_t row_bytes = static_cast<uint32_t>(D) * 2u;
@@ -340,131 +357,220 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gate_stream_kernel(
                                  : kOutOfRange;
   };
 
+  // One batch of the split: thread i takes chunks C0 + nthreads b of phase
+  // PH (chunk c: expert c % EC, phase features 8 (c / EC) ..).  Macros over
+  // the kernel's own registers (a helper taking these arrays by reference
+  // would put them in scratch memory).
+  float4 wa4[kSplitBatch], wb4[kSplitBatch];
+#define MOE_SPLIT_LOAD(PH, C0)                                               \
+  do {                                                                       \
+    _Pragma("unroll") for (int b_ = 0; b_ < kSplitBatch; ++b_) {             \
+      const int c_ = (C0) + nthreads * b_;                                   \
+      const int e_ = c_ % EC;                                                \
+      const int k_ = (PH) * P * 32 + 8 * (c_ / EC);                          \
+      wa4[b_] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);                         \
+      wb4[b_] = wa4[b_];                                                     \
+      if (c_ < nchunks && e_ < E && k_ < D) {                                \
+        const float* src_ = wg + static_cast<int64_t>(e_) * D + k_;          \
+        wa4[b_] = *reinterpret_cast<const float4*>(src_);                    \
+        wb4[b_] = *reinterpret_cast<const float4*>(src_ + 4);                \
+      }                                                                      \
+    }                                                                        \
+  } while (0)
+#define MOE_SPLIT_STORE(C0)                                                  \
+  do {                                                                       \
+    _Pragma("unroll") for (int b_ = 0; b_ < kSplitBatch; ++b_) {             \
+      const int c_ = (C0) + nthreads * b_;                                   \
+      if (c_ < nchunks) {                                                    \
+        const int e_ = c_ % EC;                                              \
+        const int k_ = 8 * (c_ / EC);                                        \
+        const float w8_[8] = {wa4[b_].x, wa4[b_].y, wa4[b_].z, wa4[b_].w,    \
+                              wb4[b_].x, wb4[b_].y, wb4[b_].z, wb4[b_].w};   \
+        u32x4 h_, m_, l_;                                                    \
+        _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) {                   \
+          const float a0_ = w8_[2 * q_], a1_ = w8_[2 * q_ + 1];              \
+          h_[q_] = pack_bf16x2(a0_, a1_);                                    \
+          const float r0_ = a0_ - bf16_lo(h_[q_]);                           \
+          const float r1_ = a1_ - bf16_hi(h_[q_]);                           \
+          m_[q_] = pack_bf16x2(r0_, r1_);                                    \
+          l_[q_] = pack_bf16x2(r0_ - bf16_lo(m_[q_]), r1_ - bf16_hi(m_[q_])); \
+        }                                                                    \
+        const int chunk_ = ((k_ >> 5) * 4 + ((k_ >> 3) & 3)) * EC + e_;      \
+        wsplit[chunk_] = h_;                                                 \
+        wsplit[stride + chunk_] = m_;                                        \
+        wsplit[2 * stride + chunk_] = l_;                                    \
+      }                                                                      \
+    }                                                                        \
+  } while (0)
+#define MOE_SPLIT_REST(PH, FIRST)                                            \
+  for (int c0_ = (FIRST); c0_ < nchunks; c0_ += nthreads * kSplitBatch) {    \
+    MOE_SPLIT_LOAD(PH, c0_);                                                 \
+    MOE_SPLIT_STORE(c0_);                                                    \
+  }
+
+  // Phase 0: the weights' first batch, then the token ring, then the split.
+  MOE_SPLIT_LOAD(0, tid);
   u32x4 xr[kRing];
 #pragma unroll
   for (int j = 0; j < kRing; ++j)
     xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff(j), 0, 0);
-
-  // The split, while the first slices are in flight.  Thread i takes the
-  // 8-feature chunks i, i + 256, ... (chunk c: expert c % EC, features
-  // 8 (c / EC) ..); a batch's weights are all loaded before any is used.
-  constexpr int kBatch = 6;
-  const int nchunks = EC * nsteps * 4;
-  for (int c0 = tid; c0 < nchunks; c0 += 64 * kStreamWaves * kBatch) {
-    float4 wa[kBatch], wb[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + 64 * kStreamWaves * b;
-      const int e = c % EC;
-      const int k = 8 * (c / EC);
-      wa[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      wb[b] = wa[b];
-      if (c < nchunks && e < E && k < D) {
-        const float* src = wg + static_cast<int64_t>(e) * D + k;
-        wa[b] = *reinterpret_cast<const float4*>(src);
-        wb[b] = *reinterpret_cast<const float4*>(src + 4);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int c = c0 + 64 * kStreamWaves * b;
-      if (c >= nchunks) break;
-      const int e = c % EC;
-      const int k = 8 * (c / EC);
-      const float w8[8] = {wa[b].x, wa[b].y, wa[b].z, wa[b].w,
-                           wb[b].x, wb[b].y, wb[b].z, wb[b].w};
-      u32x4 h, m, l;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = w8[2 * q], a1 = w8[2 * q + 1];
-        h[q] = pack_bf16x2(a0, a1);
-        const float r0 = a0 - bf16_lo(h[q]), r1 = a1 - bf16_hi(h[q]);
-        m[q] = pack_bf16x2(r0, r1);
-        l[q] = pack_bf16x2(r0 - bf16_lo(m[q]), r1 - bf16_hi(m[q]));
-      }
-      const int chunk = ((k >> 5) * 4 + ((k >> 3) & 3)) * EC + e;
-      wsplit[chunk] = h;
-      wsplit[stride + chunk] = m;
-      wsplit[2 * stride + chunk] = l;
-    }
-  }
+  MOE_SPLIT_STORE(tid);
+  MOE_SPLIT_REST(0, tid + nthreads * kSplitBatch)
   __syncthreads();
 
-  // Straight-line ring: a slice at or past nsteps loads zero features and
-  // reads the (finite) weights of the last slice, so it adds exactly zero.
-  // Lanes past the stored expert columns (E <= 8) read expert 0's chunk:
-  // their output rows are experts >= E, never used.  The three weight parts
-  // of slice s + 1 are read from LDS while slice s is multiplied (kRing is even, so the two register sets alternate in a
-  // fixed pattern).
+  // Straight-line ring over each phase's slices: slices past nsteps load
+  // zero features and read the (finite) weights of the last slice, so they
+  // add exactly zero.  Lanes past the stored expert columns (E <= 8) read
+  // expert 0's chunk: their output rows are experts >= E, never used.  The
+  // three weight parts of slice s + 1 are read from LDS while slice s is
+  // multiplied (kRing is even, so the two register sets alternate in a
+  // fixed pattern); the first slice of a phase is read after its split.
   static_assert(kRing % 2 == 0, "even ring");
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   const u32x4* const wl = wsplit + kq * EC + (col < EC ? col : 0);
-  auto wslice = [&](int s, u32x4 (&w)[3]) {
-    const int sw = (s < nsteps ? s : nsteps - 1) * 4 * EC;
-    w[0] = wl[sw];
-    w[1] = wl[stride + sw];
-    w[2] = wl[2 * stride + sw];
-  };
   u32x4 wa[3], wb[3];
-  wslice(0, wa);
-  for (int s0 = 0; s0 < nsteps; s0 += kRing) {
+  for (int s_begin = 0; s_begin < nsteps; s_begin += P) {
+    const int ph = s_begin / P;
+    const int s_last = (s_begin + P < nsteps ? s_begin + P : nsteps) - 1;
+    if (ph > 0) {
+      __syncthreads();   // every wave is done with the previous phase
+      MOE_SPLIT_REST(ph, tid)
+      __syncthreads();
+    }
+    auto wslice = [&](int s, u32x4 (&w)[3]) {
+      const int sw = ((s < s_last ? s : s_last) - s_begin) * 4 * EC;
+      w[0] = wl[sw];
+      w[1] = wl[stride + sw];
+      w[2] = wl[2 * stride + sw];
+    };
+    wslice(s_begin, wa);
+    // P is a multiple of kRing unless this is the only phase, so the ring
+    // position of slice s_begin is 0.
+    for (int s0 = s_begin; s0 <= s_last; s0 += kRing) {
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      const int s = s0 + j;
-      u32x4 (&cur)[3] = (j % 2 == 0) ? wa : wb;
-      u32x4 (&nxt)[3] = (j % 2 == 0) ? wb : wa;
-      wslice(s + 1, nxt);
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, xr[j]);
-      xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff(s + kRing), 0, 0);
-      f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < kRing; ++j) {
+        const int s = s0 + j;
+        u32x4 (&cur)[3] = (j % 2 == 0) ? wa : wb;
+        u32x4 (&nxt)[3] = (j % 2 == 0) ? wb : wa;
+        wslice(s + 1, nxt);
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, xr[j]);
+        xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff(s + kRing), 0, 0);
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int part = 0; part < 3; ++part)
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, cur[part]), xb, a, 0, 0, 0);
+        for (int part = 0; part < 3; ++part)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, cur[part]), xb, a, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += static_cast<double>(a[i]);
+        for (int i = 0; i < 4; ++i) acc[i] += static_cast<double>(a[i]);
+      }
     }
   }
 
+#undef MOE_SPLIT_LOAD
+#undef MOE_SPLIT_STORE
+#undef MOE_SPLIT_REST
+
+  // Softmax of token col over the four lanes col + 16 q.
+  const int64_t t = t0 + col;
+  const bool tok = t < N;
+  float p[4];
+  bool ok[4];
+  float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = 4 * kq + i;
-    const double b = (bias != nullptr && e < E) ? static_cast<double>(bias[e]) : 0.0;
-    lg[wave][col][e] = static_cast<float>(acc[i] + b);
+    ok[i] = e < E;
+    const double b = (bias != nullptr && ok[i]) ? static_cast<double>(bias[e]) : 0.0;
+    p[i] = static_cast<float>(acc[i] + b);
+    if (ok[i]) m = fmaxf(m, p[i]);
   }
-  __syncthreads();
-  const int64_t t = t0 + lane;
-  if (lane < 16 && t < N) {
-    float p[16];
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float sum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p[e] = lg[wave][lane][e];
-    const uint64_t sel = softmax_topk<16>(p, t, E, K, topk != 0, probs, idx, wout);
-    if (bal_p != nullptr) {
+  for (int i = 0; i < 4; ++i) {
+    p[i] = ok[i] ? expf(p[i] - m) : 0.0f;
+    sum += p[i];
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lg[wave][lane][e] = p[e];
-      taken[wave][lane] = static_cast<uint32_t>(sel);
+  for (int i = 0; i < 4; ++i) {
+    p[i] = ok[i] ? p[i] / sum : 0.0f;
+    if (tok && ok[i]) probs[t * E + 4 * kq + i] = p[i];
+  }
+
+  // Top-K: K rounds of the largest remaining (key, expert) pair, ties to
+  // the lower expert; each lane offers its best, the four lanes agree.
+  uint32_t sel = 0;   // experts selected by token col (bit e)
+  if (topk) {
+    for (int k = 0; k < K; ++k) {
+      float bk = -INFINITY, bp = 0.0f;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * kq + i;
+        if (ok[i] && !((sel >> e) & 1u)) {
+          const float key = sel_key(p[i]);
+          if (be == 0x7fffffff || key > bk) {
+            bk = key;
+            be = e;
+            bp = p[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 16; off <= 32; off *= 2) {
+        const float ok2 = __shfl_xor(bk, off);
+        const int oe = __shfl_xor(be, off);
+        const float op = __shfl_xor(bp, off);
+        if (ok2 > bk || (ok2 == bk && oe < be)) {
+          bk = ok2;
+          be = oe;
+          bp = op;
+        }
+      }
+      sel |= 1u << be;
+      if (kq == 0 && tok) {
+        idx[t * K + k] = be;
+        wout[t * K + k] = bp;
+      }
     }
   }
   if (bal_p == nullptr) return;
-  __syncthreads();
   // Whole groups only: the host takes this path when N is a multiple of 16.
-  if (lane < E && t0 < N) {
-    float s = 0.0f;
-    int32_t c = 0;
+  const uint64_t row = 0xffffull << (16 * kq);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s += lg[wave][r][lane];
-      c += static_cast<int32_t>((taken[wave][r] >> lane) & 1u);
+  for (int i = 0; i < 4; ++i) {
+    float v = tok ? p[i] : 0.0f;
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    const int e = 4 * kq + i;
+    const uint64_t hit = __ballot(tok && ((sel >> e) & 1u));
+    if (col == 0 && ok[i] && t0 < N) {
+      const int64_t o = (t0 / 16) * E + e;
+      bal_p[o] = v;
+      bal_c[o] = __popcll(hit & row);
     }
-    const int64_t o = (t0 / 16) * E + lane;
-    bal_p[o] = s;
-    bal_c[o] = c;
   }
 }
 
-// Split weights of E experts over D features fit the streaming kernel's LDS.
+// Split weights of E experts: the streaming kernel takes E <= 16 (bf16
+// tokens, any D).
 bool gate_stream_fits(int D, int E) {
-  return E <= 16 && stream_lds_bytes(D, E <= 8 ? 8 : 16) <= kStreamLdsMax;
+  (void)D;
+  return E <= 16;
+}
+
+// Waves per workgroup of the streaming gate: 8, or fewer when that leaves
+// CUs without a workgroup (short inputs).
+int gate_stream_waves(int64_t N) {
+  const int cus = cu_count();
+  int w = kStreamWaves;
+  while (w > 2 && ceil_div(N, 16 * w) < cus) w /= 2;
+  return w;
 }
 
 template <int EC>
@@ -481,12 +587,14 @@ hipError_t launch_gate_stream(const void* x, const float* wg, const float* bias,
     if (e != hipSuccess) return e;
     lds_opt_in.store(true, std::memory_order_release);
   }
+  const int waves = gate_stream_waves(N);
   hipLaunchKernelGGL((gate_stream_kernel<EC>),
-                     dim3(static_cast<unsigned>(ceil_div(N, 16 * kStreamWaves))),
-                     dim3(64 * kStreamWaves),
+                     dim3(static_cast<unsigned>(ceil_div(N, 16 * waves))),
+                     dim3(64 * waves),
                      static_cast<unsigned>(stream_lds_bytes(D, EC)), stream,
                      static_cast<const uint16_t*>(x), wg, bias, N, D, E, K,
-                     topk ? 1 : 0, probs, idx, w, bal_p, bal_c);
+                     topk ? 1 : 0, probs, idx, w, bal_p, bal_c,
+                     stream_phase_slices(D, EC));
   return hipGetLastError();
 }
 

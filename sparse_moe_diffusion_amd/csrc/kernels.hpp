@@ -8,6 +8,9 @@
 
 namespace moe {
 
+// ffn.hip: the CU count of the current device (read once per device).
+int cu_count();
+
 // gate.hip
 hipError_t launch_gate(const void* x, bool x_bf16, const float* w_gate,
                        const float* bias, int64_t N, int D, int E, int K,

@@ -55,6 +55,9 @@ GATE_CASES = [  # N, D, E, K, bias, dtype
     # bf16, E <= 16 with unused expert columns and a partial last 32-wide
     # feature slice; N leaves part of the last workgroup empty
     (777, 72, 12, 3, True, "bf16"), (129, 200, 5, 2, False, "bf16"),
+    # split gate weights past the LDS budget, streamed in phases: two phases
+    # of 96 + 4 slices (E <= 8), three of 48 slices (E <= 16)
+    (200, 3200, 8, 2, True, "bf16"), (130, 4608, 12, 3, False, "bf16"),
 ]
 
 
@@ -499,7 +502,8 @@ def test_balance(B, T, E, K, race, mode):
     (5, 64, 200, 5, 3, "bf16", "sequence", True),     # unused expert columns
     (3, 100, 256, 8, 2, "bf16", "sequence", False),   # T % 16 != 0: separate
     (2, 64, 128, 8, 2, "f32", "global", False),       # fp32 x: separate
-    (2, 32, 2048, 16, 2, "bf16", "sequence", False),  # weights exceed LDS: separate
+    (2, 32, 2048, 16, 2, "bf16", "sequence", False),  # weights split in two phases
+    (16, 1024, 2048, 16, 2, "bf16", "global", True),  # the race layer's shape
     (32, 1024, 1152, 8, 2, "bf16", "sequence", False),  # the XL layer
     (0, 16, 128, 8, 2, "bf16", "sequence", False),    # no tokens
     (0, 16, 128, 8, 2, "bf16", "global", False),
