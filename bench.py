@@ -419,16 +419,18 @@ def cpu_baseline_all(args):
 
 def cold_timings(cfg, x, wts, buf, steps, reps):
     """The HBM-bound calls of the step, each timed ``reps`` times right after
-    a 1 GiB write that evicts the 256 MB memory-side cache and the L2s (so
-    their inputs come from HBM), plus two measured-only forms: the permute
+    a read of a 1 GiB buffer that evicts the 256 MB memory-side cache and
+    the L2s (so their inputs come from HBM; a read leaves only clean lines,
+    so no write-back of the flush competes with the timed call), and ``reps``
+    times back to back (warm), plus two measured-only forms: the permute
     that also copies the rows to x_perm, and the separate combine kernel
     where the layer fuses it.  Median ms, GB/s of algorithmic bytes and the
-    fraction of the HBM peak."""
+    fraction of the HBM peak, cold and warm."""
     import torch
     import numpy as np
     from sparse_moe_diffusion_amd import layer
     import copy
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     work = kernel_work(cfg, buf.gather)
     calls = [(n, f) for n, f in steps
              if n in ("gate", "gate_balance", "permute", "combine", "balance")]
@@ -452,22 +454,27 @@ def cold_timings(cfg, x, wts, buf, steps, reps):
             extra["combine_separate"] = work["combine"][1]
     out = {}
     for name, fn in calls:
-        ts = []
-        for _ in range(reps):
-            flush.fill_(1)
+        cold, warm = [], []
+        for r in range(2 * reps):
+            if r < reps:
+                flush.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
             fn(cfg, x, wts, buf)
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = float(np.median(ts))
+            (cold if r < reps else warm).append(e0.elapsed_time(e1))
         nbytes = extra.get(name, work.get(name, ("bytes", 0))[1])
+        ms = float(np.median(cold))
+        msw = float(np.median(warm))
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "bytes": int(nbytes),
                      "gbs": round(gbs, 1),
-                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "ms_warm": round(msw, 4),
+                     "frac_hbm_peak_warm": round(nbytes / (msw * 1e-3) / 1e9 /
+                                                 HBM_PEAK_GBS, 4)}
     del flush
     torch.cuda.synchronize()
     return out

@@ -361,8 +361,9 @@ moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype,
  *   NULL;  y_rows [*][D] bf16 routed outputs;  slot_row, topk_w [N][Kmax];
  *   y [N][D] bf16 out
  * Errors: INVALID_ARGUMENT for null pointers (N > 0), N < 0, D, H or
- *   Kmax < 1; UNSUPPORTED for a dtype other than bf16, Kmax > 4, D or H
- *   not multiples of 8, N*Kmax >= 2^31.
+ *   Kmax < 1; UNSUPPORTED for a dtype other than bf16, Kmax > 16 (top-K
+ *   routing with K <= 16, or Expert Race with E <= 16), D or H not
+ *   multiples of 8, N*Kmax >= 2^31.
  */
 moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
                                 int32_t D, int32_t H, const void* w2,

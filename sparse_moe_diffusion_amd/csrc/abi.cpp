@@ -438,8 +438,8 @@ moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
   CHECK_PTR_IF(rows, slot_row); CHECK_PTR_IF(rows, topk_w); CHECK_PTR_IF(rows, y);
   if (dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
-  if (Kmax > 4)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: Kmax=%d above 4", fn, Kmax);
+  if (Kmax > 16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: Kmax=%d above 16", fn, Kmax);
   if (D % 8 != 0 || H % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "%s: D=%d and H=%d must be multiples of 8",
                 fn, D, H);

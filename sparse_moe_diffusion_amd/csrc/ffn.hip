@@ -56,8 +56,10 @@ namespace {
 // (backward of the first expert matrix).
 enum Epi { kEpiGelu = 0, kEpiStore = 1, kEpiCombine = 2, kEpiGeluGrad = 3 };
 
-// Most slots per token the fused combine takes (top-K routing, K <= 4).
-constexpr int kCombineMaxSlots = 4;
+// Most slots per token the fused combine takes: top-K routing (K <= 4) uses
+// the kernel form with 4 slot columns, Expert Race (Kmax = E <= 16) the one
+// with 16 (a larger slot table in LDS).
+constexpr int kCombineMaxSlots = 16;
 
 struct GemmParams {
   const void* a;           // activation rows [*][Kd]
@@ -73,7 +75,7 @@ struct GemmParams {
   const void* cmb_rows;      // [*][Nd] bf16 routed expert outputs
   const int32_t* cmb_slot;   // [total][cmb_kmax]
   const float* cmb_w;        // [total][cmb_kmax]
-  int cmb_kmax;              // 1..kCombineMaxSlots
+  int cmb_kmax;              // 1..kCombineMaxSlots (at most the kernel's CMAX)
   // kEpiGeluGrad only: the pre-activations u [total][Nd] bf16.
   const void* aux;
   // K-grouped form (weight gradients): C[g] [mrows][Nd] fp32 = A[rows g]^T
@@ -449,7 +451,7 @@ __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
-          bool PF, bool KG = false>
+          bool PF, bool KG = false, int CMAX = 4>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
   static_assert(EPI != kEpiGeluGrad || OUT_BF16, "gelu'(u) is applied on bf16 output");
   static_assert(!KG || (!OUT_BF16 && !PF && EPI == kEpiStore),
@@ -471,16 +473,20 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
   constexpr int kMainElems = (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2;
   constexpr int kPfElems = PF ? 256 : 0;
-  constexpr int kCmbInts = EPI == kEpiCombine ? 2 * BM * kCombineMaxSlots : 0;
+  // slot rows and weights, [BM][CMAX] each, and (CMAX > 4) each row's
+  // count of non-empty slots
+  constexpr int kCmbInts =
+      EPI == kEpiCombine ? 2 * BM * CMAX + (CMAX > 4 ? BM : 0) : 0;
   static_assert(EPI != kEpiCombine || OUT_BF16, "the combine writes bf16");
   __shared__ __attribute__((aligned(1024)))
   uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM + kCmbInts)];
   int32_t* const tab = reinterpret_cast<int32_t*>(lds + kMainElems + kPfElems);
   int32_t* const sidx = tab + kTabInts;   // 2 x BM gathered source rows
-  // kEpiCombine: the tile's slot rows and weights, [BM][cmb_kmax] each.
+  // kEpiCombine: the tile's slot rows and weights, [BM][cmb_kmax] each
+  // (cmb_kmax <= CMAX).
   int32_t* const cslot = sidx + 2 * BM;
-  const float* const cwt =
-      reinterpret_cast<const float*>(cslot + BM * kCombineMaxSlots);
+  float* const cwt = reinterpret_cast<float*>(cslot + BM * CMAX);
+  int32_t* const ccnt = cslot + 2 * BM * CMAX;
   uint16_t* const sA0 = lds;
   uint16_t* const sA1 = sA0 + BM * kBK;
   uint16_t* const sB0 = sA1 + BM * kBK;
@@ -858,7 +864,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     for (int q = wave; q < BM * km / 64; q += kWaves) {
       const uint32_t o = static_cast<uint32_t>(q * 64 + lane) * 4u;
       dma_untracked<4>(rsS, bCmb + q * 256, o);
-      dma_untracked<4>(rsW, bCmb + BM * kCombineMaxSlots * 4 + q * 256, o);
+      dma_untracked<4>(rsW, bCmb + BM * CMAX * 4 + q * 256, o);
     }
   }
 
@@ -960,35 +966,85 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       // y[t] = sum over the slots >= 0, in slot order, of w * routed row,
       // then plus the staged (bf16) shared output, in fp32, rounded once:
       // the arithmetic of the separate combine kernel.  Chunks go in
-      // batches of kB whose routed-row loads are all issued before the
-      // first multiply-add.
+      // batches of kB, slots in groups of kG: a group's routed-row loads
+      // for the whole batch are all issued before its first multiply-add.
       constexpr int kIters = (BM * kChunks + 64 * kWaves - 1) / (64 * kWaves);
-      constexpr int kB = 6;
+      constexpr int kB = CMAX > 4 ? 4 : 6;
+      constexpr int kG = 4;
       const uint16_t* const yr = static_cast<const uint16_t*>(p.cmb_rows);
-      const int km = p.cmb_kmax;
-      for (int i0 = 0; i0 < kIters; i0 += kB) {
-        uint4 v[kB][kCombineMaxSlots];
-        int32_t sl[kB][kCombineMaxSlots];
-        float wk[kB][kCombineMaxSlots];
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-          const int idx = tid + (i0 + b) * 64 * kWaves;
-          const int r = idx / kChunks;
-          const int f = loc.n0 + (idx - r * kChunks) * 8;
-          const bool ok = idx < BM * kChunks && loc.row0 + r < loc.row_end &&
-                          f < p.Nd;
-#pragma unroll
-          for (int k = 0; k < kCombineMaxSlots; ++k) {
-            sl[b][k] = -1;
-            wk[b][k] = 0.0f;
-            v[b][k] = make_uint4(0, 0, 0, 0);
-            if (ok && k < km) {
-              sl[b][k] = cslot[r * km + k];
-              wk[b][k] = cwt[r * km + k];
+      int km = p.cmb_kmax;
+      if constexpr (CMAX > 4) {
+        // Many slots, few of them used (Expert Race): move each row's
+        // non-empty slots to its front, in slot order, and count them, so
+        // that a chunk visits only the groups holding its row's slots (the
+        // sum keeps its slot order).  The table is [BM][km] from here on.
+        for (int r = tid; r < BM; r += 64 * kWaves) {
+          int n = 0;
+          for (int k = 0; k < km; ++k) {
+            const int32_t sv = cslot[r * km + k];
+            const float wv = cwt[r * km + k];
+            if (sv >= 0) {
+              cslot[r * km + n] = sv;
+              cwt[r * km + n] = wv;
+              ++n;
             }
-            if (sl[b][k] >= 0)
-              v[b][k] = *reinterpret_cast<const uint4*>(
-                  yr + static_cast<int64_t>(sl[b][k]) * p.Nd + f);
+          }
+          for (int k = n; k < km; ++k) cslot[r * km + k] = -1;
+          ccnt[r] = n;
+        }
+        stage_barrier();
+      }
+      for (int i0 = 0; i0 < kIters; i0 += kB) {
+        float a8[kB][8];
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[b][j] = 0.0f;
+        // slot groups this lane's chunks need
+        int kend = km;
+        if constexpr (CMAX > 4) {
+          kend = 0;
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+            const int idx = tid + (i0 + b) * 64 * kWaves;
+            if (idx < BM * kChunks) kend = max(kend, ccnt[idx / kChunks]);
+          }
+        }
+        for (int k0 = 0; k0 < kend; k0 += kG) {
+          uint4 v[kB][kG];
+          int32_t sl[kB][kG];
+          float wk[kB][kG];
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+            const int idx = tid + (i0 + b) * 64 * kWaves;
+            const int r = idx / kChunks;
+            const int f = loc.n0 + (idx - r * kChunks) * 8;
+            const bool ok = idx < BM * kChunks && loc.row0 + r < loc.row_end &&
+                            f < p.Nd;
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+              sl[b][k] = -1;
+              wk[b][k] = 0.0f;
+              v[b][k] = make_uint4(0, 0, 0, 0);
+              if (ok && k0 + k < km) {
+                sl[b][k] = cslot[r * km + k0 + k];
+                wk[b][k] = cwt[r * km + k0 + k];
+              }
+              if (sl[b][k] >= 0)
+                v[b][k] = *reinterpret_cast<const uint4*>(
+                    yr + static_cast<int64_t>(sl[b][k]) * p.Nd + f);
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+              if (sl[b][k] < 0) continue;
+              float yv[8];
+              unpack8(v[b][k], yv);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) a8[b][j] = fmaf(wk[b][k], yv[j], a8[b][j]);
+            }
           }
         }
 #pragma unroll
@@ -998,28 +1054,17 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           const int f = loc.n0 + (idx - r * kChunks) * 8;
           const int64_t row = loc.row0 + r;
           if (idx >= BM * kChunks || row >= loc.row_end || f >= p.Nd) continue;
-          float a8[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] = 0.0f;
-#pragma unroll
-          for (int k = 0; k < kCombineMaxSlots; ++k) {
-            if (sl[b][k] < 0) continue;
-            float yv[8];
-            unpack8(v[b][k], yv);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a8[j] = fmaf(wk[b][k], yv[j], a8[j]);
-          }
           float sh[8];
           unpack8(*reinterpret_cast<const uint4*>(
                       &lds[r * kOutPitch + (f - loc.n0)]), sh);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] += sh[j];
+          for (int j = 0; j < 8; ++j) a8[b][j] += sh[j];
           typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
           u32x4 o;
-          o[0] = pack_bf16x2(a8[0], a8[1]);
-          o[1] = pack_bf16x2(a8[2], a8[3]);
-          o[2] = pack_bf16x2(a8[4], a8[5]);
-          o[3] = pack_bf16x2(a8[6], a8[7]);
+          o[0] = pack_bf16x2(a8[b][0], a8[b][1]);
+          o[1] = pack_bf16x2(a8[b][2], a8[b][3]);
+          o[2] = pack_bf16x2(a8[b][4], a8[b][5]);
+          o[3] = pack_bf16x2(a8[b][6], a8[b][7]);
           __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(c + row * p.Nd + f));
         }
       }
@@ -1453,19 +1498,21 @@ int persistent_grid(int tiles, int occ = 1) {
 
 // Launch one forward GEMM stage: large tiles (BM x BN) or, for a problem
 // with fewer large tiles than 3/4 of the CUs, the small-tile form.
-template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM, bool PF>
+template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM, bool PF,
+          int CMAX = 4>
 void launch_stage(const GemmParams& p, hipStream_t stream) {
   const int big = tile_grid(p, BM, BN);
   if (static_cast<int64_t>(big) * 4 < static_cast<int64_t>(cu_count()) * 3) {
     hipLaunchKernelGGL(
-        (gemm_bf16_kernel<EPI, OUT_BF16, kSmBM, kSmBN, kSmWT, kSmWF, GM, PF>),
+        (gemm_bf16_kernel<EPI, OUT_BF16, kSmBM, kSmBN, kSmWT, kSmWF, GM, PF,
+                          false, CMAX>),
         dim3(persistent_grid(tile_grid(p, kSmBM, kSmBN), kSmOcc)),
         dim3(64 * kSmWT * kSmWF), 0, stream, p);
     return;
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF>),
-                     dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream,
-                     p);
+  hipLaunchKernelGGL(
+      (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF, false, CMAX>),
+      dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream, p);
 }
 
 }  // namespace
@@ -1661,8 +1708,12 @@ hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
   if (N == 0) return hipSuccess;
   GemmParams p{h,       nullptr, w2,       b2,     y, nullptr, N, 1, D, H,
                y_rows, slot_row, topk_w, Kmax};
-  launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
-      p, stream);
+  if (Kmax <= 4)
+    launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF, 4>(
+        p, stream);
+  else
+    launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
+                 kCombineMaxSlots>(p, stream);
   return hipGetLastError();
 }
 

@@ -15,9 +15,13 @@
 //     expert counts, exclusive offsets and block bases.
 //  3. permute_scatter_kernel: repeats the ballots (one per expert), so a
 //     selection's row is block base + earlier waves' count + set lanes below
-//     it; writes row_token, the block's slot_row (coalesced, from LDS), then
-//     copies each token row once from HBM to its K destination rows with
-//     16-byte lanes (row copy skipped when x_perm is null).
+//     it; writes row_token and the block's slot_row (coalesced, from LDS).
+//  4. permute_copy_kernel (only with x_perm): one thread per 16-byte chunk
+//     of every token row reads the chunk once and writes it to the token's
+//     selected rows; consecutive threads cover consecutive chunks, so both
+//     the reads and the writes are row-contiguous, and the grid is large
+//     enough to keep every CU streaming.
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -110,12 +114,10 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
   }
 }
 
-template <int VEC_BYTES>
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
-    const void* __restrict__ x, const int32_t* __restrict__ idx, int64_t N,
-    int row_bytes, int E, int Kmax, int64_t A,
+    const int32_t* __restrict__ idx, int64_t N, int E, int Kmax, int64_t A,
     const int64_t* __restrict__ block_base, int32_t* __restrict__ slot_row,
-    int32_t* __restrict__ row_token, void* __restrict__ x_perm) {
+    int32_t* __restrict__ row_token) {
   extern __shared__ int32_t s_rows[];  // [kPermTokens][Kmax]
   __shared__ int32_t wc[kPermWaves][kMaxExperts];
   const int lane = threadIdx.x & (kWave - 1);
@@ -157,24 +159,24 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
   const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
   for (int i = threadIdx.x; i < ntok * Kmax; i += kPermTokens)
     slot_row[t0 * Kmax + i] = s_rows[i];
-  if (x_perm == nullptr) return;
+}
 
-  // Row copy: each wave takes tokens wave, wave+4, ...; lanes cover the row
-  // in VEC_BYTES pieces.
-  typedef uint4 vec_t;
-  static_assert(VEC_BYTES == 16, "16-byte lanes");
-  const int nvec = row_bytes / VEC_BYTES;
-  const char* xb = static_cast<const char*>(x);
-  char* pb = static_cast<char*>(x_perm);
-  for (int tl = wave; tl < ntok; tl += kPermWaves) {
-    const vec_t* src = reinterpret_cast<const vec_t*>(xb + (t0 + tl) * row_bytes);
-    for (int c = lane; c < nvec; c += kWave) {
-      const vec_t v = src[c];
-      for (int k = 0; k < Kmax; ++k) {
-        const int32_t r = s_rows[tl * Kmax + k];
-        if (r >= 0)
-          reinterpret_cast<vec_t*>(pb + static_cast<int64_t>(r) * row_bytes)[c] = v;
-      }
+// x_perm[slot_row[t][k]] = x[t] for every slot k >= 0 of token t, 16 bytes
+// per thread: thread i copies chunk i % nvec of token i / nvec.  The token's
+// slot rows are read once per thread (the same few words for the nvec
+// threads of a token, served by the caches).
+__global__ __launch_bounds__(256) void permute_copy_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ slot_row,
+    int64_t N, int nvec, int Kmax, uint4* __restrict__ x_perm) {
+  const int64_t n = N * nvec;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = i / nvec;
+    const int c = static_cast<int>(i - t * nvec);
+    const uint4 v = x[i];
+    for (int k = 0; k < Kmax; ++k) {
+      const int32_t r = slot_row[t * Kmax + k];
+      if (r >= 0) x_perm[static_cast<int64_t>(r) * nvec + c] = v;
     }
   }
 }
@@ -241,17 +243,26 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                      block_base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nb == 0) return err;
-  const int row_bytes = D * (bf16 ? 2 : 4);
   const size_t shmem = static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
   if (shmem > 32768) {
     err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&permute_scatter_kernel<16>),
+        reinterpret_cast<const void*>(&permute_scatter_kernel),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3(static_cast<unsigned>(nb)),
-                     dim3(kPermTokens), shmem, stream, x, idx, N, row_bytes, E,
-                     Kmax, A, block_base, slot_row, row_token, x_perm);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nb)),
+                     dim3(kPermTokens), shmem, stream, idx, N, E, Kmax, A,
+                     block_base, slot_row, row_token);
+  err = hipGetLastError();
+  if (err != hipSuccess || x_perm == nullptr) return err;
+  // D is a multiple of 8, so a row is a whole number of 16-byte chunks.
+  const int nvec = D * (bf16 ? 2 : 4) / 16;
+  const int64_t chunks = N * nvec;
+  const unsigned grid =
+      static_cast<unsigned>(std::min<int64_t>(ceil_div(chunks, 256), 16384));
+  hipLaunchKernelGGL(permute_copy_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint4*>(x), slot_row, N, nvec, Kmax,
+                     static_cast<uint4*>(x_perm));
   return hipGetLastError();
 }
 

@@ -165,9 +165,9 @@ def shared_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
 
 def fuses_combine(cfg, buf: LayerBuffers) -> bool:
     """The shared experts' stage 2 and the combine run as one kernel for
-    bf16 layers with shared experts, bf16 routed outputs and at most 4 slots
-    per token."""
-    return (cfg.dtype == "bf16" and cfg.n_s > 0 and cfg.Kmax <= 4
+    bf16 layers with shared experts, bf16 routed outputs and at most 16
+    slots per token (top-K routing, or Expert Race with E <= 16)."""
+    return (cfg.dtype == "bf16" and cfg.n_s > 0 and cfg.Kmax <= 16
             and buf.y_rows.dtype == torch.bfloat16)
 
 

@@ -312,7 +312,7 @@ def _fdc(**kw):
     (dict(N=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
     (dict(Kmax=0), _lib.MOE_ERR_INVALID_ARGUMENT),
     (dict(dt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
-    (dict(Kmax=5), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(Kmax=17), _lib.MOE_ERR_UNSUPPORTED),
     (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
     (dict(N=1 << 31), _lib.MOE_ERR_UNSUPPORTED),
 ])

@@ -629,7 +629,10 @@ def test_routing_histogram_empty_batch():
     (777, 200, 136, 3, 0.5, True),
     # the large-tile form: 474 tiles of 256 x 192 (about two per persistent
     # workgroup) over 72 k stages, XL's shared hidden width per expert
-    (20000, 1152, 4608, 2, 0.05, False)])
+    (20000, 1152, 4608, 2, 0.05, False),
+    # Expert Race's slot layout: 16 slots per token, most of them empty
+    # (the 16-column form of the kernel), small and large tiles
+    (700, 256, 512, 16, 0.85, True), (5000, 2048, 1024, 16, 0.88, False)])
 def test_ffn_down_combine_matches_separate(N, D, H, Kmax, empty, bias):
     """The fused kernel gives the bits of stage 2 (one group of all tokens)
     followed by the combine kernel, and both agree with the oracle on every
