@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB_PATH names another build of the same library (the tests' host
+# sanitizer build); there is no fallback either way.
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARGUMENT = 1

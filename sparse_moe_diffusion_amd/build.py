@@ -32,9 +32,19 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI's
+# validation code (device code is built as usual): each flag applies to the
+# host compilation only.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                 "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-shared-libasan"]
+
+
+def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR,
+             extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,20 +57,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmoe.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source for gfx950 and link libmoe.so; returns its path.
+    With sanitize, the host code is instrumented with ASan and UBSan and the
+    library goes to _build/host_sanitize/libmoe.so (loaded with the clang
+    ASan runtime preloaded; see tests/test_abi_host_sanitized.py)."""
+    bdir = os.path.join(BUILD_DIR, "host_sanitize") if sanitize else BUILD_DIR
+    lib = os.path.join(bdir, "libmoe.so") if sanitize else LIB
+    extra = HOST_SANITIZE if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, verbose, bdir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs,
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -4,6 +4,9 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
+
+#include <cstring>
 
 #include <string>
 
@@ -34,7 +37,19 @@ moe_status from_hip(hipError_t err, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-bool valid_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
+// The integer a caller passed for a C enum parameter.  Any int can arrive
+// through the C ABI, and in C++ an enum object holding a value outside the
+// range of its enumerators must not be read as that type (the bits are
+// copied out instead); every check below works on the int.
+template <class Enum>
+int enum_value(const Enum& e) {
+  static_assert(sizeof(Enum) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof(v));
+  return v;
+}
+
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16; }
 
 constexpr int64_t kI32Limit = int64_t(1) << 31;
 constexpr int kMaxE = 64;
@@ -75,7 +90,8 @@ constexpr int kMaxGroups = moe::kMaxFfnGroups;
 
 extern "C" {
 
-const char* moe_status_string(moe_status status) {
+const char* moe_status_string(moe_status status_arg) {
+  const int status = enum_value(status_arg);
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
@@ -89,17 +105,20 @@ const char* moe_status_string(moe_status status) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_gate_workspace_size(int64_t N, int32_t E, int32_t K,
-                               moe_route route) {
+                               moe_route route_arg) {
+  const int route = enum_value(route_arg);
   (void)N; (void)E; (void)K;
   return route == MOE_ROUTE_EXPERT_RACE ? moe::race_workspace_bytes() : 0;
 }
 
-moe_status moe_gate_topk(const void* x, moe_dtype x_dtype,
+moe_status moe_gate_topk(const void* x, moe_dtype x_dtype_arg,
                          const float* w_gate, const float* logit_bias,
                          int64_t N, int32_t D, int32_t E, int32_t K,
-                         moe_route route, float* probs, int32_t* topk_idx,
+                         moe_route route_arg, float* probs, int32_t* topk_idx,
                          float* topk_w, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
+  const int x_dtype = enum_value(x_dtype_arg);
+  const int route = enum_value(route_arg);
   const char* fn = "moe_gate_topk";
   if (N < 0 || D < 1 || E < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, E >= 1", fn);
@@ -119,7 +138,8 @@ moe_status moe_gate_topk(const void* x, moe_dtype x_dtype,
   const int64_t Kmax = route == MOE_ROUTE_TOPK ? K : E;
   if (N * Kmax >= kI32Limit || N * E >= kI32Limit)
     return fail(MOE_ERR_UNSUPPORTED, "%s: N*Kmax must stay below 2^31", fn);
-  const size_t need = moe_gate_workspace_size(N, E, K, route);
+  const size_t need =
+      moe_gate_workspace_size(N, E, K, static_cast<moe_route>(route));
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
                 workspace_bytes, need);
@@ -144,7 +164,7 @@ size_t moe_permute_workspace_size(int64_t N, int32_t E, int32_t Kmax) {
 namespace {
 
 // Argument checks shared by moe_permute and moe_permute_noalloc.
-moe_status check_permute(const char* fn, const void* x, moe_dtype dtype,
+moe_status check_permute(const char* fn, const void* x, int dtype,
                          const int32_t* topk_idx, int64_t N, int32_t D,
                          int32_t E, int32_t Kmax, int32_t K,
                          const int32_t* expert_counts,
@@ -176,12 +196,13 @@ moe_status check_permute(const char* fn, const void* x, moe_dtype dtype,
 
 extern "C" {
 
-moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
+moe_status moe_permute(const void* x, moe_dtype dtype_arg, const int32_t* topk_idx,
                        int64_t N, int32_t D, int32_t E, int32_t Kmax, int32_t K,
                        int32_t* expert_counts, int64_t* expert_offsets,
                        int32_t* row_token, int32_t* slot_row, void* x_perm,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
   const char* fn = "moe_permute";
   const moe_status st =
       check_permute(fn, x, dtype, topk_idx, N, D, E, Kmax, K, expert_counts,
@@ -200,12 +221,13 @@ moe_status moe_permute(const void* x, moe_dtype dtype, const int32_t* topk_idx,
                   fn);
 }
 
-moe_status moe_permute_noalloc(const void* x, moe_dtype dtype,
+moe_status moe_permute_noalloc(const void* x, moe_dtype dtype_arg,
                                const int32_t* topk_idx, int64_t N, int32_t D,
                                int32_t E, int32_t Kmax, int32_t K,
                                int32_t* expert_counts, int64_t* expert_offsets,
                                int32_t* row_token, int32_t* slot_row,
                                void* x_perm, hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
   const char* fn = "moe_permute_noalloc";
   const moe_status st =
       check_permute(fn, x, dtype, topk_idx, N, D, E, Kmax, K, expert_counts,
@@ -230,13 +252,16 @@ moe_status moe_permute_noalloc(const void* x, moe_dtype dtype,
 }
 
 moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
-                           int64_t src_rows, moe_dtype dtype,
+                           int64_t src_rows, moe_dtype dtype_arg,
                            int64_t total_rows,
                            const int64_t* group_offsets, int32_t G, int32_t D,
                            int32_t H, const void* w1, const float* b1,
                            const void* w2, const float* b2, void* h_ws,
-                           void* u_ws, void* y_rows, moe_dtype y_dtype,
-                           moe_ffn_stages stages, hipStream_t stream) {
+                           void* u_ws, void* y_rows, moe_dtype y_dtype_arg,
+                           moe_ffn_stages stages_arg, hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
+  const int y_dtype = enum_value(y_dtype_arg);
+  const int stages = enum_value(stages_arg);
   const char* fn = "moe_grouped_ffn";
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -273,13 +298,15 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
 }
 
 moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
-                                 int64_t src_rows, moe_dtype dtype,
+                                 int64_t src_rows, moe_dtype dtype_arg,
                                  int64_t total_rows,
                                  const int64_t* group_offsets, int32_t G,
                                  int32_t D, int32_t H, const void* w1,
                                  const float* b1, const void* w2,
                                  const float* b2, void* y_rows,
-                                 moe_dtype y_dtype, hipStream_t stream) {
+                                 moe_dtype y_dtype_arg, hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
+  const int y_dtype = enum_value(y_dtype_arg);
   const char* fn = "moe_grouped_mlp_fused";
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -307,11 +334,14 @@ moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,
   return from_hip(moe::launch_mlp_fused(a, stream), fn);
 }
 
-moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
+moe_status moe_combine(const void* y_rows, moe_dtype y_dtype_arg,
                        const int32_t* slot_row, const float* topk_w, int64_t N,
                        int32_t D, int32_t Kmax, const void* y_shared,
-                       moe_dtype sh_dtype, void* y, moe_dtype out_dtype,
+                       moe_dtype sh_dtype_arg, void* y, moe_dtype out_dtype_arg,
                        hipStream_t stream) {
+  const int y_dtype = enum_value(y_dtype_arg);
+  const int sh_dtype = enum_value(sh_dtype_arg);
+  const int out_dtype = enum_value(out_dtype_arg);
   const char* fn = "moe_combine";
   if (N < 0 || D < 1 || Kmax < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, Kmax >= 1",
@@ -336,9 +366,10 @@ moe_status moe_combine(const void* y_rows, moe_dtype y_dtype,
 
 moe_status moe_balance_stats(const float* probs, const int32_t* topk_idx,
                              int32_t B, int32_t T, int32_t E, int32_t Kmax,
-                             int32_t K, float alpha, moe_balance_mode mode,
+                             int32_t K, float alpha, moe_balance_mode mode_arg,
                              int32_t* counts, float* prob_sums, float* loss,
                              hipStream_t stream) {
+  const int mode = enum_value(mode_arg);
   const char* fn = "moe_balance_stats";
   if (B < 0 || T < 1 || E < 1 || Kmax < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -367,14 +398,16 @@ size_t moe_gate_balance_workspace_size(int32_t B, int32_t T, int32_t E) {
   return moe::balance_partials_bytes(static_cast<int64_t>(B) * T, E);
 }
 
-moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype,
+moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype_arg,
                                  const float* w_gate, const float* logit_bias,
                                  int32_t B, int32_t T, int32_t D, int32_t E,
-                                 int32_t K, float alpha, moe_balance_mode mode,
+                                 int32_t K, float alpha, moe_balance_mode mode_arg,
                                  float* probs, int32_t* topk_idx, float* topk_w,
                                  int32_t* counts, float* prob_sums, float* loss,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
+  const int x_dtype = enum_value(x_dtype_arg);
+  const int mode = enum_value(mode_arg);
   const char* fn = "moe_gate_topk_balance";
   if (B < 0 || T < 1 || D < 1 || E < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -424,11 +457,12 @@ moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype,
                   fn);
 }
 
-moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
+moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype_arg, int64_t N,
                                 int32_t D, int32_t H, const void* w2,
                                 const float* b2, const void* y_rows,
                                 const int32_t* slot_row, const float* topk_w,
                                 int32_t Kmax, void* y, hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
   const char* fn = "moe_ffn_down_combine";
   if (N < 0 || D < 1 || H < 1 || Kmax < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -451,12 +485,14 @@ moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype, int64_t N,
                   fn);
 }
 
-moe_status moe_combine_backward(const void* dy, moe_dtype dy_dtype,
-                                const void* y_rows, moe_dtype y_dtype,
+moe_status moe_combine_backward(const void* dy, moe_dtype dy_dtype_arg,
+                                const void* y_rows, moe_dtype y_dtype_arg,
                                 const int32_t* slot_row, const float* topk_w,
                                 int64_t N, int32_t D, int32_t Kmax,
                                 void* dy_rows, float* slot_grad,
                                 hipStream_t stream) {
+  const int dy_dtype = enum_value(dy_dtype_arg);
+  const int y_dtype = enum_value(y_dtype_arg);
   const char* fn = "moe_combine_backward";
   if (N < 0 || D < 1 || Kmax < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need N >= 0, D >= 1, Kmax >= 1",
@@ -488,11 +524,13 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G, int32_t D,
 
 moe_status moe_grouped_ffn_backward(
     const void* x_rows, const int32_t* row_index, int64_t src_rows,
-    moe_dtype dtype, int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
+    moe_dtype dtype_arg, int64_t total_rows, const int64_t* group_offsets, int32_t G, int32_t D,
     int32_t H, const void* w1, const float* b1, const void* w2,
     const void* dy_rows, const void* u_rows, const void* h_rows,
-    void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype,
+    void* workspace, size_t workspace_bytes, void* dx_rows, moe_dtype dx_dtype_arg,
     float* dw1, float* dw2, hipStream_t stream) {
+  const int dtype = enum_value(dtype_arg);
+  const int dx_dtype = enum_value(dx_dtype_arg);
   const char* fn = "moe_grouped_ffn_backward";
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
@@ -536,13 +574,16 @@ size_t moe_gate_backward_workspace_size(int64_t N, int32_t E, int32_t D) {
 }
 
 moe_status moe_gate_backward(
-    const void* x, moe_dtype x_dtype, const float* w_gate, const float* probs,
+    const void* x, moe_dtype x_dtype_arg, const float* w_gate, const float* probs,
     const int32_t* topk_idx, const float* slot_grad, const int32_t* counts,
     int32_t B, int32_t T, int32_t D, int32_t E, int32_t Kmax, int32_t K,
-    float alpha, float dloss, moe_balance_mode mode, const void* dx_rows,
-    const int32_t* slot_row, const void* dx_shared, moe_dtype dx_dtype,
+    float alpha, float dloss, moe_balance_mode mode_arg, const void* dx_rows,
+    const int32_t* slot_row, const void* dx_shared, moe_dtype dx_dtype_arg,
     void* dx, float* dw_gate, float* dbias, void* workspace,
     size_t workspace_bytes, hipStream_t stream) {
+  const int x_dtype = enum_value(x_dtype_arg);
+  const int mode = enum_value(mode_arg);
+  const int dx_dtype = enum_value(dx_dtype_arg);
   const char* fn = "moe_gate_backward";
   if (B < 0 || T < 1 || D < 1 || E < 1 || Kmax < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
