@@ -194,45 +194,68 @@ __global__ __launch_bounds__(64 * kCbWaves) void combine_bwd_kernel(
 // ------------------------------------------------------------------ gate --
 
 // Per token: dP[i] = sum_k [idx[t][k] == i] dw[t][k] + dloss * dL/dP[t][i],
-// dlogits = P (dP - sum_j P_j dP_j), written to dl [N][E].
+// dlogits = P (dP - sum_j P_j dP_j), written to dl [N][E].  EP >= E bounds
+// the experts, so dP stays in registers (a slot adds to the expert it names
+// through unrolled compares, in slot order).  In global mode the balance
+// term is the same for every token: each workgroup forms it once, from the
+// counts summed over the images.
+template <int EP>
 __global__ __launch_bounds__(256) void gate_bwd_token_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ idx,
     const float* __restrict__ dw, const int32_t* __restrict__ counts, int B,
     int T, int E, int Kmax, int K, float alpha, float dloss, int global,
     float* __restrict__ dl) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  __shared__ float gcoef[EP];
   const int64_t N = static_cast<int64_t>(B) * T;
+  if (global && dloss != 0.0f) {   // uniform: every thread reaches the barrier
+    if (static_cast<int>(threadIdx.x) < E) {
+      const int i = threadIdx.x;
+      int64_t c = 0;
+      for (int bb = 0; bb < B; ++bb) c += counts[static_cast<int64_t>(bb) * E + i];
+      const float Tg = static_cast<float>(N);
+      float g = alpha * (static_cast<float>(E) / (static_cast<float>(K) * Tg)) *
+                static_cast<float>(c) / Tg;
+      gcoef[i] = g * dloss;
+    }
+    __syncthreads();
+  }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= N) return;
   const int b = static_cast<int>(t / T);
-  float dP[kMaxExperts];
-  for (int i = 0; i < E; ++i) {
+  float dP[EP];
+#pragma unroll
+  for (int i = 0; i < EP; ++i) {
     float g = 0.0f;
-    if (dloss != 0.0f) {
+    if (i < E && dloss != 0.0f) {
       if (global) {
-        int64_t c = 0;
-        for (int bb = 0; bb < B; ++bb) c += counts[static_cast<int64_t>(bb) * E + i];
-        const float Tg = static_cast<float>(N);
-        g = alpha * (static_cast<float>(E) / (static_cast<float>(K) * Tg)) *
-            static_cast<float>(c) / Tg;
+        g = gcoef[i];
       } else {
         g = alpha / static_cast<float>(B) *
             (static_cast<float>(E) / (static_cast<float>(K) * T)) *
             static_cast<float>(counts[static_cast<int64_t>(b) * E + i]) /
             static_cast<float>(T);
+        g *= dloss;
       }
-      g *= dloss;
     }
     dP[i] = g;
   }
   for (int k = 0; k < Kmax; ++k) {
     const int e = idx[t * Kmax + k];
-    if (e >= 0 && e < E) dP[e] += dw[t * Kmax + k];
+    const float d = dw[t * Kmax + k];
+#pragma unroll
+    for (int i = 0; i < EP; ++i)
+      if (i == e && i < E) dP[i] += d;
   }
   float s = 0.0f;
-  for (int i = 0; i < E; ++i) s = fmaf(probs[t * E + i], dP[i], s);
-  for (int i = 0; i < E; ++i) {
-    const float p = probs[t * E + i];
-    dl[t * E + i] = p * (dP[i] - s);
+#pragma unroll
+  for (int i = 0; i < EP; ++i)
+    if (i < E) s = fmaf(probs[t * E + i], dP[i], s);
+#pragma unroll
+  for (int i = 0; i < EP; ++i) {
+    if (i < E) {
+      const float p = probs[t * E + i];
+      dl[t * E + i] = p * (dP[i] - s);
+    }
   }
 }
 
@@ -479,10 +502,20 @@ hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
   float* part_w = dl + (N * E + 63) / 64 * 64;
   float* part_b = part_w + chunks * E * D;
   if (N > 0) {
-    hipLaunchKernelGGL(gate_bwd_token_kernel,
-                       dim3(static_cast<unsigned>(ceil_div(N, 256))), dim3(256),
-                       0, stream, probs, idx, dw, counts, B, T, E, Kmax, K,
-                       alpha, dloss, global ? 1 : 0, dl);
+    const dim3 tgrid(static_cast<unsigned>(ceil_div(N, 256)));
+#define MOE_TOKEN_BWD(EP_)                                                   \
+    hipLaunchKernelGGL(gate_bwd_token_kernel<EP_>, tgrid, dim3(256), 0, stream, \
+                       probs, idx, dw, counts, B, T, E, Kmax, K, alpha, dloss, \
+                       global ? 1 : 0, dl)
+    if (E <= 8)
+      MOE_TOKEN_BWD(8);
+    else if (E <= 16)
+      MOE_TOKEN_BWD(16);
+    else if (E <= 32)
+      MOE_TOKEN_BWD(32);
+    else
+      MOE_TOKEN_BWD(64);
+#undef MOE_TOKEN_BWD
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // dW_g / dbias partials: threads = the feature chunks rounded up to
