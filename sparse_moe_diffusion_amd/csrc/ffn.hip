@@ -1522,25 +1522,47 @@ namespace {
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Reduction splits of the K-grouped weight-gradient GEMMs ([G][M][N] out,
-// 256 x 256 tiles, `total` token rows over G groups): the largest S <= 8
-// whose S x tiles still fit one round of the chip (the current device's CU
-// count, as the persistent grids use; the workspace query and the launch
-// take the same count, so the partials always fit) and whose pieces keep
-// at least 2048 tokens of an average group.  Measured: the shared experts'
-// weight gradients of the S layer (24 tiles, 8192 tokens) take 0.28 instead
-// of 0.46 ms per backward call with S = 4; splits past one round, or into
-// short pieces, were slower (a tile's fixed cost is several k stages, and
-// fewer busy CUs run at a higher clock).
+// 256 x 256 tiles, `total` token rows over G groups).  Splitting a group's
+// token rows into S pieces makes S x more tiles, each 1/S as long, and adds
+// the fp32 partials' traffic (S written, S read back by the reduction).  The
+// estimate for S: ceil(S x tiles / CUs) rounds of tiles of ceil(rows / S)
+// tokens at about 4 TFLOP/s per CU, plus 2 S G M N 4 bytes at about 5 TB/s.
+// S runs up to 8, with pieces of at least 2048 tokens of an average group,
+// and a split is taken only when its estimate is below 0.9 of the unsplit
+// one (the estimate ignores the clock, which rises when fewer CUs are busy).
+// The CU count is the current device's, as the persistent grids use; the
+// workspace query and the launch take the same count, so the partials always
+// fit.  Measured: the shared experts' weight gradients of the S layer (24
+// tiles, 8192 tokens) take 0.28 instead of 0.46 ms per backward call with
+// S = 4; those of the XL layer (180 tiles over 184 of 256 CUs, 32768
+// tokens) split in 4 as well.
 int choose_ksplit(int G, int M, int N, int64_t total) {
   const int64_t tiles = static_cast<int64_t>(G) * ((M + kUpBM - 1) / kUpBM) *
                         ((N + kUpBN - 1) / kUpBN);
+  if (G <= 0 || tiles <= 0 || total <= 0) return 1;
   constexpr int64_t kMinTokens = 2048;
+  constexpr double kCuFlops = 4.0e12, kHbmBytes = 5.0e12;
   const int64_t cus = cu_count();
-  const int64_t per_group = G > 0 ? total / G : 0;
-  int S = 1;
-  while (S < 8 && tiles * (S + 1) <= cus && per_group / (S + 1) >= kMinTokens)
-    ++S;
-  return S;
+  const int64_t per_group = total / G;
+  const double tile_flops_per_token = 2.0 * kUpBM * kUpBN;
+  const double out_bytes = 4.0 * G * static_cast<double>(M) * N;
+  auto estimate = [&](int S) {
+    const int64_t rounds = (S * tiles + cus - 1) / cus;
+    const int64_t piece = (per_group + S - 1) / S;
+    return static_cast<double>(rounds) * piece * tile_flops_per_token / kCuFlops +
+           (S > 1 ? 2.0 * S * out_bytes / kHbmBytes : 0.0);
+  };
+  int best = 1;
+  double best_t = estimate(1);
+  const double unsplit = best_t;
+  for (int S = 2; S <= 8 && per_group / S >= kMinTokens; ++S) {
+    const double t = estimate(S);
+    if (t < best_t) {
+      best = S;
+      best_t = t;
+    }
+  }
+  return best_t < 0.9 * unsplit ? best : 1;
 }
 
 // out[i] = part[0][i] + part[1][i] + ... in split order (same bits every
