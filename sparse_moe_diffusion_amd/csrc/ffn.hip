@@ -450,10 +450,18 @@ __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
 // transfer covering rows r0..r0+7 fetches chunk (l % 8) ^ swz(r0 + l / 8) of
 // row r0 + l / 8, which is exactly the swizzled LDS slot it lands in.  One
 // workgroup per CU.
+//
+// BT: the weight operand is stored k-major, [G][Kd][Nd] (a forward weight
+// read as its own transpose), and is brought to LDS and read as the
+// K-grouped form reads its operands ([64][BN] stage tiles, transpose reads);
+// the token operand stays row-major and is read in place (no gather).
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
-          bool PF, bool KG = false, int CMAX = 4>
+          bool PF, bool KG = false, int CMAX = 4, bool BT = false>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
   static_assert(EPI != kEpiGeluGrad || OUT_BF16, "gelu'(u) is applied on bf16 output");
+  static_assert(!BT || (!KG && !PF && EPI != kEpiCombine && (BN == 128 || BN == 256)),
+                "k-major weights: whole 256- or 512-byte k rows, no prefetch, "
+                "no combine");
   static_assert(!KG || (!OUT_BF16 && !PF && EPI == kEpiStore),
                 "the K-grouped form writes fp32 without prefetch");
   static_assert(!KG || (BM == 256 && BN == 256),
@@ -582,15 +590,22 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
                     uniform64(reinterpret_cast<int64_t>(a_base))),
                 __builtin_amdgcn_readfirstlane(a_bytes));
   // Weight rows of group g: features past Nd fall outside the descriptor.
+  // BT: group g's [Kd][Nd] block from the tile's first feature of k row 0
+  // to its end; each stage moves the base down 64 k rows and shrinks the
+  // range, so k rows past Kd read zero (features past Nd read the next
+  // row's values, which only reach features that are not stored).
   const uint16_t* w_base =
       static_cast<const uint16_t*>(p.w) +
-      (KG ? static_cast<int64_t>(loc.kofs) * p.Nd + loc.n0
-          : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
+      (KG   ? static_cast<int64_t>(loc.kofs) * p.Nd + loc.n0
+       : BT ? static_cast<int64_t>(loc.g) * Kd * p.Nd + loc.n0
+            : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
   const int64_t kg_w =
-      KG ? (static_cast<int64_t>(loc.klen) * p.Nd - loc.n0) * 2 : 0;
+      KG   ? (static_cast<int64_t>(loc.klen) * p.Nd - loc.n0) * 2
+      : BT ? (static_cast<int64_t>(Kd) * p.Nd - loc.n0) * 2
+           : 0;
   const uint32_t w_bytes =
-      KG ? static_cast<uint32_t>(kg_w > 0 ? kg_w : 0)
-         : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
+      (KG || BT) ? static_cast<uint32_t>(kg_w > 0 ? kg_w : 0)
+                 : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(w_base))),
@@ -608,7 +623,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   for (int q = 0; q < NQ; ++q) {
     const int t = wave + kWaves * q;          // transfer index in the stage
     const bool isA = q < QA;                  // uniform across the wave
-    if constexpr (KG) {
+    if (KG || (BT && !isA)) {
       // 1 KB of the operand's [64][R] stage tile per transfer: lane l lands
       // at byte 16 l of it, i.e. k row kr, 16-byte slot pc, which holds
       // chunk pc ^ 4 (kr % 4) of that token row (so the transpose reads of
@@ -695,6 +710,26 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           dma16_raw(kg_wbase + sb_, w_bytes > sb_ ? w_bytes - sb_ : 0u,      \
                     (DB) + ldst[q], goff[q]);                                \
       }                                                                      \
+    } else if constexpr (BT) {                                               \
+      /* every transfer written out (the compiler would otherwise wait for */ \
+      /* builtin transfers before the weight's transpose reads); the      */ \
+      /* weight's k stage is a byte offset from k row 0, so k rows past   */ \
+      /* Kd fall outside the descriptor and read zero                     */ \
+      const bool full_ = (ikt_ + 1) * kBK <= Kd;                             \
+      const uint32_t sb_ = static_cast<uint32_t>(ikt_) * kstep_b;            \
+      _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
+        if (q < QA) {                                                        \
+          uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2); \
+          if (!full_) {                                                      \
+            const int r_ = (wave + kWaves * q) * 8 + (lane >> 3);            \
+            const int c_ = (lane & 7) ^ swz(r_);                             \
+            if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;               \
+          }                                                                  \
+          dma16_raw(kg_abase, a_bytes, (DA) + ldst[q], off_);                \
+        } else {                                                             \
+          dma16_raw(kg_wbase, w_bytes, (DB) + ldst[q], goff[q] + sb_);       \
+        }                                                                    \
+      }                                                                      \
     } else {                                                                 \
       const bool full_ = (ikt_ + 1) * kBK <= Kd;                             \
       _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
@@ -721,7 +756,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // swz(row), i.e. that offset XOR 16 ks (the row part has its low 6 bits
   // clear), so one register per fragment serves all four steps.
   int oa[FB][1], ob[TB][1];
-  if constexpr (KG) {
+  if constexpr (KG || BT) {
     // Transposed fragments (byte offsets at k step 0): lane l addresses k
     // row 8 (l / 32) + (l / 4) % 4 and the 8-byte piece of features
     // 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 of its 32-row block, in the
@@ -737,8 +772,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     }
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
-      const int c0 = (wt * (BM / WT) + j * 32) / 8;
-      ob[j][0] = kr * BM * 2 + ((c0 + cl) ^ sw) * 16 + hb;
+      if constexpr (KG) {
+        const int c0 = (wt * (BM / WT) + j * 32) / 8;
+        ob[j][0] = kr * BM * 2 + ((c0 + cl) ^ sw) * 16 + hb;
+      } else {
+        const int row = wt * (BM / WT) + j * 32 + (lane & 31);
+        ob[j][0] = row * kBK + ((khalf ^ swz(row)) * 8);
+      }
     }
   } else {
 #pragma unroll
@@ -772,6 +812,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           lds_frag_tr<BN * 2>((SB), oa[i][0] + (KS) * 16 * BN * 2);          \
       _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                \
           lds_frag_tr<BM * 2>((SA), ob[j][0] + (KS) * 16 * BM * 2);          \
+    } else if constexpr (BT) {                                               \
+      _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                 \
+          lds_frag_tr<BN * 2>((SB), oa[i][0] + (KS) * 16 * BN * 2);          \
+      _Pragma("unroll") for (int j = 0; j < TB; ++j) FB_[j] =                \
+          *reinterpret_cast<const bf16x8*>(&(SA)[ob[j][0] ^ (16 * (KS))]);   \
     } else {                                                                 \
       _Pragma("unroll") for (int i = 0; i < FB; ++i) FA[i] =                 \
           *reinterpret_cast<const bf16x8*>(&(SB)[oa[i][0] ^ (16 * (KS))]);   \
@@ -1499,19 +1544,19 @@ int persistent_grid(int tiles, int occ = 1) {
 // Launch one forward GEMM stage: large tiles (BM x BN) or, for a problem
 // with fewer large tiles than 3/4 of the CUs, the small-tile form.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM, bool PF,
-          int CMAX = 4>
+          int CMAX = 4, bool BT = false>
 void launch_stage(const GemmParams& p, hipStream_t stream) {
   const int big = tile_grid(p, BM, BN);
   if (static_cast<int64_t>(big) * 4 < static_cast<int64_t>(cu_count()) * 3) {
     hipLaunchKernelGGL(
         (gemm_bf16_kernel<EPI, OUT_BF16, kSmBM, kSmBN, kSmWT, kSmWF, GM, PF,
-                          false, CMAX>),
+                          false, CMAX, BT>),
         dim3(persistent_grid(tile_grid(p, kSmBM, kSmBN), kSmOcc)),
         dim3(64 * kSmWT * kSmWF), 0, stream, p);
     return;
   }
   hipLaunchKernelGGL(
-      (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF, false, CMAX>),
+      (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF, false, CMAX, BT>),
       dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream, p);
 }
 
@@ -1581,7 +1626,7 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(
 }
 
 struct BwdLayout {
-  size_t u, h, du, w1t, w2t, xr, part, total;
+  size_t u, h, du, w1t, xr, part, total;
 };
 
 BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
@@ -1592,7 +1637,6 @@ BwdLayout bwd_layout(int64_t total, int G, int D, int H) {
   L.h = take(static_cast<size_t>(total) * H * 2);
   L.du = take(static_cast<size_t>(total) * H * 2);
   L.w1t = take(static_cast<size_t>(G) * D * H * 2);
-  L.w2t = take(static_cast<size_t>(G) * H * D * 2);
   L.xr = take(static_cast<size_t>(total) * D * 2);
   const int S = choose_ksplit(G, D, H, total);
   L.part = take(S > 1 ? static_cast<size_t>(S) * G * D * H * 4 : 0);
@@ -1608,7 +1652,7 @@ size_t ffn_backward_workspace_bytes(int64_t total, int G, int D, int H) {
 
 // Backward of the grouped expert MLPs, given dy_rows = dLoss/d(expert output):
 //   u       = x_rows W1^T (+ b1)                   (recomputed, bf16)
-//   du      = (dy_rows W2) * gelu'(u)              (W2 transposed once)
+//   du      = (dy_rows W2) * gelu'(u)              (W2 read k-major as stored)
 //   dx_rows = du W1                                (W1 transposed once)
 //   dW2[g]  = dy_rows[g]^T gelu(u[g]),  dW1[g] = du[g]^T x_rows[g]
 // the last two as K-grouped GEMMs that read the row-major operands and
@@ -1619,7 +1663,6 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
   void* u = ws + L.u;
   void* du = ws + L.du;
   void* w1t = ws + L.w1t;
-  void* w2t = ws + L.w2t;
   // a = gelu(u) and the expert's input rows, row-major, for the weight
   // gradients: the forward's, or formed here.
   const void* hh = a.h_saved != nullptr ? a.h_saved : ws + L.h;
@@ -1632,8 +1675,8 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
     if (err != hipSuccess) return err;     \
   } while (0)
 
-  // the weights' transposes are needed even without rows (dW = 0 then)
-  MOE_TRY(launch_transpose(a.w2, G, D, H, w2t, stream));
+  // W1's transpose for dx (its 192-wide tiles take no k-major weights); W2
+  // is read as stored, k-major, by the du GEMM
   MOE_TRY(launch_transpose(a.w1, G, H, D, w1t, stream));
   if (a.total_rows > 0) {
     // u: the forward's saved pre-activations, or recomputed (with
@@ -1658,11 +1701,11 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
       MOE_TRY(launch_rows(uu, nullptr, 0, a.total_rows, H, true, ws + L.h,
                           stream));
     }
-    GemmParams pd{a.dy_rows, nullptr, w2t, nullptr, du, a.offsets,
+    GemmParams pd{a.dy_rows, nullptr, a.w2, nullptr, du, a.offsets,
                   a.total_rows, G, H, D};
     pd.aux = uu;
-    launch_stage<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(
-        pd, stream);
+    launch_stage<kEpiGeluGrad, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false,
+                 4, true>(pd, stream);
     MOE_TRY(hipGetLastError());
     GemmParams px{du, nullptr, w1t, nullptr, a.dx_rows, a.offsets,
                   a.total_rows, G, D, H};
