@@ -433,13 +433,14 @@ size_t moe_ffn_backward_workspace_size(int64_t total_rows, int32_t G,
  *   dy_rows [total_rows][D] bf16;  dx_rows [total_rows][D];
  *   dw1 [G][H][D], dw2 [G][D][H] fp32 out;  workspace of at least
  *   moe_ffn_backward_workspace_size bytes (recomputed activations,
- *   transposed weights, the gathered input rows and, when few
+ *   W1's transpose, the gathered input rows and, when few
  *   weight-gradient tiles meet long token segments, the fp32 partials of a
  *   split reduction, added in a fixed order); contents need no
  *   initialisation
  * Errors: INVALID_ARGUMENT for null pointers, bad sizes or src_rows < 1
  *   with row_index; UNSUPPORTED for non-bf16 inputs, G > 128, D or H not
- *   multiples of 8, (total_rows + 64) * max(D, H) * 2 >= 2^32, a gathered
+ *   multiples of 8, (total_rows + 64) * max(D, H) * 2 >= 2^32,
+ *   D * H * 2 >= 2^32, a gathered
  *   x_rows past the 4 GiB range of moe_grouped_ffn; WORKSPACE_TOO_SMALL.
  */
 moe_status moe_grouped_ffn_backward(

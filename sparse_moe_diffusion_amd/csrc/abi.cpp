@@ -555,6 +555,11 @@ moe_status moe_grouped_ffn_backward(
           (int64_t(1) << 32))
     return fail(MOE_ERR_UNSUPPORTED, "%s: total_rows=%lld too large", fn,
                 (long long)total_rows);
+  // the du GEMM reads a group's W2 block [D][H] k-major with 32-bit byte
+  // offsets
+  if (static_cast<int64_t>(D) * H * 2 >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: D*H=%lld too large", fn,
+                (long long)D * H);
   CHECK_GATHER(rows, row_index, src_rows, static_cast<int64_t>(D) * 2);
   if (workspace_bytes < moe::ffn_backward_workspace_bytes(total_rows, G, D, H))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace below %zu bytes",

@@ -355,6 +355,11 @@ def test_backward_entry_points_reject():
                    (dict(total=(1 << 23) - 65, wsb=16),
                     _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
                    (dict(wsb=16), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+                   # a group's W2 block is read with 32-bit byte offsets:
+                   # D * H * 2 must stay below 2^32
+                   (dict(D=1 << 16, H=1 << 15), _lib.MOE_ERR_UNSUPPORTED),
+                   (dict(D=1 << 16, H=(1 << 15) - 8, wsb=16),
+                    _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
                    (dict(ri=FAKE, src=0), _lib.MOE_ERR_INVALID_ARGUMENT),
                    # D = 128: src <= 2^24 - 2 passes the gather check and
                    # reaches the workspace check
