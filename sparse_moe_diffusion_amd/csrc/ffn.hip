@@ -368,6 +368,15 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// The same with the wave's newest KEEP transfers still allowed in flight
+// (the next-but-one stage of a three-stage ring): vmcnt(KEEP).
+template <int KEEP>
+__device__ __forceinline__ void stage_barrier_keep() {
+  static_assert(KEEP >= 0 && KEEP < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((KEEP & 0xf) | ((KEEP >> 4) << 14) | (0x7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
@@ -455,10 +464,20 @@ __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
 // read as its own transpose), and is brought to LDS and read as the
 // K-grouped form reads its operands ([64][BN] stage tiles, transpose reads);
 // the token operand stays row-major and is read in place (no gather).
+//
+// NST: token-row k stages held in LDS (the weight rows always have two).
+// With 2, stage k + 1 of both operands streams in while stage k is
+// multiplied.  With 3, stage k + 2 of the token rows streams in (with stage
+// k + 1 of the weight rows, issued first), so each token-row transfer has
+// two stages of MFMAs to arrive in: the wait at a stage's end leaves the
+// wave's newest QA transfers (the token rows of stage k + 2) in flight.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM,
-          bool PF, bool KG = false, int CMAX = 4, bool BT = false>
+          bool PF, bool KG = false, int CMAX = 4, bool BT = false, int NST = 2>
 __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p) {
   static_assert(EPI != kEpiGeluGrad || OUT_BF16, "gelu'(u) is applied on bf16 output");
+  static_assert(NST == 2 || (NST == 3 && !PF && !KG && !BT),
+                "three token-row stages: plain operands, no prefetch transfers "
+                "in the wait count");
   static_assert(!BT || (!KG && !PF && EPI != kEpiCombine && (BN == 128 || BN == 256)),
                 "k-major weights: whole 256- or 512-byte k rows, no prefetch, "
                 "no combine");
@@ -476,7 +495,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // LDS: the two k stages during the main loop; afterwards (bf16 output)
   // the finished tile, row-major with a 16-byte pad per row, so that it
   // leaves in whole-row 16-byte-per-lane stores.
-  constexpr int kStageBytes = 2 * (BM + BN) * kBK * 2;
+  constexpr int kStageBytes = (NST * BM + 2 * BN) * kBK * 2;
   constexpr int kOutPitch = BN + 8;   // staged row pitch, elements
   constexpr int kOutBytes = OUT_BF16 ? BM * kOutPitch * 2 : 0;
   constexpr int kMainElems = (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2;
@@ -495,14 +514,17 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   int32_t* const cslot = sidx + 2 * BM;
   float* const cwt = reinterpret_cast<float*>(cslot + BM * CMAX);
   int32_t* const ccnt = cslot + 2 * BM * CMAX;
+  // Token-row stage s at lds + s BM kBK, then the two weight-row stages.
   uint16_t* const sA0 = lds;
   uint16_t* const sA1 = sA0 + BM * kBK;
-  uint16_t* const sB0 = sA1 + BM * kBK;
+  uint16_t* const sA2 = sA1 + BM * kBK;   // NST == 3 only
+  uint16_t* const sB0 = lds + NST * BM * kBK;
   uint16_t* const sB1 = sB0 + BN * kBK;
+
   // The same as LDS byte addresses, for the transfers.
   const uint32_t lds0 = lds_addr(lds);
-  const uint32_t bA0 = lds0, bA1 = bA0 + BM * kBK * 2;
-  const uint32_t bB0 = bA1 + BM * kBK * 2, bB1 = bB0 + BN * kBK * 2;
+  const uint32_t bA0 = lds0, bA1 = bA0 + BM * kBK * 2, bA2 = bA1 + BM * kBK * 2;
+  const uint32_t bB0 = lds0 + NST * BM * kBK * 2, bB1 = bB0 + BN * kBK * 2;
   const uint32_t bPf = lds0 + kMainElems * 2;
   const uint32_t bIdx = bPf + kPfElems * 2 + kTabInts * 4;
   const uint32_t bCmb = bIdx + 2 * BM * 4;
@@ -747,6 +769,27 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     }                                                                        \
   } while (0)
 
+  // NST == 3: transfers in issue order i (weight rows first): i < QB are
+  // weight-row transfers QA + i of stage KTB into DB, the rest token-row
+  // transfers i - QB of stage KTA into DA.
+#define MOE_ISSUE3(KTA, KTB, DA, DB, I0, I1)                                 \
+  do {                                                                       \
+    _Pragma("unroll") for (int i_ = (I0); i_ < (I1); ++i_) {                 \
+      constexpr int QB_ = NQ - QA;                                           \
+      const int q = i_ < QB_ ? QA + i_ : i_ - QB_;                           \
+      const bool isA_ = q < QA;                                              \
+      const int ikt_ = isA_ ? (KTA) : (KTB);                                 \
+      uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);     \
+      if ((ikt_ + 1) * kBK > Kd) {                                           \
+        const int t_ = wave + kWaves * q;                                    \
+        const int r_ = (isA_ ? t_ : t_ - BM / 8) * 8 + (lane >> 3);          \
+        const int c_ = (lane & 7) ^ swz(r_);                                 \
+        if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;                   \
+      }                                                                      \
+      dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
+    }                                                                        \
+  } while (0)
+
   // Fragment rows: (lane & 31) within each 32-row block; at k step ks of a
   // stage the lane reads chunk kc = 2 ks + (lane >> 5), stored at slot
   // kc ^ swz(row).  Element offsets for all four k steps are precomputed.
@@ -860,13 +903,19 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     MOE_FRAGS(fa1, fb1, CA, CB, 1);                                          \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_MFMAS(fa0, fb0, 0, FB);                                              \
-    MOE_ISSUE(skt_ + 1, DNA, DNB, 0, kQH);                                   \
+    if constexpr (NST == 3)                                                  \
+      MOE_ISSUE3(skt_ + 2, skt_ + 1, DNA, DNB, 0, kQH);                      \
+    else                                                                     \
+      MOE_ISSUE(skt_ + 1, DNA, DNB, 0, kQH);                                 \
     MOE_INTERLEAVE(kQH);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_FRAGS(fa0, fb0, CA, CB, 2);                                          \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_MFMAS(fa1, fb1, 0, FB);                                              \
-    MOE_ISSUE(skt_ + 1, DNA, DNB, kQH, NQ);                                  \
+    if constexpr (NST == 3)                                                  \
+      MOE_ISSUE3(skt_ + 2, skt_ + 1, DNA, DNB, kQH, NQ);                     \
+    else                                                                     \
+      MOE_ISSUE(skt_ + 1, DNA, DNB, kQH, NQ);                                \
     MOE_INTERLEAVE(NQ - kQH);                                                \
     __builtin_amdgcn_sched_barrier(0);                                       \
     MOE_FRAGS(fa1, fb1, CA, CB, 3);                                          \
@@ -876,7 +925,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     MOE_MFMAS(fa1, fb1, 0, FB - FB / 2);                                     \
     __builtin_amdgcn_sched_barrier(0);                                       \
     if (more_) {                                                             \
-      stage_barrier();                                                       \
+      stage_barrier_keep<NST == 3 ? QA : 0>();                               \
       __builtin_amdgcn_sched_barrier(0);                                     \
       MOE_FRAGS(fa0, fb0, NA, NB, 0);                                        \
     }                                                                        \
@@ -914,18 +963,33 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
 
   MOE_ISSUE(0, bA0, bB0, 0, NQ);
-  stage_barrier();
+  if constexpr (NST == 3) MOE_ISSUE(1, bA1, bB1, 0, QA);   // token rows only
+  stage_barrier_keep<NST == 3 ? QA : 0>();
   MOE_FRAGS(fa0, fb0, sA0, sB0, 0);
-  // Stages alternate between the two buffers.  The last stage's transfers
-  // address k-stage nk, which lies wholly past Kd: they load zeros into the
-  // idle buffer (no branch around them, so they interleave with the MFMAs)
+  // Stages rotate through the buffers.  The last stages' transfers address
+  // k-stages from nk on, which lie wholly past Kd: they load zeros into
+  // idle buffers (no branch around them, so they interleave with the MFMAs)
   // and are drained before the epilogue.
-  for (int kt = 0; kt < nk; kt += 2) {
-    MOE_STAGE(kt, sA0, sB0, sA1, sB1, bA1, bB1);
-    if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA0, sB0, bA0, bB0);
+  if constexpr (NST == 2) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      MOE_STAGE(kt, sA0, sB0, sA1, sB1, bA1, bB1);
+      if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA0, sB0, bA0, bB0);
+    }
+  } else {
+    // token rows in three buffers, weight rows in two: the pair of buffers
+    // of stage kt is (kt % 3, kt % 2), six stages per turn
+    for (int kt = 0; kt < nk; kt += 6) {
+      MOE_STAGE(kt, sA0, sB0, sA1, sB1, bA2, bB1);
+      if (kt + 1 < nk) MOE_STAGE(kt + 1, sA1, sB1, sA2, sB0, bA0, bB0);
+      if (kt + 2 < nk) MOE_STAGE(kt + 2, sA2, sB0, sA0, sB1, bA1, bB1);
+      if (kt + 3 < nk) MOE_STAGE(kt + 3, sA0, sB1, sA1, sB0, bA2, bB0);
+      if (kt + 4 < nk) MOE_STAGE(kt + 4, sA1, sB0, sA2, sB1, bA0, bB1);
+      if (kt + 5 < nk) MOE_STAGE(kt + 5, sA2, sB1, sA0, sB0, bA1, bB0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x7 << 4);
 #undef MOE_STAGE
+#undef MOE_ISSUE3
 #undef MOE_PREFETCH
 #undef MOE_INTERLEAVE
 #undef MOE_MFMAS
@@ -1414,6 +1478,13 @@ constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
 // (h): with GM = 1 all feature tiles of a row-tile run at once, so each row
 // of h leaves HBM once.  Stage 1 (18+ feature tiles) keeps bands of 8.
 constexpr int kUpGM = 8, kDnGM = 1;
+// Stage 2 streams a long token operand (K = H) whose rows mostly miss L2:
+// its large tiles keep three token-row stages in LDS, so each transfer has
+// two stages of MFMAs to land in (0.65 -> 0.56-0.59 ms per XL launch, where
+// the two-stage form was bound by that latency: without its MFMAs it took
+// 0.61 ms).  That form takes no L2 prefetch (measured to add nothing to it);
+// the small-tile form keeps two stages and the prefetch.
+constexpr int kDnNST = 3;
 constexpr bool kDnPF = true;
 // Small problems (short sequences, narrow layers): when the large tiles
 // would occupy fewer than 3/4 of the CUs, most of the chip idles.  Those
@@ -1544,19 +1615,20 @@ int persistent_grid(int tiles, int occ = 1) {
 // Launch one forward GEMM stage: large tiles (BM x BN) or, for a problem
 // with fewer large tiles than 3/4 of the CUs, the small-tile form.
 template <int EPI, bool OUT_BF16, int BM, int BN, int WT, int WF, int GM, bool PF,
-          int CMAX = 4, bool BT = false>
+          int CMAX = 4, bool BT = false, int NST = 2>
 void launch_stage(const GemmParams& p, hipStream_t stream) {
   const int big = tile_grid(p, BM, BN);
   if (static_cast<int64_t>(big) * 4 < static_cast<int64_t>(cu_count()) * 3) {
     hipLaunchKernelGGL(
         (gemm_bf16_kernel<EPI, OUT_BF16, kSmBM, kSmBN, kSmWT, kSmWF, GM, PF,
-                          false, CMAX, BT>),
+                          false, CMAX, BT, 2>),
         dim3(persistent_grid(tile_grid(p, kSmBM, kSmBN), kSmOcc)),
         dim3(64 * kSmWT * kSmWF), 0, stream, p);
     return;
   }
   hipLaunchKernelGGL(
-      (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, PF, false, CMAX, BT>),
+      (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, NST == 3 ? false : PF,
+                        false, CMAX, BT, NST>),
       dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream, p);
 }
 
@@ -1710,10 +1782,12 @@ hipError_t launch_ffn_backward(const FfnBwdArgs& a, hipStream_t stream) {
     GemmParams px{du, nullptr, w1t, nullptr, a.dx_rows, a.offsets,
                   a.total_rows, G, D, H};
     if (a.dx_f32)
-      launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+      launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
+                   4, false, kDnNST>(
           px, stream);
     else
-      launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+      launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
+                   4, false, kDnNST>(
           px, stream);
     MOE_TRY(hipGetLastError());
     if (a.row_index != nullptr)
@@ -1774,7 +1848,8 @@ hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
   GemmParams p{h,       nullptr, w2,       b2,     y, nullptr, N, 1, D, H,
                y_rows, slot_row, topk_w, Kmax};
   if (Kmax <= 4)
-    launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF, 4>(
+    launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF, 4,
+                 false, kDnNST>(
         p, stream);
   else
     launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
@@ -1828,10 +1903,12 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
     }
     if (down) {
       if (a.y_f32)
-        launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+        launch_stage<kEpiStore, false, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
+                     4, false, kDnNST>(
             p2, stream);
       else
-        launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF>(
+        launch_stage<kEpiStore, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
+                     4, false, kDnNST>(
             p2, stream);
       return hipGetLastError();
     }
