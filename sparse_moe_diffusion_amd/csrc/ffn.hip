@@ -501,17 +501,23 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   constexpr int kMainElems = (kStageBytes > kOutBytes ? kStageBytes : kOutBytes) / 2;
   constexpr int kPfElems = PF ? 256 : 0;
   // slot rows and weights, [BM][CMAX] each, and (CMAX > 4) each row's
-  // count of non-empty slots
+  // count of non-empty slots.  With three token-row stages and CMAX > 4
+  // they do not fit beside the stages: they are loaded after the main loop
+  // into the idle stage area, past the staged output tile (kLateCmb).
+  constexpr bool kLateCmb = EPI == kEpiCombine && NST == 3 && CMAX > 4;
   constexpr int kCmbInts =
       EPI == kEpiCombine ? 2 * BM * CMAX + (CMAX > 4 ? BM : 0) : 0;
+  static_assert(!kLateCmb || kOutBytes + kCmbInts * 4 <= kMainElems * 2,
+                "the late slot table fits in the stage area");
   static_assert(EPI != kEpiCombine || OUT_BF16, "the combine writes bf16");
   __shared__ __attribute__((aligned(1024)))
-  uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM + kCmbInts)];
+  uint16_t lds[kMainElems + kPfElems + 2 * (kTabInts + 2 * BM + (kLateCmb ? 0 : kCmbInts))];
   int32_t* const tab = reinterpret_cast<int32_t*>(lds + kMainElems + kPfElems);
   int32_t* const sidx = tab + kTabInts;   // 2 x BM gathered source rows
   // kEpiCombine: the tile's slot rows and weights, [BM][cmb_kmax] each
   // (cmb_kmax <= CMAX).
-  int32_t* const cslot = sidx + 2 * BM;
+  int32_t* const cslot =
+      kLateCmb ? reinterpret_cast<int32_t*>(lds + kOutBytes / 2) : sidx + 2 * BM;
   float* const cwt = reinterpret_cast<float*>(cslot + BM * CMAX);
   int32_t* const ccnt = cslot + 2 * BM * CMAX;
   // Token-row stage s at lds + s BM kBK, then the two weight-row stages.
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const uint32_t bB0 = lds0 + NST * BM * kBK * 2, bB1 = bB0 + BN * kBK * 2;
   const uint32_t bPf = lds0 + kMainElems * 2;
   const uint32_t bIdx = bPf + kPfElems * 2 + kTabInts * 4;
-  const uint32_t bCmb = bIdx + 2 * BM * 4;
+  const uint32_t bCmb = kLateCmb ? lds0 + kOutBytes : bIdx + 2 * BM * 4;
 
   // Persistent: the grid is a multiple of 8 workgroups, about one per CU,
   // dealt round-robin to the 8 XCDs.  The pw workgroups of one XCD take
@@ -942,24 +948,29 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
 
   // kEpiCombine: the slot rows and weights of this tile's tokens, for the
-  // epilogue (rows past the end read zero and are never stored).
-  if constexpr (EPI == kEpiCombine) {
-    const int km = p.cmb_kmax;
-    const uint32_t nb = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-        min(static_cast<int>(loc.row_end - loc.row0), BM) * km * 4));
-    const __amdgpu_buffer_rsrc_t rsS = make_rsrc(
-        reinterpret_cast<const void*>(
-            uniform64(reinterpret_cast<int64_t>(p.cmb_slot + loc.row0 * km))),
-        nb);
-    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(
-        reinterpret_cast<const void*>(
-            uniform64(reinterpret_cast<int64_t>(p.cmb_w + loc.row0 * km))),
-        nb);
-    for (int q = wave; q < BM * km / 64; q += kWaves) {
-      const uint32_t o = static_cast<uint32_t>(q * 64 + lane) * 4u;
-      dma_untracked<4>(rsS, bCmb + q * 256, o);
-      dma_untracked<4>(rsW, bCmb + BM * CMAX * 4 + q * 256, o);
-    }
+  // epilogue (rows past the end read zero and are never stored); in the
+  // late form, issued at the start of the epilogue instead.
+#define MOE_CMB_DMA()                                                        \
+  do {                                                                       \
+    const int km_ = p.cmb_kmax;                                              \
+    const uint32_t nb_ = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>( \
+        min(static_cast<int>(loc.row_end - loc.row0), BM) * km_ * 4));       \
+    const __amdgpu_buffer_rsrc_t rsS_ = make_rsrc(                           \
+        reinterpret_cast<const void*>(                                       \
+            uniform64(reinterpret_cast<int64_t>(p.cmb_slot + loc.row0 * km_))), \
+        nb_);                                                                \
+    const __amdgpu_buffer_rsrc_t rsW_ = make_rsrc(                           \
+        reinterpret_cast<const void*>(                                       \
+            uniform64(reinterpret_cast<int64_t>(p.cmb_w + loc.row0 * km_))),  \
+        nb_);                                                                \
+    for (int q = wave; q < BM * km_ / 64; q += kWaves) {                     \
+      const uint32_t o_ = static_cast<uint32_t>(q * 64 + lane) * 4u;         \
+      dma_untracked<4>(rsS_, bCmb + q * 256, o_);                            \
+      dma_untracked<4>(rsW_, bCmb + BM * CMAX * 4 + q * 256, o_);            \
+    }                                                                        \
+  } while (0)
+  if constexpr (EPI == kEpiCombine && !kLateCmb) {
+    MOE_CMB_DMA();
   }
 
   MOE_ISSUE(0, bA0, bB0, 0, NQ);
@@ -1005,6 +1016,9 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     // (their bias would lie outside the array); a tile that holds none takes
     // the branch-free form.
     stage_barrier();
+    // the late slot table lands past the staged tile (waited for by the
+    // barrier after the staging)
+    if constexpr (kLateCmb) MOE_CMB_DMA();
 #define MOE_STAGE_OUT_B(CHECK, E_, B_)                                       \
     _Pragma("unroll") for (int j = 0; j < TB; ++j) {                         \
       const int t = wt * (BM / WT) + j * 32 + (lane & 31);                   \
@@ -1070,6 +1084,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     }
 #undef MOE_STAGE_OUT
 #undef MOE_STAGE_OUT_B
+#undef MOE_CMB_DMA
     stage_barrier();
     if constexpr (EPI == kEpiCombine) {
       // y[t] = sum over the slots >= 0, in slot order, of w * routed row,
@@ -1853,7 +1868,7 @@ hipError_t launch_ffn_down_combine(const void* h, int64_t N, int D, int H,
         p, stream);
   else
     launch_stage<kEpiCombine, true, kDnBM, kDnBN, kDnWT, kDnWF, kDnGM, kDnPF,
-                 kCombineMaxSlots>(p, stream);
+                 kCombineMaxSlots, false, kDnNST>(p, stream);
   return hipGetLastError();
 }
 
