@@ -292,6 +292,9 @@ def _grouped_reference(xrows, offsets, w1, w2):
     # stage 1 has 1440 large tiles of 18 k stages (several per persistent
     # workgroup), stage 2 480 tiles of 72 k stages (about two per workgroup)
     ([7000, 6000, 0, 7100], 1152, 4608, False),
+    # stage 2's large tiles (three token-row k stages in flight) with a
+    # reduction length that ends in a partial k stage (H % 64 = 8)
+    ([3000, 2500, 0, 2700], 1152, 2056, False),
 ])
 def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
     """Shapes on either side of the large/small tile switch, every row
@@ -632,7 +635,10 @@ def test_routing_histogram_empty_batch():
     (20000, 1152, 4608, 2, 0.05, False),
     # Expert Race's slot layout: 16 slots per token, most of them empty
     # (the 16-column form of the kernel), small and large tiles
-    (700, 256, 512, 16, 0.85, True), (5000, 2048, 1024, 16, 0.88, False)])
+    (700, 256, 512, 16, 0.85, True), (5000, 2048, 1024, 16, 0.88, False),
+    # large tiles whose reduction ends in a partial k stage (H % 64 = 8),
+    # with 2 and 16 slots (the 16-slot form loads its slot table late)
+    (20000, 1152, 4616, 2, 0.05, True), (5000, 2048, 1032, 16, 0.88, True)])
 def test_ffn_down_combine_matches_separate(N, D, H, Kmax, empty, bias):
     """The fused kernel gives the bits of stage 2 (one group of all tokens)
     followed by the combine kernel, and both agree with the oracle on every
