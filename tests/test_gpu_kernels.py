@@ -293,8 +293,11 @@ def _grouped_reference(xrows, offsets, w1, w2):
     # workgroup), stage 2 480 tiles of 72 k stages (about two per workgroup)
     ([7000, 6000, 0, 7100], 1152, 4608, False),
     # stage 2's large tiles (three token-row k stages in flight) with a
-    # reduction length that ends in a partial k stage (H % 64 = 8)
+    # reduction length that ends in a partial k stage (H % 64 = 8), and with
+    # one partial stage (H = 40) or two (H = 104) in all
     ([3000, 2500, 0, 2700], 1152, 2056, False),
+    ([12000, 9000], 1152, 40, False),
+    ([12000, 9000], 1152, 104, True),
 ])
 def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
     """Shapes on either side of the large/small tile switch, every row
