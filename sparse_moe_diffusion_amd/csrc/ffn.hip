@@ -619,9 +619,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
                 __builtin_amdgcn_readfirstlane(a_bytes));
   // Weight rows of group g: features past Nd fall outside the descriptor.
   // BT: group g's [Kd][Nd] block from the tile's first feature of k row 0
-  // to its end; each stage moves the base down 64 k rows and shrinks the
-  // range, so k rows past Kd read zero (features past Nd read the next
-  // row's values, which only reach features that are not stored).
+  // to its end; a stage's 64 k rows lie at a byte offset of 128 Nd per
+  // stage from there, so k rows past Kd fall outside the range and read
+  // zero (features past Nd read the next row's values, which only reach
+  // features that are not stored).
   const uint16_t* w_base =
       static_cast<const uint16_t*>(p.w) +
       (KG   ? static_cast<int64_t>(loc.kofs) * p.Nd + loc.n0
