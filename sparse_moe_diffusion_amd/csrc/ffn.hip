@@ -311,9 +311,10 @@ __device__ __forceinline__ bool locate_any(const GemmParams& p,
 }
 
 // Bias and activation of 4 consecutive output features f..f+3 of group g,
-// output row `row`.  BIAS: whether p.bias is set, decided once per tile by
-// the caller, so that the loops over a tile's outputs hold no branch (the
-// activations of consecutive groups of 4 can then be interleaved).
+// output row `row`.  BIAS: whether to add p.bias here; the staged bf16
+// epilogue adds it to the accumulators beforehand and passes false, so that
+// its loops over a tile's outputs hold no branch (the activations of
+// consecutive groups of 4 can then be interleaved).
 template <int EPI, bool BIAS>
 __device__ __forceinline__ f32x4 finish4(const GemmParams& p, int g,
                                          int64_t row, int f, f32x4 v) {
@@ -1011,16 +1012,40 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
   // feature block i, token (lane & 31) of token block j.
   if constexpr (OUT_BF16) {
+    // The bias, if any, joins the accumulators first, in one loop behind a
+    // uniform branch (u = A W^T + b, as the staging below would form it), so
+    // that the staging loops carry no bias code: two forms of them in one
+    // kernel raised the register count past 256 and spilled.
+    if (p.bias != nullptr) {
+      const float* const bg =
+          p.bias + static_cast<int64_t>(loc.g) * p.Nd + loc.n0;
+#pragma unroll
+      for (int i = 0; i < FB; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int fl = wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
+          if (loc.n0 + fl >= p.Nd) continue;
+          const float b0 = bg[fl], b1 = bg[fl + 1], b2 = bg[fl + 2],
+                      b3 = bg[fl + 3];
+#pragma unroll
+          for (int j = 0; j < TB; ++j) {
+            acc[i][j][4 * q + 0] += b0;
+            acc[i][j][4 * q + 1] += b1;
+            acc[i][j][4 * q + 2] += b2;
+            acc[i][j][4 * q + 3] += b3;
+          }
+        }
+      }
+    }
     // Every wave is done with the stages: stage the tile in LDS.  Rows past
     // the group end are staged too (finite values from the zero or re-read
-    // operand rows; the copy-out skips them).  Features past Nd are skipped
-    // (their bias would lie outside the array); a tile that holds none takes
-    // the branch-free form.
+    // operand rows; the copy-out skips them).  Features past Nd are skipped;
+    // a tile that holds none takes the branch-free form.
     stage_barrier();
     // the late slot table lands past the staged tile (waited for by the
     // barrier after the staging)
     if constexpr (kLateCmb) MOE_CMB_DMA();
-#define MOE_STAGE_OUT_B(CHECK, E_, B_)                                       \
+#define MOE_STAGE_OUT(CHECK, E_)                                             \
     _Pragma("unroll") for (int j = 0; j < TB; ++j) {                         \
       const int t = wt * (BM / WT) + j * 32 + (lane & 31);                   \
       _Pragma("unroll") for (int i = 0; i < FB; ++i) {                       \
@@ -1032,19 +1057,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           v[1] = acc[i][j][4 * q + 1];                                       \
           v[2] = acc[i][j][4 * q + 2];                                       \
           v[3] = acc[i][j][4 * q + 3];                                       \
-          v = finish4<E_, B_>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);       \
+          v = finish4<E_, false>(p, loc.g, loc.row0 + t, loc.n0 + fl, v);    \
           uint2 o;                                                           \
           o.x = pack_bf16x2(v[0], v[1]);                                     \
           o.y = pack_bf16x2(v[2], v[3]);                                     \
           *reinterpret_cast<uint2*>(&lds[t * kOutPitch + fl]) = o;           \
         }                                                                    \
       }                                                                      \
-    }
-#define MOE_STAGE_OUT(CHECK, E_)                                             \
-    if (p.bias != nullptr) {                                                 \
-      MOE_STAGE_OUT_B(CHECK, E_, true)                                       \
-    } else {                                                                 \
-      MOE_STAGE_OUT_B(CHECK, E_, false)                                      \
     }
     constexpr int kChunks = BN / 8;
     uint16_t* const c = static_cast<uint16_t*>(p.c);
@@ -1084,7 +1103,6 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       MOE_STAGE_OUT(true, EPI)
     }
 #undef MOE_STAGE_OUT
-#undef MOE_STAGE_OUT_B
 #undef MOE_CMB_DMA
     stage_barrier();
     if constexpr (EPI == kEpiCombine) {

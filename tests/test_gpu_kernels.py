@@ -267,7 +267,7 @@ def test_grouped_ffn(sizes, D, H, dtype, gather, bias):
     assert_close(y, ref, dtype, "grouped ffn")
 
 
-def _grouped_reference(xrows, offsets, w1, w2):
+def _grouped_reference(xrows, offsets, w1, w2, b1=None, b2=None):
     """oracle.expert_mlp on every row of every group, the oracle's calls on
     chunks of 1024 rows run side by side."""
     jobs = []
@@ -275,31 +275,37 @@ def _grouped_reference(xrows, offsets, w1, w2):
         a, b = int(offsets[g]), int(offsets[g + 1])
         jobs += [(g, c) for c in chunks(np.arange(a, b))]
     ref = np.zeros((xrows.shape[0], w2.shape[1]))
+    bias = lambda b, g: None if b is None else b[g]
     for (g, c), v in zip(jobs, pmap(
-            lambda j: oracle.expert_mlp(xrows[j[1]], w1[j[0]], w2[j[0]]), jobs)):
+            lambda j: oracle.expert_mlp(xrows[j[1]], w1[j[0]], w2[j[0]],
+                                        bias(b1, j[0]), bias(b2, j[0])),
+            jobs)):
         ref[c] = v
     return ref
 
 
-@pytest.mark.parametrize("sizes,D,H,y_f32", [
+@pytest.mark.parametrize("sizes,D,H,y_f32,bias", [
     # 288 / 216 large tiles in stages 1 / 2: both stages take the large tiles
-    ([3000, 2500, 0, 2700], 1152, 2048, False),
-    ([3000, 2500, 0, 2700], 1152, 2048, True),
+    ([3000, 2500, 0, 2700], 1152, 2048, False, False),
+    ([3000, 2500, 0, 2700], 1152, 2048, True, False),
     # stage 1 large (288 tiles), stage 2 small (72 large tiles, under 3/4 of
     # the CUs)
-    ([9000], 256, 2048, False),
+    ([9000], 256, 2048, False, False),
     # the XL layer's expert shapes (D = 1152, H = 4608) with ragged groups:
     # stage 1 has 1440 large tiles of 18 k stages (several per persistent
-    # workgroup), stage 2 480 tiles of 72 k stages (about two per workgroup)
-    ([7000, 6000, 0, 7100], 1152, 4608, False),
+    # workgroup), stage 2 480 tiles of 72 k stages (about two per workgroup);
+    # once more with biases on both matrices (the large tiles add them to the
+    # accumulators before staging the tile)
+    ([7000, 6000, 0, 7100], 1152, 4608, False, False),
+    ([7000, 6000, 0, 7100], 1152, 4608, False, True),
     # stage 2's large tiles (three token-row k stages in flight) with a
     # reduction length that ends in a partial k stage (H % 64 = 8), and with
     # one partial stage (H = 40) or two (H = 104) in all
-    ([3000, 2500, 0, 2700], 1152, 2056, False),
-    ([12000, 9000], 1152, 40, False),
-    ([12000, 9000], 1152, 104, True),
+    ([3000, 2500, 0, 2700], 1152, 2056, False, True),
+    ([12000, 9000], 1152, 40, False, False),
+    ([12000, 9000], 1152, 104, True, False),
 ])
-def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
+def test_grouped_ffn_tile_forms(sizes, D, H, y_f32, bias):
     """Shapes on either side of the large/small tile switch, every row
     compared with the oracle."""
     rng = np.random.default_rng(sum(sizes) + D + H)
@@ -311,11 +317,13 @@ def test_grouped_ffn_tile_forms(sizes, D, H, y_f32):
     xsrc = q(rng.standard_normal((nsrc, D)))
     w1 = q(rng.standard_normal((G, H, D)) * 0.03)
     w2 = q(rng.standard_normal((G, D, H)) * 0.03)
+    b1 = (rng.standard_normal((G, H)) * 0.1).astype(np.float32) if bias else None
+    b2 = (rng.standard_normal((G, D)) * 0.1).astype(np.float32) if bias else None
     ri = rng.permutation(nsrc)[:total]
-    y = _run_ffn(xsrc, offsets, w1, w2, None, None, "bf16", row_index=ri,
+    y = _run_ffn(xsrc, offsets, w1, w2, b1, b2, "bf16", row_index=ri,
                  y_f32=y_f32)
     assert not np.isnan(y).any()
-    ref = _grouped_reference(xsrc[ri], offsets, w1, w2)
+    ref = _grouped_reference(xsrc[ri], offsets, w1, w2, b1, b2)
     for g in range(G):
         a, b = int(offsets[g]), int(offsets[g + 1])
         if b > a:
