@@ -4,7 +4,9 @@ Usage:  python -m sparse_moe_diffusion_amd.build [-v]
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -15,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
+# The compiler's register, scratch and LDS figures of every kernel of the
+# last build (written by build(); read by the host tests, which require that
+# no GEMM kernel spills registers to scratch).
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.json")
 
 SOURCES = ["gate.hip", "permute.hip", "ffn.hip", "combine.hip", "balance.hip",
            "analytics.hip", "backward.hip", "abi.cpp"]
@@ -40,21 +46,46 @@ HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host",
                  "-Xarch_host", "-shared-libasan"]
 
 
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+_REMARK = re.compile(r"remark:\s+(.+?): (\S+) \[" + re.escape(RESOURCE_REMARKS) + r"\]")
+
+
+def parse_resource_usage(text: str) -> dict:
+    """{kernel symbol: {figure: value}} from the compiler's resource-usage
+    remarks (VGPRs, AGPRs, 'VGPRs Spill', 'ScratchSize [bytes/lane]', ...)."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
 def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR,
-             extra=()) -> str:
+             extra=()) -> tuple:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
            "-o", obj]
+    if src.endswith(".hip"):
+        cmd.append(RESOURCE_REMARKS)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    text = r.stdout + r.stderr
+    out = "\n".join(l for l in text.splitlines()
+                    if "packed-fp32-ops" not in l and RESOURCE_REMARKS[2:] not in l
+                    and not l.lstrip().startswith(("|", "^")) and
+                    not re.match(r"\s*\d+ \|", l))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
-    return obj
+    return obj, parse_resource_usage(text)
 
 
 def build(verbose: bool = False, sanitize: bool = False) -> str:
@@ -67,7 +98,15 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     extra = HOST_SANITIZE if sanitize else []
     os.makedirs(bdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, bdir, extra), SOURCES))
+        done = list(ex.map(lambda s: _compile(s, verbose, bdir, extra), SOURCES))
+    objs = [o for o, _ in done]
+    if not sanitize:
+        usage = {}
+        for src, (_, u) in zip(SOURCES, done):
+            for k, v in u.items():
+                usage[k] = dict(v, source=src)
+        with open(RESOURCES, "w") as f:
+            json.dump(usage, f, indent=1, sort_keys=True)
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs,
            "-o", tmp]
