@@ -9,7 +9,7 @@
 //
 // Kernels (gfx950):
 //  * transpose_kernel: [G][R][C] -> [G][C][R] bf16 through 64x64 LDS tiles
-//    (transposed copies of the expert weights for the data-gradient GEMMs).
+//    (W1's transposed copy for the dx GEMM; W2 is read as stored).
 //  * rows_kernel: a row copy, optionally gathered through a row index and
 //    optionally through GELU (the row-major operands of the K-grouped
 //    weight-gradient GEMM when they are not already in HBM).

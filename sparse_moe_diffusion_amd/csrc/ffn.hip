@@ -13,9 +13,11 @@
 // 256-token x 256-feature (up-projection) or 256 x 192 (down-projection)
 // output tile; each wave accumulates its 128 x 64 or 64 x 96 slice with
 // v_mfma_f32_32x32x16_bf16 in fp32.  Operands move from HBM straight into
-// LDS with buffer_load ... lds transfers (no staging registers), two
-// 64-wide k stages deep: the next stage is in flight while the current one
-// feeds the matrix cores, and its transfers are spread between the MFMAs.
+// LDS with buffer_load ... lds transfers (no staging registers), in 64-wide
+// k stages: the next stage is in flight while the current one feeds the
+// matrix cores, and its transfers are spread between the MFMAs.  The
+// down-projection's large tiles keep a third stage of token rows, so each of
+// those transfers has two stages of MFMAs to arrive in.
 // Both operands are k-contiguous rows; LDS rows are 128 bytes and the
 // 16-byte chunk c of row r sits at slot c ^ swz(r), which keeps the MFMA
 // fragment reads free of bank conflicts (measured: zero).  Fragments are
@@ -27,7 +29,8 @@
 // The weight gradients of the backward run the same kernel in a K-grouped
 // form: the reduction runs down the token rows of row-major operands, which
 // land in LDS as [64 tokens][256 features] stage tiles and reach the matrix
-// cores through LDS transpose reads (ds_read_b64_tr_b16).
+// cores through LDS transpose reads (ds_read_b64_tr_b16).  The backward's
+// du GEMM reads W2 as stored (k-major) the same way, on the weight tile only.
 //
 // The MFMA computes out^T: weight rows are the 32-row "A" operand and token
 // rows the "B" operand, so each lane ends up holding 4 consecutive output

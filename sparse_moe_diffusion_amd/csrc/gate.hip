@@ -7,7 +7,13 @@
 // candidates.
 //
 // Kernel layout (gfx950):
-//  * gate_mfma_kernel (bf16 tokens): logits on the matrix cores from an
+//  * gate_stream_kernel (bf16 tokens, E <= 16, the layer's gate): each wave
+//    streams its own 16 tokens' features through a ring of register loads
+//    and multiplies them on the matrix cores against an exact three-way
+//    bf16 split of the fp32 gate weights held in LDS (slice sums in fp64);
+//    softmax, top-K and, for top-K routing, the balance statistic's
+//    per-16-token partial sums follow in registers.  See the kernel.
+//  * gate_mfma_kernel (bf16 tokens, E > 16): logits on the matrix cores from an
 //    exact three-way bf16 split of the fp32 gate weights, partial sums
 //    added in fp64; see the kernel.  gate_f32_kernel (fp32 tokens): the same
 //    logits from VALU fp64 FMAs.  Both leave 64 tokens' logits in LDS after
@@ -579,13 +585,17 @@ hipError_t launch_gate_stream(const void* x, const float* wg, const float* bias,
                               float* probs, int32_t* idx, float* w,
                               float* bal_p, int32_t* bal_c,
                               hipStream_t stream) {
-  static std::atomic<bool> lds_opt_in{false};
-  if (!lds_opt_in.load(std::memory_order_acquire)) {
+  // the LDS opt-in is a property of the kernel on each device: set once per
+  // device
+  static std::atomic<bool> lds_opt_in[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!lds_opt_in[dev].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gate_stream_kernel<EC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLdsMax);
     if (e != hipSuccess) return e;
-    lds_opt_in.store(true, std::memory_order_release);
+    lds_opt_in[dev].store(true, std::memory_order_release);
   }
   const int waves = gate_stream_waves(N);
   hipLaunchKernelGGL((gate_stream_kernel<EC>),

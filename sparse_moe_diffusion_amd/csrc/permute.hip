@@ -6,7 +6,7 @@
 // as one dense row block.  Rows of expert e are its selections in ascending
 // (token, slot) order.
 //
-// Three launches, no host synchronisation:
+// Three launches (a fourth with x_perm), no host synchronisation:
 //  1. permute_count_kernel: workgroup b covers 256 consecutive tokens (one
 //     per thread); each token's experts form a bit mask, and one wave ballot
 //     per expert counts the wave's selections.  Writes block_counts[b][e].
