@@ -133,6 +133,9 @@ def kernel_work(cfg, gather: bool):
         "gate_balance": ("bytes", N * D * eb + E * D * 4 + N * E * 4 +
                          N * Kmax * 8 + cfg.B * E * 8),
     }
+    # the gate, the balance statistic and the permutation's index tensors in
+    # one call (routed rows gathered in the GEMM)
+    w["gate_route"] = ("bytes", w["gate_balance"][1] + N * Kmax * 4 * 2 + A * 4)
     return w
 
 
@@ -422,10 +425,11 @@ def cold_timings(cfg, x, wts, buf, steps, reps):
     a read of a 1 GiB buffer that evicts the 256 MB memory-side cache and
     the L2s (so their inputs come from HBM; a read leaves only clean lines,
     so no write-back of the flush competes with the timed call), and ``reps``
-    times back to back (warm), plus two measured-only forms: the permute
-    that also copies the rows to x_perm, and the separate combine kernel
-    where the layer fuses it.  Median ms, GB/s of algorithmic bytes and the
-    fraction of the HBM peak, cold and warm."""
+    times back to back (warm), plus measured-only forms: the permute that
+    also copies the rows to x_perm, the separate combine kernel where the
+    layer fuses it, and the gate-with-balance and index-only permute calls
+    where the layer routes in one call.  Median ms, GB/s of algorithmic
+    bytes and the fraction of the HBM peak, cold and warm."""
     import torch
     import numpy as np
     from sparse_moe_diffusion_amd import layer
@@ -433,8 +437,13 @@ def cold_timings(cfg, x, wts, buf, steps, reps):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     work = kernel_work(cfg, buf.gather)
     calls = [(n, f) for n, f in steps
-             if n in ("gate", "gate_balance", "permute", "combine", "balance")]
+             if n in ("gate", "gate_balance", "gate_route", "permute", "combine",
+                      "balance")]
     extra = {}
+    if any(n == "gate_route" for n, _ in calls):
+        # the two calls the fused routing call replaces, measured only
+        calls.append(("gate_balance", lambda c, x_, w, b: layer.gate_balance(c, x_, w, b)))
+        calls.append(("permute", lambda c, x_, w, b: layer.permute(c, x_, b)))
     if cfg.dtype == "bf16":
         eb = 2
         xp = torch.empty(cfg.A, cfg.D, dtype=x.dtype, device="cuda")

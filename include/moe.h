@@ -343,6 +343,44 @@ moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* Bytes of device workspace moe_gate_route needs. */
+size_t moe_gate_route_workspace_size(int32_t B, int32_t T, int32_t E);
+
+/*
+ * Top-K gate, balance statistic and expert permutation in one call
+ * ("DiT-MoE" hub page, section 1: the gate returns the selected experts,
+ * their weights and the auxiliary loss; "Scaling Diffusion Transformers to
+ * 16 Billion Parameters", MoE-DiT eq. L_balance, and MoE recap: only the
+ * selected experts are evaluated, so their rows are grouped by expert).
+ * Computes exactly what moe_gate_topk_balance followed by moe_permute
+ * (Kmax = K, x_perm = NULL) compute, bit for bit, for N = B*T tokens.
+ *
+ * When moe_gate_topk_balance takes its fused form (bf16 x, T a multiple of
+ * 16, E <= 16) this runs three kernels: the gate, which also writes the
+ * balance statistic's per-16-token partial sums and selection counts; one
+ * launch of two workgroups, the balance finish beside the permutation's
+ * expert scan over those selection counts (they replace the permutation's
+ * count pass); and the permutation's scatter.  Otherwise it runs the two
+ * calls' kernels in turn.
+ *
+ *   arguments as moe_gate_topk_balance, then as moe_permute's outputs
+ *   (expert_counts [E], expert_offsets [E+1], row_token [K*N],
+ *   slot_row [N][K]);
+ *   workspace  device scratch of at least moe_gate_route_workspace_size()
+ *              bytes, 256-byte aligned (contents need no initialisation)
+ * Errors: as moe_gate_topk_balance and moe_permute (K*N below 2^31);
+ *   WORKSPACE_TOO_SMALL.
+ */
+moe_status moe_gate_route(const void* x, moe_dtype x_dtype,
+                          const float* w_gate, const float* logit_bias,
+                          int32_t B, int32_t T, int32_t D, int32_t E, int32_t K,
+                          float alpha, moe_balance_mode mode, float* probs,
+                          int32_t* topk_idx, float* topk_w, int32_t* counts,
+                          float* prob_sums, float* loss, int32_t* expert_counts,
+                          int64_t* expert_offsets, int32_t* row_token,
+                          int32_t* slot_row, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Stage 2 of the shared experts fused with the weighted combine ("Scaling
  * Diffusion Transformers to 16 Billion Parameters": eq. MLP for the shared

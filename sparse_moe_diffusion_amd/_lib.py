@@ -60,6 +60,10 @@ SIGNATURES = {
     "moe_gate_topk_balance": (_E, [_P, _E, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                    _F, _E, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                    _P]),
+    "moe_gate_route_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "moe_gate_route": (_E, [_P, _E, _P, _P, _I32, _I32, _I32, _I32, _I32, _F,
+                            _E, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P]),
     "moe_ffn_down_combine": (_E, [_P, _E, _I64, _I32, _I32, _P, _P, _P, _P, _P,
                                   _I32, _P, _P]),
     "moe_combine_backward": (_E, [_P, _E, _P, _E, _P, _P, _I64, _I32, _I32, _P,

@@ -457,6 +457,85 @@ moe_status moe_gate_topk_balance(const void* x, moe_dtype x_dtype_arg,
                   fn);
 }
 
+size_t moe_gate_route_workspace_size(int32_t B, int32_t T, int32_t E) {
+  if (B < 0 || T < 1 || E < 1) return 0;
+  const int64_t N = static_cast<int64_t>(B) * T;
+  return moe::balance_partials_bytes(N, E) + moe::permute_workspace_bytes(N, E);
+}
+
+moe_status moe_gate_route(const void* x, moe_dtype x_dtype_arg,
+                          const float* w_gate, const float* logit_bias,
+                          int32_t B, int32_t T, int32_t D, int32_t E, int32_t K,
+                          float alpha, moe_balance_mode mode_arg, float* probs,
+                          int32_t* topk_idx, float* topk_w, int32_t* counts,
+                          float* prob_sums, float* loss, int32_t* expert_counts,
+                          int64_t* expert_offsets, int32_t* row_token,
+                          int32_t* slot_row, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  const int x_dtype = enum_value(x_dtype_arg);
+  const int mode = enum_value(mode_arg);
+  const char* fn = "moe_gate_route";
+  if (B < 0 || T < 1 || D < 1 || E < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "%s: need B >= 0, T >= 1, D >= 1, E >= 1", fn);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: K=%d outside [1, E=%d]", fn, K, E);
+  if (mode != MOE_BAL_PER_SEQUENCE && mode != MOE_BAL_GLOBAL)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: unknown mode %d", fn, (int)mode);
+  const int64_t N = static_cast<int64_t>(B) * T;
+  CHECK_PTR(w_gate); CHECK_PTR(loss);
+  CHECK_PTR_IF(N > 0, x); CHECK_PTR_IF(N > 0, probs);
+  CHECK_PTR_IF(N > 0, topk_w); CHECK_PTR_IF(N > 0, counts);
+  CHECK_PTR_IF(N > 0, prob_sums);
+  // the permutation's own checks (the index form: no x_perm)
+  const moe_status st =
+      check_permute(fn, x, x_dtype, topk_idx, N, D, E, K, K, expert_counts,
+                    expert_offsets, row_token, slot_row, nullptr);
+  if (st != MOE_OK) return st;
+  if (N * E >= kI32Limit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: B*T*E must stay below 2^31", fn);
+  const size_t need = moe_gate_route_workspace_size(B, T, E);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, need);
+  CHECK_PTR(workspace);
+  const bool bf16 = x_dtype == MOE_BF16;
+  const bool global = mode == MOE_BAL_GLOBAL;
+  const int64_t A = static_cast<int64_t>(K) * N;
+  // the gate's partial sums (fp32 half, then the int32 selection counts),
+  // then the permutation's workspace
+  const size_t pbytes = moe::balance_partials_bytes(N, E);
+  char* const pws = static_cast<char*>(workspace) + pbytes;
+  hipError_t err;
+  if (moe::gate_balance_fuses(bf16, N, T, D, E)) {
+    float* part_p = static_cast<float*>(workspace);
+    int32_t* part_c = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                 pbytes / 2);
+    int64_t* block_base = reinterpret_cast<int64_t*>(pws);
+    err = moe::launch_gate_balance_partials(x, w_gate, logit_bias, N, D, E, K,
+                                            probs, topk_idx, topk_w, part_p,
+                                            part_c, stream);
+    if (err != hipSuccess) return from_hip(err, fn);
+    err = moe::launch_route_finish(workspace, B, T, E, K, alpha, global, counts,
+                                   prob_sums, loss, expert_counts,
+                                   expert_offsets, block_base, stream);
+    if (err != hipSuccess) return from_hip(err, fn);
+    return from_hip(moe::launch_permute_scatter(topk_idx, N, E, K, A, block_base,
+                                                slot_row, row_token, stream),
+                    fn);
+  }
+  err = moe::launch_gate(x, bf16, w_gate, logit_bias, N, D, E, K, true, probs,
+                         topk_idx, topk_w, stream);
+  if (err != hipSuccess) return from_hip(err, fn);
+  err = moe::launch_balance(probs, topk_idx, B, T, E, K, K, alpha, global,
+                            counts, prob_sums, loss, stream);
+  if (err != hipSuccess) return from_hip(err, fn);
+  return from_hip(moe::launch_permute(x, bf16, topk_idx, N, D, E, K, A,
+                                      expert_counts, expert_offsets, row_token,
+                                      slot_row, nullptr, pws, stream),
+                  fn);
+}
+
 moe_status moe_ffn_down_combine(const void* h, moe_dtype dtype_arg, int64_t N,
                                 int32_t D, int32_t H, const void* w2,
                                 const float* b2, const void* y_rows,

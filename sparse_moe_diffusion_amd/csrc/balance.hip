@@ -15,8 +15,12 @@
 //  * balance_partials_kernel: when the gate kernel has already reduced each
 //    16-token group (partials [N/16][E]), one workgroup adds each image's
 //    T/16 partials in group order and then computes the loss as above.
+//  * route_finish_kernel (the fused routing call): the same in workgroup 0,
+//    and in workgroup 1 the permutation's expert scan over the gate's
+//    per-16-token selection counts.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scan.hpp"
 
 namespace moe {
 
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kBalThreads) void balance_loss_kernel(
 constexpr int kPartBatch = 16;
 constexpr int kPartLds = 2048;
 
-__global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
+__device__ inline void balance_from_partials(
     const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
     int B, int T, int E, int K, float alpha, int global,
     int32_t* __restrict__ counts, float* __restrict__ psum,
@@ -237,12 +241,61 @@ __global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
     balance_loss_body(counts, psum, B, T, E, K, alpha, global, loss);
 }
 
+__global__ __launch_bounds__(kSeqThreads) void balance_partials_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
+    int B, int T, int E, int K, float alpha, int global,
+    int32_t* __restrict__ counts, float* __restrict__ psum,
+    float* __restrict__ loss) {
+  balance_from_partials(part_p, part_c, B, T, E, K, alpha, global, counts,
+                        psum, loss);
+}
+
+// The fused routing call's second launch, two workgroups side by side.
+// Workgroup 0 finishes the balance statistic from the gate's partials, as
+// balance_partials_kernel does.  Workgroup 1 is the permutation's expert
+// scan, fed with the gate's per-16-token selection counts (part_c), 16 of
+// them per 256-token block: the block counts the permute's count kernel
+// would form, so that kernel is not needed.
+__global__ __launch_bounds__(kSeqThreads) void route_finish_kernel(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_c,
+    int B, int T, int E, int K, float alpha, int global,
+    int32_t* __restrict__ counts, float* __restrict__ psum,
+    float* __restrict__ loss, int32_t* __restrict__ expert_counts,
+    int64_t* __restrict__ expert_offsets, int64_t* __restrict__ block_base) {
+  static_assert(kSeqThreads == kScanThreads && kPermTokens % 16 == 0,
+                "one workgroup size; whole 16-token groups per block");
+  if (blockIdx.x == 0) {
+    balance_from_partials(part_p, part_c, B, T, E, K, alpha, global, counts,
+                          psum, loss);
+  } else {
+    const int64_t N = static_cast<int64_t>(B) * T;
+    const int nblocks = static_cast<int>(ceil_div(N, kPermTokens));
+    expert_scan(part_c, nblocks, kPermTokens / 16, N / 16, E, expert_counts,
+                expert_offsets, block_base);
+  }
+}
+
 }  // namespace
 
 size_t balance_partials_bytes(int64_t N, int E) {
   const size_t words = static_cast<size_t>((N + 15) / 16) * E;
   const size_t half = (words * 4 + 255) / 256 * 256;
   return 2 * half;
+}
+
+hipError_t launch_route_finish(const void* partials, int B, int T, int E,
+                               int K, float alpha, bool global, int32_t* counts,
+                               float* psum, float* loss, int32_t* expert_counts,
+                               int64_t* expert_offsets, int64_t* block_base,
+                               hipStream_t stream) {
+  const int64_t N = static_cast<int64_t>(B) * T;
+  const float* part_p = static_cast<const float*>(partials);
+  const int32_t* part_c = reinterpret_cast<const int32_t*>(
+      static_cast<const char*>(partials) + balance_partials_bytes(N, E) / 2);
+  hipLaunchKernelGGL(route_finish_kernel, dim3(2), dim3(kSeqThreads), 0, stream,
+                     part_p, part_c, B, T, E, K, alpha, global ? 1 : 0, counts,
+                     psum, loss, expert_counts, expert_offsets, block_base);
+  return hipGetLastError();
 }
 
 hipError_t launch_balance_from_partials(const void* partials, int B, int T,

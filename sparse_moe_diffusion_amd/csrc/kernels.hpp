@@ -41,6 +41,13 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                           int32_t* counts, int64_t* offsets, int32_t* row_token,
                           int32_t* slot_row, void* x_perm, void* workspace,
                           hipStream_t stream);
+// The permute's last step alone: ranks every selection inside its 256-token
+// block from the block bases (block_base [ceil(N/256)][E] int64, as the
+// scan writes them) and writes slot_row and row_token.
+hipError_t launch_permute_scatter(const int32_t* idx, int64_t N, int E,
+                                  int Kmax, int64_t A, const int64_t* block_base,
+                                  int32_t* slot_row, int32_t* row_token,
+                                  hipStream_t stream);
 
 // ffn.hip
 // Most groups (experts) one grouped-FFN launch takes.
@@ -88,6 +95,14 @@ hipError_t launch_balance_from_partials(const void* partials, int B, int T,
                                         int E, int K, float alpha, bool global,
                                         int32_t* counts, float* psum,
                                         float* loss, hipStream_t stream);
+// Fused routing call, second launch: the balance finish from the gate's
+// partials and the permutation's expert scan over its per-16-token
+// selection counts (two workgroups of one launch).
+hipError_t launch_route_finish(const void* partials, int B, int T, int E,
+                               int K, float alpha, bool global, int32_t* counts,
+                               float* psum, float* loss, int32_t* expert_counts,
+                               int64_t* expert_offsets, int64_t* block_base,
+                               hipStream_t stream);
 hipError_t launch_balance(const float* probs, const int32_t* idx, int B, int T,
                           int E, int Kmax, int K, float alpha, bool global,
                           int32_t* counts, float* psum, float* loss,

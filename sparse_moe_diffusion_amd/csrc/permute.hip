@@ -26,14 +26,13 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scan.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kPermTokens = 256;
 constexpr int kPermWaves = kPermTokens / kWave;
-constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ uint64_t token_mask(const int32_t* __restrict__ idx,
                                                int64_t t, int Kmax, int E) {
@@ -65,53 +64,13 @@ __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
   }
 }
 
-// Thread (c, e) of a C x E grid (C = 1024 / E chunks of consecutive count
-// blocks) sums its chunk's counts of expert e; a scan over the chunks in
-// LDS gives each chunk its base within the expert, a scan over the experts
-// gives the expert offsets, and each thread then writes the block bases of
-// its chunk in block order.
+// One workgroup: expert counts, offsets and block bases from the block
+// counts (see expert_scan).
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     const int32_t* __restrict__ block_counts, int nblocks, int E,
     int32_t* __restrict__ counts, int64_t* __restrict__ offsets,
     int64_t* __restrict__ block_base) {
-  __shared__ int64_t part[kScanThreads];
-  __shared__ int64_t tot[kMaxExperts];
-  const int C = kScanThreads / E;
-  const int tid = threadIdx.x;
-  const int c = tid / E;
-  const int e = tid - c * E;
-  const bool active = c < C;
-  const int b0 = static_cast<int>(static_cast<int64_t>(c) * nblocks / C);
-  const int b1 = static_cast<int>(static_cast<int64_t>(c + 1) * nblocks / C);
-  int64_t sum = 0;
-  if (active)
-    for (int b = b0; b < b1; ++b)
-      sum += block_counts[static_cast<int64_t>(b) * E + e];
-  part[tid] = sum;
-  __syncthreads();
-  // inclusive scan over chunks, per expert (Hillis-Steele)
-  for (int off = 1; off < C; off *= 2) {
-    int64_t v = part[tid];
-    if (active && c >= off) v += part[tid - off * E];
-    __syncthreads();
-    part[tid] = v;
-    __syncthreads();
-  }
-  if (active && c == C - 1) tot[e] = part[tid];
-  __syncthreads();
-  if (!active) return;
-  int64_t base = 0;
-  for (int j = 0; j < e; ++j) base += tot[j];
-  if (c == 0) {
-    counts[e] = static_cast<int32_t>(tot[e]);
-    offsets[e] = base;
-    if (e == E - 1) offsets[E] = base + tot[e];
-  }
-  int64_t run = base + (c > 0 ? part[tid - E] : 0);
-  for (int b = b0; b < b1; ++b) {
-    block_base[static_cast<int64_t>(b) * E + e] = run;
-    run += block_counts[static_cast<int64_t>(b) * E + e];
-  }
+  expert_scan(block_counts, nblocks, 1, nblocks, E, counts, offsets, block_base);
 }
 
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
@@ -221,6 +180,25 @@ hipError_t permute_scratch(void** ptr) {
   return hipSuccess;
 }
 
+hipError_t launch_permute_scatter(const int32_t* idx, int64_t N, int E,
+                                  int Kmax, int64_t A, const int64_t* block_base,
+                                  int32_t* slot_row, int32_t* row_token,
+                                  hipStream_t stream) {
+  const int64_t nb = ceil_div(N, kPermTokens);
+  if (nb == 0) return hipSuccess;
+  const size_t shmem = static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
+  if (shmem > 32768) {
+    const hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&permute_scatter_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nb)),
+                     dim3(kPermTokens), shmem, stream, idx, N, E, Kmax, A,
+                     block_base, slot_row, row_token);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                           int64_t N, int D, int E, int Kmax, int64_t A,
                           int32_t* counts, int64_t* offsets, int32_t* row_token,
@@ -242,19 +220,10 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
                      block_counts, static_cast<int>(nb), E, counts, offsets,
                      block_base);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || nb == 0) return err;
-  const size_t shmem = static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
-  if (shmem > 32768) {
-    err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&permute_scatter_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nb)),
-                     dim3(kPermTokens), shmem, stream, idx, N, E, Kmax, A,
-                     block_base, slot_row, row_token);
-  err = hipGetLastError();
-  if (err != hipSuccess || x_perm == nullptr) return err;
+  if (err != hipSuccess) return err;
+  err = launch_permute_scatter(idx, N, E, Kmax, A, block_base, slot_row,
+                               row_token, stream);
+  if (err != hipSuccess || nb == 0 || x_perm == nullptr) return err;
   // D is a multiple of 8, so a row is a whole number of 16-byte chunks.
   const int nvec = D * (bf16 ? 2 : 4) / 16;
   const int64_t chunks = N * nvec;

@@ -108,11 +108,14 @@ class LayerBuffers:
             self.shared_offsets = self.h_shared = self.y_shared = None
             self.u_shared = None
         self.y = torch.empty(N, D, dtype=dt, device=dev)
-        self.gate_bal_ws = None
+        self.gate_bal_ws = self.route_ws = None
         if route == ROUTES["topk"]:
             bws = ops.gate_balance_workspace_size(cfg.B, cfg.T, E)
             self.gate_bal_ws = torch.empty(max(bws, 1), dtype=torch.uint8,
                                            device=dev)
+            rws = ops.gate_route_workspace_size(cfg.B, cfg.T, E)
+            self.route_ws = torch.empty(max(rws, 1), dtype=torch.uint8,
+                                        device=dev)
         self.bal_counts = torch.empty(cfg.B, E, dtype=i32, device=dev)
         self.bal_psum = torch.empty(cfg.B, E, dtype=f32, device=dev)
         self.loss = torch.empty(1, dtype=f32, device=dev)
@@ -135,6 +138,22 @@ def gate_balance(cfg, x, wts: LayerWeights, buf: LayerBuffers,
                               cfg.alpha, BALANCE[mode], buf.probs,
                               buf.topk_idx, buf.topk_w, buf.bal_counts,
                               buf.bal_psum, buf.loss, buf.gate_bal_ws)
+
+
+def fuses_route(cfg, buf: LayerBuffers) -> bool:
+    """Top-K layers whose routed rows are gathered in the GEMM (no x_perm)
+    route in one call: the gate, the balance statistic and the permutation's
+    index tensors."""
+    return fuses_balance(cfg) and buf.gather
+
+
+def gate_route(cfg, x, wts: LayerWeights, buf: LayerBuffers,
+               mode: str = "sequence"):
+    ops.moe_gate_route(x, wts.w_gate, wts.bias, cfg.B, cfg.T, cfg.K,
+                       cfg.alpha, BALANCE[mode], buf.probs, buf.topk_idx,
+                       buf.topk_w, buf.bal_counts, buf.bal_psum, buf.loss,
+                       buf.expert_counts, buf.expert_offsets, buf.row_token,
+                       buf.slot_row, buf.route_ws)
 
 
 def permute(cfg, x, buf: LayerBuffers):
@@ -204,10 +223,12 @@ STEPS = (("gate", lambda c, x, w, b: gate(c, x, w, b)),
          ("balance", lambda c, x, w, b: balance(c, b)))
 
 # The fused calls forward() makes instead: the gate with the balance
-# statistic (top-K routing), and the shared experts' stage 2 with the combine
-# (when fuses_combine(cfg, buf)): y bit for bit the same either way.
+# statistic (top-K routing) and, when the routed rows are gathered in the
+# GEMM, also with the permutation; and the shared experts' stage 2 with the
+# combine (when fuses_combine(cfg, buf)): y bit for bit the same either way.
 GATE_BALANCE_STEP = ("gate_balance",
                      lambda c, x, w, b: gate_balance(c, x, w, b))
+GATE_ROUTE_STEP = ("gate_route", lambda c, x, w, b: gate_route(c, x, w, b))
 DOWN_COMBINE_STEP = ("shared_down_combine",
                      lambda c, x, w, b: shared_down_combine(c, w, b))
 
@@ -221,9 +242,13 @@ def steps(cfg, buf: LayerBuffers):
             continue
         if fuses_balance(cfg) and name == "balance":
             continue
+        if fuses_route(cfg, buf) and name == "permute":
+            continue
         if fuses_combine(cfg, buf) and name == "combine":
             continue
-        if fuses_balance(cfg) and name == "gate":
+        if fuses_route(cfg, buf) and name == "gate":
+            s = GATE_ROUTE_STEP
+        elif fuses_balance(cfg) and name == "gate":
             s = GATE_BALANCE_STEP
         elif fuses_combine(cfg, buf) and name == "shared_down":
             s = DOWN_COMBINE_STEP
@@ -234,11 +259,14 @@ def steps(cfg, buf: LayerBuffers):
 def forward(cfg, x: torch.Tensor, wts: LayerWeights, buf: LayerBuffers,
             balance_mode: str = "sequence") -> LayerBuffers:
     """One pass of the whole layer; results land in ``buf``."""
-    if fuses_balance(cfg):
-        gate_balance(cfg, x, wts, buf, balance_mode)
+    if fuses_route(cfg, buf):
+        gate_route(cfg, x, wts, buf, balance_mode)
     else:
-        gate(cfg, x, wts, buf)
-    permute(cfg, x, buf)
+        if fuses_balance(cfg):
+            gate_balance(cfg, x, wts, buf, balance_mode)
+        else:
+            gate(cfg, x, wts, buf)
+        permute(cfg, x, buf)
     routed_ffn(cfg, x, wts, buf, UP)
     shared_ffn(cfg, x, wts, buf, UP)
     routed_ffn(cfg, x, wts, buf, DOWN)

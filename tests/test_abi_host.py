@@ -265,6 +265,55 @@ def test_gate_balance_workspace():
     assert lib.moe_gate_balance_workspace_size(3, 100, 8) >= 2 * 19 * 8 * 4
 
 
+def _gate_route(**kw):
+    a = dict(x=FAKE, dt=_lib.MOE_BF16, wg=FAKE, bias=None, B=4, T=16, D=128,
+             E=8, K=2, alpha=ctypes.c_float(0.01),
+             mode=_lib.MOE_BAL_PER_SEQUENCE, probs=FAKE, idx=FAKE, w=FAKE,
+             counts=FAKE, ps=FAKE, loss=FAKE, ecounts=FAKE, eoffs=FAKE,
+             row_token=FAKE, slot_row=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_gate_route", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(loss=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(counts=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(ecounts=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(eoffs=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(row_token=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(slot_row=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(idx=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(K=9), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(T=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(mode=2), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(E=65, K=2), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(dt=5), _lib.MOE_ERR_UNSUPPORTED),
+    # K*N (and B*T*E) at 2^31
+    (dict(B=1 << 15, T=1 << 15, E=2, K=2, wsb=1 << 62), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(wsb=0), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_gate_route_rejects(kw, status):
+    ensure_built()
+    assert _gate_route(**kw) == status
+    assert _lib.last_error()
+
+
+def test_gate_route_workspace():
+    lib = ensure_built()
+    # the gate's partials, then the permutation's workspace
+    for B, T, E in [(32, 1024, 8), (3, 100, 16), (0, 16, 8), (1, 16, 1)]:
+        N = B * T
+        assert (lib.moe_gate_route_workspace_size(B, T, E) ==
+                lib.moe_gate_balance_workspace_size(B, T, E) +
+                lib.moe_permute_workspace_size(N, E, 2))
+    assert lib.moe_gate_route_workspace_size(-1, 16, 8) == 0
+
+
 def test_binding_raises_on_error():
     ensure_built()
     with pytest.raises(_lib.MoEError, match="MOE_ERR_INVALID_ARGUMENT"):

@@ -574,6 +574,73 @@ def test_gate_balance_matches_separate(B, T, D, E, K, dtype, mode, bias):
     assert abs(float(f[5][0]) - float(s[5][0])) <= 1e-5 * abs(l_o)
 
 
+@pytest.mark.parametrize("B,T,D,E,K,dtype,mode,bias", [
+    (1, 16, 64, 1, 1, "bf16", "sequence", False),     # one group, E = 1
+    (4, 256, 1152, 8, 2, "bf16", "sequence", True),
+    (3, 272, 384, 16, 2, "bf16", "global", False),    # last 256-token block partial
+    (5, 48, 200, 12, 3, "bf16", "sequence", True),    # E = 12, K = 3
+    (1, 4096, 384, 16, 1, "bf16", "sequence", False),  # one image, K = 1
+    (3, 100, 256, 8, 2, "bf16", "sequence", False),   # T % 16 != 0: separate
+    (2, 64, 128, 8, 2, "f32", "global", False),       # fp32 x: separate
+    (16, 1024, 2048, 16, 2, "bf16", "global", True),  # the race layer's shape
+    (32, 1024, 1152, 8, 2, "bf16", "sequence", False),  # the XL layer
+    (0, 16, 128, 8, 2, "bf16", "sequence", False),    # no tokens
+])
+def test_gate_route_matches_separate(B, T, D, E, K, dtype, mode, bias):
+    """moe_gate_route against moe_gate_topk_balance followed by moe_permute
+    (index form) on the same inputs: every output bit for bit, twice in a row
+    on a workspace full of garbage; and the permutation against the oracle's
+    on the routing the GPU chose."""
+    _lib, ops = _ops()
+    rng = np.random.default_rng(B * T + D + E + K)
+    N = B * T
+    x32 = rng.standard_normal((N, D)).astype(np.float32)
+    x = _bits_tensor(x32, dtype)
+    wg = torch.from_numpy((rng.standard_normal((E, D)) * 0.05).astype(np.float32)).to(DEV)
+    bt = (torch.from_numpy(rng.standard_normal(E).astype(np.float32)).to(DEV)
+          if bias else None)
+    mc = _lib.MOE_BAL_GLOBAL if mode == "global" else _lib.MOE_BAL_PER_SEQUENCE
+    f32, i32, i64 = torch.float32, torch.int32, torch.int64
+
+    def bufs():
+        return (torch.full((N, E), -1.0, dtype=f32, device=DEV),
+                torch.full((N, K), -7, dtype=i32, device=DEV),
+                torch.full((N, K), -1.0, dtype=f32, device=DEV),
+                torch.full((B, E), -7, dtype=i32, device=DEV),
+                torch.full((B, E), -1.0, dtype=f32, device=DEV),
+                torch.full((1,), -1.0, dtype=f32, device=DEV),
+                torch.full((E,), -7, dtype=i32, device=DEV),
+                torch.full((E + 1,), -7, dtype=i64, device=DEV),
+                torch.full((max(K * N, 1),), -7, dtype=i32, device=DEV),
+                torch.full((N, K), -7, dtype=i32, device=DEV))
+
+    sep = bufs()
+    gws = torch.empty(max(ops.gate_balance_workspace_size(B, T, E), 1),
+                      dtype=torch.uint8, device=DEV)
+    ops.moe_gate_topk_balance(x, wg, bt, B, T, K, 0.01, mc, *sep[:6], gws)
+    pws = torch.empty(max(ops.permute_workspace_size(N, E, K), 1),
+                      dtype=torch.uint8, device=DEV)
+    ops.moe_permute(x, sep[1], E, K, sep[6], sep[7], sep[8], sep[9], None, pws)
+    fus = bufs()
+    ws = torch.empty(max(ops.gate_route_workspace_size(B, T, E), 1),
+                     dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)
+    for _ in range(2):   # the workspace needs no initialisation
+        ops.moe_gate_route(x, wg, bt, B, T, K, 0.01, mc, *fus, ws)
+    torch.cuda.synchronize()
+    s, f = [to_np(t) for t in sep], [to_np(t) for t in fus]
+    names = ("probs", "idx", "w", "counts", "prob_sums", "loss",
+             "expert_counts", "expert_offsets", "row_token", "slot_row")
+    for i, name in enumerate(names):
+        assert np.array_equal(s[i], f[i]), name
+    if B == 0:
+        assert float(f[5][0]) == 0.0 and f[7].tolist() == [0] * (E + 1)
+        return
+    c_o, o_o, rt_o, sr_o = oracle.permute(f[1].astype(np.int32), E)
+    assert np.array_equal(f[6], c_o) and np.array_equal(f[7], o_o)
+    assert np.array_equal(f[8][:K * N], rt_o) and np.array_equal(f[9], sr_o)
+
+
 # ------------------------------------------------------- routing analytics --
 
 def _run_hist(idx, B, T, E, tags, n_tags, calls=1):
