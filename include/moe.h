@@ -237,6 +237,42 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                            void* u_ws, void* y_rows, moe_dtype y_dtype,
                            moe_ffn_stages stages, hipStream_t stream);
 
+/* Bytes of device workspace moe_grouped_ffn_split needs on the current
+ * device (a small header and one 256 x 192 fp32 tile per compute unit). */
+size_t moe_grouped_ffn_split_workspace_size(void);
+
+/*
+ * moe_grouped_ffn with a workspace that lets stage 2 (bf16 inputs, large
+ * tiles) split its last round of tiles along k: the expert GEMM keeps one
+ * workgroup per compute unit walking its tiles, and when the tile count is
+ * not a multiple of the workgroups, the R tiles of the last, partial round
+ * are cut into S = min(workgroups / R, k stages) >= 2 pieces each, which
+ * the workgroups that would otherwise idle multiply; one small kernel then
+ * adds each tile's pieces in piece order, adds b2 and rounds once.  Stage 1
+ * and the other stage-2 forms run as in moe_grouped_ffn.  Same arguments
+ * and checks as moe_grouped_ffn; y is computed as there (fp32 accumulation
+ * of the same products), with the k sums of the split tiles associated
+ * piece by piece: results agree to fp32 rounding, deterministically for a
+ * given routing.
+ *
+ *   workspace  device scratch of at least
+ *              moe_grouped_ffn_split_workspace_size() bytes, 16-byte
+ *              aligned (contents need no initialisation; calls that share
+ *              one workspace must not overlap)
+ * Errors: as moe_grouped_ffn; WORKSPACE_TOO_SMALL; INVALID_ARGUMENT for a
+ *   null or misaligned workspace.
+ */
+moe_status moe_grouped_ffn_split(const void* x_rows, const int32_t* row_index,
+                                 int64_t src_rows, moe_dtype dtype,
+                                 int64_t total_rows,
+                                 const int64_t* group_offsets, int32_t G,
+                                 int32_t D, int32_t H, const void* w1,
+                                 const float* b1, const void* w2,
+                                 const float* b2, void* h_ws, void* u_ws,
+                                 void* y_rows, moe_dtype y_dtype,
+                                 moe_ffn_stages stages, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /*
  * The experts' MLPs of moe_grouped_ffn in one kernel, for narrow layers
  * (same page and equations as moe_grouped_ffn): for each group g and row r,

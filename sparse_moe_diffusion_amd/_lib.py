@@ -51,6 +51,10 @@ SIGNATURES = {
                                  _P, _P, _P, _P, _P]),
     "moe_grouped_ffn": (_E, [_P, _P, _I64, _E, _I64, _P, _I32, _I32, _I32, _P,
                              _P, _P, _P, _P, _P, _P, _E, _E, _P]),
+    "moe_grouped_ffn_split_workspace_size": (_SZ, []),
+    "moe_grouped_ffn_split": (_E, [_P, _P, _I64, _E, _I64, _P, _I32, _I32,
+                                   _I32, _P, _P, _P, _P, _P, _P, _P, _E, _E,
+                                   _P, _SZ, _P]),
     "moe_grouped_mlp_fused": (_E, [_P, _P, _I64, _E, _I64, _P, _I32, _I32,
                                    _I32, _P, _P, _P, _P, _P, _E, _P]),
     "moe_combine": (_E, [_P, _E, _P, _P, _I64, _I32, _I32, _P, _E, _P, _E, _P]),

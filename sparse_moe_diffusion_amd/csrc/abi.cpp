@@ -251,18 +251,20 @@ moe_status moe_permute_noalloc(const void* x, moe_dtype dtype_arg,
                   fn);
 }
 
-moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
-                           int64_t src_rows, moe_dtype dtype_arg,
-                           int64_t total_rows,
-                           const int64_t* group_offsets, int32_t G, int32_t D,
-                           int32_t H, const void* w1, const float* b1,
-                           const void* w2, const float* b2, void* h_ws,
-                           void* u_ws, void* y_rows, moe_dtype y_dtype_arg,
-                           moe_ffn_stages stages_arg, hipStream_t stream) {
-  const int dtype = enum_value(dtype_arg);
-  const int y_dtype = enum_value(y_dtype_arg);
-  const int stages = enum_value(stages_arg);
-  const char* fn = "moe_grouped_ffn";
+}  // extern "C"
+
+namespace {
+
+// moe_grouped_ffn and moe_grouped_ffn_split: the same checks and launches;
+// split_ws (checked by the caller) is the latter's workspace or null.  The
+// enum arguments arrive as the callers read them (enum_value).
+moe_status grouped_ffn(const char* fn, const void* x_rows,
+                       const int32_t* row_index, int64_t src_rows, int dtype,
+                       int64_t total_rows, const int64_t* group_offsets,
+                       int32_t G, int32_t D, int32_t H, const void* w1,
+                       const float* b1, const void* w2, const float* b2,
+                       void* h_ws, void* u_ws, void* y_rows, int y_dtype,
+                       int stages, void* split_ws, hipStream_t stream) {
   if (total_rows < 0 || G < 1 || D < 1 || H < 1)
     return fail(MOE_ERR_INVALID_ARGUMENT,
                 "%s: need total_rows >= 0, G >= 1, D >= 1, H >= 1", fn);
@@ -294,7 +296,55 @@ moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
                  dtype == MOE_BF16,  y_dtype == MOE_F32};
   a.u = up ? u_ws : nullptr;
   a.src_rows = src_rows;
+  a.split_ws = static_cast<float*>(split_ws);
   return from_hip(moe::launch_ffn(a, up, down, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_ffn(const void* x_rows, const int32_t* row_index,
+                           int64_t src_rows, moe_dtype dtype_arg,
+                           int64_t total_rows,
+                           const int64_t* group_offsets, int32_t G, int32_t D,
+                           int32_t H, const void* w1, const float* b1,
+                           const void* w2, const float* b2, void* h_ws,
+                           void* u_ws, void* y_rows, moe_dtype y_dtype_arg,
+                           moe_ffn_stages stages_arg, hipStream_t stream) {
+  return grouped_ffn("moe_grouped_ffn", x_rows, row_index, src_rows,
+                     enum_value(dtype_arg), total_rows, group_offsets, G, D, H,
+                     w1, b1, w2, b2, h_ws, u_ws, y_rows, enum_value(y_dtype_arg),
+                     enum_value(stages_arg), nullptr, stream);
+}
+
+size_t moe_grouped_ffn_split_workspace_size(void) {
+  return moe::ffn_split_workspace_bytes();
+}
+
+moe_status moe_grouped_ffn_split(const void* x_rows, const int32_t* row_index,
+                                 int64_t src_rows, moe_dtype dtype_arg,
+                                 int64_t total_rows,
+                                 const int64_t* group_offsets, int32_t G,
+                                 int32_t D, int32_t H, const void* w1,
+                                 const float* b1, const void* w2,
+                                 const float* b2, void* h_ws, void* u_ws,
+                                 void* y_rows, moe_dtype y_dtype_arg,
+                                 moe_ffn_stages stages_arg, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_grouped_ffn_split";
+  const size_t need = moe_grouped_ffn_split_workspace_size();
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+                workspace_bytes, need);
+  CHECK_PTR(workspace);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned",
+                fn);
+  return grouped_ffn(fn, x_rows, row_index, src_rows, enum_value(dtype_arg),
+                     total_rows, group_offsets, G, D, H, w1, b1, w2, b2, h_ws,
+                     u_ws, y_rows, enum_value(y_dtype_arg),
+                     enum_value(stages_arg), workspace, stream);
 }
 
 moe_status moe_grouped_mlp_fused(const void* x_rows, const int32_t* row_index,

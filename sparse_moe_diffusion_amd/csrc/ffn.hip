@@ -96,7 +96,19 @@ struct GemmParams {
   // With a_index: the rows of a.  Index entries outside [0, a_rows) read
   // zero rows (the gathered rows' descriptor spans exactly a_rows rows).
   int64_t a_rows;
+  // Large store-form tiles (three token-row stages, plain operands): if
+  // set, the last, partial round of tiles is split along k over the
+  // workgroups that would otherwise idle, each piece's fp32 partial sums
+  // going to this workspace (layout: kSplitHdrBytes of header, then one
+  // BM x BN fp32 slot per workgroup), and splitk_tail_kernel finishes
+  // those tiles.
+  float* sk_ws = nullptr;
 };
+
+// The split workspace's header: int64 [0] pieces per tile S (0: no split),
+// [1] split tiles R, then per split tile r: [2 + 3 r] first row, [3 + 3 r]
+// row end, [4 + 3 r] group << 32 | first feature.  At most 1023 split tiles.
+constexpr size_t kSplitHdrBytes = 3 * 8 * 1024;
 
 struct TileLoc {
   int g;
@@ -555,6 +567,32 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   else
     build_group_table<BM, BN>(p, tab, wave, tid0 & 63);
 
+  // Split of the last round (see GemmParams::sk_ws): T tiles on Gw
+  // workgroups are F whole rounds and R more tiles.  With S = Gw / R >= 2
+  // (at most one piece per k stage), workgroup w < R S takes, after its F
+  // tiles, piece w % S of the k stages of tile F Gw + w / S.
+  constexpr bool kCanSplit = EPI == kEpiStore && NST == 3 && !KG && !BT && !PF;
+  int skS = 0, skF = 0, skR = 0, piece_s = -1;
+  const int nkt = (Kd0 + kBK - 1) / kBK;
+  if constexpr (kCanSplit) {
+    if (p.sk_ws != nullptr && p.a_index == nullptr) {
+      const int T = __builtin_amdgcn_readfirstlane(tab[2 * kTabCol + p.G]);
+      const int Gw = gridDim.x;
+      const int F = T / Gw, R = T - F * Gw;
+      const int S = R > 0 ? min(Gw / R, nkt) : 0;
+      if (S >= 2 && R <= 1023) {
+        skS = S;
+        skF = F;
+        skR = R;
+      }
+      if (blockIdx.x == 0 && tid0 == 0) {
+        int64_t* const h = reinterpret_cast<int64_t*>(p.sk_ws);
+        h[0] = skS;
+        h[1] = skR;
+      }
+    }
+  }
+
   // Token rows: gathered through a_index from the whole activation matrix,
   // or read in place from the tile's first row.  Rows past the group end
   // re-read row 0 (gather) or the tile's first row; their results are never
@@ -579,7 +617,28 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   const int pj = blockIdx.x >> 3, pxcd = blockIdx.x & 7, pw = gridDim.x >> 3;
   int pc = pxcd, it = 0;
   TileLoc loc;
-  bool have = locate_any<KG, BM, BN, GM>(p, tab, tid0 & 63, pc * pw + pj, loc);
+  // The next tile of this workgroup: its share of the whole rounds, then
+  // (split) its piece of a tile of the last round.
+#define MOE_NEXT_TILE(LANE)                                                  \
+  do {                                                                       \
+    const int l_ = pc * pw + pj;                                             \
+    have = (skS == 0 || l_ < skF * static_cast<int>(gridDim.x)) &&           \
+           locate_any<KG, BM, BN, GM>(p, tab, (LANE), l_, loc);              \
+    if constexpr (kCanSplit) {                                               \
+      if (piece_s >= 0) {                                                    \
+        have = false;                                                        \
+      } else if (!have && skS > 0 &&                                         \
+                 static_cast<int>(blockIdx.x) < skR * skS) {                 \
+        piece_s = static_cast<int>(blockIdx.x) % skS;                        \
+        have = locate_any<KG, BM, BN, GM>(                                   \
+            p, tab, (LANE),                                                  \
+            skF * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x) / skS, \
+            loc);                                                            \
+      }                                                                      \
+    }                                                                        \
+  } while (0)
+  bool have = false;
+  MOE_NEXT_TILE(tid0 & 63);
   if (gather && have) MOE_FETCH_ROWS(loc, 0, tid0 & 63);
   stage_barrier();
   while (have) {
@@ -598,6 +657,15 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // is 64 token rows, kept in LDS as [64][BM] and [64][BN] tiles.
   const int Kd = KG ? loc.klen : Kd0;
   const uint32_t row_bytes = row_bytes0;
+  // A piece of a split tile: k stages [pk0, pk1) of it.  Its operand
+  // descriptors start pk0 stages into every row, and its reduction length Kl
+  // ends at the piece (or at Kd), so the k-tail checks below zero-fill
+  // whatever lies past it.  Otherwise Kl = Kd.
+  const bool piece = kCanSplit && piece_s >= 0;
+  const int pk0 = piece ? piece_s * nkt / skS : 0;
+  const int pk1 = piece ? (piece_s + 1) * nkt / skS : nkt;
+  const int Kl = piece ? min(Kd - pk0 * kBK, (pk1 - pk0) * kBK) : Kd;
+  const int64_t kshift = piece ? static_cast<int64_t>(pk0) * kBK : 0;
   const uint32_t kstep_a = static_cast<uint32_t>(p.mrows) * 128u;   // KG only
   const uint32_t kstep_b = static_cast<uint32_t>(p.Nd) * 128u;
   const int64_t kg_m = KG ? loc.row0 - static_cast<int64_t>(loc.g) * p.mrows : 0;
@@ -605,7 +673,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       static_cast<const uint16_t*>(p.a) +
       (gather ? int64_t(0)
               : KG ? static_cast<int64_t>(loc.kofs) * p.mrows + kg_m
-                   : loc.row0 * Kd);
+                   : loc.row0 * Kd + kshift);
   // KG: from the tile's first feature of the piece's first row to the end
   // of its last row.  Rows past the piece read zero; tile features past the
   // operand's C read the next row's (finite) values, which only reach
@@ -616,7 +684,8 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       gather ? static_cast<uint32_t>(p.a_rows) * row_bytes
       : KG   ? static_cast<uint32_t>(kg_a > 0 ? kg_a : 0)
              : static_cast<uint32_t>(min(static_cast<int>(loc.row_end - loc.row0), BM)) *
-                   row_bytes;
+                       row_bytes -
+                   static_cast<uint32_t>(kshift * 2);
   const __amdgpu_buffer_rsrc_t rsA =
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(a_base))),
@@ -631,14 +700,15 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       static_cast<const uint16_t*>(p.w) +
       (KG   ? static_cast<int64_t>(loc.kofs) * p.Nd + loc.n0
        : BT ? static_cast<int64_t>(loc.g) * Kd * p.Nd + loc.n0
-            : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd);
+            : (static_cast<int64_t>(loc.g) * p.Nd + loc.n0) * Kd + kshift);
   const int64_t kg_w =
       KG   ? (static_cast<int64_t>(loc.klen) * p.Nd - loc.n0) * 2
       : BT ? (static_cast<int64_t>(Kd) * p.Nd - loc.n0) * 2
            : 0;
   const uint32_t w_bytes =
       (KG || BT) ? static_cast<uint32_t>(kg_w > 0 ? kg_w : 0)
-                 : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes;
+                 : static_cast<uint32_t>(min(p.Nd - loc.n0, BN)) * row_bytes -
+                       static_cast<uint32_t>(kshift * 2);
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(reinterpret_cast<const void*>(
                     uniform64(reinterpret_cast<int64_t>(w_base))),
@@ -688,7 +758,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     }
   }
 
-  const int nk = (Kd + kBK - 1) / kBK;
+  const int nk = (Kl + kBK - 1) / kBK;
 
   // L2 prefetch (PF, in-place token rows only): the tiles an XCD runs at once
   // read the same row chunks at about the same time, so without it they all
@@ -716,7 +786,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     if constexpr (PF) {                                                      \
       if (wave < 2) {                                                        \
         const int pkt_ = (KT);                                               \
-        const uint32_t o_ = (pf_off == kOutOfRange || pkt_ * kBK >= Kd)      \
+        const uint32_t o_ = (pf_off == kOutOfRange || pkt_ * kBK >= Kl)      \
                                 ? kOutOfRange                                \
                                 : pf_off + static_cast<uint32_t>(pkt_) * (kBK * 2); \
         dma_untracked<4>(pf_rs, pf_lds, o_);                                 \
@@ -748,7 +818,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       /* builtin transfers before the weight's transpose reads); the      */ \
       /* weight's k stage is a byte offset from k row 0, so k rows past   */ \
       /* Kd fall outside the descriptor and read zero                     */ \
-      const bool full_ = (ikt_ + 1) * kBK <= Kd;                             \
+      const bool full_ = (ikt_ + 1) * kBK <= Kl;                             \
       const uint32_t sb_ = static_cast<uint32_t>(ikt_) * kstep_b;            \
       _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
         if (q < QA) {                                                        \
@@ -756,7 +826,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           if (!full_) {                                                      \
             const int r_ = (wave + kWaves * q) * 8 + (lane >> 3);            \
             const int c_ = (lane & 7) ^ swz(r_);                             \
-            if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;               \
+            if (ikt_ * kBK + c_ * 8 >= Kl) off_ = kOutOfRange;               \
           }                                                                  \
           dma16_raw(kg_abase, a_bytes, (DA) + ldst[q], off_);                \
         } else {                                                             \
@@ -764,7 +834,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
         }                                                                    \
       }                                                                      \
     } else {                                                                 \
-      const bool full_ = (ikt_ + 1) * kBK <= Kd;                             \
+      const bool full_ = (ikt_ + 1) * kBK <= Kl;                             \
       _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                  \
         const bool isA_ = q < QA;                                            \
         uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);   \
@@ -773,7 +843,7 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
           const int t_ = wave + kWaves * q;                                  \
           const int r_ = (isA_ ? t_ : t_ - BM / 8) * 8 + (lane >> 3);        \
           const int c_ = (lane & 7) ^ swz(r_);                               \
-          if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;                 \
+          if (ikt_ * kBK + c_ * 8 >= Kl) off_ = kOutOfRange;                 \
         }                                                                    \
         dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
       }                                                                      \
@@ -791,11 +861,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
       const bool isA_ = q < QA;                                              \
       const int ikt_ = isA_ ? (KTA) : (KTB);                                 \
       uint32_t off_ = goff[q] + static_cast<uint32_t>(ikt_) * (kBK * 2);     \
-      if ((ikt_ + 1) * kBK > Kd) {                                           \
+      if ((ikt_ + 1) * kBK > Kl) {                                           \
         const int t_ = wave + kWaves * q;                                    \
         const int r_ = (isA_ ? t_ : t_ - BM / 8) * 8 + (lane >> 3);          \
         const int c_ = (lane & 7) ^ swz(r_);                                 \
-        if (ikt_ * kBK + c_ * 8 >= Kd) off_ = kOutOfRange;                   \
+        if (ikt_ * kBK + c_ * 8 >= Kl) off_ = kOutOfRange;                   \
       }                                                                      \
       dma_untracked<16>(isA_ ? rsA : rsB, (isA_ ? (DA) : (DB)) + ldst[q], off_); \
     }                                                                        \
@@ -1014,7 +1084,38 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 
   // acc[i][j] register r: feature 8 (r / 4) + 4 (lane >> 5) + r % 4 of
   // feature block i, token (lane & 31) of token block j.
-  if constexpr (OUT_BF16) {
+  if (piece) {
+    // A piece of a split tile: its fp32 partial sums, [BM][BN] row-major in
+    // this workgroup's slot (every row and feature, as they are; the
+    // finishing kernel adds the bias and skips what is not stored), and,
+    // from the tile's first piece, where the tile lies.
+    float* const part = p.sk_ws + kSplitHdrBytes / 4 +
+                        static_cast<int64_t>(blockIdx.x) * (BM * BN);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int t = wt * (BM / WT) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < FB; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int fl = wf * (BN / WF) + i * 32 + 8 * q + 4 * khalf;
+          f32x4 v;
+          v[0] = acc[i][j][4 * q + 0];
+          v[1] = acc[i][j][4 * q + 1];
+          v[2] = acc[i][j][4 * q + 2];
+          v[3] = acc[i][j][4 * q + 3];
+          *reinterpret_cast<f32x4*>(part + t * BN + fl) = v;
+        }
+      }
+    }
+    if (piece_s == 0 && tid == 0) {
+      int64_t* const h = reinterpret_cast<int64_t*>(p.sk_ws) +
+                         2 + 3 * (static_cast<int>(blockIdx.x) / skS);
+      h[0] = loc.row0;
+      h[1] = loc.row_end;
+      h[2] = (static_cast<int64_t>(loc.g) << 32) | loc.n0;
+    }
+  } else if constexpr (OUT_BF16) {
     // The bias, if any, joins the accumulators first, in one loop behind a
     // uniform branch (u = A W^T + b, as the staging below would form it), so
     // that the staging loops carry no bias code: two forms of them in one
@@ -1283,8 +1384,58 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   }
   pc += 8;
   ++it;
-  have = locate_any<KG, BM, BN, GM>(p, tab, lane, pc * pw + pj, loc);
+  MOE_NEXT_TILE(lane);
   }  // tile loop
+#undef MOE_NEXT_TILE
+}
+
+// Finishes the tiles of a split last round (GemmParams::sk_ws): the S
+// partials of each split tile added in piece order, then the bias, stored
+// as the store epilogue does (rounded once).  A tile's BM x BN outputs are
+// spread over kSplitFinishWgs workgroups, 4 consecutive features per
+// thread, the loads of a batch of pieces issued before their additions.
+// Rows past the group end and features past Nd are skipped.
+constexpr int kSplitFinishBatch = 8;
+template <int BM, int BN>
+constexpr int split_finish_wgs() { return BM * BN / (256 * 4); }
+
+template <bool OUT_BF16, int BM, int BN>
+__global__ __launch_bounds__(256) void splitk_tail_kernel(GemmParams p) {
+  static_assert(BM * BN % (256 * 4) == 0, "whole workgroups per tile");
+  constexpr int kW = split_finish_wgs<BM, BN>();
+  const int64_t* const h = reinterpret_cast<const int64_t*>(p.sk_ws);
+  const int S = static_cast<int>(h[0]), R = static_cast<int>(h[1]);
+  const int r = blockIdx.x / kW;
+  if (S < 2 || r >= R) return;
+  const int idx = (blockIdx.x - r * kW) * 1024 + threadIdx.x * 4;
+  const int64_t row0 = h[2 + 3 * r], row_end = h[3 + 3 * r];
+  const int g = static_cast<int>(h[4 + 3 * r] >> 32);
+  const int n0 = static_cast<int>(h[4 + 3 * r] & 0xffffffff);
+  const int t = idx / BN, f = idx - t * BN;
+  const int64_t row = row0 + t;
+  if (row >= row_end || n0 + f >= p.Nd) return;
+  const float* const part = p.sk_ws + kSplitHdrBytes / 4 +
+                            static_cast<int64_t>(r) * S * (BM * BN) + idx;
+  f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < S; s0 += kSplitFinishBatch) {
+    f32x4 w[kSplitFinishBatch];
+#pragma unroll
+    for (int b = 0; b < kSplitFinishBatch; ++b)
+      if (s0 + b < S)
+        w[b] = *reinterpret_cast<const f32x4*>(
+            part + static_cast<int64_t>(s0 + b) * (BM * BN));
+#pragma unroll
+    for (int b = 0; b < kSplitFinishBatch; ++b) {
+      if (s0 + b < S) {
+        if (s0 + b == 0) {
+          v = w[b];
+        } else {
+          v[0] += w[b][0]; v[1] += w[b][1]; v[2] += w[b][2]; v[3] += w[b][3];
+        }
+      }
+    }
+  }
+  store4<kEpiStore, OUT_BF16>(p, g, row, n0 + f, v);
 }
 
 // ------------------------------------------- single-kernel expert MLP ----
@@ -1663,10 +1814,18 @@ void launch_stage(const GemmParams& p, hipStream_t stream) {
         dim3(64 * kSmWT * kSmWF), 0, stream, p);
     return;
   }
+  const int grid = persistent_grid(big);
   hipLaunchKernelGGL(
       (gemm_bf16_kernel<EPI, OUT_BF16, BM, BN, WT, WF, GM, NST == 3 ? false : PF,
                         false, CMAX, BT, NST>),
-      dim3(persistent_grid(big)), dim3(64 * WT * WF), 0, stream, p);
+      dim3(grid), dim3(64 * WT * WF), 0, stream, p);
+  // the split last round's tiles (at most one per two workgroups)
+  if constexpr (EPI == kEpiStore && NST == 3 && !BT) {
+    if (p.sk_ws != nullptr && p.a_index == nullptr)
+      hipLaunchKernelGGL((splitk_tail_kernel<OUT_BF16, BM, BN>),
+                         dim3((grid + 1) / 2 * split_finish_wgs<BM, BN>()),
+                         dim3(256), 0, stream, p);
+  }
 }
 
 }  // namespace
@@ -1922,6 +2081,12 @@ hipError_t launch_mlp_fused(const FfnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+size_t ffn_split_workspace_bytes() {
+  // one slot per workgroup of the largest persistent grid
+  return kSplitHdrBytes + static_cast<size_t>(cu_count() / 8 * 8) * kDnBM *
+                              kDnBN * sizeof(float);
+}
+
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
                       hipStream_t stream) {
   if (a.total_rows == 0) return hipSuccess;
@@ -1931,6 +2096,7 @@ hipError_t launch_ffn(const FfnArgs& a, bool up, bool down,
   p1.a_rows = a.src_rows;
   GemmParams p2{a.h, nullptr, a.w2, a.b2, a.y, a.offsets, a.total_rows,
                 a.G, a.D, a.H};
+  p2.sk_ws = a.split_ws;
   if (a.bf16) {
     if (up) {
       launch_stage<kEpiGelu, true, kUpBM, kUpBN, kUpWT, kUpWF, kUpGM, false>(

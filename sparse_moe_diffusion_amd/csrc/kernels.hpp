@@ -68,7 +68,11 @@ struct FfnArgs {
   bool y_f32;               // output dtype
   void* u = nullptr;        // [total][H] bf16 pre-activations out, or null
   int64_t src_rows = 0;     // rows of x when row_index is given
+  // stage 2 (bf16 inputs): ffn_split_workspace_bytes() of device scratch
+  // for splitting its last round of tiles along k, or null
+  float* split_ws = nullptr;
 };
+size_t ffn_split_workspace_bytes();
 hipError_t launch_ffn(const FfnArgs& a, bool up, bool down, hipStream_t stream);
 // Both stages in one kernel (bf16, D in {128, 256, 384}, H % 64 == 0); h is
 // not used.

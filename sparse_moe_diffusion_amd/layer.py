@@ -108,6 +108,11 @@ class LayerBuffers:
             self.shared_offsets = self.h_shared = self.y_shared = None
             self.u_shared = None
         self.y = torch.empty(N, D, dtype=dt, device=dev)
+        # the routed experts' stage 2 splits its last round of tiles along k
+        # into this workspace (bf16 layers)
+        self.split_ws = (torch.empty(ops.ffn_split_workspace_size(),
+                                     dtype=torch.uint8, device=dev)
+                         if cfg.dtype == "bf16" else None)
         self.gate_bal_ws = self.route_ws = None
         if route == ROUTES["topk"]:
             bws = ops.gate_balance_workspace_size(cfg.B, cfg.T, E)
@@ -167,11 +172,11 @@ def routed_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,
     if buf.gather:
         ops.moe_grouped_ffn(x, buf.row_token, cfg.A, buf.expert_offsets, wts.w1,
                             None, wts.w2, None, buf.h, buf.y_rows, stages,
-                            buf.u)
+                            buf.u, buf.split_ws)
     else:
         ops.moe_grouped_ffn(buf.x_perm, None, cfg.A, buf.expert_offsets, wts.w1,
                             None, wts.w2, None, buf.h, buf.y_rows, stages,
-                            buf.u)
+                            buf.u, buf.split_ws)
 
 
 def shared_ffn(cfg, x, wts: LayerWeights, buf: LayerBuffers,

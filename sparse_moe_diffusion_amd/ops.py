@@ -82,19 +82,30 @@ def moe_permute_noalloc(x, topk_idx, E: int, K: int, expert_counts,
               _ptr(x_perm), _stream())
 
 
+def ffn_split_workspace_size() -> int:
+    return _lib.load().moe_grouped_ffn_split_workspace_size()
+
+
 def moe_grouped_ffn(x_rows, row_index, total_rows: int, group_offsets, w1, b1,
                     w2, b2, h_ws, y_rows, stages: int = _lib.MOE_FFN_BOTH,
-                    u_ws=None):
+                    u_ws=None, split_ws=None):
+    """moe_grouped_ffn, or with split_ws (a uint8 tensor of at least
+    ffn_split_workspace_size() bytes) moe_grouped_ffn_split."""
     if w1 is not None:
         G, H, D = w1.shape
     else:                      # stage 2 alone
         G, D, H = w2.shape
-    _lib.call("moe_grouped_ffn", _ptr(x_rows), _ptr(row_index),
-              _src_rows(x_rows), dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
-              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(u_ws),
-              _ptr(y_rows),
-              dtype_code(y_rows.dtype if y_rows is not None else h_ws.dtype),
-              stages, _stream())
+    args = [_ptr(x_rows), _ptr(row_index), _src_rows(x_rows),
+            dtype_code(h_ws.dtype), total_rows, _ptr(group_offsets), G, D, H,
+            _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(h_ws), _ptr(u_ws),
+            _ptr(y_rows),
+            dtype_code(y_rows.dtype if y_rows is not None else h_ws.dtype),
+            stages]
+    if split_ws is None:
+        _lib.call("moe_grouped_ffn", *args, _stream())
+    else:
+        _lib.call("moe_grouped_ffn_split", *args, _ptr(split_ws),
+                  split_ws.numel() * split_ws.element_size(), _stream())
 
 
 def moe_grouped_mlp_fused(x_rows, row_index, total_rows: int, group_offsets,

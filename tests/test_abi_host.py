@@ -314,6 +314,39 @@ def test_gate_route_workspace():
     assert lib.moe_gate_route_workspace_size(-1, 16, 8) == 0
 
 
+def _ffn_split(**kw):
+    a = dict(x=FAKE, ri=None, src=0, dt=_lib.MOE_BF16, total=16, offs=FAKE,
+             G=1, D=128, H=256, w1=FAKE, b1=None, w2=FAKE, b2=None, h=FAKE,
+             u=None, y=FAKE, ydt=_lib.MOE_BF16, stages=_lib.MOE_FFN_BOTH,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return _lib.call_status("moe_grouped_ffn_split", *a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wsb=0), _lib.MOE_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(ws=ctypes.c_void_p(0x1008)), _lib.MOE_ERR_INVALID_ARGUMENT),
+    # the checks of moe_grouped_ffn
+    (dict(G=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(stages=0), _lib.MOE_ERR_INVALID_ARGUMENT),
+    (dict(D=100), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(h=None), _lib.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_grouped_ffn_split_rejects(kw, status):
+    ensure_built()
+    assert _ffn_split(**kw) == status
+    assert _lib.last_error()
+
+
+def test_grouped_ffn_split_workspace():
+    lib = ensure_built()
+    n = lib.moe_grouped_ffn_split_workspace_size()
+    # header + one 256 x 192 fp32 tile per compute unit (at least 8 CUs)
+    assert n >= 3 * 8 * 1024 + 8 * 256 * 192 * 4
+    assert (n - 3 * 8 * 1024) % (8 * 256 * 192 * 4) == 0
+
+
 def test_binding_raises_on_error():
     ensure_built()
     with pytest.raises(_lib.MoEError, match="MOE_ERR_INVALID_ARGUMENT"):

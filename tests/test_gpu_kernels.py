@@ -330,6 +330,100 @@ def test_grouped_ffn_tile_forms(sizes, D, H, y_f32, bias):
             assert_close(y[a:b], ref[a:b], "bf16", f"group {g}")
 
 
+def _split_case(sizes, D, H, y_f32, bias, rng):
+    """One moe_grouped_ffn_split call (gathered rows) and its oracle."""
+    _, ops = _ops()
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)])
+    total = int(offsets[-1])
+    q = lambda a: synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32)))
+    nsrc = total + 3
+    xsrc = q(rng.standard_normal((nsrc, D)))
+    w1 = q(rng.standard_normal((G, H, D)) * 0.03)
+    w2 = q(rng.standard_normal((G, D, H)) * 0.03)
+    b1 = (rng.standard_normal((G, H)) * 0.1).astype(np.float32) if bias else None
+    b2 = (rng.standard_normal((G, D)) * 0.1).astype(np.float32) if bias else None
+    ri = rng.permutation(nsrc)[:total]
+    return dict(xsrc=xsrc, offsets=offsets, w1=w1, w2=w2, b1=b1, b2=b2, ri=ri,
+                y_f32=y_f32)
+
+
+def _run_split(c, ws):
+    _, ops = _ops()
+    G, H, D = c["w1"].shape
+    total = int(c["offsets"][-1])
+    x = _bits_tensor(c["xsrc"], "bf16")
+    ri = torch.from_numpy(c["ri"].astype(np.int32)).to(DEV)
+    ot = torch.from_numpy(c["offsets"].astype(np.int64)).to(DEV)
+    w1t, w2t = _bits_tensor(c["w1"], "bf16"), _bits_tensor(c["w2"], "bf16")
+    b1t = None if c["b1"] is None else torch.from_numpy(c["b1"]).to(DEV)
+    b2t = None if c["b2"] is None else torch.from_numpy(c["b2"]).to(DEV)
+    h = torch.empty(total, H, dtype=torch.bfloat16, device=DEV)
+    ydt = torch.float32 if c["y_f32"] else torch.bfloat16
+    y = torch.full((total, D), float("nan"), dtype=ydt, device=DEV)
+    ops.moe_grouped_ffn(x, ri, total, ot, w1t, b1t, w2t, b2t, h, y,
+                        split_ws=ws)
+    return y
+
+
+@pytest.mark.parametrize("sizes,D,H,y_f32,bias", [
+    # 44 row-tiles x 6 feature tiles = 264 stage-2 tiles on 256 workgroups:
+    # the last 8 split into 32 pieces of one k stage each (H = 2048)
+    ([256 * 15 + 10, 256 * 14 + 100, 256 * 13], 1152, 2048, False, True),
+    # 43 row-tiles: 2 tiles left over, 72 pieces of one stage (H = 4608)
+    ([256 * 43 - 5], 1152, 4608, True, False),
+    # 1560 tiles (about the XL layer's routed stage 2): 24 tiles in 10
+    # pieces of 7 or 8 stages
+    ([8292, 8092, 8292, 8092, 8192, 8192, 8292, 8092], 1152, 4608, False, False),
+    # a whole number of rounds (768 tiles): no split
+    ([256 * 32, 256 * 48, 256 * 48], 1152, 2048, False, False),
+])
+def test_grouped_ffn_split(sizes, D, H, y_f32, bias):
+    """moe_grouped_ffn_split, every row against the oracle, where stage 2's
+    last round of tiles is split along k (or not, for a whole number of
+    rounds); and against moe_grouped_ffn to fp32-summation accuracy."""
+    _, ops = _ops()
+    rng = np.random.default_rng(sum(sizes) + H)
+    c = _split_case(sizes, D, H, y_f32, bias, rng)
+    ws = torch.empty(ops.ffn_split_workspace_size(), dtype=torch.uint8,
+                     device=DEV)
+    ws.fill_(0xFF)   # needs no initialisation
+    y = to_np(_run_split(c, ws))
+    torch.cuda.synchronize()
+    assert not np.isnan(y).any()
+    ref = _grouped_reference(c["xsrc"][c["ri"]], c["offsets"], c["w1"],
+                             c["w2"], c["b1"], c["b2"])
+    offs = c["offsets"]
+    for g in range(len(sizes)):
+        a, b = int(offs[g]), int(offs[g + 1])
+        if b > a:
+            assert_close(y[a:b], ref[a:b], "bf16", f"group {g}")
+    y0 = to_np(_run_split(c, None))
+    if y_f32:
+        assert np.allclose(y, y0, rtol=1e-4, atol=1e-4 * np.abs(y0).max())
+    else:
+        # bf16 outputs: the two roundings of sums that differ in the last
+        # fp32 bits agree to one bf16 step
+        assert np.abs(y - y0).max() <= 2 ** -7 * np.abs(y0).max()
+
+
+def test_grouped_ffn_split_workspace_reuse():
+    """Two split calls in a row on one workspace, the second with another
+    split (the header is rewritten every call), then one with no split."""
+    _, ops = _ops()
+    rng = np.random.default_rng(7)
+    ws = torch.empty(ops.ffn_split_workspace_size(), dtype=torch.uint8,
+                     device=DEV)
+    for sizes, H in (([256 * 15 + 10, 256 * 14 + 100, 256 * 13], 2048),
+                     ([256 * 43 - 5], 1024),
+                     ([256 * 32, 256 * 48, 256 * 48], 1024)):
+        c = _split_case(sizes, 1152, H, False, True, rng)
+        y = to_np(_run_split(c, ws))
+        ref = _grouped_reference(c["xsrc"][c["ri"]], c["offsets"], c["w1"],
+                                 c["w2"], c["b1"], c["b2"])
+        assert_close(y, ref, "bf16", f"sizes {sizes}")
+
+
 @pytest.mark.parametrize("rows,D,H", [(3000, 256, 1024), (12800, 256, 1024)],
                          ids=["small_tiles", "large_tiles"])
 def test_gelu_saturation(rows, D, H):
