@@ -1392,9 +1392,11 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 // Finishes the tiles of a split last round (GemmParams::sk_ws): the S
 // partials of each split tile added in piece order, then the bias, stored
 // as the store epilogue does (rounded once).  A tile's BM x BN outputs are
-// spread over kSplitFinishWgs workgroups, 4 consecutive features per
-// thread, the loads of a batch of pieces issued before their additions.
-// Rows past the group end and features past Nd are skipped.
+// cut into split_finish_wgs() chunks of 1024 (4 consecutive features per
+// thread); the workgroups walk the R tiles' chunks, and the loads of a
+// batch of pieces are issued before their additions.  Rows past the group
+// end and features past Nd are skipped.  With no split every workgroup
+// returns after reading the header.
 constexpr int kSplitFinishBatch = 8;
 template <int BM, int BN>
 constexpr int split_finish_wgs() { return BM * BN / (256 * 4); }
@@ -1405,37 +1407,39 @@ __global__ __launch_bounds__(256) void splitk_tail_kernel(GemmParams p) {
   constexpr int kW = split_finish_wgs<BM, BN>();
   const int64_t* const h = reinterpret_cast<const int64_t*>(p.sk_ws);
   const int S = static_cast<int>(h[0]), R = static_cast<int>(h[1]);
-  const int r = blockIdx.x / kW;
-  if (S < 2 || r >= R) return;
-  const int idx = (blockIdx.x - r * kW) * 1024 + threadIdx.x * 4;
-  const int64_t row0 = h[2 + 3 * r], row_end = h[3 + 3 * r];
-  const int g = static_cast<int>(h[4 + 3 * r] >> 32);
-  const int n0 = static_cast<int>(h[4 + 3 * r] & 0xffffffff);
-  const int t = idx / BN, f = idx - t * BN;
-  const int64_t row = row0 + t;
-  if (row >= row_end || n0 + f >= p.Nd) return;
-  const float* const part = p.sk_ws + kSplitHdrBytes / 4 +
-                            static_cast<int64_t>(r) * S * (BM * BN) + idx;
-  f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s0 = 0; s0 < S; s0 += kSplitFinishBatch) {
-    f32x4 w[kSplitFinishBatch];
+  if (S < 2) return;
+  for (int item = blockIdx.x; item < R * kW; item += gridDim.x) {
+    const int r = item / kW;
+    const int idx = (item - r * kW) * 1024 + threadIdx.x * 4;
+    const int64_t row0 = h[2 + 3 * r], row_end = h[3 + 3 * r];
+    const int g = static_cast<int>(h[4 + 3 * r] >> 32);
+    const int n0 = static_cast<int>(h[4 + 3 * r] & 0xffffffff);
+    const int t = idx / BN, f = idx - t * BN;
+    const int64_t row = row0 + t;
+    if (row >= row_end || n0 + f >= p.Nd) continue;
+    const float* const part = p.sk_ws + kSplitHdrBytes / 4 +
+                              static_cast<int64_t>(r) * S * (BM * BN) + idx;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < S; s0 += kSplitFinishBatch) {
+      f32x4 w[kSplitFinishBatch];
 #pragma unroll
-    for (int b = 0; b < kSplitFinishBatch; ++b)
-      if (s0 + b < S)
-        w[b] = *reinterpret_cast<const f32x4*>(
-            part + static_cast<int64_t>(s0 + b) * (BM * BN));
+      for (int b = 0; b < kSplitFinishBatch; ++b)
+        if (s0 + b < S)
+          w[b] = *reinterpret_cast<const f32x4*>(
+              part + static_cast<int64_t>(s0 + b) * (BM * BN));
 #pragma unroll
-    for (int b = 0; b < kSplitFinishBatch; ++b) {
-      if (s0 + b < S) {
-        if (s0 + b == 0) {
-          v = w[b];
-        } else {
-          v[0] += w[b][0]; v[1] += w[b][1]; v[2] += w[b][2]; v[3] += w[b][3];
+      for (int b = 0; b < kSplitFinishBatch; ++b) {
+        if (s0 + b < S) {
+          if (s0 + b == 0) {
+            v = w[b];
+          } else {
+            v[0] += w[b][0]; v[1] += w[b][1]; v[2] += w[b][2]; v[3] += w[b][3];
+          }
         }
       }
     }
+    store4<kEpiStore, OUT_BF16>(p, g, row, n0 + f, v);
   }
-  store4<kEpiStore, OUT_BF16>(p, g, row, n0 + f, v);
 }
 
 // ------------------------------------------- single-kernel expert MLP ----
@@ -1822,8 +1826,7 @@ void launch_stage(const GemmParams& p, hipStream_t stream) {
   // the split last round's tiles (at most one per two workgroups)
   if constexpr (EPI == kEpiStore && NST == 3 && !BT) {
     if (p.sk_ws != nullptr && p.a_index == nullptr)
-      hipLaunchKernelGGL((splitk_tail_kernel<OUT_BF16, BM, BN>),
-                         dim3((grid + 1) / 2 * split_finish_wgs<BM, BN>()),
+      hipLaunchKernelGGL((splitk_tail_kernel<OUT_BF16, BM, BN>), dim3(grid),
                          dim3(256), 0, stream, p);
   }
 }
