@@ -74,10 +74,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_expert_gemm_xl_8e2a_5
 FFN_SOURCE = os.path.join(ROOT, "sparse_moe_diffusion_amd", "csrc", "ffn.hip")
 
 
+def code_hash(path):
+    """sha256 of a C++ source with its comments and whitespace removed: the
+    code the counters were taken on, unchanged by edits to its comments."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256(re.sub(r"\s+", "", text).encode()).hexdigest()
+
+
 def measured_traffic(stage):
     """Bytes per launch of expert GEMM stage 1 or 2 from the counter summary,
-    or None when it is missing or was taken on another version of ffn.hip."""
-    import hashlib
+    or None when it is missing or was taken on other code than the current
+    ffn.hip's."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -88,12 +99,11 @@ def measured_traffic(stage):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip().lower()] = v.strip().strip("`")
-    want = fields.get("ffn.hip sha256")
+    want = fields.get("ffn.hip code sha256")
     val = fields.get(f"stage {stage} traffic bytes per launch")
     if not want or not val:
         return None
-    have = hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()
-    return float(val) if have == want else None
+    return float(val) if code_hash(FFN_SOURCE) == want else None
 
 
 def copy_calibration(nbytes):

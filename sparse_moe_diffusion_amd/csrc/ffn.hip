@@ -568,9 +568,10 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
     build_group_table<BM, BN>(p, tab, wave, tid0 & 63);
 
   // Split of the last round (see GemmParams::sk_ws): T tiles on Gw
-  // workgroups are F whole rounds and R more tiles.  With S = Gw / R >= 2
-  // (at most one piece per k stage), workgroup w < R S takes, after its F
-  // tiles, piece w % S of the k stages of tile F Gw + w / S.
+  // workgroups are F whole rounds and R more tiles.  With S = min(Gw / R,
+  // k stages) >= 2 and R within the header (at most 1023 tiles), workgroup
+  // w < R S takes, after its F tiles, piece w % S of the k stages of tile
+  // F Gw + w / S.
   constexpr bool kCanSplit = EPI == kEpiStore && NST == 3 && !KG && !BT && !PF;
   int skS = 0, skF = 0, skR = 0, piece_s = -1;
   const int nkt = (Kd0 + kBK - 1) / kBK;
