@@ -377,6 +377,9 @@ def _run_split(c, ws):
     ([8292, 8092, 8292, 8092, 8192, 8192, 8292, 8092], 1152, 4608, False, False),
     # a whole number of rounds (768 tiles): no split
     ([256 * 32, 256 * 48, 256 * 48], 1152, 2048, False, False),
+    # a reduction that ends in a partial k stage (H % 64 = 8, 33 stages):
+    # the last piece of each split tile carries the k tail
+    ([256 * 15 + 10, 256 * 14 + 100, 256 * 13], 1152, 2056, True, True),
 ])
 def test_grouped_ffn_split(sizes, D, H, y_f32, bias):
     """moe_grouped_ffn_split, every row against the oracle, where stage 2's
