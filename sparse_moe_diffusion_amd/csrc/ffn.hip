@@ -39,7 +39,7 @@
 // Tile order: the bf16 kernels are persistent, about one workgroup per CU;
 // workgroups are dealt round-robin to the 8 XCDs, and the workgroups of an
 // XCD walk chunks of consecutive tiles; within a group, tiles go in bands of
-// GM row-tiles, feature-tile major, so tiles running at once share both
+// about GM row-tiles, feature-tile major, so tiles running at once share both
 // their token rows and their weight rows in the XCD's L2.
 #include <algorithm>
 #include <atomic>
@@ -140,6 +140,34 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return xcd * q + min(xcd, r) + j;
 }
 
+// Tile Lg of a group of mt row-tiles and ntn feature tiles: its row tile m
+// and feature tile n.  The row tiles form nb = max(1, round(mt / GM)) bands
+// of near-equal size (the first mt % nb bands one row tile larger), each
+// walked feature-tile major.  Balanced bands keep a group's last band from
+// holding one or two row tiles: such a band's tiles running at once would
+// share their token rows but each read weight rows of its own.
+template <int GM>
+__device__ __forceinline__ void band_tile(int Lg, int mt, int ntn, int& m,
+                                          int& n) {
+  const int nb = max(1, (mt + GM / 2) / GM);
+  const int q = mt / nb, r = mt - q * nb;
+  const int big = r * (q + 1) * ntn;   // tiles of the larger bands
+  int m_first, gm, rem;
+  if (Lg < big) {
+    const int band = Lg / ((q + 1) * ntn);
+    m_first = band * (q + 1);
+    gm = q + 1;
+    rem = Lg - band * (q + 1) * ntn;
+  } else {
+    const int band = (Lg - big) / (q * ntn);
+    m_first = r * (q + 1) + band * q;
+    gm = q;
+    rem = Lg - big - band * q * ntn;
+  }
+  m = m_first + rem % gm;
+  n = rem / gm;
+}
+
 template <int BM, int BN, int GM>
 __device__ __forceinline__ bool locate_tile(const GemmParams& p, int L,
                                             TileLoc& loc) {
@@ -151,15 +179,13 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int L,
     const int mt = static_cast<int>((r1 - r0 + BM - 1) / BM);
     const int tiles = mt * ntn;
     if (L < tiles) {
-      const int band = L / (GM * ntn);
-      const int rem = L - band * GM * ntn;
-      const int m_first = band * GM;
-      const int gm = min(GM, mt - m_first);
+      int m, n;
+      band_tile<GM>(L, mt, ntn, m, n);
       // All wave-uniform: keep them in scalar registers.
       loc.g = __builtin_amdgcn_readfirstlane(g);
-      loc.row0 = uniform64(r0 + static_cast<int64_t>(m_first + rem % gm) * BM);
+      loc.row0 = uniform64(r0 + static_cast<int64_t>(m) * BM);
       loc.row_end = uniform64(r1);
-      loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+      loc.n0 = __builtin_amdgcn_readfirstlane(n * BN);
       return true;
     }
     L -= tiles;
@@ -236,15 +262,12 @@ __device__ __forceinline__ bool locate_tile_tab(const GemmParams& p,
   const int ntn = (p.Nd + BN - 1) / BN;
   const int mt = (r1 - r0 + BM - 1) / BM;
   const int Lg = L - __builtin_amdgcn_readfirstlane(first[g]);
-  const int band = Lg / (GM * ntn);
-  const int rem = Lg - band * GM * ntn;
-  const int m_first = band * GM;
-  const int gm = min(GM, mt - m_first);
+  int m, n;
+  band_tile<GM>(Lg, mt, ntn, m, n);
   loc.g = g;
-  loc.row0 = uniform64(static_cast<int64_t>(r0) +
-                       static_cast<int64_t>(m_first + rem % gm) * BM);
+  loc.row0 = uniform64(static_cast<int64_t>(r0) + static_cast<int64_t>(m) * BM);
   loc.row_end = uniform64(r1);
-  loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+  loc.n0 = __builtin_amdgcn_readfirstlane(n * BN);
   return true;
 }
 
@@ -279,8 +302,8 @@ __device__ __forceinline__ void build_kseg_table(const GemmParams& p,
 }
 
 // Tile L of a K-grouped launch: virtual group v = L / (row tiles x feature
-// tiles) is split v / G of group g = v % G, bands of GM row tiles within
-// it.  Output rows are v * mrows + row (the split's partial).
+// tiles) is split v / G of group g = v % G, bands of about GM row tiles
+// within it.  Output rows are v * mrows + row (the split's partial).
 template <int BM, int BN, int GM>
 __device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
                                                const int32_t* tab, int L,
@@ -293,15 +316,13 @@ __device__ __forceinline__ bool locate_tile_kg(const GemmParams& p,
   const int v = L / per;
   const int g = v % p.G, sp = v / p.G;
   const int Lg = L - v * per;
-  const int band = Lg / (GM * ntn);
-  const int rem = Lg - band * GM * ntn;
-  const int m_first = band * GM;
-  const int gm = min(GM, mt - m_first);
+  int m, n;
+  band_tile<GM>(Lg, mt, ntn, m, n);
   const int64_t base = static_cast<int64_t>(v) * p.mrows;
   loc.g = __builtin_amdgcn_readfirstlane(v);
-  loc.row0 = uniform64(base + static_cast<int64_t>(m_first + rem % gm) * BM);
+  loc.row0 = uniform64(base + static_cast<int64_t>(m) * BM);
   loc.row_end = uniform64(base + p.mrows);
-  loc.n0 = __builtin_amdgcn_readfirstlane((rem / gm) * BN);
+  loc.n0 = __builtin_amdgcn_readfirstlane(n * BN);
   // the split's piece of the group's rows (a multiple of 64 rows except
   // the last piece, possibly empty: the partial is then zero)
   const int kofs = __builtin_amdgcn_readfirstlane(tab[g]);
@@ -1666,7 +1687,8 @@ __global__ __launch_bounds__(64 * kMlpWaves, 1) void mlp_fused_kernel(
 // waves of 64 tokens x 96 features.
 constexpr int kUpBM = 256, kUpBN = 256, kUpWT = 2, kUpWF = 4;
 constexpr int kDnBM = 256, kDnBN = 192, kDnWT = 4, kDnWF = 2;
-// Tile order within a group (bands of GM row-tiles, feature-tile major).
+// Tile order within a group (bands of about GM row-tiles, feature-tile
+// major).
 // Stage 2 has few feature tiles (1152 / 192 = 6) and a large token operand
 // (h): with GM = 1 all feature tiles of a row-tile run at once, so each row
 // of h leaves HBM once.  Stage 1 (18+ feature tiles) keeps bands of 8.

@@ -304,6 +304,9 @@ def _grouped_reference(xrows, offsets, w1, w2, b1=None, b2=None):
     ([3000, 2500, 0, 2700], 1152, 2056, False, True),
     ([12000, 9000], 1152, 40, False, False),
     ([12000, 9000], 1152, 104, True, False),
+    # groups of 9, 33, 13, 1 and 17 row tiles: stage 1's bands of about 8
+    # row tiles come out as [9], [9, 8, 8, 8], [7, 6], [1] and [9, 8]
+    ([2100, 8300, 3200, 200, 4300], 1152, 2048, False, True),
 ])
 def test_grouped_ffn_tile_forms(sizes, D, H, y_f32, bias):
     """Shapes on either side of the large/small tile switch, every row
