@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kSeqThreads) void route_finish_kernel(
   } else {
     const int64_t N = static_cast<int64_t>(B) * T;
     const int nblocks = static_cast<int>(ceil_div(N, kPermTokens));
-    expert_scan(part_c, nblocks, kPermTokens / 16, N / 16, E, expert_counts,
+    expert_scan<kPermTokens / 16>(part_c, nblocks, N / 16, E, expert_counts,
                 expert_offsets, block_base);
   }
 }

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     const int32_t* __restrict__ block_counts, int nblocks, int E,
     int32_t* __restrict__ counts, int64_t* __restrict__ offsets,
     int64_t* __restrict__ block_base) {
-  expert_scan(block_counts, nblocks, 1, nblocks, E, counts, offsets, block_base);
+  expert_scan<1>(block_counts, nblocks, nblocks, E, counts, offsets, block_base);
 }
 
 __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(

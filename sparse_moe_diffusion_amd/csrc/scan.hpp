@@ -18,29 +18,42 @@ namespace moe {
 constexpr int kPermTokens = 256;
 constexpr int kScanThreads = 1024;
 
-// Selections of expert e in token block b.  The counts come as gpb
-// consecutive groups per block, ngroups in all (gpb = 1: one count per
-// block).  Integer sums: the grouping does not change the result.
+// Selections of expert e in token block b.  The counts come as GPB
+// consecutive groups per block, ngroups in all (GPB = 1: one count per
+// block).  Integer sums: the grouping does not change the result.  The GPB
+// loads are independent, so they are in flight together (the counts were
+// just written by another kernel, so each load may go past the L2).
+template <int GPB>
 __device__ __forceinline__ int64_t block_count(const int32_t* __restrict__ cnt,
-                                               int64_t b, int e, int E, int gpb,
+                                               int64_t b, int e, int E,
                                                int64_t ngroups) {
-  const int64_t g0 = b * gpb;
-  const int64_t g1 = g0 + gpb < ngroups ? g0 + gpb : ngroups;
-  int64_t s = 0;
-  for (int64_t g = g0; g < g1; ++g) s += cnt[g * E + e];
+  // groups past the end re-read the last one (no branch around the loads)
+  // and count zero; a block holds at most 256 x 64 selections, so the sum
+  // fits int32
+  int32_t v[GPB];
+#pragma unroll
+  for (int u = 0; u < GPB; ++u) {
+    const int64_t g = b * GPB + u;
+    v[u] = cnt[(g < ngroups ? g : ngroups - 1) * E + e];
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < GPB; ++u)
+    if (b * GPB + u < ngroups) s += v[u];
   return s;
 }
 
-// Called by all kScanThreads threads of one workgroup.  Thread (c, e) of a
-// C x E grid (C = kScanThreads / E chunks of consecutive blocks) sums its
-// chunk's counts of expert e; a scan over the chunks in LDS gives each chunk
-// its base within the expert, a scan over the experts gives the expert
-// offsets, and each thread then writes the block bases of its chunk in block
-// order:
+// Called by all kScanThreads threads of one workgroup, with GPB count
+// groups per block.  Thread (c, e) of a C x E grid (C = kScanThreads / E
+// chunks of consecutive blocks) sums its chunk's counts of expert e; a scan
+// over the chunks in LDS gives each chunk its base within the expert, a scan
+// over the experts gives the expert offsets, and each thread then writes the
+// block bases of its chunk in block order:
 //   counts[e] (int32), offsets[e] (exclusive, offsets[E] = total),
 //   block_base[b][e] = offsets[e] + selections of e in blocks before b.
+template <int GPB>
 __device__ inline void expert_scan(const int32_t* __restrict__ cnt,
-                                   int nblocks, int gpb, int64_t ngroups,
+                                   int nblocks, int64_t ngroups,
                                    int E, int32_t* __restrict__ counts,
                                    int64_t* __restrict__ offsets,
                                    int64_t* __restrict__ block_base) {
@@ -55,7 +68,7 @@ __device__ inline void expert_scan(const int32_t* __restrict__ cnt,
   const int b1 = static_cast<int>(static_cast<int64_t>(c + 1) * nblocks / C);
   int64_t sum = 0;
   if (active)
-    for (int b = b0; b < b1; ++b) sum += block_count(cnt, b, e, E, gpb, ngroups);
+    for (int b = b0; b < b1; ++b) sum += block_count<GPB>(cnt, b, e, E, ngroups);
   part[tid] = sum;
   __syncthreads();
   // inclusive scan over chunks, per expert (Hillis-Steele)
@@ -79,7 +92,7 @@ __device__ inline void expert_scan(const int32_t* __restrict__ cnt,
   int64_t run = base + (c > 0 ? part[tid - E] : 0);
   for (int b = b0; b < b1; ++b) {
     block_base[static_cast<int64_t>(b) * E + e] = run;
-    run += block_count(cnt, b, e, E, gpb, ngroups);
+    run += block_count<GPB>(cnt, b, e, E, ngroups);
   }
 }
 
