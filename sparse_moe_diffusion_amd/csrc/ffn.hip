@@ -1415,11 +1415,13 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
 // partials of each split tile added in piece order, then the bias, stored
 // as the store epilogue does (rounded once).  A tile's BM x BN outputs are
 // cut into split_finish_wgs() chunks of 1024 (4 consecutive features per
-// thread); the workgroups walk the R tiles' chunks, and the loads of a
-// batch of pieces are issued before their additions.  Rows past the group
-// end and features past Nd are skipped.  With no split every workgroup
-// returns after reading the header.
-constexpr int kSplitFinishBatch = 8;
+// thread); the workgroups (four per CU, so about one chunk each) walk the R
+// tiles' chunks, and the loads of a batch of up to 16 pieces are issued
+// before their additions: a chunk costs the header read and one round trip
+// per batch.  Rows past the group end and features past Nd are skipped.
+// With no split every workgroup returns after reading the header.
+constexpr int kSplitFinishBatch = 16;
+constexpr int kSplitFinishPerCu = 4;
 template <int BM, int BN>
 constexpr int split_finish_wgs() { return BM * BN / (256 * 4); }
 
@@ -1849,8 +1851,8 @@ void launch_stage(const GemmParams& p, hipStream_t stream) {
   // the split last round's tiles (at most one per two workgroups)
   if constexpr (EPI == kEpiStore && NST == 3 && !BT) {
     if (p.sk_ws != nullptr && p.a_index == nullptr)
-      hipLaunchKernelGGL((splitk_tail_kernel<OUT_BF16, BM, BN>), dim3(grid),
-                         dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((splitk_tail_kernel<OUT_BF16, BM, BN>),
+                         dim3(grid * kSplitFinishPerCu), dim3(256), 0, stream, p);
   }
 }
 
