@@ -49,28 +49,34 @@ __global__ __launch_bounds__(kSeqThreads) void balance_seq_kernel(
   const int chunk = R * (kSeqThreads / R);
   for (int c0 = 0; c0 < T; c0 += chunk) {
     {
+      // the token's slots 8 at a time, all 8 loads in flight (slots past
+      // Kmax and tokens past T re-read a valid slot and are not counted)
       const int t = c0 + static_cast<int>(threadIdx.x);
+      const bool in = threadIdx.x < chunk && t < T;
+      const int32_t* s = idx + (t0 + (t < T ? t : T - 1)) * Kmax;
       uint64_t m = 0;
-      if (threadIdx.x < chunk && t < T) {
-        const int32_t* s = idx + (t0 + t) * Kmax;
-        for (int k = 0; k < Kmax; ++k) {
-          const int v = s[k];
-          if (v >= 0 && v < 64) m |= 1ull << v;
-        }
+      for (int k0 = 0; k0 < Kmax; k0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s[k0 + u < Kmax ? k0 + u : Kmax - 1];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (k0 + u < Kmax && v[u] >= 0 && v[u] < 64) m |= 1ull << v[u];
       }
-      tmask[threadIdx.x] = m;
+      tmask[threadIdx.x] = in ? m : 0ull;
     }
     __syncthreads();
     if (r < R) {
       const int c1 = min(T, c0 + chunk);
-      // tokens c0 + r, c0 + r + R, ...; four loads in flight
+      // tokens c0 + r, c0 + r + R, ...; eight loads in flight, added in
+      // token order
       int t = c0 + r;
-      for (; t + 3 * R < c1; t += 4 * R) {
-        float q[4];
+      for (; t + 7 * R < c1; t += 8 * R) {
+        float q[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) q[u] = probs[(t0 + t + u * R) * E + e];
+        for (int u = 0; u < 8; ++u) q[u] = probs[(t0 + t + u * R) * E + e];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           p += q[u];
           c += static_cast<int32_t>((tmask[t + u * R - c0] >> e) & 1ull);
         }

@@ -24,8 +24,9 @@
 //    of 8 bits; each pass a histogram over 256 workgroups and a one-
 //    workgroup digit choice), then the flat index of the last kept entry
 //    among keys equal to it.
-//  * race_emit_kernel: one thread per token writes its kept experts in
-//    ascending order.
+//  * race_emit_kernel: one thread per token finds its kept experts in
+//    ascending order, staged in LDS and written out by the block with
+//    consecutive threads on consecutive slots.
 #include <atomic>
 
 #include "common.hpp"
@@ -637,6 +638,7 @@ __device__ __forceinline__ uint32_t race_key(float p) {
 // atomic instead of 64 colliding atomics.
 constexpr int kRaceBlocks = 256;
 constexpr int kRaceHistThreads = 256;
+constexpr int kRaceHistLoads = 4;
 static_assert(kRaceBlocks % 64 == 0, "whole batches of 16 per quarter");
 
 struct RaceState {
@@ -659,24 +661,36 @@ __global__ __launch_bounds__(kRaceHistThreads) void race_hist_kernel(
   const int64_t per = (total + kRaceBlocks - 1) / kRaceBlocks;
   const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per;
   const int64_t b1 = min(total, b0 + per);
-  for (int64_t i0 = b0; i0 < b1; i0 += kRaceHistThreads) {
-    const int64_t i = i0 + tid;
-    const uint32_t k = i < b1 ? race_key(probs[i]) : 0u;
-    bool live = i < b1 && (k & mask) == prefix;
-    const uint32_t d = (k >> shift) & 255u;
-    if (pass == 0) {
-      // one round per distinct digit among the wave's live lanes
-      uint64_t left = __ballot(live);
-      while (left != 0) {
-        const int leader = __builtin_ctzll(left);
-        const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
-        const uint64_t same = __ballot(live && d == dl);
-        if (lane == leader) atomicAdd(&h[dl], static_cast<uint32_t>(__popcll(same)));
-        if (d == dl) live = false;
-        left = __ballot(live);
+  // kRaceHistLoads keys per thread in flight (past the slice they re-read
+  // its last key and are not counted)
+  for (int64_t i0 = b0; i0 < b1; i0 += kRaceHistThreads * kRaceHistLoads) {
+    float pv[kRaceHistLoads];
+#pragma unroll
+    for (int u = 0; u < kRaceHistLoads; ++u) {
+      const int64_t i = i0 + u * kRaceHistThreads + tid;
+      pv[u] = probs[i < b1 ? i : b1 - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+#pragma unroll
+    for (int u = 0; u < kRaceHistLoads; ++u) {
+      const int64_t i = i0 + u * kRaceHistThreads + tid;
+      const uint32_t k = race_key(pv[u]);
+      bool live = i < b1 && (k & mask) == prefix;
+      const uint32_t d = (k >> shift) & 255u;
+      if (pass == 0) {
+        // one round per distinct digit among the wave's live lanes
+        uint64_t left = __ballot(live);
+        while (left != 0) {
+          const int leader = __builtin_ctzll(left);
+          const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+          const uint64_t same = __ballot(live && d == dl);
+          if (lane == leader) atomicAdd(&h[dl], static_cast<uint32_t>(__popcll(same)));
+          if (d == dl) live = false;
+          left = __ballot(live);
+        }
+      } else if (live) {
+        atomicAdd(&h[d], 1u);
       }
-    } else if (live) {
-      atomicAdd(&h[d], 1u);
     }
   }
   __syncthreads();
@@ -785,28 +799,61 @@ __global__ __launch_bounds__(kRaceThreads) void race_cut_kernel(
   }
 }
 
+// A block of tokens (256 when E <= 16, else 64: at most 4096 slots) finds
+// each token's kept experts from its probabilities (loaded 16 at a time, all
+// in flight) into LDS rows padded to E + 1 entries (no bank conflicts
+// between consecutive tokens), then copies the block's [tokens][E] slots
+// out with consecutive threads on consecutive slots.
+constexpr int kEmitSlots = 4096;
+__host__ __device__ constexpr int emit_tokens(int E) { return E <= 16 ? 256 : 64; }
+
 __global__ __launch_bounds__(256) void race_emit_kernel(
     const float* __restrict__ probs, int64_t N, int E,
     const uint32_t* __restrict__ sel, int32_t* __restrict__ idx,
     float* __restrict__ w) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= N) return;
-  const uint32_t tau = sel[0];
-  const int64_t cut = sel[1];
-  int n = 0;
-  for (int e = 0; e < E; ++e) {
-    const float p = probs[t * E + e];
-    const uint32_t k = race_key(p);
-    const int64_t flat = t * E + e;
-    if (k > tau || (k == tau && flat <= cut)) {
-      idx[t * E + n] = e;
-      w[t * E + n] = p;
-      ++n;
+  __shared__ int32_t s_i[kEmitSlots + 256];
+  __shared__ float s_w[kEmitSlots + 256];
+  const int tid = threadIdx.x, TB = blockDim.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int ntok = static_cast<int>(min<int64_t>(TB, N - t0));
+  const int pitch = E + 1;
+  if (tid < ntok) {
+    const int64_t t = t0 + tid;
+    const uint32_t tau = sel[0];
+    const int64_t cut = sel[1];
+    int32_t* const ri = s_i + tid * pitch;
+    float* const rw = s_w + tid * pitch;
+    int n = 0;
+    // past E the loads re-read the last probability and are not used
+    for (int e0 = 0; e0 < E; e0 += 16) {
+      float pv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) pv[u] = probs[t * E + (e0 + u < E ? e0 + u : E - 1)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + u;
+        if (e >= E) break;
+        const uint32_t k = race_key(pv[u]);
+        const int64_t flat = t * E + e;
+        if (k > tau || (k == tau && flat <= cut)) {
+          ri[n] = e;
+          rw[n] = pv[u];
+          ++n;
+        }
+      }
+    }
+    for (; n < E; ++n) {
+      ri[n] = -1;
+      rw[n] = 0.0f;
     }
   }
-  for (; n < E; ++n) {
-    idx[t * E + n] = -1;
-    w[t * E + n] = 0.0f;
+  __syncthreads();
+  const int nslots = ntok * E;
+  for (int i = tid; i < nslots; i += TB) {
+    const int tk = i / E;
+    const int j = tk * pitch + (i - tk * E);
+    idx[t0 * E + i] = s_i[j];
+    w[t0 * E + i] = s_w[j];
   }
 }
 
@@ -900,8 +947,12 @@ hipError_t launch_race(const float* probs, int64_t N, int E, int K,
                      probs, total, st + 4, sel);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  const int tb = emit_tokens(E);
+  static_assert(emit_tokens(16) * 17 <= kEmitSlots + 256 &&
+                    emit_tokens(kMaxExperts) * (kMaxExperts + 1) <= kEmitSlots + 256,
+                "a block's padded slot rows fit the LDS rows");
   hipLaunchKernelGGL(race_emit_kernel,
-                     dim3(static_cast<unsigned>(ceil_div(N, 256))), dim3(256),
+                     dim3(static_cast<unsigned>(ceil_div(N, tb))), dim3(tb),
                      0, stream, probs, N, E, sel, idx, w);
   return hipGetLastError();
 }

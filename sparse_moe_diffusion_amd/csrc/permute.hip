@@ -8,14 +8,17 @@
 //
 // Three launches (a fourth with x_perm), no host synchronisation:
 //  1. permute_count_kernel: workgroup b covers 256 consecutive tokens (one
-//     per thread); each token's experts form a bit mask, and one wave ballot
-//     per expert counts the wave's selections.  Writes block_counts[b][e].
+//     per thread); the block's slots are read into LDS together, each
+//     token's experts form a bit mask, and one wave ballot per expert counts
+//     the wave's selections.  Writes block_counts[b][e].
 //  2. permute_scan_kernel: one 1024-thread workgroup scans the block counts
 //     (chunks of blocks x experts, then a scan over chunks and experts):
 //     expert counts, exclusive offsets and block bases.
-//  3. permute_scatter_kernel: repeats the ballots (one per expert), so a
-//     selection's row is block base + earlier waves' count + set lanes below
-//     it; writes row_token and the block's slot_row (coalesced, from LDS).
+//  3. permute_scatter_kernel: repeats the slot read and the ballots (one per
+//     expert, kept in LDS), so each slot's row is block base (read once into
+//     LDS) + earlier waves' count + set lanes below it in its expert's
+//     ballot; writes row_token and the block's slot_row (coalesced, from
+//     LDS).
 //  4. permute_copy_kernel (only with x_perm): one thread per 16-byte chunk
 //     of every token row reads the chunk once and writes it to the token's
 //     selected rows; consecutive threads cover consecutive chunks, so both
@@ -34,12 +37,41 @@ namespace {
 
 constexpr int kPermWaves = kPermTokens / kWave;
 
-__device__ __forceinline__ uint64_t token_mask(const int32_t* __restrict__ idx,
-                                               int64_t t, int Kmax, int E) {
+// The block's slots, idx[t0 .. t0 + ntok) (ntok Kmax values, contiguous),
+// into s_rows: consecutive threads read consecutive values, 8 loads in
+// flight per thread (past the end they re-read the last value and are not
+// stored, so no branch separates the loads).  Then each thread's own Kmax
+// slots are sanitised in place (outside [0, E), or a token past N: -1) and
+// their experts returned as a bit mask.  Called by every thread of the
+// block; ends with the slots in place for this thread only.
+constexpr int kSlotLoads = 8;
+__device__ __forceinline__ uint64_t block_slots(const int32_t* __restrict__ idx,
+                                                int64_t t0, int ntok, int Kmax,
+                                                int E, int32_t* s_rows) {
+  const int n = ntok * Kmax;
+  const int32_t* const src = idx + t0 * Kmax;
+  for (int i0 = 0; i0 < n; i0 += kPermTokens * kSlotLoads) {
+    int32_t v[kSlotLoads];
+#pragma unroll
+    for (int u = 0; u < kSlotLoads; ++u) {
+      const int i = i0 + u * kPermTokens + static_cast<int>(threadIdx.x);
+      v[u] = src[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotLoads; ++u) {
+      const int i = i0 + u * kPermTokens + static_cast<int>(threadIdx.x);
+      if (i < n) s_rows[i] = v[u];
+    }
+  }
+  __syncthreads();
+  int32_t* const my = s_rows + threadIdx.x * Kmax;
+  const bool valid = static_cast<int>(threadIdx.x) < ntok;
   uint64_t m = 0;
   for (int k = 0; k < Kmax; ++k) {
-    const int e = idx[t * Kmax + k];
-    if (e >= 0 && e < E) m |= 1ull << e;
+    const int e = valid ? my[k] : -1;
+    const bool ok = e >= 0 && e < E;   // contents outside [0, E): empty
+    my[k] = ok ? e : -1;
+    if (ok) m |= 1ull << e;
   }
   return m;
 }
@@ -47,11 +79,13 @@ __device__ __forceinline__ uint64_t token_mask(const int32_t* __restrict__ idx,
 __global__ __launch_bounds__(kPermTokens) void permute_count_kernel(
     const int32_t* __restrict__ idx, int64_t N, int E, int Kmax,
     int32_t* __restrict__ block_counts) {
+  extern __shared__ int32_t s_rows[];  // [kPermTokens][Kmax]
   __shared__ int32_t wc[kPermWaves][kMaxExperts];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermTokens + threadIdx.x;
-  const uint64_t m = (t < N) ? token_mask(idx, t, Kmax, E) : 0ull;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermTokens;
+  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
+  const uint64_t m = block_slots(idx, t0, ntok, Kmax, E, s_rows);
   for (int e = 0; e < E; ++e) {
     const uint64_t b = __ballot((m >> e) & 1ull);
     if (lane == 0) wc[wave][e] = __popcll(b);
@@ -79,43 +113,45 @@ __global__ __launch_bounds__(kPermTokens) void permute_scatter_kernel(
     int32_t* __restrict__ row_token) {
   extern __shared__ int32_t s_rows[];  // [kPermTokens][Kmax]
   __shared__ int32_t wc[kPermWaves][kMaxExperts];
+  __shared__ uint64_t wb[kPermWaves][kMaxExperts];
+  __shared__ int64_t sbase[kMaxExperts];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermTokens;
   const int64_t t = t0 + threadIdx.x;
-  const bool valid = t < N;
-  const uint64_t m = valid ? token_mask(idx, t, Kmax, E) : 0ull;
+  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
+  // the block's first row of each expert, read once (the expert loop below
+  // would otherwise wait on one global load per expert)
+  if (static_cast<int>(threadIdx.x) < E)
+    sbase[threadIdx.x] = block_base[static_cast<int64_t>(blockIdx.x) * E + threadIdx.x];
+  // the token's slots, sanitised, in s_rows (see block_slots; its barrier
+  // also orders sbase)
+  const uint64_t m = block_slots(idx, t0, ntok, Kmax, E, s_rows);
+  // One ballot per expert (taken by the whole wave), kept with its count.
   for (int e = 0; e < E; ++e) {
     const uint64_t b = __ballot((m >> e) & 1ull);
-    if (lane == 0) wc[wave][e] = __popcll(b);
-  }
-  __syncthreads();
-  const int64_t* base = block_base + static_cast<int64_t>(blockIdx.x) * E;
-  // The token's slots, then one ballot per expert (taken by the whole
-  // wave): a lane holding expert ee finds its rank and writes it into the
-  // slot that names ee.  Slots naming no valid expert keep -1.
-  int32_t* const my = s_rows + threadIdx.x * Kmax;
-  for (int k = 0; k < Kmax; ++k) {
-    const int v = valid ? idx[t * Kmax + k] : -1;
-    my[k] = (v >= 0 && v < E) ? v : -1;   // contents outside [0, E): empty
-  }
-  for (int ee = 0; ee < E; ++ee) {
-    const bool has = (m >> ee) & 1ull;
-    const uint64_t b = __ballot(has);
-    if (has) {
-      int64_t r = base[ee] + lanes_below(b);
-      for (int w = 0; w < wave; ++w) r += wc[w][ee];
-      const int32_t row = (r < A) ? static_cast<int32_t>(r) : -1;
-      for (int k = 0; k < Kmax; ++k)
-        if (my[k] == ee) my[k] = -2 - row;   // marked: no longer an expert
-      if (row >= 0) row_token[row] = static_cast<int32_t>(t);
+    if (lane == 0) {
+      wc[wave][e] = __popcll(b);
+      wb[wave][e] = b;
     }
   }
-  // Marked slots hold -2 - row; the rest (empty or invalid) become -1.
-  for (int k = 0; k < Kmax; ++k) my[k] = my[k] <= -2 ? -2 - my[k] : -1;
+  __syncthreads();
+  // Each slot naming expert e takes row block base + earlier waves' count +
+  // set lanes below it in the wave's ballot of e (a token naming e twice
+  // gets the same row in both slots).  Slots naming no valid expert, and
+  // rows past A, keep -1.
+  int32_t* const my = s_rows + threadIdx.x * Kmax;
+  for (int k = 0; k < Kmax; ++k) {
+    const int e = my[k];
+    if (e < 0) continue;
+    int64_t r = sbase[e] + lanes_below(wb[wave][e]);
+    for (int w = 0; w < wave; ++w) r += wc[w][e];
+    const int32_t row = (r < A) ? static_cast<int32_t>(r) : -1;
+    my[k] = row;
+    if (row >= 0) row_token[row] = static_cast<int32_t>(t);
+  }
   __syncthreads();
   // slot_row of the block's tokens, coalesced.
-  const int ntok = static_cast<int>(min<int64_t>(kPermTokens, N - t0));
   for (int i = threadIdx.x; i < ntok * Kmax; i += kPermTokens)
     slot_row[t0 * Kmax + i] = s_rows[i];
 }
@@ -180,19 +216,32 @@ hipError_t permute_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+
+// Dynamic LDS of the count and scatter kernels: the block's slots.  Past
+// 32 KB (Kmax > 32) the kernel must opt in.
+size_t slots_lds(int Kmax) {
+  return static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
+}
+
+hipError_t opt_in_lds(const void* kernel, size_t shmem) {
+  if (shmem <= 32768) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(shmem));
+}
+
+}  // namespace
+
 hipError_t launch_permute_scatter(const int32_t* idx, int64_t N, int E,
                                   int Kmax, int64_t A, const int64_t* block_base,
                                   int32_t* slot_row, int32_t* row_token,
                                   hipStream_t stream) {
   const int64_t nb = ceil_div(N, kPermTokens);
   if (nb == 0) return hipSuccess;
-  const size_t shmem = static_cast<size_t>(kPermTokens) * Kmax * sizeof(int32_t);
-  if (shmem > 32768) {
-    const hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&permute_scatter_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shmem));
-    if (err != hipSuccess) return err;
-  }
+  const size_t shmem = slots_lds(Kmax);
+  const hipError_t err = opt_in_lds(
+      reinterpret_cast<const void*>(&permute_scatter_kernel), shmem);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(nb)),
                      dim3(kPermTokens), shmem, stream, idx, N, E, Kmax, A,
                      block_base, slot_row, row_token);
@@ -210,10 +259,14 @@ hipError_t launch_permute(const void* x, bool bf16, const int32_t* idx,
   int64_t* block_base =
       reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + a);
   if (nb > 0) {
+    const size_t shmem = slots_lds(Kmax);
+    hipError_t err = opt_in_lds(
+        reinterpret_cast<const void*>(&permute_count_kernel), shmem);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_count_kernel, dim3(static_cast<unsigned>(nb)),
-                       dim3(kPermTokens), 0, stream, idx, N, E, Kmax,
+                       dim3(kPermTokens), shmem, stream, idx, N, E, Kmax,
                        block_counts);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
