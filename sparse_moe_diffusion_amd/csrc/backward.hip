@@ -16,8 +16,9 @@
 //  * combine_bwd_kernel: one wave per token; the routed rows' output
 //    gradients w * dy and the slot-weight gradients <dy, y_row>.
 //  * gate_bwd_token_kernel, gate_bwd_wgrad_kernel, gate_bwd_reduce_kernel,
-//    gate_bwd_dx_kernel: dP -> dlogits per token; dW_g and dbias partials
-//    per token chunk and their fixed-order sum; dx assembled per token.
+//    gate_bwd_dx_tok_kernel (E <= 8) / gate_bwd_dx_kernel: dP -> dlogits
+//    per token; dW_g and dbias partials per token chunk and their
+//    fixed-order sum; dx assembled per token.
 #include <algorithm>
 
 #include "common.hpp"
@@ -263,8 +264,11 @@ constexpr int kGbTokens = 64;    // tokens per workgroup of the dW_g pass
 constexpr int kGbBatch = 8;      // x rows loaded ahead in that pass
 
 // dx[t] = sum_k dx_rows[slot_row[t][k]] + dx_shared[t] + sum_i dl[t][i] W_g[i]
-// in fp32, rounded once.  One thread per 8 features of a token; slot rows
-// in groups of 4, loaded before they are added (in slot order).
+// in fp32, rounded once, added in that order.  One thread per 8 features of
+// a token.  No load sits behind a branch, so they go out together: the
+// shared row and the first 8 experts' dl and W_g before the slot rows, the
+// slot rows in groups of 4 (an empty slot, or a missing operand, reads the
+// token's own dx chunk, a valid address, and is not added).
 template <bool OB>
 __global__ __launch_bounds__(256) void gate_bwd_dx_kernel(
     const float* __restrict__ wg, const float* __restrict__ dl, int64_t N,
@@ -277,6 +281,20 @@ __global__ __launch_bounds__(256) void gate_bwd_dx_kernel(
   const uint32_t tq = i / nch;
   const int64_t t = tq;
   const int c = static_cast<int>(i - tq * nch);
+  // the shared experts' row and the first 8 experts, loaded first
+  float sh[8];
+  ld8<OB>(dx_shared != nullptr ? dx_shared : dx, t, D, c, sh);
+  float d[8];
+  float4 wa[8], wb[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = u < E ? u : E - 1;
+    d[u] = dl[t * E + e];
+    const float4* wp =
+        reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * D) + 2 * c;
+    wa[u] = wp[0];
+    wb[u] = wp[1];
+  }
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.0f;
@@ -285,36 +303,123 @@ __global__ __launch_bounds__(256) void gate_bwd_dx_kernel(
       int32_t r[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        r[q] = (k0 + q < Kmax) ? slot_row[t * Kmax + k0 + q] : -1;
+        r[q] = slot_row[t * Kmax + (k0 + q < Kmax ? k0 + q : Kmax - 1)];
       float v[4][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (r[q] >= 0) ld8<OB>(dx_rows, r[q], D, c, v[q]);
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = k0 + q < Kmax && r[q] >= 0;
+        ld8<OB>(ok ? dx_rows : static_cast<const void*>(dx), ok ? r[q] : t, D, c,
+                v[q]);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (r[q] >= 0) {
+        if (k0 + q < Kmax && r[q] >= 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) o[j] += v[q][j];
         }
     }
   }
   if (dx_shared != nullptr) {
-    float v[8];
-    ld8<OB>(dx_shared, t, D, c, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] += v[j];
+    for (int j = 0; j < 8; ++j) o[j] += sh[j];
   }
-  for (int e = 0; e < E; ++e) {
-    const float d = dl[t * E + e];
-    const float4* wp =
-        reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * D) + 2 * c;
-    const float4 a = wp[0], b = wp[1];
-    o[0] = fmaf(d, a.x, o[0]); o[1] = fmaf(d, a.y, o[1]);
-    o[2] = fmaf(d, a.z, o[2]); o[3] = fmaf(d, a.w, o[3]);
-    o[4] = fmaf(d, b.x, o[4]); o[5] = fmaf(d, b.y, o[5]);
-    o[6] = fmaf(d, b.z, o[6]); o[7] = fmaf(d, b.w, o[7]);
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    if (e0 > 0) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u < E ? e0 + u : E - 1;
+        d[u] = dl[t * E + e];
+        const float4* wp =
+            reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * D) + 2 * c;
+        wa[u] = wp[0];
+        wb[u] = wp[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (e0 + u >= E) break;
+      const float4 a = wa[u], b = wb[u];
+      o[0] = fmaf(d[u], a.x, o[0]); o[1] = fmaf(d[u], a.y, o[1]);
+      o[2] = fmaf(d[u], a.z, o[2]); o[3] = fmaf(d[u], a.w, o[3]);
+      o[4] = fmaf(d[u], b.x, o[4]); o[5] = fmaf(d[u], b.y, o[5]);
+      o[6] = fmaf(d[u], b.z, o[6]); o[7] = fmaf(d[u], b.w, o[7]);
+    }
   }
   st8<OB>(dx, t, D, c, o);
+}
+
+// The same for E <= EB (8): a thread owns one 8-feature chunk of kDxTokens
+// consecutive tokens and keeps that chunk of W_g (EB x 8 floats) in
+// registers, so W_g is read once per kDxTokens tokens instead of once per
+// token (at D = 1152, E = 8 that is 37 KB per token).  Same order of
+// additions, same bits.
+constexpr int kDxTokens = 8;
+template <bool OB, int EB>
+__global__ __launch_bounds__(256) void gate_bwd_dx_tok_kernel(
+    const float* __restrict__ wg, const float* __restrict__ dl, int64_t N,
+    int D, int E, int Kmax, const void* __restrict__ dx_rows,
+    const int32_t* __restrict__ slot_row, const void* __restrict__ dx_shared,
+    void* __restrict__ dx) {
+  const uint32_t nch = static_cast<uint32_t>(D / 8);
+  const uint32_t ng = static_cast<uint32_t>((N + kDxTokens - 1) / kDxTokens);
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= ng * nch) return;
+  const uint32_t tg = i / nch;
+  const int c = static_cast<int>(i - tg * nch);
+  float4 wa[EB], wb[EB];
+#pragma unroll
+  for (int u = 0; u < EB; ++u) {
+    const float4* wp = reinterpret_cast<const float4*>(
+                           wg + static_cast<int64_t>(u < E ? u : E - 1) * D) + 2 * c;
+    wa[u] = wp[0];
+    wb[u] = wp[1];
+  }
+  const int64_t t1 = min<int64_t>(N, (static_cast<int64_t>(tg) + 1) * kDxTokens);
+  for (int64_t t = static_cast<int64_t>(tg) * kDxTokens; t < t1; ++t) {
+    float sh[8];
+    ld8<OB>(dx_shared != nullptr ? dx_shared : dx, t, D, c, sh);
+    float d[EB];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) d[u] = dl[t * E + (u < E ? u : E - 1)];
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = 0.0f;
+    if (slot_row != nullptr) {
+      for (int k0 = 0; k0 < Kmax; k0 += 4) {
+        int32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          r[q] = slot_row[t * Kmax + (k0 + q < Kmax ? k0 + q : Kmax - 1)];
+        float v[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = k0 + q < Kmax && r[q] >= 0;
+          ld8<OB>(ok ? dx_rows : static_cast<const void*>(dx), ok ? r[q] : t, D,
+                  c, v[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k0 + q < Kmax && r[q] >= 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] += v[q][j];
+          }
+      }
+    }
+    if (dx_shared != nullptr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] += sh[j];
+    }
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      if (u >= E) break;
+      const float4 a = wa[u], b = wb[u];
+      o[0] = fmaf(d[u], a.x, o[0]); o[1] = fmaf(d[u], a.y, o[1]);
+      o[2] = fmaf(d[u], a.z, o[2]); o[3] = fmaf(d[u], a.w, o[3]);
+      o[4] = fmaf(d[u], b.x, o[4]); o[5] = fmaf(d[u], b.y, o[5]);
+      o[6] = fmaf(d[u], b.z, o[6]); o[7] = fmaf(d[u], b.w, o[7]);
+    }
+    st8<OB>(dx, t, D, c, o);
+  }
 }
 
 // Workgroup = kGbTokens tokens; their dl rows are staged in LDS.  Thread =
@@ -345,10 +450,12 @@ __global__ __launch_bounds__(256) void gate_bwd_wgrad_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
       for (int tb = 0; tb < nt; tb += kGbBatch) {
+        // every row of the batch in flight (past the chunk: its last token's
+        // row again, not used)
         float xv[kGbBatch][8];
 #pragma unroll
         for (int b = 0; b < kGbBatch; ++b)
-          if (tb + b < nt) ld8<XB>(x, t0 + tb + b, D, c, xv[b]);
+          ld8<XB>(x, t0 + (tb + b < nt ? tb + b : nt - 1), D, c, xv[b]);
 #pragma unroll
         for (int b = 0; b < kGbBatch; ++b) {
           if (tb + b >= nt) break;
@@ -533,15 +640,22 @@ hipError_t launch_gate_backward(const void* x, bool x_bf16, const float* wg,
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (dx != nullptr) {
+      // E <= 8: W_g's chunk in registers over kDxTokens tokens per thread
+      // (16 experts' chunks would be kept in scratch memory)
+      const dim3 gt(static_cast<unsigned>(ceil_div(ceil_div(N, kDxTokens) * nch, 256)));
       const dim3 g2(static_cast<unsigned>(ceil_div(N * nch, 256)));
-      if (dx_bf16)
-        hipLaunchKernelGGL(gate_bwd_dx_kernel<true>, g2, dim3(256), 0, stream,
-                           wg, dl, N, D, E, Kmax, dx_rows, slot_row, dx_shared,
-                           dx);
+#define MOE_DX(KERNEL, GRID)                                                 \
+      hipLaunchKernelGGL(KERNEL, GRID, dim3(256), 0, stream, wg, dl, N, D, E, \
+                         Kmax, dx_rows, slot_row, dx_shared, dx)
+      if (E <= 8 && dx_bf16)
+        MOE_DX((gate_bwd_dx_tok_kernel<true, 8>), gt);
+      else if (E <= 8)
+        MOE_DX((gate_bwd_dx_tok_kernel<false, 8>), gt);
+      else if (dx_bf16)
+        MOE_DX(gate_bwd_dx_kernel<true>, g2);
       else
-        hipLaunchKernelGGL(gate_bwd_dx_kernel<false>, g2, dim3(256), 0, stream,
-                           wg, dl, N, D, E, Kmax, dx_rows, slot_row, dx_shared,
-                           dx);
+        MOE_DX(gate_bwd_dx_kernel<false>, g2);
+#undef MOE_DX
       err = hipGetLastError();
       if (err != hipSuccess) return err;
     }
