@@ -205,6 +205,35 @@ def test_permute(N, D, E, Kmax, K, dtype):
     assert np.array_equal(rt2, rt_o) and np.array_equal(sr2, sr_o)
 
 
+@pytest.mark.parametrize("E,Kmax,K", [(8, 2, 2), (16, 16, 2)])
+def test_permute_out_of_range_slots_are_empty(E, Kmax, K):
+    """Slot contents outside [-1, E) are treated as empty (the header's
+    contract): the result is the oracle's on those slots set to -1, and the
+    routed rows past the valid selections are not written."""
+    rng = np.random.default_rng(E + Kmax)
+    N, D = 700, 64
+    if Kmax == K:
+        idx = np.stack([rng.choice(E, size=K, replace=False) for _ in range(N)])
+    else:
+        idx = np.full((N, E), -1)
+        for t in range(N):
+            sel = np.sort(rng.choice(E, size=K, replace=False))
+            idx[t, :K] = sel
+    bad = rng.random(idx.shape) < 0.15
+    junk = rng.choice([E, E + 3, 1 << 20, -2, -9], size=idx.shape)
+    idx_in = np.where(bad & (idx >= 0), junk, idx)
+    clean = np.where((idx_in >= 0) & (idx_in < E), idx_in, -1)
+    x = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((N, D)).astype(np.float32)))
+    counts, offs, rt, sr, xp = _run_permute(x, idx_in, E, K, "bf16")
+    c_o, o_o, rt_o, sr_o = oracle.permute(clean.astype(np.int32), E)
+    n = int(o_o[-1])
+    assert n < K * N
+    assert np.array_equal(counts, c_o) and np.array_equal(offs, o_o)
+    assert np.array_equal(sr, sr_o)
+    assert np.array_equal(rt[:n], rt_o) and np.all(rt[n:] == -7)
+    assert np.array_equal(xp[:n], x[rt_o])
+
+
 def _run_ffn(xs, offsets, w1, w2, b1, b2, dtype, row_index=None, y_f32=False):
     _, ops = _ops()
     G, H, D = w1.shape
