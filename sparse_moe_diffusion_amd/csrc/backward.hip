@@ -374,8 +374,17 @@ __global__ __launch_bounds__(256) void gate_bwd_dx_tok_kernel(
     wa[u] = wp[0];
     wb[u] = wp[1];
   }
-  const int64_t t1 = min<int64_t>(N, (static_cast<int64_t>(tg) + 1) * kDxTokens);
-  for (int64_t t = static_cast<int64_t>(tg) * kDxTokens; t < t1; ++t) {
+  const int64_t tb = static_cast<int64_t>(tg) * kDxTokens;
+  const int64_t t1 = min<int64_t>(N, tb + kDxTokens);
+  // The first four slot rows of the next token are read while this token's
+  // rows are in flight, so a token costs one round trip to memory, not two
+  // (an index, then the rows it names).
+  int32_t rn[4];
+  if (slot_row != nullptr) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rn[q] = slot_row[tb * Kmax + (q < Kmax ? q : Kmax - 1)];
+  }
+  for (int64_t t = tb; t < t1; ++t) {
     float sh[8];
     ld8<OB>(dx_shared != nullptr ? dx_shared : dx, t, D, c, sh);
     float d[EB];
@@ -385,7 +394,28 @@ __global__ __launch_bounds__(256) void gate_bwd_dx_tok_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.0f;
     if (slot_row != nullptr) {
-      for (int k0 = 0; k0 < Kmax; k0 += 4) {
+      {
+        int32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = rn[q];
+        float v[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = q < Kmax && r[q] >= 0;
+          ld8<OB>(ok ? dx_rows : static_cast<const void*>(dx), ok ? r[q] : t, D, c,
+                  v[q]);
+        }
+        const int64_t tn = t + 1 < t1 ? t + 1 : t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rn[q] = slot_row[tn * Kmax + (q < Kmax ? q : Kmax - 1)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < Kmax && r[q] >= 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] += v[q][j];
+          }
+      }
+      for (int k0 = 4; k0 < Kmax; k0 += 4) {
         int32_t r[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)

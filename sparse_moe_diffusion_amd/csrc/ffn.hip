@@ -470,6 +470,14 @@ __device__ __forceinline__ void dma_untracked(__amdgpu_buffer_rsrc_t r,
 // v_readfirstlane, and a VMEM instruction needs 5 wait states after a VALU
 // write of an SGPR it reads (the M0 write needs 1).  The M0 write and
 // s_nop 4 give 6.
+// M0 is a reserved register: the compiler neither saves it around the block
+// nor learns that the block changed it (hipcc warns of the clobber).  That is
+// safe only because the two forms that use this transfer (K-grouped, and
+// k-major weights) contain no compiler-built LDS transfer, the only M0
+// reader in these kernels: their gathered-row fetch is compiled out, and
+// they take no prefetch and no combine table (static checks in the
+// kernel), so no value of the compiler's own is live in M0 across the
+// block.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma16_raw(const char* base, uint32_t bytes,
                                           uint32_t dst, uint32_t off) {
@@ -622,7 +630,9 @@ __global__ __launch_bounds__(64 * WT * WF, 1) void gemm_bf16_kernel(GemmParams p
   // (tile count & 1) of sidx: the next tile's are transferred there before
   // this tile's first k stage, so a tile starts without waiting on global
   // memory.
-  const bool gather = p.a_index != nullptr;
+  // (never in the K-grouped and k-major forms: their transfers write M0
+  // themselves, see dma16_raw)
+  const bool gather = !KG && !BT && p.a_index != nullptr;
 #define MOE_FETCH_ROWS(L, B, LANE)                                           \
   do {                                                                       \
     if (wave < BM / 64) {                                                    \
