@@ -123,10 +123,13 @@ def test_grouped_ffn_backward(sizes, D, H, gather, saved):
     assert_close(to_np(dw2), ref_dw2, "bf16", "dW2")
 
 
-@pytest.mark.parametrize("B,T,D,E,K,mode,with_rows", [
-    (2, 64, 128, 8, 2, "sequence", True), (3, 100, 64, 16, 2, "global", False),
-    (1, 37, 1152, 5, 3, "sequence", True)])
-def test_gate_backward(B, T, D, E, K, mode, with_rows):
+@pytest.mark.parametrize("B,T,D,E,K,mode,with_rows,empty", [
+    (2, 64, 128, 8, 2, "sequence", True, 0.0), (3, 100, 64, 16, 2, "global", False, 0.0),
+    (1, 37, 1152, 5, 3, "sequence", True, 0.0),
+    # E <= 8 with more than four slots per token (the dx pass's second slot
+    # batch) and empty slots (slot row -1) in both batches
+    (2, 45, 256, 8, 6, "sequence", True, 0.3), (1, 70, 128, 8, 2, "global", True, 0.5)])
+def test_gate_backward(B, T, D, E, K, mode, with_rows, empty):
     _lib, ops = _ops()
     rng = np.random.default_rng(B * T + E)
     N = B * T
@@ -138,6 +141,7 @@ def test_gate_backward(B, T, D, E, K, mode, with_rows):
     counts = oracle.selection_indicator(idx, E).reshape(B, T, E).sum(1).astype(np.int32)
     A = N * K
     sr = rng.permutation(A).reshape(N, K).astype(np.int32)
+    sr[rng.random((N, K)) < empty] = -1
     dxr = q(rng.standard_normal((A, D)))
     dxs = q(rng.standard_normal((N, D)))
     dloss, alpha = 2.5, 0.01
@@ -160,7 +164,8 @@ def test_gate_backward(B, T, D, E, K, mode, with_rows):
     ref_dx = dl @ wg.astype(np.float64)
     if with_rows:
         for k in range(K):
-            ref_dx += dxr[sr[:, k]]
+            kept = sr[:, k] >= 0
+            ref_dx[kept] += dxr[sr[kept, k]]
         ref_dx += dxs
     assert_close(to_np(dx), ref_dx, "bf16", "dx")
     assert_close(to_np(dwg), dl.T @ x.astype(np.float64), "f32", "dW_g")
